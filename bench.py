@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged KV cache on one MI355X.
+
+A step is one decode step of one attention layer over a batch of sequences:
+the C++ allocator appends one token per sequence (copy-on-write where blocks are
+shared), the step's slot mapping / block tables go to the device, then
+block_copy -> kv_append -> paged_attention_decode (+ partition merge) run on one
+stream.  Inputs (cache contents, per-step q and new K/V) are resident in HBM
+before the timed region starts.
+
+Default workload: bf16 MHA decode, 64 sequences, context lengths U[128, 2048],
+32 query / 32 KV heads, head_dim 128, 16-token blocks in a shuffled pool.
+The first timed step attends over exactly those lengths; each later step one
+token more.
+
+Prints one JSON line: value = algorithmic HBM bytes of the whole step / step
+time (GB/s), plus seq-tokens/s per layer, the main attention kernel's roofline
+(bytes / its HIP-event-timed duration against 8 TB/s) and the fp64 oracle timed
+on the host as a CPU baseline.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "decode attention achieved HBM GB/s (% of peak) + seq-tokens/sec per layer"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+FOREIGN = -1
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for the CPU baseline")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this size before the steps (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the paged decode path has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from paged_kv_cache_358_amd.engine import PagedDecodeLayer
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W, K = args.warmup, args.steps
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+    def up(a, dtype):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" else torch.from_numpy(a)
+        return t.to(dev)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ------------------------------------------------------------------ workload
+    if args.workload == "c4":
+        cfg = synth.C4
+        if W + K > cfg.steps:
+            sys.exit(f"c4 runs at most {cfg.steps} decode steps")
+        S, hq, hkv, D, dtype = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.dtype
+        max_blocks = -(-(cfg.prefix_len + cfg.steps) // 16)
+        layer = PagedDecodeLayer(cfg.pool_blocks(), hkv, D, hq, tdt[dtype], S, max_blocks,
+                                 free_order=cfg.free_order(), partition_size=cfg.partition_size, device=dev)
+        for i in range(cfg.num_prompts):
+            root = i * cfg.samples
+            k, v = cfg.prefix_kv(i)
+            layer.add(root)
+            layer.prefill(root, up(k, dtype), up(v, dtype))
+            for c in range(1, cfg.samples):
+                layer.fork(root, root + c)
+        step_inputs = []
+        for st in range(1, W + K + 1):
+            kn, vn = cfg.step_kv(st)
+            step_inputs.append((up(cfg.step_q(st), dtype), up(kn, dtype), up(vn, dtype)))
+        scale = cfg.softmax_scale
+        kvbpt = cfg.kv_bytes_per_token()
+        workload = {"workload": cfg.name, "prompts": cfg.num_prompts, "samples": cfg.samples,
+                    "prefix_len": cfg.prefix_len, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D,
+                    "block_size": 16, "partition_size": cfg.partition_size,
+                    "timed_steps": f"{W + 1}..{W + K}"}
+        lens0 = None
+    else:
+        cfg = synth.CONFIGS[{"c2": "c2_mha_bf16", "c3": "c3_gqa_bf16", "c5": "c5_long_bf16"}[args.workload]]
+        if W + K > cfg.pool_slack_tokens:
+            sys.exit(f"{cfg.name}: warmup + steps must be <= {cfg.pool_slack_tokens}")
+        S, hq, hkv, D, dtype = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.dtype
+        lens0 = synth.context_lens(cfg)                # context at the first timed step
+        plan = synth.pool_plan(cfg, lens0)
+        prefill = np.maximum(lens0 - W - 1, 0)
+        max_blocks = int(synth.blocks_for(lens0.max() + K))
+        layer = PagedDecodeLayer(plan.num_blocks, hkv, D, hq, tdt[dtype], S, max_blocks,
+                                 free_order=plan.free_order, partition_size=cfg.partition_size, device=dev)
+        if plan.preoccupy_blocks:
+            layer.alloc.add(FOREIGN)
+            layer.alloc.append(FOREIGN, plan.preoccupy_blocks * 16)
+        for s in range(S):
+            layer.add(s)
+            if prefill[s]:
+                k, v = synth.seq_kv(cfg, s, int(prefill[s]))
+                layer.prefill(s, up(k, dtype), up(v, dtype))
+        step_inputs = []
+        for st in range(W + K):
+            kn, vn = synth.new_tokens_kv(cfg.cfg_id, 1000 + st, S, hkv, D, dtype)
+            step_inputs.append((up(synth.queries(cfg, step=1000 + st), dtype), up(kn, dtype), up(vn, dtype)))
+        scale = cfg.softmax_scale
+        kvbpt = cfg.kv_bytes_per_token()
+        workload = {"workload": cfg.name, "num_seqs": S, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D,
+                    "block_size": 16, "partition_size": cfg.partition_size, "context_lens": cfg.lens,
+                    "mean_context": float(lens0.mean()), "pool_blocks": plan.num_blocks}
+    torch.cuda.synchronize()
+    seqs = list(range(S))
+    eb = synth.ELEM_BYTES[dtype]
+    out = torch.empty(S, hq, D, dtype=tdt[dtype], device=dev)
+
+    for i in range(W):
+        q, kn, vn = step_inputs[i]
+        layer.decode_step(seqs, q, kn, vn, out, scale)
+    torch.cuda.synchronize()
+
+    events = []
+    for _ in range(K):
+        trio = tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+        for e in trio:
+            e.record(layer.stream)  # torch creates events lazily; materialise before timing
+        events.append(trio)
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------ timed region
+    step_lens, step_pairs = [], []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        q, kn, vn = step_inputs[W + i]
+        step_pairs.append(layer.decode_step(seqs, q, kn, vn, out, scale, timing=events[i]))
+        step_lens.append(layer.last_lens)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+
+    main_ms = [a.elapsed_time(b) for a, b, _ in events]
+    merge_ms = [b.elapsed_time(c) for _, b, c in events]
+    block_bytes = hkv * D * 16 * eb
+
+    def attn_bytes(lens):
+        lens = np.asarray(lens, dtype=np.int64)
+        return int(lens.sum() * kvbpt + S * hq * D * eb * 2 + synth.blocks_for(lens).sum() * 4 + S * 4)
+
+    attn = [attn_bytes(l) for l in step_lens]
+    append_b = S * hkv * D * eb * 2 * 2 + S * 4
+    copy_b = [p * block_bytes * 2 * 2 for p in step_pairs]
+    total_bytes = sum(attn) + K * append_b + sum(copy_b)
+    value = total_bytes / elapsed / 1e9
+    mean_main_s = float(np.mean(main_ms)) / 1e3
+    achieved = float(np.mean(attn)) / mean_main_s / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded context lengths and shuffled block pool)",
+        "config": workload,
+        "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "seq_tokens_per_s_per_layer": round(S / (elapsed / K), 1),
+        "context_tokens_per_s_per_layer": round(float(np.mean([np.sum(l) for l in step_lens])) / (elapsed / K), 1),
+        "attention_ms": {"main_kernel": round(float(np.mean(main_ms)), 4),
+                         "partition_merge": round(float(np.mean(merge_ms)), 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "decode_mfma_kernel" if dtype != "f32" else "decode_generic_kernel",
+                     "bytes_per_launch": int(np.mean(attn))},
+        "copy_on_write_blocks": int(sum(step_pairs)),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, cfg, lens0, kvbpt)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, cfg, lens0, kvbpt):
+    """The fp64 oracle on a bounded sample of the same workload, one host thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle.attention import decode_attention_seq
+
+    if lens0 is None:  # parallel sampling: every sample at its final context, prefix + appended tokens
+        n_ctx = cfg.prefix_len + cfg.steps
+        steps = [cfg.step_kv(t) for t in range(1, cfg.steps + 1)]
+
+        def draw(s):
+            pk, pv = cfg.prefix_kv(s // cfg.samples)
+            return (np.concatenate([pk, np.stack([k[s] for k, _ in steps])]),
+                    np.concatenate([pv, np.stack([v[s] for _, v in steps])]))
+        lens = [n_ctx] * cfg.num_seqs
+    else:
+        draw = lambda s: synth.seq_kv(cfg, s, int(lens0[s]))
+        lens = lens0.tolist()
+    q = synth.queries(cfg) if lens0 is not None else cfg.step_q(cfg.steps)
+    order = np.random.default_rng(0).permutation(len(lens))
+    spent, done, ctx_tokens = 0.0, 0, 0
+    with threadpool_limits(limits=1):
+        for s in order:
+            k, v = draw(int(s))
+            k64, v64 = synth.decode_f64(k, cfg.dtype), synth.decode_f64(v, cfg.dtype)
+            q64 = synth.decode_f64(q[s], cfg.dtype)
+            t = time.perf_counter()
+            decode_attention_seq(q64, k64, v64, cfg.softmax_scale)
+            spent += time.perf_counter() - t
+            done += 1
+            ctx_tokens += int(lens[s])
+            if spent >= args.cpu_seconds:
+                break
+    gbs = ctx_tokens * kvbpt / spent / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seq_tokens_per_s_per_layer": round(done / spent, 2),
+            "sample": f"fp64 oracle over {done} of {len(lens)} sequences (all {cfg.num_q_heads} query heads, "
+                      f"{ctx_tokens} context tokens), {spent:.1f} s on 1 host thread; inputs decoded to "
+                      f"float64 beforehand"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * pagedattn.h — C ABI of the paged KV-cache decode library (gfx950 / MI355X).
+ *
+ * The KV cache of one attention layer is cut into fixed-size blocks of
+ * block_size tokens (16 here); a per-sequence block table maps the sequence's
+ * logical blocks to physical blocks anywhere in the pool ("Stop Wasting GPU
+ * Memory: A Deep Dive Into vLLM's PagedAttention", Technical Details, "Core
+ * Architecture"; the ml-canon page "49 vLLM / PagedAttention", box "Paging for
+ * the KV cache" and its block-table sketch).  This library provides:
+ *
+ *   paged_attention_decode  single-query attention per head, gathering K/V
+ *                           through the block tables (zhichai.net page "How
+ *                           Virtual Memory Paging Solved LLM KV Cache Waste",
+ *                           "Why it matters": the kernel gathers scattered
+ *                           blocks; Key points: transformer math unchanged);
+ *   kv_append               write each new token's K/V into its cache slot
+ *                           (the sketch's write into the last block; Technical
+ *                           Details, "Single Sequence Generation");
+ *   block_copy              the copy-on-write block copy at divergence
+ *                           (Technical Details, "Copy-on-Write for Parallel
+ *                           Sampling");
+ *   pa_alloc_* / pa_seq_*   the host block allocator: free pool, per-block
+ *                           reference counts, copy-on-write, release at zero
+ *                           (Technical Details, "Copy-on-Write ..." and "Beam
+ *                           Search Optimization").
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned device memory (e.g. torch tensors); the
+ *     library never allocates or frees device memory.  Host pointers are
+ *     caller-owned host memory.
+ *   - GPU entry points are asynchronous on the given HIP stream (a hipStream_t
+ *     passed as void*; NULL = the null stream).  Argument errors are detected
+ *     synchronously on the host and nothing is launched.
+ *   - Every call returns a pa_status; no C++ exception crosses the ABI.
+ *
+ * Cache layout (all tensors densely packed, element type = dtype):
+ *   k_cache  [num_blocks][num_kv_heads][head_dim / X][block_size][X]
+ *   v_cache  [num_blocks][num_kv_heads][head_dim][block_size]
+ *   X = 16 / sizeof(element)  (8 for bf16/fp16, 4 for fp32)
+ * i.e. each (block, kv head) is one contiguous tile of block_size tokens; K is
+ * stored in 16-byte token-interleaved chunks and V transposed (tokens fastest),
+ * so that one wavefront load instruction reads a contiguous run.  A token at
+ * logical position p of a sequence with table T lives in block T[p / B] at
+ * slot p % B; its flat slot number is T[p / B] * B + p % B.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,    /* null pointer, negative size, bad shape, unknown sequence */
+  PA_ERR_UNSUPPORTED = 2,    /* valid request outside the compiled fast paths (dtype, block size, head_dim) */
+  PA_ERR_OUT_OF_BLOCKS = 3,  /* allocator pool exhausted; allocator state unchanged */
+  PA_ERR_HIP = 4,            /* a HIP launch or runtime call failed */
+  PA_ERR_WORKSPACE = 5       /* workspace missing or smaller than paged_attention_workspace_bytes() */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
+
+/* Shape of one layer's paged KV cache (see layout above). */
+typedef struct pa_cache_desc {
+  int64_t num_blocks;    /* physical blocks in the pool, > 0 */
+  int32_t num_kv_heads;  /* H_kv, > 0 */
+  int32_t head_dim;      /* D, a multiple of X; the decode fast path covers 64 and 128 */
+  int32_t block_size;    /* tokens per block; 16 */
+  int32_t dtype;         /* pa_dtype of K and V */
+} pa_cache_desc;
+
+/* Parameters of one paged_attention_decode call. */
+typedef struct pa_decode_params {
+  int32_t num_seqs;            /* S >= 0 */
+  int32_t num_q_heads;         /* H_q, a multiple of num_kv_heads; query head j reads KV head j / (H_q / H_kv) */
+  int32_t max_blocks_per_seq;  /* row stride (in int32) of block_tables, >= 1 */
+  int32_t max_context_len;     /* host-known upper bound of context_lens[]; sizes the grid without a device->host copy */
+  int32_t partition_size;      /* tokens per split-context partition, a multiple of block_size in [16, 1024]; 0 = 512 */
+  int32_t out_dtype;           /* PA_F32, or the cache dtype */
+  pa_cache_desc cache;
+  void* workspace;             /* device scratch for partition partials, >= paged_attention_workspace_bytes(); may be
+                                  NULL when that is 0 */
+  size_t workspace_bytes;
+  void* stream;                /* hipStream_t */
+  void* timing_event;          /* hipEvent_t or NULL: if set, recorded on the stream after the main attention
+                                  kernel and before the partition merge, so a caller can time the two apart */
+} pa_decode_params;
+
+/* Human-readable name of a status code (static string). */
+const char* pa_status_string(int32_t status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int32_t pa_version(void);
+
+/* ----------------------------------------------------------------------- decode attention */
+
+/* Device workspace bytes paged_attention_decode needs for these parameters:
+ * num_seqs * H_q * ceil(max_context_len / partition_size) * (head_dim + 2) * 4 when more than one partition
+ * can occur, else 0.  Returns 0 for invalid parameters (the decode call then reports the error). */
+size_t paged_attention_workspace_bytes(const pa_decode_params* p);
+
+/*
+ * Single-query decode attention over a paged KV cache.
+ *
+ * For each sequence s (context length n = context_lens[s]), query head j and
+ * its KV head h = j / (H_q / H_kv):
+ *     out[s, j, :] = sum_t softmax_t(scale * q[s, j, :] . K_s[t, h, :]) * V_s[t, h, :],   t < n
+ * where K_s[t] / V_s[t] are read from block block_tables[s * max_blocks_per_seq + t / B], slot t % B.
+ * A sequence with n == 0 gets out = 0.  Contexts longer than one partition are split into partitions whose
+ * softmax partials (max, sum, normalised output) go to the workspace and are merged by a second kernel.
+ *
+ *   q             device [num_seqs][H_q][head_dim], cache dtype
+ *   k_cache/v_cache  device, layout above
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries past ceil(n / B) are never read
+ *   context_lens  device int32 [num_seqs]; values are clamped to [0, min(max_context_len,
+ *                 max_blocks_per_seq * B)]
+ *   scale         softmax scale (usually 1/sqrt(head_dim)), taken as float32
+ *   out           device [num_seqs][H_q][head_dim], out_dtype
+ * Table entries outside [0, num_blocks) are a caller error: the kernel never dereferences them and treats
+ * their tokens as absent.  Slots of a block past n, and blocks not in any table, are never read, so they may
+ * hold anything (including NaN).  Results are deterministic (no floating-point atomics) and do not depend on
+ * which physical blocks hold the tokens.
+ */
+int32_t paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* context_lens, float scale,
+                               void* out, const pa_decode_params* p);
+
+/* ----------------------------------------------------------------------- cache writes */
+
+/*
+ * kv_append: for i in [0, num_tokens): if slot_mapping[i] is in [0, num_blocks * B), write
+ * k_new[i, :, :] and v_new[i, :, :] into that slot (block slot / B, offset slot % B) of k_cache / v_cache;
+ * other slots (-1 = padding) are skipped.
+ *   k_new, v_new   device [num_tokens][num_kv_heads][head_dim], cache dtype
+ *   slot_mapping   device int32 [num_tokens]
+ * Two tokens naming the same slot race (which one lands is undefined); the allocator never produces that.
+ */
+int32_t kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping, int32_t num_tokens,
+                  void* k_cache, void* v_cache, const pa_cache_desc* cache, void* stream);
+
+/*
+ * block_copy: for each pair i in [0, num_pairs), copy physical block pairs[2i] (source) onto block
+ * pairs[2i + 1] (destination): every slot, every KV head, K and V.  Pairs with an index outside
+ * [0, num_blocks) are skipped.  Destinations must be distinct and must not be a source of the same call
+ * (the allocator's copy-on-write pairs satisfy both); otherwise the result is undefined.
+ *   pairs   device int32 [num_pairs][2]
+ */
+int32_t block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                   const pa_cache_desc* cache, void* stream);
+
+/* ----------------------------------------------------------------------- host block allocator */
+
+typedef struct pa_allocator pa_allocator;
+
+/* Create an allocator over blocks [0, num_blocks).  free_order (nullable, host int32[num_blocks], a
+ * permutation) is the order a fresh pool hands blocks out; NULL = 0, 1, 2, ...  The pool is a LIFO stack:
+ * freed blocks are handed out again first.  num_blocks * block_size must fit in int32. */
+int32_t pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order, pa_allocator** out);
+void pa_alloc_destroy(pa_allocator* a);
+
+/* New empty sequence.  PA_ERR_INVALID_ARG if the id exists. */
+int32_t pa_seq_add(pa_allocator* a, int64_t id);
+
+/* child shares all of parent's blocks (each block's reference count + 1) and its length. */
+int32_t pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child);
+
+/*
+ * Append n tokens to sequence id.  A token opens a fresh block when the last block is full (length % B == 0);
+ * a token written into a partial last block that other sequences share (reference count > 1) first moves
+ * the sequence onto a private copy: a fresh block is taken, (old, new) is emitted as a copy pair, the old
+ * block's count drops by one.  slots_out[i] (host int32[n]) receives each token's flat slot; pairs_out
+ * (host int32[pairs_cap][2], at most one pair per call) the copy pairs, *n_pairs their count.  If the pool
+ * lacks the blocks the call needs it returns PA_ERR_OUT_OF_BLOCKS and changes nothing.
+ */
+int32_t pa_seq_append(pa_allocator* a, int64_t id, int32_t n, int32_t* slots_out, int32_t* pairs_out,
+                      int32_t pairs_cap, int32_t* n_pairs);
+
+/*
+ * Batched form of pa_seq_append for one decode step: sequences ids[0..n_seqs) in order append counts[i]
+ * tokens each; slots_out receives all slots concatenated in that order, pairs_out all copy pairs in order.
+ * Atomic: if the whole batch does not fit in the pool (or in pairs_cap), nothing changes.
+ */
+int32_t pa_seq_append_batch(pa_allocator* a, const int64_t* ids, int32_t n_seqs, const int32_t* counts,
+                            int32_t* slots_out, int32_t* pairs_out, int32_t pairs_cap, int32_t* n_pairs);
+
+/* Release a sequence: each block of its table (in logical order) loses one reference; blocks reaching zero
+ * go back to the free pool at once. */
+int32_t pa_seq_free(pa_allocator* a, int64_t id);
+
+/* Copy a sequence's block table into out (host int32[cap]); *n = its length in blocks. */
+int32_t pa_seq_table(const pa_allocator* a, int64_t id, int32_t* out, int32_t cap, int32_t* n);
+
+/* Tokens held by a sequence, or -1 if unknown. */
+int64_t pa_seq_len(const pa_allocator* a, int64_t id);
+
+/* Blocks in the free pool. */
+int32_t pa_num_free(const pa_allocator* a);
+
+/* Reference count of a block, or -1 if out of range. */
+int32_t pa_refcount(const pa_allocator* a, int32_t block);
+
+/* The free pool, bottom of the stack first (the last entry is handed out next). */
+int32_t pa_free_list(const pa_allocator* a, int32_t* out, int32_t cap, int32_t* n);
+
+/* Block tables of sequences ids[0..n) as rows of max_blocks int32 padded with -1 (host
+ * tables_out[n][max_blocks]), and their lengths (host lens_out[n]). */
+int32_t pa_build_batch(const pa_allocator* a, const int64_t* ids, int32_t n, int32_t max_blocks,
+                       int32_t* tables_out, int32_t* lens_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,122 @@
+// kv_append and block_copy for the paged KV cache (gfx950).
+//
+// kv_append writes each new token's K and V into the slot its slot mapping names
+// (the ml-canon page's block-table sketch writes the token into the sequence's last
+// block; "Stop Wasting GPU Memory" page, Technical Details, "Single Sequence
+// Generation": new tokens fill the remaining slots of the current block).
+// block_copy is the device half of copy-on-write: only the diverging block is
+// duplicated (same page, "Copy-on-Write for Parallel Sampling").
+//
+// Both are pure byte movement: bit-exact, no arithmetic on the values.
+#include "pa_device.h"
+
+namespace pa {
+
+// One thread per (token, kv head, 16-byte chunk of head_dim).  K goes to the 16-byte
+// chunk [blk][h][chunk][off][0..X) as one vector store; V goes to [blk][h][d][off]
+// element by element (V is stored with tokens fastest).
+template <int EB>
+__global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restrict__ k_new,
+                                                        const uint8_t* __restrict__ v_new,
+                                                        const int32_t* __restrict__ slots, int64_t total,
+                                                        uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                                        int64_t num_slots, int H, int D, int B) {
+  constexpr int X = 16 / EB;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const int chunks = D / X;
+  const int c = static_cast<int>(gid % chunks);
+  const int64_t th = gid / chunks;
+  const int h = static_cast<int>(th % H);
+  const int64_t t = th / H;
+  const int32_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / B;
+  const int off = slot % B;
+  const int64_t src = ((t * H + h) * D + static_cast<int64_t>(c) * X) * EB;
+  const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(k_new + src);
+  const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(v_new + src);
+  const int64_t kdst = ((((blk * H + h) * chunks + c) * B + off) * X) * EB;
+  *reinterpret_cast<u32x4_t*>(k_cache + kdst) = kv;
+  const int64_t vrow = (blk * H + h) * D + static_cast<int64_t>(c) * X;  // element index of (blk, h, d=c*X)
+  if constexpr (EB == 4) {
+    float* vc = reinterpret_cast<float*>(v_cache);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vc[(vrow + e) * B + off] = __uint_as_float(vv[e]);
+  } else {
+    uint16_t* vc = reinterpret_cast<uint16_t*>(v_cache);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vc[(vrow + e) * B + off] = static_cast<uint16_t>(vv[e / 2] >> (16 * (e % 2)));
+  }
+}
+
+// Grid x = pair * chunks_per_block + chunk (4 KiB per workgroup), y = 0 for K, 1 for V.
+__global__ __launch_bounds__(256) void block_copy_kernel(uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                                         const int32_t* __restrict__ pairs, int64_t num_blocks,
+                                                         int64_t block_bytes, int64_t chunks_per_block) {
+  const int64_t pair = blockIdx.x / chunks_per_block;
+  const int64_t chunk = blockIdx.x % chunks_per_block;
+  const int32_t src = pairs[2 * pair];
+  const int32_t dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint8_t* base = blockIdx.y == 0 ? k_cache : v_cache;
+  const int64_t off = chunk * 4096 + static_cast<int64_t>(threadIdx.x) * 16;
+  if (off >= block_bytes) return;
+  const u32x4_t x = *reinterpret_cast<const u32x4_t*>(base + src * block_bytes + off);
+  *reinterpret_cast<u32x4_t*>(base + dst * block_bytes + off) = x;
+}
+
+static bool cache_desc_ok(const pa_cache_desc* c) {
+  if (!c || c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 || c->block_size <= 0) return false;
+  if (!valid_dtype(c->dtype)) return false;
+  const int x = 16 / elem_bytes(c->dtype);
+  return c->head_dim % x == 0;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" int32_t kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping, int32_t num_tokens,
+                             void* k_cache, void* v_cache, const pa_cache_desc* cache, void* stream) {
+  if (!cache_desc_ok(cache) || num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID_ARG;
+  const int eb = elem_bytes(cache->dtype);
+  const int64_t total = static_cast<int64_t>(num_tokens) * cache->num_kv_heads * (cache->head_dim / (16 / eb));
+  const int64_t num_slots = cache->num_blocks * cache->block_size;
+  const dim3 grid(static_cast<uint32_t>((total + 255) / 256));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (eb == 4) {
+    hipLaunchKernelGGL(kv_append_kernel<4>, grid, dim3(256), 0, s, static_cast<const uint8_t*>(k_new),
+                       static_cast<const uint8_t*>(v_new), slot_mapping, total, static_cast<uint8_t*>(k_cache),
+                       static_cast<uint8_t*>(v_cache), num_slots, cache->num_kv_heads, cache->head_dim,
+                       cache->block_size);
+  } else {
+    hipLaunchKernelGGL(kv_append_kernel<2>, grid, dim3(256), 0, s, static_cast<const uint8_t*>(k_new),
+                       static_cast<const uint8_t*>(v_new), slot_mapping, total, static_cast<uint8_t*>(k_cache),
+                       static_cast<uint8_t*>(v_cache), num_slots, cache->num_kv_heads, cache->head_dim,
+                       cache->block_size);
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" int32_t block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                              const pa_cache_desc* cache, void* stream) {
+  if (!cache_desc_ok(cache) || num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !pairs) return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID_ARG;
+  const int64_t block_bytes = static_cast<int64_t>(cache->num_kv_heads) * cache->head_dim * cache->block_size *
+                              elem_bytes(cache->dtype);
+  const int64_t chunks = (block_bytes + 4095) / 4096;
+  const int64_t nwg = chunks * num_pairs;
+  if (nwg > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(block_copy_kernel, dim3(static_cast<uint32_t>(nwg), 2), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                     pairs, cache->num_blocks, block_bytes, chunks);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}

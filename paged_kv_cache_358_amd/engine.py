@@ -1,0 +1,131 @@
+"""One decode layer driven end to end: allocator step -> copies -> appends -> attention.
+
+Host orchestration only; all device work is the library's kernels.  Per decode
+step the C++ allocator appends one token to each sequence (opening blocks as
+they fill, copy-on-write for shared partial blocks: "Stop Wasting GPU Memory"
+page, Technical Details, "Single Sequence Generation" and "Copy-on-Write for
+Parallel Sampling"), its slot mapping, copy pairs and block tables are staged in
+pinned host memory and copied to the device on the compute stream, then
+``block_copy`` -> ``kv_append`` -> ``paged_attention_decode`` run on that stream
+in that order.  Nothing in a step waits for the device, except when a pinned
+staging buffer is about to be reused while its previous copy is still pending.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (BlockAllocator, alloc_kv_cache, block_copy, kv_append, paged_attention_decode,
+               paged_attention_workspace_bytes)
+
+
+class _Staging:
+    """Pinned host buffers + device buffers for one step's metadata."""
+
+    def __init__(self, max_seqs: int, max_blocks: int, max_tokens: int, device):
+        pin = dict(dtype=torch.int32, pin_memory=True)
+        self.h_slots = torch.empty(max_tokens, **pin)
+        self.h_pairs = torch.empty(max_seqs, 2, **pin)
+        self.h_tables = torch.empty(max_seqs, max_blocks, **pin)
+        self.h_lens = torch.empty(max_seqs, **pin)
+        self.d_slots = torch.empty(max_tokens, dtype=torch.int32, device=device)
+        self.d_pairs = torch.empty(max_seqs, 2, dtype=torch.int32, device=device)
+        self.d_tables = torch.empty(max_seqs, max_blocks, dtype=torch.int32, device=device)
+        self.d_lens = torch.empty(max_seqs, dtype=torch.int32, device=device)
+        self.done = None  # event recorded after this buffer's last host->device copy
+
+
+class PagedDecodeLayer:
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, num_q_heads: int, dtype,
+                 max_seqs: int, max_blocks_per_seq: int, free_order=None, partition_size: int = 512,
+                 device="cuda", stream=None):
+        self.alloc = BlockAllocator(num_blocks, 16, free_order)
+        self.k_cache, self.v_cache = alloc_kv_cache(num_blocks, num_kv_heads, head_dim, dtype, device)
+        self.num_q_heads = num_q_heads
+        self.num_kv_heads = num_kv_heads
+        self.head_dim = head_dim
+        self.dtype = dtype
+        self.max_seqs = max_seqs
+        self.max_blocks = max_blocks_per_seq
+        self.partition_size = partition_size
+        self.device = device
+        self.stream = torch.cuda.current_stream() if stream is None else stream
+        self._stage = [_Staging(max_seqs, max_blocks_per_seq, max_seqs, device) for _ in range(2)]
+        self._turn = 0
+        probe_q = torch.empty(max_seqs, num_q_heads, head_dim, dtype=dtype, device=device)
+        probe_t = torch.empty(max_seqs, max_blocks_per_seq, dtype=torch.int32, device=device)
+        ws = paged_attention_workspace_bytes(probe_q, self.k_cache, self.v_cache, probe_t,
+                                             torch.empty_like(probe_q, dtype=torch.float32),
+                                             max_blocks_per_seq * 16, partition_size)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
+        self.max_len = {}  # host view of each sequence's length
+
+    # ------------------------------------------------------------------ sequence management
+    def add(self, seq: int):
+        self.alloc.add(seq)
+        self.max_len[seq] = 0
+
+    def fork(self, parent: int, child: int):
+        self.alloc.fork(parent, child)
+        self.max_len[child] = self.max_len[parent]
+
+    def free(self, seq: int):
+        self.alloc.free(seq)
+        del self.max_len[seq]
+
+    def prefill(self, seq: int, k, v):
+        """Place a prompt's K/V [n, H_kv, D] (device tensors) into the cache."""
+        n = k.shape[0]
+        slots, pairs = self.alloc.append(seq, n)
+        with torch.cuda.stream(self.stream):
+            if len(pairs):
+                block_copy(self.k_cache, self.v_cache, torch.from_numpy(pairs).to(self.device), stream=self.stream)
+            kv_append(k, v, torch.from_numpy(slots).to(self.device), self.k_cache, self.v_cache, stream=self.stream)
+        self.max_len[seq] += n
+
+    # ------------------------------------------------------------------ one decode step
+    def decode_step(self, seqs, q, k_new, v_new, out, scale: float, timing=None):
+        """Each of ``seqs`` appends one token (k_new/v_new [S, H_kv, D]) and attends
+        with q [S, H_q, D] over its whole context; writes out [S, H_q, D].
+
+        ``timing`` = (start, mid, end) torch.cuda.Events (already recorded once) are
+        recorded around the attention call: start..mid spans the main attention kernel,
+        mid..end the partition merge.  Returns the number of copy-on-write block copies."""
+        S = len(seqs)
+        st = self._stage[self._turn]
+        self._turn ^= 1
+        if st.done is not None:
+            st.done.synchronize()  # previous copies out of this pinned buffer have finished
+        slots, pairs = self.alloc.append_batch(seqs, np.ones(S, np.int32), st.h_slots.numpy(),
+                                               st.h_pairs.numpy())
+        np_tables = st.h_tables.numpy()[:S]
+        np_lens = st.h_lens.numpy()[:S]
+        t, l = self.alloc.build_batch(seqs, self.max_blocks)
+        np_tables[...] = t
+        np_lens[...] = l
+        max_ctx = 0
+        for s in seqs:
+            self.max_len[s] += 1
+            max_ctx = max(max_ctx, self.max_len[s])
+        npairs = len(pairs)
+        with torch.cuda.stream(self.stream):
+            st.d_slots[:S].copy_(st.h_slots[:S], non_blocking=True)
+            st.d_tables[:S].copy_(st.h_tables[:S], non_blocking=True)
+            st.d_lens[:S].copy_(st.h_lens[:S], non_blocking=True)
+            if npairs:
+                st.d_pairs[:npairs].copy_(st.h_pairs[:npairs], non_blocking=True)
+            st.done = torch.cuda.Event()
+            st.done.record(self.stream)
+            if npairs:
+                block_copy(self.k_cache, self.v_cache, st.d_pairs[:npairs], stream=self.stream)
+            kv_append(k_new, v_new, st.d_slots[:S], self.k_cache, self.v_cache, stream=self.stream)
+            if timing is not None:
+                timing[0].record(self.stream)
+            paged_attention_decode(q, self.k_cache, self.v_cache, st.d_tables[:S], st.d_lens[:S], scale, out,
+                                   max_context_len=max_ctx, partition_size=self.partition_size,
+                                   workspace=self.workspace, stream=self.stream,
+                                   timing_event=None if timing is None else timing[1])
+            if timing is not None:
+                timing[2].record(self.stream)
+        self.last_lens = np_lens.copy()
+        return npairs

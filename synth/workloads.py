@@ -42,9 +42,14 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     Returns the 16-bit patterns as uint16.  NaN maps to the quiet NaN 0x7FC0.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    bias = ((u >> 16) & 1) + 0x7FFF
-    out = ((u + bias) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # uint32 arithmetic wraps only for patterns above 0xFFFF8000, which are NaNs
+    # and are overwritten below.
+    out = (u >> 16) & np.uint32(1)
+    out += np.uint32(0x7FFF)
+    out += u
+    out >>= np.uint32(16)
+    out = out.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = 0x7FC0

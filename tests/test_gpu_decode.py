@@ -1,0 +1,164 @@
+"""Paged decode attention on the GPU against the fp64 oracle.
+
+Tolerance (max abs error, fp32 output): 1e-5 for fp32 inputs, 5e-3 for bf16/fp16
+inputs with fp32 accumulation.  Pool memory the kernels must not read (free
+blocks, a foreign sequence's blocks, slots past each context) holds NaN.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from paged_setup import PagedDecode, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def max_err(out: torch.Tensor, pd: PagedDecode, seqs=None, heads=None):
+    o = out.float().cpu().numpy()
+    worst = 0.0
+    for s in (range(pd.cfg.num_seqs) if seqs is None else seqs):
+        hs = list(range(pd.cfg.num_q_heads)) if heads is None else heads
+        ref = pd.oracle(s, hs)
+        assert np.all(np.isfinite(o[s, hs]))
+        worst = max(worst, float(np.max(np.abs(o[s, hs] - ref))))
+    return worst
+
+
+def test_c1_tiny_fp32_all_outputs():
+    pd = PagedDecode(synth.C1)
+    out = pd.run()
+    assert max_err(out, pd) <= 1e-5
+    # context of one token: the output is that token's V, bit for bit
+    k, v = pd.truth[0]
+    assert np.array_equal(out[0].cpu().numpy(), v[0])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_single_token_context_is_exact(dtype):
+    cfg = synth.scaled(synth.C3, lens=[1, 1, 17, 1], dtype=dtype)
+    pd = PagedDecode(cfg)
+    out = pd.run().cpu().numpy()
+    for s in (0, 1, 3):
+        _, v = pd.truth[s]
+        expect = synth.decode_f64(v[0], dtype).astype(np.float32)     # [H_kv, D]
+        assert np.array_equal(out[s], np.repeat(expect, cfg.group, axis=0))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_mha_ragged(dtype):
+    # MHA head layout of the 64-sequence workload; lengths span partial blocks,
+    # partition edges and several partitions.
+    lens = [1, 2, 15, 16, 17, 31, 33, 128, 500, 511, 512, 513, 1024, 1500, 2048, 2047]
+    cfg = synth.scaled(synth.C2, lens=lens, dtype=dtype)
+    pd = PagedDecode(cfg)
+    out = pd.run()
+    assert max_err(out, pd) <= tol_for(dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_gqa_fragmented_pool(dtype):
+    cfg = synth.scaled(synth.C3, num_seqs=24, dtype=dtype, lens_args=(300.0, 1.0, 16, 3000))
+    pd = PagedDecode(cfg)
+    assert pd.alloc.num_free() < pd.num_blocks * 0.75          # foreign sequence holds ~30%
+    out = pd.run()
+    assert max_err(out, pd) <= tol_for(dtype)
+
+
+def test_head_dim_64_and_group_4():
+    cfg = synth.DecodeConfig("d64_g4", 31, 6, 16, 4, 64, "bf16", "fixed", (1, 40, 700, 16, 1025, 64))
+    pd = PagedDecode(cfg)
+    out = pd.run()
+    assert max_err(out, pd) <= 5e-3
+
+
+def test_generic_path_shapes():
+    # group 32 (> 16 query heads per KV head) and head_dim 256 take the VALU kernel
+    for cfg in (synth.DecodeConfig("g32", 32, 3, 32, 1, 128, "bf16", "fixed", (5, 600, 1100)),
+                synth.DecodeConfig("d256", 33, 3, 4, 2, 256, "bf16", "fixed", (7, 530, 40)),
+                synth.DecodeConfig("f32_gqa", 34, 3, 8, 2, 64, "f32", "fixed", (3, 1030, 48))):
+        pd = PagedDecode(cfg)
+        out = pd.run()
+        assert max_err(out, pd) <= tol_for(cfg.dtype), cfg.name
+
+
+@pytest.mark.parametrize("part", [16, 64, 256, 512, 1024])
+def test_partition_size_does_not_change_the_result(part):
+    cfg = synth.scaled(synth.C3, lens=[16, 100, 1024, 3000, 4097], num_seqs=None)
+    pd = PagedDecode(cfg)
+    out = pd.run(partition_size=part)
+    assert max_err(out, pd) <= 5e-3
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_physical_block_permutation_is_bitwise_invisible(dtype):
+    base = synth.scaled(synth.C3, lens=[5, 77, 600, 1500], dtype=dtype)
+    a = PagedDecode(base)
+    n = a.num_blocks
+    b = PagedDecode(base, free_order=np.random.default_rng(99).permutation(n))
+    assert not np.array_equal(a.tables_np, b.tables_np)
+    oa, ob = a.run(), b.run()
+    assert torch.equal(oa, ob)
+
+
+def test_empty_context_gives_zero():
+    cfg = synth.scaled(synth.C3, lens=[0, 20, 0])
+    pd = PagedDecode(cfg)
+    out = pd.run().cpu().numpy()
+    assert np.all(out[0] == 0) and np.all(out[2] == 0)
+    assert np.max(np.abs(out[1] - pd.oracle(1))) <= 5e-3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_16bit_output(dtype):
+    cfg = synth.scaled(synth.C3, lens=[3, 333, 2222], dtype=dtype)
+    pd = PagedDecode(cfg)
+    out = pd.run(out_dtype=torch.bfloat16 if dtype == "bf16" else torch.float16).float().cpu().numpy()
+    frac_bits = 7 if dtype == "bf16" else 10
+    for s in range(3):
+        ref = pd.oracle(s)
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - frac_bits)
+        assert np.all(np.abs(out[s] - ref) <= 5e-3 + 0.5 * ulp)
+
+
+def test_tables_past_context_are_never_read():
+    # Garbage (out-of-range ids) in table entries past each context must not matter.
+    cfg = synth.scaled(synth.C3, lens=[20, 300, 1])
+    pd = PagedDecode(cfg)
+    ref = pd.run()
+    t = pd.tables_np.copy()
+    for s, n in enumerate(pd.lens):
+        t[s, -(-int(n) // 16):] = 2 ** 30
+    out = pd.run(block_tables=torch.from_numpy(t).cuda())
+    assert torch.equal(ref, out)
+
+
+# ----------------------------------------------------------------- full-size workloads, sampled outputs
+def _sampled_check(cfg, n_seq_samples, n_head_samples, seed):
+    pd = PagedDecode(cfg, keep_truth=False)
+    out = pd.run().cpu().numpy()
+    assert np.all(np.isfinite(out))
+    rng = np.random.default_rng(seed)
+    seqs = rng.choice(cfg.num_seqs, size=min(n_seq_samples, cfg.num_seqs), replace=False)
+    worst = 0.0
+    for s in seqs:
+        heads = sorted(rng.choice(cfg.num_q_heads, size=n_head_samples, replace=False).tolist())
+        ref = pd.oracle_sampled(int(s), heads)
+        worst = max(worst, float(np.max(np.abs(out[s, heads] - ref))))
+    assert worst <= tol_for(cfg.dtype), worst
+    return pd, out
+
+
+def test_full_c2_mha_sampled():
+    _sampled_check(synth.C2, 8, 4, 2)
+
+
+def test_full_c3_gqa_sampled():
+    pd, _ = _sampled_check(synth.C3, 8, 4, 3)
+    assert pd.lens.max() > 4096
+
+
+def test_full_c5_long_context_sampled():
+    _sampled_check(synth.C5, 2, 3, 5)
