@@ -96,6 +96,10 @@ const char* pa_status_string(int32_t status);
 /* Library ABI version (major * 10000 + minor * 100 + patch). */
 int32_t pa_version(void);
 
+/* Text of the HIP error behind the most recent PA_ERR_HIP returned on the calling thread ("" if none).
+ * The string is owned by the library and valid until the thread's next failing call. */
+const char* pa_last_error(void);
+
 /* ----------------------------------------------------------------------- decode attention */
 
 /* Device workspace bytes paged_attention_decode needs for these parameters:

@@ -4,7 +4,7 @@ A thin ctypes layer over ``libpagedattn.so`` (C ABI in ``include/pagedattn.h``):
 argument marshalling only.  Every step of the hot path runs in the library's HIP
 kernels or its C++ allocator; there is no CPU or PyTorch fallback, and importing
 this package fails if the library has not been built
-(``python -m paged_kv_cache_358_amd.build``).
+(``python paged_kv_cache_358_amd/build.py``).
 
 PyTorch supplies device memory and streams: tensors are passed by data pointer,
 the stream is torch's current stream unless one is given.
@@ -44,6 +44,7 @@ _PAllocPtr = ctypes.POINTER(_vp)
 SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_version": (_i32, []),
+    "pa_last_error": (ctypes.c_char_p, []),
     "paged_attention_workspace_bytes": (_sz, [ctypes.POINTER(DecodeParams)]),
     "paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, ctypes.POINTER(DecodeParams)]),
     "kv_append": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc), _vp]),
@@ -66,8 +67,13 @@ SIGNATURES = {
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_358_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python paged_kv_cache_358_amd/build.py` "
                           "(the library has no CPU fallback)")
+    # torch ships its own HIP runtime.  Loading it first makes the library's
+    # libamdhip64.so.7 dependency resolve (by soname) to that same runtime; the
+    # other order puts two HIP/HSA runtimes in the process and the second one
+    # finds no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
@@ -83,7 +89,8 @@ class PagedAttnError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
         self.status_name = lib.pa_status_string(status).decode()
-        super().__init__(f"{what}: {self.status_name}")
+        detail = f" ({lib.pa_last_error().decode()})" if status == PA_ERR_HIP else ""
+        super().__init__(f"{what}: {self.status_name}{detail}")
 
 
 def _check(status: int, what: str):

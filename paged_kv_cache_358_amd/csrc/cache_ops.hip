@@ -9,6 +9,7 @@
 //
 // Both are pure byte movement: bit-exact, no arithmetic on the values.
 #include "pa_device.h"
+#include "pa_status.h"
 
 namespace pa {
 
@@ -90,6 +91,7 @@ extern "C" int32_t kv_append(const void* k_new, const void* v_new, const int32_t
   const int64_t num_slots = cache->num_blocks * cache->block_size;
   const dim3 grid(static_cast<uint32_t>((total + 255) / 256));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind
   if (eb == 4) {
     hipLaunchKernelGGL(kv_append_kernel<4>, grid, dim3(256), 0, s, static_cast<const uint8_t*>(k_new),
                        static_cast<const uint8_t*>(v_new), slot_mapping, total, static_cast<uint8_t*>(k_cache),
@@ -101,7 +103,7 @@ extern "C" int32_t kv_append(const void* k_new, const void* v_new, const int32_t
                        static_cast<uint8_t*>(v_cache), num_slots, cache->num_kv_heads, cache->head_dim,
                        cache->block_size);
   }
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return PA_HIP_STATUS("kv_append", hipGetLastError());
 }
 
 extern "C" int32_t block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
@@ -115,8 +117,9 @@ extern "C" int32_t block_copy(void* k_cache, void* v_cache, const int32_t* pairs
   const int64_t chunks = (block_bytes + 4095) / 4096;
   const int64_t nwg = chunks * num_pairs;
   if (nwg > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind
   hipLaunchKernelGGL(block_copy_kernel, dim3(static_cast<uint32_t>(nwg), 2), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
                      pairs, cache->num_blocks, block_bytes, chunks);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return PA_HIP_STATUS("block_copy", hipGetLastError());
 }

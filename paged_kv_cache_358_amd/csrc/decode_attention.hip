@@ -40,6 +40,7 @@
 #include <cmath>
 
 #include "pa_device.h"
+#include "pa_status.h"
 
 namespace pa {
 
@@ -556,7 +557,10 @@ int32_t launch_decode(const DecodeArgs& args, hipStream_t st, void* timing_event
     if (nwg > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(decode_generic_kernel<DT>, dim3(static_cast<uint32_t>(nwg)), dim3(kWave), 0, st, args);
   }
-  if (timing_event && hipEventRecord(static_cast<hipEvent_t>(timing_event), st) != hipSuccess) return PA_ERR_HIP;
+  if (timing_event) {
+    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(timing_event), st);
+    if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_decode: timing event", e);
+  }
   if (args.max_parts > 1) launch_reduce<DT>(args, st);
   return PA_OK;
 }
@@ -605,6 +609,7 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   a.num_blocks = p->cache.num_blocks;
 
   hipStream_t stream = static_cast<hipStream_t>(p->stream);
+  (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind
   int32_t rc;
   switch (p->cache.dtype) {
     case PA_F32: rc = launch_decode<PA_F32>(a, stream, p->timing_event); break;
@@ -612,5 +617,5 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
     default: rc = launch_decode<PA_F16>(a, stream, p->timing_event); break;
   }
   if (rc != PA_OK) return rc;
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return PA_HIP_STATUS("paged_attention_decode", hipGetLastError());
 }

@@ -1,5 +1,17 @@
-// Status strings and ABI version.
+// Status strings, ABI version and the last HIP error text.
+#include <cstdio>
+
 #include "pagedattn.h"
+#include "pa_status.h"
+
+namespace pa {
+static thread_local char g_last_error[256] = "";
+
+int32_t record_hip_error(const char* where, int code, const char* name, const char* text) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d): %s", where, name, code, text);
+  return PA_ERR_HIP;
+}
+}  // namespace pa
 
 extern "C" {
 
@@ -16,5 +28,7 @@ const char* pa_status_string(int32_t status) {
 }
 
 int32_t pa_version(void) { return 100; }
+
+const char* pa_last_error(void) { return pa::g_last_error; }
 
 }  // extern "C"
