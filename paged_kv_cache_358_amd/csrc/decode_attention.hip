@@ -216,10 +216,10 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
     const st* vb = vc + base;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      r.k[kk] = *reinterpret_cast<const u32x4_t*>(kb + ((kk * 4 + grp) * kBlockTokens + col) * 8);
+      r.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + ((kk * 4 + grp) * kBlockTokens + col) * 8));
 #pragma unroll
     for (int nn = 0; nn < NV; ++nn)
-      r.v[nn] = *reinterpret_cast<const u32x2_t*>(vb + (nn * 16 + col) * kBlockTokens + grp * 4);
+      r.v[nn] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(vb + (nn * 16 + col) * kBlockTokens + grp * 4));
   };
 
   f32x4_t o[NV];
@@ -228,13 +228,14 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
   float m = -INFINITY;
   float l = 0.f;
 
+  // Branch-free: a block whose id is out of range counts as empty (nv = 0), and the
+  // masking below then leaves m, l and o unchanged, so no path skips a wait.
   auto compute = [&](KVRegs<D>& r, int i) {
     const int bl = b0 + w + kWaves * i;
     const int32_t phys = __builtin_amdgcn_readlane(my_id, i);
     int nv = n - bl * kBlockTokens;
     nv = nv > kBlockTokens ? kBlockTokens : nv;
     if (phys < 0 || phys >= a.num_blocks) nv = 0;
-    if (nv <= 0) return;
 
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -247,44 +248,51 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
     const float m_new = fmaxf(m, bm);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    const float alpha = (m == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
     float pr[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_new);
+    for (int e = 0; e < 4; ++e) pr[e] = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m_new);
     l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m = m_new;
     const u32x4_t pop = PSplit<DT>::split(pr);
 
-    if (nv < kBlockTokens) {  // zero V of absent tokens: they may hold anything, even NaN
-      uint32_t keep[2];
+    // Absent tokens' V may hold anything, even NaN: select them out (P is 0 there too).
+    uint32_t keep[2];
 #pragma unroll
-      for (int wd = 0; wd < 2; ++wd) {
-        const int t0 = grp * 4 + 2 * wd;
-        keep[wd] = (t0 < nv ? 0x0000ffffu : 0u) | (t0 + 1 < nv ? 0xffff0000u : 0u);
-      }
-#pragma unroll
-      for (int nn = 0; nn < NV; ++nn) {
-        r.v[nn][0] &= keep[0];
-        r.v[nn][1] &= keep[1];
-      }
+    for (int wd = 0; wd < 2; ++wd) {
+      const int t0 = grp * 4 + 2 * wd;
+      keep[wd] = (t0 < nv ? 0x0000ffffu : 0u) | (t0 + 1 < nv ? 0xffff0000u : 0u);
     }
 #pragma unroll
     for (int nn = 0; nn < NV; ++nn) {
+      const uint32_t v0 = r.v[nn][0] & keep[0];
+      const uint32_t v1 = r.v[nn][1] & keep[1];
       o[nn] *= alpha;
-      const u32x4_t vop = {r.v[nn][0], r.v[nn][1], r.v[nn][0], r.v[nn][1]};
+      const u32x4_t vop = {v0, v1, v0, v1};
       o[nn] = mfma16x16x32<DT>(vop, pop, o[nn]);
     }
   };
 
-  // Two register sets: the next block's loads are in flight while this one computes.
+  // Two register sets: block i+1's loads are in flight while block i computes.  The
+  // steady-state loop issues its loads unconditionally so that each wait covers only
+  // the block about to be used; the last one or two blocks are peeled off.
   KVRegs<D> ra, rb;
-  if (my_n > 0) load(ra, 0);
-  for (int i = 0; i < my_n; i += 2) {
-    if (i + 1 < my_n) load(rb, i + 1);
-    compute(ra, i);
-    if (i + 1 >= my_n) break;
-    if (i + 2 < my_n) load(ra, i + 2);
-    compute(rb, i + 1);
+  if (my_n > 0) {
+    load(ra, 0);
+    int i = 0;
+    for (; i + 2 < my_n; i += 2) {
+      load(rb, i + 1);
+      compute(ra, i);
+      load(ra, i + 2);
+      compute(rb, i + 1);
+    }
+    if (i + 1 < my_n) {
+      load(rb, i + 1);
+      compute(ra, i);
+      compute(rb, i + 1);
+    } else {
+      compute(ra, i);
+    }
   }
 
   // Per-wave totals: the sum over the four k-groups of this head column.
