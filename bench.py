@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="split-context partition in tokens (0 = the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -79,12 +81,13 @@ def main():
     # ------------------------------------------------------------------ workload
     if args.workload == "c4":
         cfg = synth.C4
+        part = args.partition_size or cfg.partition_size
         if W + K > cfg.steps:
             sys.exit(f"c4 runs at most {cfg.steps} decode steps")
         S, hq, hkv, D, dtype = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.dtype
         max_blocks = -(-(cfg.prefix_len + cfg.steps) // 16)
         layer = PagedDecodeLayer(cfg.pool_blocks(), hkv, D, hq, tdt[dtype], S, max_blocks,
-                                 free_order=cfg.free_order(), partition_size=cfg.partition_size, device=dev)
+                                 free_order=cfg.free_order(), partition_size=part, device=dev)
         for i in range(cfg.num_prompts):
             root = i * cfg.samples
             k, v = cfg.prefix_kv(i)
@@ -100,11 +103,12 @@ def main():
         kvbpt = cfg.kv_bytes_per_token()
         workload = {"workload": cfg.name, "prompts": cfg.num_prompts, "samples": cfg.samples,
                     "prefix_len": cfg.prefix_len, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D,
-                    "block_size": 16, "partition_size": cfg.partition_size,
+                    "block_size": 16, "partition_size": part,
                     "timed_steps": f"{W + 1}..{W + K}"}
         lens0 = None
     else:
         cfg = synth.CONFIGS[{"c2": "c2_mha_bf16", "c3": "c3_gqa_bf16", "c5": "c5_long_bf16"}[args.workload]]
+        part = args.partition_size or cfg.partition_size
         if W + K > cfg.pool_slack_tokens:
             sys.exit(f"{cfg.name}: warmup + steps must be <= {cfg.pool_slack_tokens}")
         S, hq, hkv, D, dtype = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.dtype
@@ -113,7 +117,7 @@ def main():
         prefill = np.maximum(lens0 - W - 1, 0)
         max_blocks = int(synth.blocks_for(lens0.max() + K))
         layer = PagedDecodeLayer(plan.num_blocks, hkv, D, hq, tdt[dtype], S, max_blocks,
-                                 free_order=plan.free_order, partition_size=cfg.partition_size, device=dev)
+                                 free_order=plan.free_order, partition_size=part, device=dev)
         if plan.preoccupy_blocks:
             layer.alloc.add(FOREIGN)
             layer.alloc.append(FOREIGN, plan.preoccupy_blocks * 16)
@@ -129,7 +133,7 @@ def main():
         scale = cfg.softmax_scale
         kvbpt = cfg.kv_bytes_per_token()
         workload = {"workload": cfg.name, "num_seqs": S, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D,
-                    "block_size": 16, "partition_size": cfg.partition_size, "context_lens": cfg.lens,
+                    "block_size": 16, "partition_size": part, "context_lens": cfg.lens,
                     "mean_context": float(lens0.mean()), "pool_blocks": plan.num_blocks}
     torch.cuda.synchronize()
     seqs = list(range(S))

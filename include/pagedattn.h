@@ -102,9 +102,11 @@ const char* pa_last_error(void);
 
 /* ----------------------------------------------------------------------- decode attention */
 
-/* Device workspace bytes paged_attention_decode needs for these parameters:
- * num_seqs * H_q * ceil(max_context_len / partition_size) * (head_dim + 2) * 4 when more than one partition
- * can occur, else 0.  Returns 0 for invalid parameters (the decode call then reports the error). */
+/* Device workspace bytes paged_attention_decode needs for these parameters: when more than one partition
+ * can occur, P = num_seqs * H_q * ceil(max_context_len / partition_size) fp32 partial rows of head_dim + 2
+ * values (P * (head_dim + 2) * 4 bytes) followed by num_seqs + 1 int32 (the block prefix sums the
+ * partition merge uses); else 0.  Returns 0 for invalid parameters (the decode call then reports the
+ * error).  The contents need no initialisation and are scratch between calls. */
 size_t paged_attention_workspace_bytes(const pa_decode_params* p);
 
 /*

@@ -38,6 +38,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "pa_device.h"
 #include "pa_status.h"
@@ -65,6 +68,8 @@ struct DecodeArgs {
   int32_t max_parts;
   int32_t out_f32;
   int64_t num_blocks;
+  int32_t* run_pre;   // persistent split: H_kv-scaled block prefix sums [S + 1] (workspace)
+  int32_t run_grid;   // persistent split: workgroups of the main kernel; 0 = one run per partition
 };
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s) {
@@ -87,13 +92,27 @@ __device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t idx, floa
   }
 }
 
+// Four consecutive outputs (16-byte aligned for fp32, 8-byte for 16-bit types).
+template <int DT>
+__device__ __forceinline__ void store_out4(const DecodeArgs& a, int64_t idx, const f32x4_t& v) {
+  if (a.out_f32) {
+    *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + idx) = v;
+  } else {
+    uint32_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = Elem<DT>::from_float(v[e]);
+    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + idx) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  }
+}
+
 // ------------------------------------------------------------------ MFMA fast path
 
-// P (4 probabilities of one head for tokens 4j..4j+3) -> B operand of the PV MFMA:
-// slots 0..3 hold the high parts, slots 4..7 the low parts (p - high).
+// P (4 probabilities of one head for tokens 4j..4j+3) split as P = hi + lo, both in the
+// cache's 16-bit type; each half is the B operand of one PV MFMA, so the probabilities
+// enter the product with ~16 significant bits while the accumulation stays fp32.
 template <int DT> struct PSplit;
 template <> struct PSplit<PA_BF16> {
-  __device__ static u32x4_t split(const float p[4]) {
+  __device__ static void split(const float p[4], u32x2_t& hi_out, u32x2_t& lo_out) {
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -103,16 +122,12 @@ template <> struct PSplit<PA_BF16> {
       hi[r] = u;
       lo[r] = (ru + 0x7fffu + ((ru >> 16) & 1u)) & 0xffff0000u;    // bf16, round to nearest even
     }
-    u32x4_t out;
-    out[0] = (hi[0] >> 16) | hi[1];
-    out[1] = (hi[2] >> 16) | hi[3];
-    out[2] = (lo[0] >> 16) | lo[1];
-    out[3] = (lo[2] >> 16) | lo[3];
-    return out;
+    hi_out = u32x2_t{(hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3]};
+    lo_out = u32x2_t{(lo[0] >> 16) | lo[1], (lo[2] >> 16) | lo[3]};
   }
 };
 template <> struct PSplit<PA_F16> {
-  __device__ static u32x4_t split(const float p[4]) {
+  __device__ static void split(const float p[4], u32x2_t& hi_out, u32x2_t& lo_out) {
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -121,23 +136,32 @@ template <> struct PSplit<PA_F16> {
       hi[r] = __builtin_bit_cast(uint16_t, h);
       lo[r] = __builtin_bit_cast(uint16_t, l);
     }
-    u32x4_t out;
-    out[0] = hi[0] | (hi[1] << 16);
-    out[1] = hi[2] | (hi[3] << 16);
-    out[2] = lo[0] | (lo[1] << 16);
-    out[3] = lo[2] | (lo[3] << 16);
-    return out;
+    hi_out = u32x2_t{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+    lo_out = u32x2_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
   }
 };
 
+// S^T tile: v_mfma_f32_16x16x32 (8 elements of the contraction per lane).
 template <int DT>
-__device__ __forceinline__ f32x4_t mfma16x16x32(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+__device__ __forceinline__ f32x4_t mfma_qk(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
   if constexpr (DT == PA_BF16) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                    c, 0, 0, 0);
   } else {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
                                                   0, 0, 0);
+  }
+}
+
+// O^T tile: v_mfma_f32_16x16x16 (4 tokens per lane), V straight from its load registers.
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_pv(const u32x2_t& a, const u32x2_t& b, const f32x4_t& c) {
+  if constexpr (DT == PA_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, b),
+                                                     c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0,
+                                                 0, 0);
   }
 }
 
@@ -148,11 +172,22 @@ struct KVRegs {
 };
 
 constexpr int kWaves = 4;
+constexpr int kRing = 2;                // register sets per wave (blocks in flight + 1)
+constexpr int kRsrcWord3 = 0x00020000;  // raw (unstructured) buffer, 32-bit data format
+constexpr int kLoadNT = 2;              // buffer-load cache policy: non-temporal (streamed once)
 
-template <int DT, int D>
+// One workgroup = kWaves wavefronts per (partition, KV head, sequence).  Each wave walks
+// its blocks with a ring of NBUF register sets: block i+NBUF-1 is being fetched while
+// block i computes.  Every (block, KV head) tile is read through a buffer resource
+// covering exactly that tile; a slot of the ring past the wave's last block, or a block
+// id outside the pool, gets an empty resource, whose loads return zeros and touch no
+// memory.  So each iteration issues the same loads, and the compiler's wait counts
+// cover exactly the block about to be used.
+template <int DT, int D, int NBUF>
 __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KK = D / 32;
   constexpr int NV = D / 16;
+  constexpr int kTileBytes = D * kBlockTokens * 2;
   __shared__ float sm_o[kWaves][16][D];
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
@@ -168,7 +203,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform by construction
   const int col = lane & 15;  // MFMA row/column index of this lane
   const int grp = lane >> 4;  // MFMA k-group of this lane
   const int g = a.group;
@@ -184,10 +219,10 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
   const int nblk = (n + kBlockTokens - 1) / kBlockTokens;
   const int b0 = p * a.part_blocks;
   const int b1 = min(nblk, b0 + a.part_blocks);
-  const int my_n = (b1 - b0 > w) ? (b1 - b0 - w + kWaves - 1) / kWaves : 0;
+  const int my_n = (b1 - b0 > w) ? (b1 - b0 - w + kWaves - 1) / kWaves : 0;  // <= 16
 
-  // Physical ids of this wave's blocks b0 + w + 4 i, one per lane (my_n <= 64).
-  int32_t my_id = 0;
+  // Physical ids of this wave's blocks b0 + w + 4 i, one per lane; -1 past the last.
+  int32_t my_id = -1;
   if (lane < my_n) my_id = a.block_tables[static_cast<int64_t>(s) * a.max_blocks + b0 + w + kWaves * lane];
 
   // Q^T operand: lane (column = head col, k-group grp) holds dims (kk*4 + grp)*8 .. +8.
@@ -204,22 +239,29 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
     }
   }
 
-  const st* kc = static_cast<const st*>(a.k);
-  const st* vc = static_cast<const st*>(a.v);
-  const int64_t head_stride = static_cast<int64_t>(D) * kBlockTokens;  // elements per (block, kv head)
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + static_cast<int64_t>(h) * kTileBytes;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + static_cast<int64_t>(h) * kTileBytes;
+  const int64_t blk_stride = static_cast<int64_t>(a.hkv) * kTileBytes;
+  // K tile [D/8][16 tokens][8]: lane reads 16 B at lane*16 (+1 KiB per QK MFMA).
+  // V tile [D][16 tokens]: lane reads tokens grp*4..+3 of dim col (+16 dims per PV MFMA).
+  const int k_off = lane * 16;
+  const int v_off = col * 32 + grp * 8;
 
   auto load = [&](KVRegs<D>& r, int i) {
-    int32_t phys = __builtin_amdgcn_readlane(my_id, i);
-    if (phys < 0 || phys >= a.num_blocks) phys = 0;  // masked below; never dereference a bad id
-    const int64_t base = (static_cast<int64_t>(phys) * a.hkv + h) * head_stride;
-    const st* kb = kc + base;
-    const st* vb = vc + base;
+    const int32_t phys = __builtin_amdgcn_readlane(my_id, i < 63 ? i : 63);
+    const bool ok = i < my_n && phys >= 0 && phys < a.num_blocks;
+    const int64_t off = ok ? static_cast<int64_t>(phys) * blk_stride : 0;
+    const int nrec = ok ? kTileBytes : 0;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kbase + off), 0, nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vbase + off), 0, nrec, kRsrcWord3);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      r.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + ((kk * 4 + grp) * kBlockTokens + col) * 8));
+      r.k[kk] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, kk * 1024, kLoadNT));
 #pragma unroll
     for (int nn = 0; nn < NV; ++nn)
-      r.v[nn] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(vb + (nn * 16 + col) * kBlockTokens + grp * 4));
+      r.v[nn] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, nn * 512, kLoadNT));
   };
 
   f32x4_t o[NV];
@@ -229,8 +271,8 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
   float l = 0.f;
 
   // Branch-free: a block whose id is out of range counts as empty (nv = 0), and the
-  // masking below then leaves m, l and o unchanged, so no path skips a wait.
-  auto compute = [&](KVRegs<D>& r, int i) {
+  // masking below then leaves m, l and o unchanged.
+  auto compute = [&](const KVRegs<D>& r, int i) {
     const int bl = b0 + w + kWaves * i;
     const int32_t phys = __builtin_amdgcn_readlane(my_id, i);
     int nv = n - bl * kBlockTokens;
@@ -239,7 +281,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
 
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) sacc = mfma16x16x32<DT>(r.k[kk], qop[kk], sacc);
+    for (int kk = 0; kk < KK; ++kk) sacc = mfma_qk<DT>(r.k[kk], qop[kk], sacc);
 
     float x[4];
 #pragma unroll
@@ -254,7 +296,8 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
     for (int e = 0; e < 4; ++e) pr[e] = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m_new);
     l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m = m_new;
-    const u32x4_t pop = PSplit<DT>::split(pr);
+    u32x2_t p_hi, p_lo;
+    PSplit<DT>::split(pr, p_hi, p_lo);
 
     // Absent tokens' V may hold anything, even NaN: select them out (P is 0 there too).
     uint32_t keep[2];
@@ -265,33 +308,22 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
     }
 #pragma unroll
     for (int nn = 0; nn < NV; ++nn) {
-      const uint32_t v0 = r.v[nn][0] & keep[0];
-      const uint32_t v1 = r.v[nn][1] & keep[1];
+      const u32x2_t vv = {r.v[nn][0] & keep[0], r.v[nn][1] & keep[1]};
       o[nn] *= alpha;
-      const u32x4_t vop = {v0, v1, v0, v1};
-      o[nn] = mfma16x16x32<DT>(vop, pop, o[nn]);
+      o[nn] = mfma_pv<DT>(vv, p_hi, o[nn]);
+      o[nn] = mfma_pv<DT>(vv, p_lo, o[nn]);
     }
   };
 
-  // Two register sets: block i+1's loads are in flight while block i computes.  The
-  // steady-state loop issues its loads unconditionally so that each wait covers only
-  // the block about to be used; the last one or two blocks are peeled off.
-  KVRegs<D> ra, rb;
-  if (my_n > 0) {
-    load(ra, 0);
-    int i = 0;
-    for (; i + 2 < my_n; i += 2) {
-      load(rb, i + 1);
-      compute(ra, i);
-      load(ra, i + 2);
-      compute(rb, i + 1);
-    }
-    if (i + 1 < my_n) {
-      load(rb, i + 1);
-      compute(ra, i);
-      compute(rb, i + 1);
-    } else {
-      compute(ra, i);
+  KVRegs<D> ring[NBUF];
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j) load(ring[j], j);
+  for (int i0 = 0; i0 < my_n; i0 += NBUF) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      if (i0 + j >= my_n) break;
+      load(ring[(j + NBUF - 1) % NBUF], i0 + j + NBUF - 1);
+      compute(ring[j], i0 + j);
     }
   }
 
@@ -336,6 +368,362 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
         a.part_ml[prow * 2 + 1] = L;
       }
     }
+  }
+}
+
+// ------------------------------------------------------------------ persistent MFMA path
+
+constexpr int kMaxScanSeqs = 2048;  // sequences the persistent kernel's in-LDS index covers
+constexpr int kPersistRing = 2;     // ring depth of the persistent kernel
+constexpr int kXcds = 8;            // accelerator complex dies of an MI355X, each with its own L2
+
+// Work split of the persistent kernel.  The partitions of all (sequence, KV head) pairs
+// are laid end to end in (sequence, KV head, partition) order, each weighted by its
+// block count; W is the total.  Workgroup k of G owns the partitions whose first block
+// lies in [k*W/G, (k+1)*W/G): a contiguous run, so each workgroup streams about W/G
+// blocks.  Consecutive partitions of one (sequence, KV head) inside a workgroup's run are
+// merged on chip (the online softmax simply continues); only where a run ends inside a
+// sequence's context is a partial (max, sum, output) written, to the slot of the run's
+// first partition.  run_owner / run_lo below are shared with the merge kernel.
+__device__ __forceinline__ int64_t run_lo(int64_t k, int64_t W, int64_t G) { return k * W / G; }
+__device__ __forceinline__ int64_t run_owner(int64_t off, int64_t W, int64_t G) { return ((off + 1) * G - 1) / W; }
+
+// One partition of one (sequence, KV head) as a workgroup sees it.
+struct Item {
+  int32_t s, h, p, n;  // sequence, KV head, partition, context length
+  int32_t b0, my_n;    // first block of the partition; blocks of this wave (b0 + w + 4i)
+  int32_t np, len;     // partitions of the sequence; blocks in this partition
+};
+
+// Persistent form of the MFMA kernel: about (CUs x resident workgroups) workgroups each
+// walk their run of partitions.  Each wave keeps a ring of NBUF register sets that
+// looks NBUF-1 positions ahead across partition boundaries, so the next partition's
+// first blocks are already loading while the current one finishes.  The next
+// partition's block ids and query are loaded one partition ahead into the other of two
+// slots (A/B), so no loaded value is copied before it is used.  Per-block arithmetic is
+// that of decode_mfma_kernel.
+// At least two waves per SIMD: the compiler keeps the kernel within 256 VGPRs.
+template <int DT, int D, int NBUF>
+__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_persistent_kernel(
+    DecodeArgs a) {
+  constexpr int KK = D / 32;
+  constexpr int NV = D / 16;
+  constexpr int kTileBytes = D * kBlockTokens * 2;
+  constexpr int kThreads = kWaves * kWave;
+  __shared__ __attribute__((aligned(16))) float sm_o[kWaves][16][D];
+  __shared__ float sm_m[kWaves][16];
+  __shared__ float sm_l[kWaves][16];
+  __shared__ int32_t blkpre[kMaxScanSeqs + 1];  // H_kv * (blocks of the sequences before s)
+  __shared__ int32_t nb_s[kMaxScanSeqs];        // blocks of sequence s
+  __shared__ int32_t ctx_s[kMaxScanSeqs];       // clamped context length of s
+  __shared__ int32_t scan[kThreads];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int S = a.num_seqs;
+  const int PB = a.part_blocks;
+  const int hkv = a.hkv;
+  const int g = a.group;
+  const int G = gridDim.x;
+  // Run k of the split.  Workgroups are dealt to the 8 XCDs round-robin (workgroup i on XCD
+  // i % 8); giving XCD x the runs [x*G/8, (x+1)*G/8) keeps neighbouring runs (e.g. samples
+  // forked from one prompt, which share its blocks) on one XCD and its L2 while they run.
+  const int k = (G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds : blockIdx.x;
+
+  // ---- prefix sums of blocks over sequences (every workgroup builds its own copy)
+  const int per = (S + kThreads - 1) / kThreads;
+  int cnt = 0;
+  for (int j = 0; j < per; ++j) {
+    const int s = tid * per + j;
+    if (s < S) cnt += (clamp_ctx(a, s) + kBlockTokens - 1) / kBlockTokens;
+  }
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  {
+    int base = scan[tid] - cnt;
+    for (int j = 0; j < per; ++j) {
+      const int s = tid * per + j;
+      if (s < S) {
+        const int n = clamp_ctx(a, s);
+        const int nb = (n + kBlockTokens - 1) / kBlockTokens;
+        blkpre[s] = base * hkv;
+        nb_s[s] = nb;
+        ctx_s[s] = n;
+        base += nb;
+      }
+    }
+    if (tid == kThreads - 1) blkpre[S] = scan[kThreads - 1] * hkv;
+  }
+  __syncthreads();
+  const int W = __builtin_amdgcn_readfirstlane(blkpre[S]);
+
+  // The merge kernel recomputes run boundaries from the same prefix sums.
+  if (k == 0 && a.run_pre != nullptr)
+    for (int s = tid; s <= S; s += kThreads) a.run_pre[s] = blkpre[s];
+  // Zero-length sequences own no partition: their output is 0.
+  for (int s = k; s < S; s += G) {
+    if (ctx_s[s] == 0)
+      for (int i = tid; i < a.hq * D; i += kThreads) store_out<DT>(a, static_cast<int64_t>(s) * a.hq * D + i, 0.0f);
+  }
+  if (W == 0) return;
+
+  const int64_t lo = run_lo(k, W, G);
+  const int64_t hi = run_lo(k + 1, W, G);
+
+  // Sequence holding global block offset off: the last s with blkpre[s] <= off (that skips
+  // zero-length sequences, which share their successor's prefix).
+  auto seq_of = [&](int64_t off) {
+    int lo_s = 0, hi_s = S - 1;
+    while (lo_s < hi_s) {
+      const int mid = (lo_s + hi_s + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(blkpre[mid]) <= off) lo_s = mid; else hi_s = mid - 1;
+    }
+    return lo_s;
+  };
+
+  // One partition (off = the global offset of its first block) and the data loaded for
+  // it ahead of time.
+  struct Slot {
+    Item it;
+    bool ok;
+    int32_t ids;    // this wave's block ids, one per lane; lanes >= my_n are never used
+    u32x4_t q[KK];  // Q^T operand
+  };
+  using st = uint16_t;
+  const st* qp = static_cast<const st*>(a.q);
+  // Decode the partition starting at off and issue the loads of its block ids and query
+  // without waiting for them.  The table read is clamped into the row so that it is
+  // issued unconditionally; query columns >= g repeat head 0 of the group (their scores
+  // only feed their own, discarded, columns).
+  auto prepare = [&](int64_t off, Slot& sl) {
+    Item& it = sl.it;
+    it = Item{0, 0, 0, 0, 0, 0, 1, 0};
+    sl.ok = off < hi;
+    if (sl.ok) {
+      const int s = seq_of(off);
+      const int nb = __builtin_amdgcn_readfirstlane(nb_s[s]);
+      const int r = static_cast<int>(off - __builtin_amdgcn_readfirstlane(blkpre[s]));
+      it.s = s;
+      it.h = r / nb;
+      it.p = (r % nb) / PB;
+      it.n = __builtin_amdgcn_readfirstlane(ctx_s[s]);
+      it.np = (nb + PB - 1) / PB;
+      it.b0 = it.p * PB;
+      it.len = min(PB, nb - it.b0);
+      it.my_n = (it.len > w) ? (it.len - w + kWaves - 1) / kWaves : 0;
+    }
+    const int b = min(it.b0 + w + kWaves * lane, a.max_blocks - 1);
+    sl.ids = a.block_tables[static_cast<int64_t>(it.s) * a.max_blocks + b];
+    // Keep the id load ahead of the query loads: the lookahead waits for it while the
+    // query loads may still be in flight.
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t qrow = (static_cast<int64_t>(it.s) * a.hq + it.h * g + (col < g ? col : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) sl.q[kk] = *reinterpret_cast<const u32x4_t*>(qp + qrow + (kk * 4 + grp) * 8);
+  };
+
+  const uint8_t* kc = static_cast<const uint8_t*>(a.k);
+  const uint8_t* vc = static_cast<const uint8_t*>(a.v);
+  const int64_t blk_stride = static_cast<int64_t>(hkv) * kTileBytes;
+  const int k_off = lane * 16;
+  const int v_off = col * 32 + grp * 8;
+  // phys = the block id of ring position i of a partition with my_n blocks for this wave.
+  auto load_tile = [&](KVRegs<D>& r, int32_t phys, int i, int my_n, int h) {
+    const bool ok = i < my_n && phys >= 0 && phys < a.num_blocks;
+    const int64_t off = ok ? static_cast<int64_t>(phys) * blk_stride + static_cast<int64_t>(h) * kTileBytes : 0;
+    const int nrec = ok ? kTileBytes : 0;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kc + off), 0, nrec,
+                                                                        kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vc + off), 0, nrec,
+                                                                        kRsrcWord3);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      r.k[kk] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, kk * 1024, kLoadNT));
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn)
+      r.v[nn] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, nn * 512, kLoadNT));
+  };
+  // Ring positions per partition: a multiple of NBUF, at least NBUF; those past my_n are empty.
+  auto steps_of = [&](const Item& it) { return max(NBUF, (it.my_n + NBUF - 1) / NBUF * NBUF); };
+
+  KVRegs<D> ring[NBUF];
+  f32x4_t o[NV];
+  float m = -INFINITY, l = 0.f;
+  int seg_p0 = 0;     // first partition of the current (sequence, KV head) segment
+  int wave_turn = 0;  // which wave writes the next segment's results
+
+  // Stream one partition's blocks (looking ahead into the next one).  At the end of a
+  // segment, merge the four waves and write the output or the run's partial.
+  auto run = [&](const Item cur, const int32_t cur_ids, const u32x4_t (&qc)[KK], const Item nxi, const bool nx_ok,
+                 const int32_t nx_ids) {
+    auto compute = [&](const KVRegs<D>& r, int i) {
+      const int bl = cur.b0 + w + kWaves * i;
+      const int32_t phys = __builtin_amdgcn_readlane(cur_ids, i < 63 ? i : 63);
+      int nv = cur.n - bl * kBlockTokens;
+      nv = nv > kBlockTokens ? kBlockTokens : nv;
+      if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
+
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) sacc = mfma_qk<DT>(r.k[kk], qc[kk], sacc);
+
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (grp * 4 + e < nv) ? sacc[e] * a.scale_log2 : -INFINITY;
+      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float m_new = fmaxf(m, bm);
+      const float alpha = (m == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
+      float pr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pr[e] = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m_new);
+      l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      m = m_new;
+      u32x2_t p_hi, p_lo;
+      PSplit<DT>::split(pr, p_hi, p_lo);
+      uint32_t keep[2];
+#pragma unroll
+      for (int wd = 0; wd < 2; ++wd) {
+        const int t0 = grp * 4 + 2 * wd;
+        keep[wd] = (t0 < nv ? 0x0000ffffu : 0u) | (t0 + 1 < nv ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) {
+        const u32x2_t vv = {r.v[nn][0] & keep[0], r.v[nn][1] & keep[1]};
+        o[nn] *= alpha;
+        o[nn] = mfma_pv<DT>(vv, p_hi, o[nn]);
+        o[nn] = mfma_pv<DT>(vv, p_lo, o[nn]);
+      }
+    };
+
+    const int steps = steps_of(cur);
+    const int nx_my_n = nx_ok ? nxi.my_n : 0;
+    for (int i = 0; i < steps; i += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        // Ring lookahead position; past this partition's last step it is the next one's.
+        int la = i + j + NBUF - 1;
+        int32_t phys;
+        int mn = cur.my_n, hh = cur.h;
+        if (la >= steps) {
+          // The next partition's ids were loaded after this one's first blocks.  Reading
+          // them only here (the empty asm keeps the read inside the branch) keeps every
+          // other wait of the loop counting only ring loads.
+          int32_t t = nx_ids;
+          asm volatile("" : "+v"(t));
+          la -= steps;
+          phys = __builtin_amdgcn_readlane(t, la < 63 ? la : 63);
+          mn = nx_my_n;
+          hh = nxi.h;
+        } else {
+          phys = __builtin_amdgcn_readlane(cur_ids, la < 63 ? la : 63);
+        }
+        load_tile(ring[(j + NBUF - 1) % NBUF], phys, la, mn, hh);
+        compute(ring[j], i + j);
+      }
+    }
+
+    if (nx_ok && nxi.s == cur.s && nxi.h == cur.h) return;  // the segment goes on
+
+    // ---- end of segment: merge the four waves through LDS
+    float lt = l;
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (grp == 0) {
+      sm_m[w][col] = m;
+      sm_l[w][col] = lt;
+    }
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm_o[w][col][nn * 16 + grp * 4 + e] = o[nn][e];
+    __syncthreads();
+    // One wave, rotating per segment, merges and writes; the others go straight on.  The
+    // counter of outstanding vector-memory operations also counts stores, so a wave that
+    // stores cannot use its later loads before the stores complete.
+    if (w == (wave_turn & (kWaves - 1))) {
+      const bool final = seg_p0 == 0 && cur.p == cur.np - 1;  // the segment is the whole context
+      constexpr int kChunks = D / 4;                            // 4 consecutive dims per lane and store
+      for (int c4 = lane; c4 < g * kChunks; c4 += kWave) {
+        const int cc = c4 / kChunks, d0 = (c4 % kChunks) * 4;
+        float mx = sm_m[0][cc];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, sm_m[ww][cc]);
+        float L = 0.f;
+        f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+        if (mx != -INFINITY) {
+#pragma unroll
+          for (int ww = 0; ww < kWaves; ++ww) {
+            const float e = __builtin_amdgcn_exp2f(sm_m[ww][cc] - mx);
+            L += e * sm_l[ww][cc];
+            O += e * *reinterpret_cast<const f32x4_t*>(&sm_o[ww][cc][d0]);
+          }
+        }
+        f32x4_t res;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[e] = L > 0.f ? O[e] / L : 0.f;
+        const int64_t row = static_cast<int64_t>(cur.s) * a.hq + cur.h * g + cc;
+        if (final) {
+          store_out4<DT>(a, row * D + d0, res);
+        } else {
+          const int64_t prow = row * a.max_parts + seg_p0;
+          *reinterpret_cast<f32x4_t*>(a.part_o + prow * D + d0) = res;
+          if (d0 == 0) *reinterpret_cast<f32x2_t*>(a.part_ml + prow * 2) = f32x2_t{mx, L};
+        }
+      }
+    }
+    ++wave_turn;
+    __syncthreads();
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.f;
+    seg_p0 = nxi.p;
+  };
+
+  // First partition: the first one whose first block is at or after lo.
+  int64_t off;
+  {
+    const int s = seq_of(lo);
+    const int nb = __builtin_amdgcn_readfirstlane(nb_s[s]);
+    const int r = static_cast<int>(lo - __builtin_amdgcn_readfirstlane(blkpre[s]));
+    int h = r / nb, b = r % nb;
+    b = (b + PB - 1) / PB * PB;
+    if (b >= nb) {
+      b = 0;
+      ++h;
+    }
+    off = __builtin_amdgcn_readfirstlane(blkpre[s]) + static_cast<int64_t>(h) * nb + b;
+  }
+  Slot A, B;
+  prepare(off, A);
+  if (!A.ok) return;  // the run holds no partition start
+#pragma unroll
+  for (int nn = 0; nn < NV; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  seg_p0 = A.it.p;
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j) load_tile(ring[j], __builtin_amdgcn_readlane(A.ids, j), j, A.it.my_n, A.it.h);
+  off += A.it.len;
+  prepare(off, B);
+  while (true) {
+    run(A.it, A.ids, A.q, B.it, B.ok, B.ids);
+    if (!B.ok) break;
+    off += B.it.len;
+    prepare(off, A);
+    run(B.it, B.ids, B.q, A.it, A.ok, A.ids);
+    if (!A.ok) break;
+    off += A.it.len;
+    prepare(off, B);
   }
 }
 
@@ -434,63 +822,100 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ partition merge
 
-// One workgroup per (sequence, query head) with more than one partition:
-//   M = max_p m_p,  w_p = 2^(m_p - M) * l_p,  out = sum_p w_p * O_p / sum_p w_p
-// where O_p is partition p's normalised output.  Fixed summation order: deterministic.
+// One workgroup per (sequence, KV head) with more than one partition merges the partials
+// of that sequence's runs, for all g query heads of the KV head:
+//   M = max_r m_r,  w_r = 2^(m_r - M) * l_r,  out = sum_r w_r * O_r / sum_r w_r
+// where O_r is run r's normalised output (done as an online merge, in a fixed order:
+// deterministic).  A run is one partition (run_grid == 0) or the stretch of partitions one
+// workgroup of the persistent kernel streamed; its partial sits at the slot of its first
+// partition.  Zero-length and single-run sequences were written by the main kernel.
 template <int DT>
 __global__ __launch_bounds__(256) void reduce_partitions_kernel(DecodeArgs a) {
-  extern __shared__ float wts[];  // [max_parts]
-  __shared__ float red[256];
-  __shared__ float acc_s[256];
-  const int s = blockIdx.x / a.hq;
-  const int j = blockIdx.x % a.hq;
+  __shared__ float red_m[256];
+  __shared__ float red_l[256];
+  __shared__ __attribute__((aligned(16))) f32x4_t red_o[256];
+  const int s = blockIdx.x / a.hkv;
+  const int kvh = blockIdx.x % a.hkv;
   const int n = clamp_ctx(a, s);
-  const int np = num_parts(n, a.part_blocks);
+  if (n == 0) return;
+  const int PB = a.part_blocks;
+  const int nb = (n + kBlockTokens - 1) / kBlockTokens;
+  const int np = (nb + PB - 1) / PB;
   if (np <= 1) return;
-  const int tid = threadIdx.x;
   const int D = a.head_dim;
-  const int64_t row = static_cast<int64_t>(s) * a.hq + j;
-  const float* ml = a.part_ml + row * a.max_parts * 2;
-  const float* po = a.part_o + row * a.max_parts * D;
+  const int g = a.group;
 
-  float mx = -INFINITY;
-  for (int p = tid; p < np; p += 256) mx = fmaxf(mx, ml[2 * p]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
+  const bool split = a.run_grid > 0;
+  const int64_t G = a.run_grid;
+  int64_t W = 0, A = 0;
+  int k0 = 0, k1 = np - 1;  // runs k0..k1 (partitions themselves when !split)
+  if (split) {
+    W = a.run_pre[a.num_seqs];
+    A = a.run_pre[s] + static_cast<int64_t>(kvh) * nb;
+    k0 = static_cast<int>(run_owner(A, W, G));
+    k1 = static_cast<int>(run_owner(A + static_cast<int64_t>(np - 1) * PB, W, G));
+    if (k0 == k1) return;
   }
-  mx = red[0];
-  __syncthreads();
-  float ls = 0.f;
-  for (int p = tid; p < np; p += 256) {
-    const float w = (mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[2 * p] - mx) * ml[2 * p + 1];
-    wts[p] = w;
-    ls += w;
-  }
-  red[tid] = ls;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  const float L = red[0];
+  // First partition of run k (k in k0..k1+1; run k1+1 starts past the end).
+  auto run_start = [&](int k) -> int {
+    if (k > k1) return np;
+    if (!split) return k;
+    if (k == k0) return 0;
+    return static_cast<int>((run_lo(k, W, G) - A + PB - 1) / PB);
+  };
 
-  // Threads split as (lane group g over partitions) x (dims): D <= 256.
-  const int groups = 256 / D;
-  const int gi = tid / D;
-  const int d = tid % D;
-  float acc = 0.f;
-  if (gi < groups) {
-    for (int p = gi; p < np; p += groups) acc = fmaf(wts[p], po[static_cast<int64_t>(p) * D + d], acc);
-  }
-  acc_s[tid] = acc;
-  __syncthreads();
-  if (tid < D) {
-    float t = 0.f;
-    for (int q = 0; q < groups; ++q) t += acc_s[q * D + tid];
-    store_out<DT>(a, row * D + tid, L > 0.f ? t / L : 0.f);
+  const int nout4 = g * D / 4;
+  const int C = nout4 < 256 ? nout4 : 256;
+  const int RG = 256 / C;  // run groups: threads of group rg take runs k0+rg, k0+rg+RG, ...
+  const int tid = threadIdx.x;
+  const int rg = tid / C;
+  const int col4 = tid % C;
+  for (int c4 = col4; c4 < nout4; c4 += C) {  // a single pass unless g*D/4 > 256 (then RG == 1)
+    const int cc = c4 / (D / 4), d0 = (c4 % (D / 4)) * 4;
+    const int64_t row = static_cast<int64_t>(s) * a.hq + kvh * g + cc;
+    float M = -INFINITY, L = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    if (rg < RG) {
+      for (int k = k0 + rg; k <= k1; k += RG) {
+        const int ps = run_start(k);
+        if (ps >= run_start(k + 1)) continue;  // a workgroup whose stretch starts no partition here
+        const int64_t prow = row * a.max_parts + ps;
+        const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(a.part_ml + prow * 2);
+        const f32x4_t O = *reinterpret_cast<const f32x4_t*>(a.part_o + prow * D + d0);
+        if (!(ml[1] > 0.f)) continue;
+        const float Mn = fmaxf(M, ml[0]);
+        const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        const float wr = __builtin_amdgcn_exp2f(ml[0] - Mn) * ml[1];
+        acc = acc * sc + O * wr;
+        L = L * sc + wr;
+        M = Mn;
+      }
+    }
+    if (RG > 1) {
+      red_m[tid] = M;
+      red_l[tid] = L;
+      red_o[tid] = acc;
+      __syncthreads();
+      if (rg == 0) {
+        for (int r = 1; r < RG; ++r) {
+          const int t = r * C + col4;
+          const float mr = red_m[t];
+          if (!(red_l[t] > 0.f)) continue;
+          const float Mn = fmaxf(M, mr);
+          const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+          const float sr = __builtin_amdgcn_exp2f(mr - Mn);
+          acc = acc * sc + red_o[t] * sr;
+          L = L * sc + red_l[t] * sr;
+          M = Mn;
+        }
+      }
+    }
+    if (rg == 0) {
+      f32x4_t res;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) res[e] = L > 0.f ? acc[e] / L : 0.f;
+      store_out4<DT>(a, row * D + d0, res);
+    }
   }
 }
 
@@ -505,6 +930,7 @@ struct Plan {
   int32_t part_blocks;
   int32_t ctx_limit;
   int32_t max_parts;
+  size_t prefix_offset;  // byte offset of the block prefix sums in the workspace
   size_t workspace;
 };
 
@@ -525,14 +951,16 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
   const int64_t limit64 = std::min<int64_t>(p->max_context_len, int64_t{p->max_blocks_per_seq} * kBlockTokens);
   const int32_t limit = static_cast<int32_t>(std::min<int64_t>(limit64, INT32_MAX));
   const int32_t parts = std::max<int32_t>(1, static_cast<int32_t>((int64_t{limit} + pt - 1) / pt));
-  if (parts > 8192) return PA_ERR_UNSUPPORTED;  // reduce kernel keeps one weight per partition in LDS
+  if (parts > 8192) return PA_ERR_UNSUPPORTED;
   out->part_tokens = pt;
   out->part_blocks = pt / kBlockTokens;
   out->ctx_limit = limit;
   out->max_parts = parts;
-  out->workspace = parts > 1 ? static_cast<size_t>(p->num_seqs) * p->num_q_heads * parts *
-                                   (static_cast<size_t>(c.head_dim) + 2) * sizeof(float)
-                             : 0;
+  // Partials [S][H_q][parts][D] and [S][H_q][parts][2] (fp32), then the persistent split's
+  // block prefix sums [S + 1] (int32).
+  const size_t rows = static_cast<size_t>(p->num_seqs) * p->num_q_heads * parts;
+  out->prefix_offset = rows * (static_cast<size_t>(c.head_dim) + 2) * sizeof(float);
+  out->workspace = parts > 1 ? out->prefix_offset + (static_cast<size_t>(p->num_seqs) + 1) * sizeof(int32_t) : 0;
   return PA_OK;
 }
 
@@ -540,24 +968,79 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 template <int DT>
 void launch_reduce(const DecodeArgs& args, hipStream_t st) {
-  const size_t lds = static_cast<size_t>(args.max_parts) * sizeof(float);
-  hipLaunchKernelGGL(reduce_partitions_kernel<DT>, dim3(static_cast<uint32_t>(args.num_seqs) * args.hq), dim3(256),
-                     lds, st, args);
+  hipLaunchKernelGGL(reduce_partitions_kernel<DT>, dim3(static_cast<uint32_t>(args.num_seqs) * args.hkv), dim3(256),
+                     0, st, args);
+}
+
+// Workgroups of a persistent kernel that fit on the current device at once
+// (compute units x resident workgroups per CU), looked up once per (device, kernel).
+int32_t resident_workgroups(const void* kernel, int* out) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_decode: hipGetDevice", e);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({dev, kernel});
+  if (it != cache.end()) {
+    *out = it->second;
+    return PA_OK;
+  }
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_decode: CU count", e);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWaves * kWave, 0);
+  if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_decode: occupancy", e);
+  *out = std::max(1, cus) * std::max(1, per_cu);
+  cache[{dev, kernel}] = *out;
+  return PA_OK;
+}
+
+template <int DT, int D>
+int32_t launch_persistent(const DecodeArgs& args, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&decode_persistent_kernel<DT, D, kPersistRing>);
+  int resident = 0;
+  const int32_t rc = resident_workgroups(fn, &resident);
+  if (rc != PA_OK) return rc;
+  const int64_t items = int64_t{args.max_parts} * args.hkv * args.num_seqs;  // upper bound
+  DecodeArgs a = args;
+  a.run_grid = static_cast<int32_t>(std::min<int64_t>(items, resident));
+  hipLaunchKernelGGL((decode_persistent_kernel<DT, D, kPersistRing>), dim3(static_cast<uint32_t>(a.run_grid)),
+                     dim3(kWaves * kWave), 0, st, a);
+  return PA_OK;
 }
 
 template <int DT>
-int32_t launch_decode(const DecodeArgs& args, hipStream_t st, void* timing_event) {
+int32_t launch_decode(DecodeArgs args, hipStream_t st, void* timing_event) {
   const int64_t D = args.head_dim;
   const bool fast = DT != PA_F32 && (D == 64 || D == 128) && args.group <= 16;
-  if (fast) {
+  // The persistent kernel indexes blocks of all (sequence, KV head) pairs with int32.
+  const bool persistent = fast && args.num_seqs <= kMaxScanSeqs &&
+                          int64_t{args.num_seqs} * args.hkv * args.max_blocks < 0x7fffffffLL;
+  args.run_grid = 0;
+  if (persistent) {
+    if (int64_t{args.max_parts} * args.hkv * args.num_seqs > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    if constexpr (DT != PA_F32) {
+      const int32_t rc = D == 64 ? launch_persistent<DT, 64>(args, st) : launch_persistent<DT, 128>(args, st);
+      if (rc != PA_OK) return rc;
+      // the merge kernel must see the grid the split was made for
+      int resident = 0;
+      const void* fn = D == 64 ? reinterpret_cast<const void*>(&decode_persistent_kernel<DT, 64, kPersistRing>)
+                               : reinterpret_cast<const void*>(&decode_persistent_kernel<DT, 128, kPersistRing>);
+      const int32_t rc2 = resident_workgroups(fn, &resident);
+      if (rc2 != PA_OK) return rc2;
+      args.run_grid = static_cast<int32_t>(
+          std::min<int64_t>(int64_t{args.max_parts} * args.hkv * args.num_seqs, resident));
+    }
+  } else if (fast) {
     const int64_t nwg = int64_t{args.max_parts} * args.hkv * args.num_seqs;
     if (nwg > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
     if constexpr (DT != PA_F32) {
       if (D == 64)
-        hipLaunchKernelGGL((decode_mfma_kernel<DT, 64>), dim3(static_cast<uint32_t>(nwg)), dim3(kWaves * kWave), 0,
+        hipLaunchKernelGGL((decode_mfma_kernel<DT, 64, kRing>), dim3(static_cast<uint32_t>(nwg)), dim3(kWaves * kWave), 0,
                            st, args);
       else
-        hipLaunchKernelGGL((decode_mfma_kernel<DT, 128>), dim3(static_cast<uint32_t>(nwg)), dim3(kWaves * kWave), 0,
+        hipLaunchKernelGGL((decode_mfma_kernel<DT, 128, kRing>), dim3(static_cast<uint32_t>(nwg)), dim3(kWaves * kWave), 0,
                            st, args);
     }
   } else {
@@ -615,6 +1098,9 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   a.max_parts = plan.max_parts;
   a.out_f32 = p->out_dtype == PA_F32 ? 1 : 0;
   a.num_blocks = p->cache.num_blocks;
+  a.run_pre = plan.workspace > 0
+                  ? reinterpret_cast<int32_t*>(static_cast<uint8_t*>(p->workspace) + plan.prefix_offset)
+                  : nullptr;
 
   hipStream_t stream = static_cast<hipStream_t>(p->stream);
   (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind

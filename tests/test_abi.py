@@ -51,9 +51,10 @@ def test_workspace_bytes():
     ws = pa.lib.paged_attention_workspace_bytes
     assert ws(ctypes.byref(_params())) == 0                      # one partition: no workspace
     p = _params(S=4, hq=64, hkv=8, d=128, maxb=8192, maxctx=131072, dtype=pa.PA_BF16, out=pa.PA_F32)
-    assert ws(ctypes.byref(p)) == 4 * 64 * 256 * (128 + 2) * 4
+    # partials (output row + max + sum per query head and partition), then S + 1 int32 prefix sums
+    assert ws(ctypes.byref(p)) == 4 * 64 * 256 * (128 + 2) * 4 + (4 + 1) * 4
     p = _params(maxb=100, maxctx=1000, part=256)
-    assert ws(ctypes.byref(p)) == 4 * 4 * 4 * (64 + 2) * 4
+    assert ws(ctypes.byref(p)) == 4 * 4 * 4 * (64 + 2) * 4 + (4 + 1) * 4
     assert ws(None) == 0
 
 
