@@ -136,6 +136,7 @@ def main():
                     "block_size": 16, "partition_size": part, "context_lens": cfg.lens,
                     "mean_context": float(lens0.mean()), "pool_blocks": plan.num_blocks}
     torch.cuda.synchronize()
+    print(f"[bench] {workload['workload']}: workload resident on the GPU", file=sys.stderr, flush=True)
     seqs = list(range(S))
     eb = synth.ELEM_BYTES[dtype]
     out = torch.empty(S, hq, D, dtype=tdt[dtype], device=dev)
@@ -154,32 +155,50 @@ def main():
     torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ timed region
+    shared = args.workload == "c4"  # forked samples share blocks: count each physical block once
     step_lens, step_pairs = [], []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    step_tables = []
     for i in range(K):
         q, kn, vn = step_inputs[W + i]
         step_pairs.append(layer.decode_step(seqs, q, kn, vn, out, scale, timing=events[i]))
         step_lens.append(layer.last_lens)
+        if shared:
+            step_tables.append(layer.last_tables.copy())
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
+    print(f"[bench] {K} timed steps: {elapsed / K * 1e3:.3f} ms/step", file=sys.stderr, flush=True)
 
     main_ms = [a.elapsed_time(b) for a, b, _ in events]
     merge_ms = [b.elapsed_time(c) for _, b, c in events]
     block_bytes = hkv * D * 16 * eb
 
-    def attn_bytes(lens):
+    # Algorithmic bytes of one attention launch: K/V of every cached token (2 * H_kv * D * elem per
+    # token), q and out, the block-table entries and context lengths read.  With shared blocks the
+    # HBM-bound quantity counts each physical block once, at the most tokens any sequence uses of it.
+    def attn_bytes(lens, tables=None):
         lens = np.asarray(lens, dtype=np.int64)
-        return int(lens.sum() * kvbpt + S * hq * D * eb * 2 + synth.blocks_for(lens).sum() * 4 + S * 4)
+        fixed = S * hq * D * eb * 2 + int(synth.blocks_for(lens).sum()) * 4 + S * 4
+        if tables is None:
+            return int(lens.sum() * kvbpt) + fixed
+        used = {}
+        for s_, n in enumerate(lens.tolist()):
+            for b in range(-(-n // 16)):
+                phys = int(tables[s_, b])
+                used[phys] = max(used.get(phys, 0), min(16, n - 16 * b))
+        return int(sum(used.values()) * kvbpt) + fixed
 
-    attn = [attn_bytes(l) for l in step_lens]
+    logical = [attn_bytes(l) for l in step_lens]
+    attn = [attn_bytes(l, t) for l, t in zip(step_lens, step_tables)] if shared else logical
     append_b = S * hkv * D * eb * 2 * 2 + S * 4
     copy_b = [p * block_bytes * 2 * 2 for p in step_pairs]
     total_bytes = sum(attn) + K * append_b + sum(copy_b)
     value = total_bytes / elapsed / 1e9
     mean_main_s = float(np.mean(main_ms)) / 1e3
     achieved = float(np.mean(attn)) / mean_main_s / 1e9
+    kernel = main_kernel_name(dtype, D, hq // hkv, S)
 
     result = {
         "metric": METRIC,
@@ -201,15 +220,42 @@ def main():
         "attention_ms": {"main_kernel": round(float(np.mean(main_ms)), 4),
                          "partition_merge": round(float(np.mean(merge_ms)), 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "decode_mfma_kernel" if dtype != "f32" else "decode_generic_kernel",
-                     "bytes_per_launch": int(np.mean(attn))},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(kernel, workload["workload"]),
+                     "kernel": kernel, "bytes_per_launch": int(np.mean(attn))},
         "copy_on_write_blocks": int(sum(step_pairs)),
     }
+    if shared:
+        result["logical_attention_bytes_per_launch"] = int(np.mean(logical))
+        result["effective_logical_gbs"] = round(float(np.mean(logical)) / mean_main_s / 1e9, 1)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, cfg, lens0, kvbpt)
     print(json.dumps(result), flush=True)
+
+
+def main_kernel_name(dtype, head_dim, group, num_seqs):
+    """The library's dominant kernel for this shape (its dispatch rule, restated)."""
+    if dtype == "f32" or head_dim not in (64, 128) or group > 16:
+        return "decode_generic_kernel"
+    return "decode_persistent_kernel" if num_seqs <= 2048 else "decode_mfma_kernel"
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
+    profiles/hbm_traffic.txt, if they were taken on the current kernel source; else None."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    src = os.path.join(root, "paged_kv_cache_358_amd", "csrc", "decode_attention.hip")
+    table = os.path.join(root, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(table):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for line in open(table):
+        f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
+        if f.get("kernel") == kernel and f.get("workload") == workload and f.get("source_sha256") == sha:
+            return int(f["traffic_bytes"])
+    return None
 
 
 def cpu_baseline(args, cfg, lens0, kvbpt):
@@ -234,25 +280,33 @@ def cpu_baseline(args, cfg, lens0, kvbpt):
         lens = lens0.tolist()
     q = synth.queries(cfg) if lens0 is not None else cfg.step_q(cfg.steps)
     order = np.random.default_rng(0).permutation(len(lens))
+    # One pass over the sequences; each is drawn once and the oracle is re-run on it until its
+    # share of the time budget is used (at least once), so memory stays one sequence deep.
+    share = args.cpu_seconds / len(order)
     spent, done, ctx_tokens = 0.0, 0, 0
     with threadpool_limits(limits=1):
-        for s in order:
+        for i, s in enumerate(order):
             k, v = draw(int(s))
             k64, v64 = synth.decode_f64(k, cfg.dtype), synth.decode_f64(v, cfg.dtype)
             q64 = synth.decode_f64(q[s], cfg.dtype)
-            t = time.perf_counter()
-            decode_attention_seq(q64, k64, v64, cfg.softmax_scale)
-            spent += time.perf_counter() - t
-            done += 1
-            ctx_tokens += int(lens[s])
-            if spent >= args.cpu_seconds:
-                break
+            mine = 0.0
+            while mine < share or mine == 0.0:
+                t = time.perf_counter()
+                decode_attention_seq(q64, k64, v64, cfg.softmax_scale)
+                mine += time.perf_counter() - t
+                done += 1
+                ctx_tokens += int(lens[s])
+            spent += mine
+            if i % 16 == 15 or i == len(order) - 1:
+                print(f"[bench] cpu baseline: {i + 1}/{len(order)} sequences, {spent:.1f} s", file=sys.stderr,
+                      flush=True)
     gbs = ctx_tokens * kvbpt / spent / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seq_tokens_per_s_per_layer": round(done / spent, 2),
-            "sample": f"fp64 oracle over {done} of {len(lens)} sequences (all {cfg.num_q_heads} query heads, "
-                      f"{ctx_tokens} context tokens), {spent:.1f} s on 1 host thread; inputs decoded to "
-                      f"float64 beforehand"}
+            "sample": f"fp64 oracle, {done} sequence evaluations over all {len(lens)} sequences of the "
+                      f"workload (each drawn once and evaluated until it had {share:.2f} s; all "
+                      f"{cfg.num_q_heads} query heads; {ctx_tokens} context tokens in total), {spent:.1f} s "
+                      f"on 1 host thread; inputs decoded to float64 beforehand"}
 
 
 if __name__ == "__main__":

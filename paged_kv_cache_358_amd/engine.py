@@ -128,4 +128,5 @@ class PagedDecodeLayer:
             if timing is not None:
                 timing[2].record(self.stream)
         self.last_lens = np_lens.copy()
+        self.last_tables = np_tables  # view into the pinned staging buffer: valid until two steps later
         return npairs
