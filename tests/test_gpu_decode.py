@@ -162,3 +162,50 @@ def test_full_c3_gqa_sampled():
 
 def test_full_c5_long_context_sampled():
     _sampled_check(synth.C5, 2, 3, 5)
+
+
+# ----------------------------------------------------------------- scheduling paths of the MFMA kernels
+def test_more_sequences_than_the_persistent_index_covers():
+    # 2100 sequences (> 2048) take the one-workgroup-per-partition kernel, with partials
+    # (256-token partitions, contexts up to 700).
+    lens = np.random.default_rng(11).integers(1, 700, size=2100)
+    cfg = synth.DecodeConfig("many_seqs", 41, 2100, 8, 2, 64, "bf16", "fixed", tuple(int(x) for x in lens),
+                             partition_size=256)
+    pd = PagedDecode(cfg)
+    out = pd.run()
+    assert torch.isfinite(out).all()
+    picks = np.random.default_rng(12).choice(cfg.num_seqs, size=60, replace=False)
+    assert max_err(out, pd, seqs=picks.tolist()) <= 5e-3
+
+
+def test_mixed_empty_short_and_long_contexts():
+    # Zero-length, one-token, partial-block and multi-partition contexts side by side:
+    # the persistent split cuts runs inside long contexts and the merge recombines them.
+    rng = np.random.default_rng(13)
+    lens = [0, 1, 17, 5000, 0, 2, 3000, 16, 700, 4097] + rng.integers(1, 300, size=50).tolist()
+    cfg = synth.scaled(synth.C3, lens=lens)
+    pd = PagedDecode(cfg)
+    out = pd.run()
+    o = out.cpu().numpy()
+    assert np.all(o[0] == 0) and np.all(o[4] == 0)
+    assert max_err(out, pd, seqs=[s for s in range(cfg.num_seqs) if lens[s] > 0]) <= 5e-3
+
+
+def test_fewer_blocks_than_workgroups():
+    # A few blocks in all: most workgroups of the persistent grid own no partition.
+    cfg = synth.DecodeConfig("tiny_bf16", 42, 2, 4, 4, 128, "bf16", "fixed", (3, 40))
+    pd = PagedDecode(cfg)
+    out = pd.run()
+    assert max_err(out, pd) <= 5e-3
+
+
+@pytest.mark.parametrize("part", [16, 128])
+def test_long_context_small_partitions(part):
+    # Many partitions per context: runs hold several partitions merged on chip.
+    cfg = synth.scaled(synth.C5, lens=[20000, 7777], partition_size=part)
+    pd = PagedDecode(cfg, keep_truth=False)
+    out = pd.run().cpu().numpy()
+    for s in range(2):
+        heads = [0, 9, 63]
+        ref = pd.oracle_sampled(s, heads)
+        assert np.max(np.abs(out[s, heads] - ref)) <= 5e-3
