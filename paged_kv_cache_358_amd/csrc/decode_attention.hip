@@ -504,20 +504,21 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   // without waiting for them.  The table read is clamped into the row so that it is
   // issued unconditionally; query columns >= g repeat head 0 of the group (their scores
   // only feed their own, discarded, columns).
-  auto prepare = [&](int64_t off, Slot& sl) {
+  // Fill a slot with partition p of (sequence s, KV head h) and issue the loads of its block
+  // ids and query without waiting for them.  ok = false gives an empty slot (its loads still
+  // go to valid addresses, row 0).
+  auto fill = [&](Slot& sl, bool ok, int s, int h, int p) {
     Item& it = sl.it;
     it = Item{0, 0, 0, 0, 0, 0, 1, 0};
-    sl.ok = off < hi;
-    if (sl.ok) {
-      const int s = seq_of(off);
+    sl.ok = ok;
+    if (ok) {
       const int nb = __builtin_amdgcn_readfirstlane(nb_s[s]);
-      const int r = static_cast<int>(off - __builtin_amdgcn_readfirstlane(blkpre[s]));
       it.s = s;
-      it.h = r / nb;
-      it.p = (r % nb) / PB;
+      it.h = h;
+      it.p = p;
       it.n = __builtin_amdgcn_readfirstlane(ctx_s[s]);
       it.np = (nb + PB - 1) / PB;
-      it.b0 = it.p * PB;
+      it.b0 = p * PB;
       it.len = min(PB, nb - it.b0);
       it.my_n = (it.len > w) ? (it.len - w + kWaves - 1) / kWaves : 0;
     }
@@ -529,6 +530,21 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     const int64_t qrow = (static_cast<int64_t>(it.s) * a.hq + it.h * g + (col < g ? col : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) sl.q[kk] = *reinterpret_cast<const u32x4_t*>(qp + qrow + (kk * 4 + grp) * 8);
+  };
+  // The partition after `cur` in (sequence, KV head, partition) order, at global block
+  // offset off (= cur's offset + cur.len); empty when off reaches the end of the run.
+  auto prepare_next = [&](const Item& cur, int64_t off, Slot& sl) {
+    int s = cur.s, h = cur.h, p = cur.p + 1;
+    if (p >= cur.np) {
+      p = 0;
+      if (++h >= hkv) {
+        h = 0;
+        const bool more = off < hi;  // then a sequence with blocks follows
+        do ++s; while (more && s < S && __builtin_amdgcn_readfirstlane(nb_s[s]) == 0);
+        if (s >= S) s = 0;
+      }
+    }
+    fill(sl, off < hi, s, h, p);
   };
 
   const uint8_t* kc = static_cast<const uint8_t*>(a.k);
@@ -629,7 +645,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
           phys = __builtin_amdgcn_readlane(cur_ids, la < 63 ? la : 63);
         }
         load_tile(ring[(j + NBUF - 1) % NBUF], phys, la, mn, hh);
-        compute(ring[j], i + j);
+        if (i + j < cur.my_n) compute(ring[j], i + j);  // positions past my_n only pad the ring
       }
     }
 
@@ -706,7 +722,18 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     off = __builtin_amdgcn_readfirstlane(blkpre[s]) + static_cast<int64_t>(h) * nb + b;
   }
   Slot A, B;
-  prepare(off, A);
+  {
+    const bool ok = off < hi;
+    int s0 = 0, h0 = 0, p0 = 0;
+    if (ok) {
+      s0 = seq_of(off);
+      const int nb = __builtin_amdgcn_readfirstlane(nb_s[s0]);
+      const int r = static_cast<int>(off - __builtin_amdgcn_readfirstlane(blkpre[s0]));
+      h0 = r / nb;
+      p0 = (r % nb) / PB;
+    }
+    fill(A, ok, s0, h0, p0);
+  }
   if (!A.ok) return;  // the run holds no partition start
 #pragma unroll
   for (int nn = 0; nn < NV; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -714,16 +741,16 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int j = 0; j < NBUF - 1; ++j) load_tile(ring[j], __builtin_amdgcn_readlane(A.ids, j), j, A.it.my_n, A.it.h);
   off += A.it.len;
-  prepare(off, B);
+  prepare_next(A.it, off, B);
   while (true) {
     run(A.it, A.ids, A.q, B.it, B.ok, B.ids);
     if (!B.ok) break;
     off += B.it.len;
-    prepare(off, A);
+    prepare_next(B.it, off, A);
     run(B.it, B.ids, B.q, A.it, A.ok, A.ids);
     if (!A.ok) break;
     off += A.it.len;
-    prepare(off, B);
+    prepare_next(A.it, off, B);
   }
 }
 

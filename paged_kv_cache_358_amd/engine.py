@@ -20,19 +20,37 @@ from . import (BlockAllocator, alloc_kv_cache, block_copy, kv_append, paged_atte
 
 
 class _Staging:
-    """Pinned host buffers + device buffers for one step's metadata."""
+    """One pinned host buffer and one device buffer holding a step's metadata, int32:
+    context lengths [max_seqs] | slots [max_tokens] | copy pairs [max_seqs, 2] | block
+    tables [max_seqs, max_blocks].  A step moves the used prefix in one host->device copy."""
 
     def __init__(self, max_seqs: int, max_blocks: int, max_tokens: int, device):
-        pin = dict(dtype=torch.int32, pin_memory=True)
-        self.h_slots = torch.empty(max_tokens, **pin)
-        self.h_pairs = torch.empty(max_seqs, 2, **pin)
-        self.h_tables = torch.empty(max_seqs, max_blocks, **pin)
-        self.h_lens = torch.empty(max_seqs, **pin)
-        self.d_slots = torch.empty(max_tokens, dtype=torch.int32, device=device)
-        self.d_pairs = torch.empty(max_seqs, 2, dtype=torch.int32, device=device)
-        self.d_tables = torch.empty(max_seqs, max_blocks, dtype=torch.int32, device=device)
-        self.d_lens = torch.empty(max_seqs, dtype=torch.int32, device=device)
+        self.o_lens = 0
+        self.o_slots = max_seqs
+        self.o_pairs = self.o_slots + max_tokens
+        self.o_tables = self.o_pairs + 2 * max_seqs
+        total = self.o_tables + max_seqs * max_blocks
+        self.max_blocks = max_blocks
+        self.host = torch.empty(total, dtype=torch.int32, pin_memory=True)
+        self.dev = torch.empty(total, dtype=torch.int32, device=device)
+        h = self.host.numpy()
+        self.h_lens = h[self.o_lens:self.o_slots]
+        self.h_slots = h[self.o_slots:self.o_pairs]
+        self.h_pairs = h[self.o_pairs:self.o_tables].reshape(max_seqs, 2)
+        self.h_tables = h[self.o_tables:].reshape(max_seqs, max_blocks)
         self.done = None  # event recorded after this buffer's last host->device copy
+
+    def d_lens(self, n):
+        return self.dev[self.o_lens:self.o_lens + n]
+
+    def d_slots(self, n):
+        return self.dev[self.o_slots:self.o_slots + n]
+
+    def d_pairs(self, n):
+        return self.dev[self.o_pairs:self.o_pairs + 2 * n].view(n, 2)
+
+    def d_tables(self, n):
+        return self.dev[self.o_tables:self.o_tables + n * self.max_blocks].view(n, self.max_blocks)
 
 
 class PagedDecodeLayer:
@@ -96,11 +114,10 @@ class PagedDecodeLayer:
         self._turn ^= 1
         if st.done is not None:
             st.done.synchronize()  # previous copies out of this pinned buffer have finished
-        slots, pairs = self.alloc.append_batch(seqs, np.ones(S, np.int32), st.h_slots.numpy(),
-                                               st.h_pairs.numpy())
-        np_tables = st.h_tables.numpy()[:S]
-        np_lens = st.h_lens.numpy()[:S]
+        slots, pairs = self.alloc.append_batch(seqs, np.ones(S, np.int32), st.h_slots, st.h_pairs)
         t, l = self.alloc.build_batch(seqs, self.max_blocks)
+        np_tables = st.h_tables[:S]
+        np_lens = st.h_lens[:S]
         np_tables[...] = t
         np_lens[...] = l
         max_ctx = 0
@@ -108,20 +125,17 @@ class PagedDecodeLayer:
             self.max_len[s] += 1
             max_ctx = max(max_ctx, self.max_len[s])
         npairs = len(pairs)
+        used = st.o_tables + S * self.max_blocks  # lengths, slots, pairs and the first S table rows
         with torch.cuda.stream(self.stream):
-            st.d_slots[:S].copy_(st.h_slots[:S], non_blocking=True)
-            st.d_tables[:S].copy_(st.h_tables[:S], non_blocking=True)
-            st.d_lens[:S].copy_(st.h_lens[:S], non_blocking=True)
-            if npairs:
-                st.d_pairs[:npairs].copy_(st.h_pairs[:npairs], non_blocking=True)
+            st.dev[:used].copy_(st.host[:used], non_blocking=True)
             st.done = torch.cuda.Event()
             st.done.record(self.stream)
             if npairs:
-                block_copy(self.k_cache, self.v_cache, st.d_pairs[:npairs], stream=self.stream)
-            kv_append(k_new, v_new, st.d_slots[:S], self.k_cache, self.v_cache, stream=self.stream)
+                block_copy(self.k_cache, self.v_cache, st.d_pairs(npairs), stream=self.stream)
+            kv_append(k_new, v_new, st.d_slots(S), self.k_cache, self.v_cache, stream=self.stream)
             if timing is not None:
                 timing[0].record(self.stream)
-            paged_attention_decode(q, self.k_cache, self.v_cache, st.d_tables[:S], st.d_lens[:S], scale, out,
+            paged_attention_decode(q, self.k_cache, self.v_cache, st.d_tables(S), st.d_lens(S), scale, out,
                                    max_context_len=max_ctx, partition_size=self.partition_size,
                                    workspace=self.workspace, stream=self.stream,
                                    timing_event=None if timing is None else timing[1])
