@@ -238,7 +238,7 @@ def main_kernel_name(dtype, head_dim, group, num_seqs):
     """The library's dominant kernel for this shape (its dispatch rule, restated)."""
     if dtype == "f32" or head_dim not in (64, 128) or group > 16:
         return "decode_generic_kernel"
-    return "decode_persistent_kernel" if num_seqs <= 2048 else "decode_mfma_kernel"
+    return "decode_split_kernel" if num_seqs <= 2048 else "decode_mfma_kernel"
 
 
 def measured_traffic(kernel, workload):

@@ -68,8 +68,9 @@ struct DecodeArgs {
   int32_t max_parts;
   int32_t out_f32;
   int64_t num_blocks;
-  int32_t* run_pre;   // persistent split: H_kv-scaled block prefix sums [S + 1] (workspace)
-  int32_t run_grid;   // persistent split: workgroups of the main kernel; 0 = one run per partition
+  int32_t* run_pre;   // split: H_kv-scaled block prefix sums [S + 1] (workspace)
+  int32_t run_grid;   // split: chunks (workgroups) of the main kernel; 0 = one run per partition
+  int32_t run_rounds; // split: rounds of the chunk schedule
 };
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s) {
@@ -371,22 +372,37 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
   }
 }
 
-// ------------------------------------------------------------------ persistent MFMA path
+// ------------------------------------------------------------------ split MFMA path
 
-constexpr int kMaxScanSeqs = 2048;  // sequences the persistent kernel's in-LDS index covers
-constexpr int kPersistRing = 2;     // ring depth of the persistent kernel
+constexpr int kMaxScanSeqs = 2048;  // sequences the split kernel's in-LDS index covers
+constexpr int kPersistRing = 2;     // ring depth of the split kernel
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X, each with its own L2
 
-// Work split of the persistent kernel.  The partitions of all (sequence, KV head) pairs
-// are laid end to end in (sequence, KV head, partition) order, each weighted by its
-// block count; W is the total.  Workgroup k of G owns the partitions whose first block
-// lies in [k*W/G, (k+1)*W/G): a contiguous run, so each workgroup streams about W/G
-// blocks.  Consecutive partitions of one (sequence, KV head) inside a workgroup's run are
-// merged on chip (the online softmax simply continues); only where a run ends inside a
-// sequence's context is a partial (max, sum, output) written, to the slot of the run's
-// first partition.  run_owner / run_lo below are shared with the merge kernel.
-__device__ __forceinline__ int64_t run_lo(int64_t k, int64_t W, int64_t G) { return k * W / G; }
-__device__ __forceinline__ int64_t run_owner(int64_t off, int64_t W, int64_t G) { return ((off + 1) * G - 1) / W; }
+// Work split.  The partitions of all (sequence, KV head) pairs are laid end to end in
+// (sequence, KV head, partition) order, each weighted by its block count; W is the total.
+// The split cuts [0, W) into chunks of decreasing size: NR rounds of R chunks (R = the
+// workgroups resident at once), round r covering [W - W/2^r, W - W/2^(r+1)) (the last round
+// runs to W), so the first chunks take half the work and the last ones fill the tail.  One
+// workgroup per chunk owns the partitions whose first block lies in the chunk: a contiguous
+// run.  Consecutive partitions of one (sequence, KV head) inside a run are merged on chip
+// (the online softmax simply continues); only where a run ends inside a sequence's context
+// is a partial (max, sum, output) written, to the slot of the run's first partition.
+// chunk_lo / chunk_owner are shared with the merge kernel.
+__device__ __forceinline__ int64_t chunk_lo(int64_t j, int64_t W, int R, int NR) {
+  const int r = static_cast<int>(j / R), t = static_cast<int>(j % R);
+  if (r >= NR) return W;
+  const int64_t T0 = W - (W >> r);
+  const int64_t T1 = (r + 1 >= NR) ? W : W - (W >> (r + 1));
+  return T0 + (T1 - T0) * t / R;
+}
+// The chunk whose range holds global block offset off (0 <= off < W).
+__device__ __forceinline__ int64_t chunk_owner(int64_t off, int64_t W, int R, int NR) {
+  int r = 0;
+  while (r + 1 < NR && W - (W >> (r + 1)) <= off) ++r;
+  const int64_t T0 = W - (W >> r);
+  const int64_t T1 = (r + 1 >= NR) ? W : W - (W >> (r + 1));
+  return static_cast<int64_t>(r) * R + ((off - T0 + 1) * R - 1) / (T1 - T0);
+}
 
 // One partition of one (sequence, KV head) as a workgroup sees it.
 struct Item {
@@ -395,16 +411,15 @@ struct Item {
   int32_t np, len;     // partitions of the sequence; blocks in this partition
 };
 
-// Persistent form of the MFMA kernel: about (CUs x resident workgroups) workgroups each
-// walk their run of partitions.  Each wave keeps a ring of NBUF register sets that
-// looks NBUF-1 positions ahead across partition boundaries, so the next partition's
-// first blocks are already loading while the current one finishes.  The next
-// partition's block ids and query are loaded one partition ahead into the other of two
-// slots (A/B), so no loaded value is copied before it is used.  Per-block arithmetic is
-// that of decode_mfma_kernel.
+// Split form of the MFMA kernel: one workgroup per chunk of the schedule above walks its run
+// of partitions.  Each wave keeps a ring of NBUF register sets that looks NBUF-1 positions
+// ahead across partition boundaries, so the next partition's first blocks are already
+// loading while the current one finishes.  The next partition's block ids and query are
+// loaded one partition ahead into the other of two slots (A/B), so no loaded value is copied
+// before it is used.  Per-block arithmetic is that of decode_mfma_kernel.
 // At least two waves per SIMD: the compiler keeps the kernel within 256 VGPRs.
 template <int DT, int D, int NBUF>
-__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_persistent_kernel(
+__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(
     DecodeArgs a) {
   constexpr int KK = D / 32;
   constexpr int NV = D / 16;
@@ -427,11 +442,18 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   const int PB = a.part_blocks;
   const int hkv = a.hkv;
   const int g = a.group;
-  const int G = gridDim.x;
-  // Run k of the split.  Workgroups are dealt to the 8 XCDs round-robin (workgroup i on XCD
-  // i % 8); giving XCD x the runs [x*G/8, (x+1)*G/8) keeps neighbouring runs (e.g. samples
-  // forked from one prompt, which share its blocks) on one XCD and its L2 while they run.
-  const int k = (G % kXcds == 0) ? (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds : blockIdx.x;
+  const int J = gridDim.x;          // chunks = NR rounds of R
+  const int NR = a.run_rounds;
+  const int R = J / NR;
+  // Chunk k of the split.  Workgroups are dealt to the 8 XCDs round-robin (workgroup i on XCD
+  // i % 8); within a round, giving XCD x the chunks [x*R/8, (x+1)*R/8) keeps neighbouring
+  // runs (e.g. samples forked from one prompt, which share its blocks) on one XCD and its L2
+  // while they run.
+  int k = blockIdx.x;
+  if (R % kXcds == 0) {
+    const int r = k / R, t = k % R;
+    k = r * R + (t % kXcds) * (R / kXcds) + t / kXcds;
+  }
 
   // ---- prefix sums of blocks over sequences (every workgroup builds its own copy)
   const int per = (S + kThreads - 1) / kThreads;
@@ -467,17 +489,18 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   const int W = __builtin_amdgcn_readfirstlane(blkpre[S]);
 
   // The merge kernel recomputes run boundaries from the same prefix sums.
-  if (k == 0 && a.run_pre != nullptr)
+  if (blockIdx.x == 0 && a.run_pre != nullptr)
     for (int s = tid; s <= S; s += kThreads) a.run_pre[s] = blkpre[s];
   // Zero-length sequences own no partition: their output is 0.
-  for (int s = k; s < S; s += G) {
+  for (int s = blockIdx.x; s < S; s += J) {
     if (ctx_s[s] == 0)
       for (int i = tid; i < a.hq * D; i += kThreads) store_out<DT>(a, static_cast<int64_t>(s) * a.hq * D + i, 0.0f);
   }
   if (W == 0) return;
 
-  const int64_t lo = run_lo(k, W, G);
-  const int64_t hi = run_lo(k + 1, W, G);
+  const int64_t lo = chunk_lo(k, W, R, NR);
+  const int64_t hi = chunk_lo(k + 1, W, R, NR);
+  if (lo >= hi) return;  // an empty chunk (small W): no partition starts in it
 
   // Sequence holding global block offset off: the last s with blkpre[s] <= off (that skips
   // zero-length sequences, which share their successor's prefix).
@@ -849,15 +872,19 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ partition merge
 
-// One workgroup per (sequence, KV head) with more than one partition merges the partials
-// of that sequence's runs, for all g query heads of the KV head:
+constexpr int kMaxRuns = 1024;  // runs per context whose starts the merge keeps in LDS (more: recomputed)
+
+// One workgroup per (sequence, KV head, column slice) with more than one partition merges
+// the partials of that sequence's runs for its slice of the g query heads x D outputs:
 //   M = max_r m_r,  w_r = 2^(m_r - M) * l_r,  out = sum_r w_r * O_r / sum_r w_r
-// where O_r is run r's normalised output (done as an online merge, in a fixed order:
-// deterministic).  A run is one partition (run_grid == 0) or the stretch of partitions one
-// workgroup of the persistent kernel streamed; its partial sits at the slot of its first
-// partition.  Zero-length and single-run sequences were written by the main kernel.
+// where O_r is run r's normalised output.  A run is one partition (run_grid == 0) or the
+// stretch of partitions one chunk of the split kernel streamed; its partial sits at the slot
+// of its first partition.  Threads form RG groups that take every RG-th run, merge online,
+// then combine in a fixed order: deterministic.  Zero-length and single-run sequences were
+// written by the main kernel.
 template <int DT>
 __global__ __launch_bounds__(256) void reduce_partitions_kernel(DecodeArgs a) {
+  __shared__ int32_t ps[kMaxRuns + 1];  // run i covers partitions [ps[i], ps[i + 1])
   __shared__ float red_m[256];
   __shared__ float red_l[256];
   __shared__ __attribute__((aligned(16))) f32x4_t red_o[256];
@@ -871,78 +898,85 @@ __global__ __launch_bounds__(256) void reduce_partitions_kernel(DecodeArgs a) {
   if (np <= 1) return;
   const int D = a.head_dim;
   const int g = a.group;
+  const int tid = threadIdx.x;
 
   const bool split = a.run_grid > 0;
-  const int64_t G = a.run_grid;
-  int64_t W = 0, A = 0;
-  int k0 = 0, k1 = np - 1;  // runs k0..k1 (partitions themselves when !split)
+  int64_t W = 0, A = 0, k0 = 0;
+  int R = 1, NR = 1, nruns = np;
   if (split) {
     W = a.run_pre[a.num_seqs];
     A = a.run_pre[s] + static_cast<int64_t>(kvh) * nb;
-    k0 = static_cast<int>(run_owner(A, W, G));
-    k1 = static_cast<int>(run_owner(A + static_cast<int64_t>(np - 1) * PB, W, G));
+    NR = a.run_rounds;
+    R = a.run_grid / NR;
+    k0 = chunk_owner(A, W, R, NR);
+    const int64_t k1 = chunk_owner(A + static_cast<int64_t>(np - 1) * PB, W, R, NR);
     if (k0 == k1) return;
+    nruns = static_cast<int>(k1 - k0 + 1);
   }
-  // First partition of run k (k in k0..k1+1; run k1+1 starts past the end).
-  auto run_start = [&](int k) -> int {
-    if (k > k1) return np;
-    if (!split) return k;
-    if (k == k0) return 0;
-    return static_cast<int>((run_lo(k, W, G) - A + PB - 1) / PB);
+  // First partition of run i (i in 0..nruns; run nruns starts past the end).
+  auto run_start = [&](int i) -> int {
+    if (i >= nruns) return np;
+    if (!split) return i;
+    if (i == 0) return 0;
+    return static_cast<int>((chunk_lo(k0 + i, W, R, NR) - A + PB - 1) / PB);
   };
+  const bool in_lds = nruns <= kMaxRuns;
+  if (in_lds)
+    for (int i = tid; i <= nruns; i += 256) ps[i] = run_start(i);
+  __syncthreads();
 
   const int nout4 = g * D / 4;
-  const int C = nout4 < 256 ? nout4 : 256;
-  const int RG = 256 / C;  // run groups: threads of group rg take runs k0+rg, k0+rg+RG, ...
-  const int tid = threadIdx.x;
+  const int C = (nout4 + gridDim.y - 1) / gridDim.y;  // columns per slice, <= 256
+  const int c_begin = blockIdx.y * C;
+  const int RG = 256 / C;  // run groups
   const int rg = tid / C;
-  const int col4 = tid % C;
-  for (int c4 = col4; c4 < nout4; c4 += C) {  // a single pass unless g*D/4 > 256 (then RG == 1)
-    const int cc = c4 / (D / 4), d0 = (c4 % (D / 4)) * 4;
-    const int64_t row = static_cast<int64_t>(s) * a.hq + kvh * g + cc;
-    float M = -INFINITY, L = 0.f;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (rg < RG) {
-      for (int k = k0 + rg; k <= k1; k += RG) {
-        const int ps = run_start(k);
-        if (ps >= run_start(k + 1)) continue;  // a workgroup whose stretch starts no partition here
-        const int64_t prow = row * a.max_parts + ps;
-        const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(a.part_ml + prow * 2);
-        const f32x4_t O = *reinterpret_cast<const f32x4_t*>(a.part_o + prow * D + d0);
-        if (!(ml[1] > 0.f)) continue;
-        const float Mn = fmaxf(M, ml[0]);
+  const int c4 = c_begin + tid % C;
+  const bool active = rg < RG && c4 < nout4;
+  const int cc = active ? c4 / (D / 4) : 0, d0 = active ? (c4 % (D / 4)) * 4 : 0;
+  const int64_t row = static_cast<int64_t>(s) * a.hq + kvh * g + cc;
+  float M = -INFINITY, L = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    for (int i = rg; i < nruns; i += RG) {
+      const int p0 = in_lds ? ps[i] : run_start(i);
+      const int p1 = in_lds ? ps[i + 1] : run_start(i + 1);
+      if (p0 >= p1) continue;  // a chunk that starts no partition of this context
+      const int64_t prow = row * a.max_parts + p0;
+      const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(a.part_ml + prow * 2);
+      const f32x4_t O = *reinterpret_cast<const f32x4_t*>(a.part_o + prow * D + d0);
+      if (!(ml[1] > 0.f)) continue;
+      const float Mn = fmaxf(M, ml[0]);
+      const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      const float wr = __builtin_amdgcn_exp2f(ml[0] - Mn) * ml[1];
+      acc = acc * sc + O * wr;
+      L = L * sc + wr;
+      M = Mn;
+    }
+  }
+  if (RG > 1) {
+    red_m[tid] = M;
+    red_l[tid] = L;
+    red_o[tid] = acc;
+    __syncthreads();
+    if (active && rg == 0) {
+      for (int r = 1; r < RG; ++r) {
+        const int t = r * C + tid;
+        if (!(red_l[t] > 0.f)) continue;
+        const float mr = red_m[t];
+        const float Mn = fmaxf(M, mr);
         const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-        const float wr = __builtin_amdgcn_exp2f(ml[0] - Mn) * ml[1];
-        acc = acc * sc + O * wr;
-        L = L * sc + wr;
+        const float sr = __builtin_amdgcn_exp2f(mr - Mn);
+        acc = acc * sc + red_o[t] * sr;
+        L = L * sc + red_l[t] * sr;
         M = Mn;
       }
     }
-    if (RG > 1) {
-      red_m[tid] = M;
-      red_l[tid] = L;
-      red_o[tid] = acc;
-      __syncthreads();
-      if (rg == 0) {
-        for (int r = 1; r < RG; ++r) {
-          const int t = r * C + col4;
-          const float mr = red_m[t];
-          if (!(red_l[t] > 0.f)) continue;
-          const float Mn = fmaxf(M, mr);
-          const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-          const float sr = __builtin_amdgcn_exp2f(mr - Mn);
-          acc = acc * sc + red_o[t] * sr;
-          L = L * sc + red_l[t] * sr;
-          M = Mn;
-        }
-      }
-    }
-    if (rg == 0) {
-      f32x4_t res;
+  }
+  if (active && rg == 0) {
+    f32x4_t res;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) res[e] = L > 0.f ? acc[e] / L : 0.f;
-      store_out4<DT>(a, row * D + d0, res);
-    }
+    for (int e = 0; e < 4; ++e) res[e] = L > 0.f ? acc[e] / L : 0.f;
+    store_out4<DT>(a, row * D + d0, res);
   }
 }
 
@@ -983,7 +1017,7 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
   out->part_blocks = pt / kBlockTokens;
   out->ctx_limit = limit;
   out->max_parts = parts;
-  // Partials [S][H_q][parts][D] and [S][H_q][parts][2] (fp32), then the persistent split's
+  // Partials [S][H_q][parts][D] and [S][H_q][parts][2] (fp32), then the split kernel's
   // block prefix sums [S + 1] (int32).
   const size_t rows = static_cast<size_t>(p->num_seqs) * p->num_q_heads * parts;
   out->prefix_offset = rows * (static_cast<size_t>(c.head_dim) + 2) * sizeof(float);
@@ -995,11 +1029,18 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 template <int DT>
 void launch_reduce(const DecodeArgs& args, hipStream_t st) {
-  hipLaunchKernelGGL(reduce_partitions_kernel<DT>, dim3(static_cast<uint32_t>(args.num_seqs) * args.hkv), dim3(256),
-                     0, st, args);
+  // Output columns (4 dims each) of one (sequence, KV head) are cut into slices so that each
+  // workgroup has at most 256 columns and, for few sequences, enough workgroups overall.
+  const int nout4 = args.group * args.head_dim / 4;
+  const int lo = (nout4 + 255) / 256;
+  const int hi = std::max(lo, nout4 / 32);
+  const int want = std::max(1, 2048 / std::max(1, args.num_seqs * args.hkv));
+  const int nsl = std::min(hi, std::max(lo, want));
+  hipLaunchKernelGGL(reduce_partitions_kernel<DT>, dim3(static_cast<uint32_t>(args.num_seqs) * args.hkv, nsl),
+                     dim3(256), 0, st, args);
 }
 
-// Workgroups of a persistent kernel that fit on the current device at once
+// Workgroups of a kernel that fit on the current device at once
 // (compute units x resident workgroups per CU), looked up once per (device, kernel).
 int32_t resident_workgroups(const void* kernel, int* out) {
   static std::mutex mu;
@@ -1023,17 +1064,22 @@ int32_t resident_workgroups(const void* kernel, int* out) {
   return PA_OK;
 }
 
+// Rounds of the split kernel's chunk schedule, each cut into one chunk per resident
+// workgroup.  One round (equal chunks) measured best on MI355X: later, smaller rounds even
+// out the finish times but add partials and workgroup start-up costs that outweigh that.
+constexpr int kSplitRounds = 1;
+
+// Launch the split kernel; sets args->run_grid / run_rounds for the merge kernel.
 template <int DT, int D>
-int32_t launch_persistent(const DecodeArgs& args, hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&decode_persistent_kernel<DT, D, kPersistRing>);
+int32_t launch_split(DecodeArgs* args, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&decode_split_kernel<DT, D, kPersistRing>);
   int resident = 0;
   const int32_t rc = resident_workgroups(fn, &resident);
   if (rc != PA_OK) return rc;
-  const int64_t items = int64_t{args.max_parts} * args.hkv * args.num_seqs;  // upper bound
-  DecodeArgs a = args;
-  a.run_grid = static_cast<int32_t>(std::min<int64_t>(items, resident));
-  hipLaunchKernelGGL((decode_persistent_kernel<DT, D, kPersistRing>), dim3(static_cast<uint32_t>(a.run_grid)),
-                     dim3(kWaves * kWave), 0, st, a);
+  args->run_rounds = kSplitRounds;
+  args->run_grid = kSplitRounds * resident;
+  hipLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing>), dim3(static_cast<uint32_t>(args->run_grid)),
+                     dim3(kWaves * kWave), 0, st, *args);
   return PA_OK;
 }
 
@@ -1041,23 +1087,15 @@ template <int DT>
 int32_t launch_decode(DecodeArgs args, hipStream_t st, void* timing_event) {
   const int64_t D = args.head_dim;
   const bool fast = DT != PA_F32 && (D == 64 || D == 128) && args.group <= 16;
-  // The persistent kernel indexes blocks of all (sequence, KV head) pairs with int32.
-  const bool persistent = fast && args.num_seqs <= kMaxScanSeqs &&
-                          int64_t{args.num_seqs} * args.hkv * args.max_blocks < 0x7fffffffLL;
+  // The split kernel indexes blocks of all (sequence, KV head) pairs with int32.
+  const bool split = fast && args.num_seqs <= kMaxScanSeqs &&
+                     int64_t{args.num_seqs} * args.hkv * args.max_blocks < 0x7fffffffLL;
   args.run_grid = 0;
-  if (persistent) {
-    if (int64_t{args.max_parts} * args.hkv * args.num_seqs > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  args.run_rounds = 0;
+  if (split) {
     if constexpr (DT != PA_F32) {
-      const int32_t rc = D == 64 ? launch_persistent<DT, 64>(args, st) : launch_persistent<DT, 128>(args, st);
+      const int32_t rc = D == 64 ? launch_split<DT, 64>(&args, st) : launch_split<DT, 128>(&args, st);
       if (rc != PA_OK) return rc;
-      // the merge kernel must see the grid the split was made for
-      int resident = 0;
-      const void* fn = D == 64 ? reinterpret_cast<const void*>(&decode_persistent_kernel<DT, 64, kPersistRing>)
-                               : reinterpret_cast<const void*>(&decode_persistent_kernel<DT, 128, kPersistRing>);
-      const int32_t rc2 = resident_workgroups(fn, &resident);
-      if (rc2 != PA_OK) return rc2;
-      args.run_grid = static_cast<int32_t>(
-          std::min<int64_t>(int64_t{args.max_parts} * args.hkv * args.num_seqs, resident));
     }
   } else if (fast) {
     const int64_t nwg = int64_t{args.max_parts} * args.hkv * args.num_seqs;
