@@ -158,6 +158,17 @@ int32_t kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapp
 int32_t block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                    const pa_cache_desc* cache, void* stream);
 
+/*
+ * pa_stage_copy: copy `bytes` (a multiple of 4) from src to dst with one kernel on `stream`.  It moves
+ * the host allocator's per-step output (block tables, context lengths, slot mapping, copy pairs) to
+ * the device ahead of kv_append / block_copy / paged_attention_decode, on the same queue as those
+ * kernels, so they need not wait on a separate copy engine.
+ *   src   pinned host memory the device can address (hipHostMalloc, torch pin_memory), 16-byte aligned;
+ *         it must stay unchanged until the copy has run (record an event after the call)
+ *   dst   device memory, 16-byte aligned
+ */
+int32_t pa_stage_copy(void* dst, const void* src, size_t bytes, void* stream);
+
 /* ----------------------------------------------------------------------- host block allocator */
 
 typedef struct pa_allocator pa_allocator;

@@ -49,6 +49,7 @@ SIGNATURES = {
     "paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, ctypes.POINTER(DecodeParams)]),
     "kv_append": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc), _vp]),
     "block_copy": (_i32, [_vp, _vp, _vp, _i32, ctypes.POINTER(CacheDesc), _vp]),
+    "pa_stage_copy": (_i32, [_vp, _vp, _sz, _vp]),
     "pa_alloc_create": (_i32, [_i32, _i32, _P32, _PAllocPtr]),
     "pa_alloc_destroy": (None, [_vp]),
     "pa_seq_add": (_i32, [_vp, _i64]),
@@ -244,6 +245,15 @@ def block_copy(k_cache, v_cache, pairs, *, stream=None):
            "block_copy")
 
 
+def stage_copy(dst, src, nbytes: int, *, stream=None):
+    """Copy nbytes from pinned host tensor src to device tensor dst with one kernel on the stream."""
+    if not dst.is_cuda or src.is_cuda or not src.is_pinned():
+        raise ValueError("stage_copy copies a pinned host tensor into a device tensor")
+    if nbytes > min(dst.numel() * dst.element_size(), src.numel() * src.element_size()):
+        raise ValueError("nbytes exceeds a buffer")
+    _check(lib.pa_stage_copy(_ptr(dst), _ptr(src), int(nbytes), _stream_ptr(stream)), "pa_stage_copy")
+
+
 # ----------------------------------------------------------------------------- allocator
 def _as_i32(a):
     a = np.ascontiguousarray(a, dtype=np.int32)
@@ -339,6 +349,7 @@ class BlockAllocator:
         return tables[:len(ids), :max_blocks], lens[:len(ids)]
 
 
-__all__ = ["paged_attention_decode", "paged_attention_workspace_bytes", "kv_append", "block_copy", "BlockAllocator",
+__all__ = ["paged_attention_decode", "paged_attention_workspace_bytes", "kv_append", "block_copy", "stage_copy",
+           "BlockAllocator",
            "alloc_kv_cache", "cache_shapes", "cache_desc", "PagedAttnError", "lib", "LIB_PATH", "SIGNATURES",
            "PA_F32", "PA_BF16", "PA_F16", "BLOCK_SIZE"]

@@ -67,6 +67,20 @@ __global__ __launch_bounds__(256) void block_copy_kernel(uint8_t* __restrict__ k
   *reinterpret_cast<u32x4_t*>(base + dst * block_bytes + off) = x;
 }
 
+
+// Copy bytes (a multiple of 4) from pinned host memory the device can address into device
+// memory, 16 bytes per thread and a tail of 4-byte words: one kernel on the caller's stream.
+__global__ __launch_bounds__(256) void stage_copy_kernel(uint32_t* __restrict__ dst, const uint32_t* __restrict__ src,
+                                                         int64_t words) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t v = i * 4;
+  if (v + 3 < words) {
+    *reinterpret_cast<u32x4_t*>(dst + v) = *reinterpret_cast<const u32x4_t*>(src + v);
+  } else {
+    for (int64_t w = v; w < words; ++w) dst[w] = src[w];
+  }
+}
+
 static bool cache_desc_ok(const pa_cache_desc* c) {
   if (!c || c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 || c->block_size <= 0) return false;
   if (!valid_dtype(c->dtype)) return false;
@@ -122,4 +136,26 @@ extern "C" int32_t block_copy(void* k_cache, void* v_cache, const int32_t* pairs
                      static_cast<hipStream_t>(stream), static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
                      pairs, cache->num_blocks, block_bytes, chunks);
   return PA_HIP_STATUS("block_copy", hipGetLastError());
+}
+
+extern "C" int32_t pa_stage_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (bytes == 0) return PA_OK;
+  if (!dst || !src || bytes % 4 != 0) return PA_ERR_INVALID_ARG;
+  if (!aligned16(dst) || !aligned16(src)) return PA_ERR_INVALID_ARG;
+  const int64_t words = static_cast<int64_t>(bytes / 4);
+  const int64_t threads = (words + 3) / 4;
+  if ((threads + 255) / 256 > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind
+  // src must be pinned host memory the device can address; use the address HIP reports for it.
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, src) != hipSuccess || attr.type != hipMemoryTypeHost ||
+      attr.devicePointer == nullptr) {
+    (void)hipGetLastError();
+    return PA_ERR_INVALID_ARG;
+  }
+  const uint32_t* dsrc = static_cast<const uint32_t*>(attr.devicePointer);
+  if (!aligned16(dsrc)) return PA_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(stage_copy_kernel, dim3(static_cast<uint32_t>((threads + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint32_t*>(dst), dsrc, words);
+  return PA_HIP_STATUS("pa_stage_copy", hipGetLastError());
 }

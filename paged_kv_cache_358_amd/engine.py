@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 from . import (BlockAllocator, alloc_kv_cache, block_copy, kv_append, paged_attention_decode,
-               paged_attention_workspace_bytes)
+               paged_attention_workspace_bytes, stage_copy)
 
 
 class _Staging:
@@ -29,7 +29,7 @@ class _Staging:
         self.o_slots = max_seqs
         self.o_pairs = self.o_slots + max_tokens
         self.o_tables = self.o_pairs + 2 * max_seqs
-        total = self.o_tables + max_seqs * max_blocks
+        total = (self.o_tables + max_seqs * max_blocks + 3) // 4 * 4
         self.max_blocks = max_blocks
         self.host = torch.empty(total, dtype=torch.int32, pin_memory=True)
         self.dev = torch.empty(total, dtype=torch.int32, device=device)
@@ -127,7 +127,7 @@ class PagedDecodeLayer:
         npairs = len(pairs)
         used = st.o_tables + S * self.max_blocks  # lengths, slots, pairs and the first S table rows
         with torch.cuda.stream(self.stream):
-            st.dev[:used].copy_(st.host[:used], non_blocking=True)
+            stage_copy(st.dev, st.host, used * 4, stream=self.stream)
             st.done = torch.cuda.Event()
             st.done.record(self.stream)
             if npairs:

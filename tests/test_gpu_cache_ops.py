@@ -1,5 +1,7 @@
 """kv_append and block_copy on the GPU against the oracle's paged-layout model,
 byte for byte."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -76,3 +78,23 @@ def test_block_copy_empty():
     pa.block_copy(k_cache, v_cache, torch.empty(0, 2, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert np.array_equal(raw_view(k_cache), storage_raw(kh, "bf16"))
+
+
+def test_stage_copy_moves_pinned_host_words():
+    import paged_kv_cache_358_amd as pa
+    host = torch.arange(1, 1 + 4099, dtype=torch.int32).pin_memory()  # 4099 words: vector part + tail
+    dev = torch.full((4100,), -7, dtype=torch.int32, device="cuda")
+    pa.stage_copy(dev, host, 4099 * 4)
+    torch.cuda.synchronize()
+    got = dev.cpu()
+    assert torch.equal(got[:4099], host) and got[4099].item() == -7
+
+
+def test_stage_copy_rejects_pageable_source():
+    import paged_kv_cache_358_amd as pa
+    host = torch.arange(64, dtype=torch.int32)  # pageable: not addressable by the device
+    dev = torch.empty(64, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        pa.stage_copy(dev, host, 256)
+    rc = pa.lib.pa_stage_copy(ctypes.c_void_p(dev.data_ptr()), ctypes.c_void_p(host.data_ptr()), 256, None)
+    assert rc == pa.PA_ERR_INVALID_ARG
