@@ -104,9 +104,9 @@ const char* pa_last_error(void);
 
 /* Device workspace bytes paged_attention_decode needs for these parameters: when more than one partition
  * can occur, P = num_seqs * H_q * ceil(max_context_len / partition_size) fp32 partial rows of head_dim + 2
- * values (P * (head_dim + 2) * 4 bytes) followed by num_seqs + 1 int32 (the block prefix sums the
- * partition merge uses); else 0.  Returns 0 for invalid parameters (the decode call then reports the
- * error).  The contents need no initialisation and are scratch between calls. */
+ * values (P * (head_dim + 2) * 4 bytes), then num_seqs * H_kv uint64 arrival counters; else 0.  Returns 0 for invalid parameters (the decode
+ * call then reports the error).  The contents need no initialisation (the counters carry a per-call tag)
+ * and are scratch between calls; two calls in flight at once must not share a workspace. */
 size_t paged_attention_workspace_bytes(const pa_decode_params* p);
 
 /*

@@ -339,14 +339,23 @@ class BlockAllocator:
                "pa_free_list")
         return out[:n.value].tolist()
 
-    def build_batch(self, seqs, max_blocks: int):
-        """(tables int32[n, max_blocks] padded with -1, lens int32[n])."""
+    def build_batch(self, seqs, max_blocks: int, tables_out=None, lens_out=None):
+        """(tables int32[n, max_blocks] padded with -1, lens int32[n]).  ``tables_out`` /
+        ``lens_out`` (C-contiguous int32 of at least that shape) receive them in place."""
         ids = np.ascontiguousarray(seqs, dtype=np.int64)
-        tables = np.empty((max(len(ids), 1), max(max_blocks, 1)), np.int32)
-        lens = np.empty(max(len(ids), 1), np.int32)
-        _check(lib.pa_build_batch(self._h, ids.ctypes.data_as(_P64), len(ids), max_blocks,
-                                  tables.ctypes.data_as(_P32), lens.ctypes.data_as(_P32)), "pa_build_batch")
-        return tables[:len(ids), :max_blocks], lens[:len(ids)]
+        n = len(ids)
+        if tables_out is None:
+            tables_out = np.empty((max(n, 1), max(max_blocks, 1)), np.int32)
+        if lens_out is None:
+            lens_out = np.empty(max(n, 1), np.int32)
+        for arr, shape in ((tables_out, (n, max_blocks)), (lens_out, (n,))):
+            if (arr.dtype != np.int32 or not arr.flags.c_contiguous or arr.ndim != len(shape)
+                    or any(a < b for a, b in zip(arr.shape, shape))
+                    or (arr.ndim == 2 and n > 1 and arr.shape[1] != max_blocks)):
+                raise ValueError(f"build_batch: output must be C-contiguous int32 of shape >= {shape}")
+        _check(lib.pa_build_batch(self._h, ids.ctypes.data_as(_P64), n, max_blocks,
+                                  tables_out.ctypes.data_as(_P32), lens_out.ctypes.data_as(_P32)), "pa_build_batch")
+        return tables_out[:n, :max_blocks], lens_out[:n]
 
 
 __all__ = ["paged_attention_decode", "paged_attention_workspace_bytes", "kv_append", "block_copy", "stage_copy",

@@ -38,6 +38,10 @@
 
 #include <algorithm>
 #include <cmath>
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -68,9 +72,10 @@ struct DecodeArgs {
   int32_t max_parts;
   int32_t out_f32;
   int64_t num_blocks;
-  int32_t* run_pre;   // split: H_kv-scaled block prefix sums [S + 1] (workspace)
   int32_t run_grid;   // split: chunks (workgroups) of the main kernel; 0 = one run per partition
   int32_t run_rounds; // split: rounds of the chunk schedule
+  uint64_t* run_done; // split: per (sequence, KV head) arrival counters [S * H_kv] (workspace); tag << 32 | partitions
+  uint32_t launch_tag; // split: this launch's counter tag
 };
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s) {
@@ -377,6 +382,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
 constexpr int kMaxScanSeqs = 2048;  // sequences the split kernel's in-LDS index covers
 constexpr int kPersistRing = 2;     // ring depth of the split kernel
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X, each with its own L2
+constexpr int kMaxSplitGrid = 4095;  // chunks (workgroups) of the split kernel, at most
 
 // Work split.  The partitions of all (sequence, KV head) pairs are laid end to end in
 // (sequence, KV head, partition) order, each weighted by its block count; W is the total.
@@ -386,8 +392,8 @@ constexpr int kXcds = 8;            // accelerator complex dies of an MI355X, ea
 // workgroup per chunk owns the partitions whose first block lies in the chunk: a contiguous
 // run.  Consecutive partitions of one (sequence, KV head) inside a run are merged on chip
 // (the online softmax simply continues); only where a run ends inside a sequence's context
-// is a partial (max, sum, output) written, to the slot of the run's first partition.
-// chunk_lo / chunk_owner are shared with the merge kernel.
+// is a partial (max, sum, output) written, to the slot of the run's first partition; the
+// run that finishes such a context last merges its runs' partials (chunk_owner finds them).
 __device__ __forceinline__ int64_t chunk_lo(int64_t j, int64_t W, int R, int NR) {
   const int r = static_cast<int>(j / R), t = static_cast<int>(j % R);
   if (r >= NR) return W;
@@ -402,6 +408,22 @@ __device__ __forceinline__ int64_t chunk_owner(int64_t off, int64_t W, int R, in
   const int64_t T0 = W - (W >> r);
   const int64_t T1 = (r + 1 >= NR) ? W : W - (W >> (r + 1));
   return static_cast<int64_t>(r) * R + ((off - T0 + 1) * R - 1) / (T1 - T0);
+}
+
+// Arrival count of one (sequence, KV head): the high 32 bits hold the tag of the launch
+// that last wrote it, the low 32 the partitions whose runs have published their partials.
+// A counter still holding another launch's tag counts as 0, so the workspace needs no
+// clearing between calls.  Returns the partitions published before this call's `add`.
+// Lock-free: each failed exchange means another run published, and every run publishes once.
+__device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t tag, uint32_t add) {
+  uint64_t cur = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (true) {
+    const bool fresh = static_cast<uint32_t>(cur >> 32) == tag;
+    const uint64_t want = fresh ? cur + add : ((static_cast<uint64_t>(tag) << 32) | add);
+    if (__hip_atomic_compare_exchange_strong(ctr, &cur, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return fresh ? static_cast<uint32_t>(cur) : 0u;
+  }
 }
 
 // One partition of one (sequence, KV head) as a workgroup sees it.
@@ -432,6 +454,8 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   __shared__ int32_t nb_s[kMaxScanSeqs];        // blocks of sequence s
   __shared__ int32_t ctx_s[kMaxScanSeqs];       // clamped context length of s
   __shared__ int32_t scan[kThreads];
+  __shared__ int32_t merge_flag[2];  // thread 0's arrivals completed these contexts
+  static_assert(kWaves * 16 * D > kMaxSplitGrid, "run starts of one context fit in sm_o");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -488,9 +512,6 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   __syncthreads();
   const int W = __builtin_amdgcn_readfirstlane(blkpre[S]);
 
-  // The merge kernel recomputes run boundaries from the same prefix sums.
-  if (blockIdx.x == 0 && a.run_pre != nullptr)
-    for (int s = tid; s <= S; s += kThreads) a.run_pre[s] = blkpre[s];
   // Zero-length sequences own no partition: their output is 0.
   for (int s = blockIdx.x; s < S; s += J) {
     if (ctx_s[s] == 0)
@@ -599,6 +620,70 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   float m = -INFINITY, l = 0.f;
   int seg_p0 = 0;     // first partition of the current (sequence, KV head) segment
   int wave_turn = 0;  // which wave writes the next segment's results
+  int npend = 0;      // partial segments written (at most 2: the run's first and last)
+  int pend0_s = 0, pend0_h = 0, pend0_c = 0, pend0_np = 0;
+  int pend1_s = 0, pend1_h = 0, pend1_c = 0, pend1_np = 0;
+
+  // Merge the partials of all runs of (sequence s, KV head h) and write its g outputs, with
+  // the whole workgroup: the runs' first partitions go to LDS (the partial of a run sits at
+  // the slot of its first partition), then each thread takes 4 dims of one query head and
+  // loads the runs' partials 8 at a time.  Partials are read with device-scope loads: runs on
+  // other XCDs wrote them through to memory.  Called by every thread, after the stream.
+  int32_t* const run_p0 = reinterpret_cast<int32_t*>(&sm_o[0][0][0]);
+  auto merge_ctx = [&](int s, int h, int np, int nb) {
+    const int64_t A = static_cast<int64_t>(blkpre[s]) + static_cast<int64_t>(h) * nb;
+    const int64_t k0 = chunk_owner(A, W, R, NR);
+    const int64_t k1 = chunk_owner(A + static_cast<int64_t>(np - 1) * PB, W, R, NR);
+    const int nr = static_cast<int>(k1 - k0 + 1);
+    for (int i = tid; i <= nr; i += kThreads)
+      run_p0[i] = i == 0 ? 0 : i == nr ? np : static_cast<int>((chunk_lo(k0 + i, W, R, NR) - A + PB - 1) / PB);
+    __syncthreads();
+    constexpr int kChunks = D / 4;
+    constexpr int kBatch = 8;
+    for (int c4 = tid; c4 < g * kChunks; c4 += kThreads) {
+      const int cc = c4 / kChunks, d0 = (c4 % kChunks) * 4;
+      const int64_t row = static_cast<int64_t>(s) * a.hq + h * g + cc;
+      float M = -INFINITY, Lsum = 0.f;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int r0 = 0; r0 < nr; r0 += kBatch) {
+        float pm[kBatch], pl[kBatch];
+        f32x4_t po[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int r = r0 + j;
+          const int p0 = r < nr ? run_p0[r] : 0;
+          const bool ok = r < nr && p0 < run_p0[r + 1];  // a run may hold no partition start
+          pm[j] = -INFINITY;
+          pl[j] = 0.f;
+          po[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (ok) {
+            const int64_t prow = row * a.max_parts + p0;
+            pm[j] = __hip_atomic_load(a.part_ml + prow * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pl[j] = __hip_atomic_load(a.part_ml + prow * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              po[j][e] = __hip_atomic_load(a.part_o + prow * D + d0 + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (pl[j] > 0.f) {
+            const float Mn = fmaxf(M, pm[j]);
+            const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+            const float wr = __builtin_amdgcn_exp2f(pm[j] - Mn) * pl[j];
+            acc = acc * sc + po[j] * wr;
+            Lsum = Lsum * sc + wr;
+            M = Mn;
+          }
+        }
+      }
+      f32x4_t res;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) res[e] = Lsum > 0.f ? acc[e] / Lsum : 0.f;
+      store_out4<DT>(a, row * D + d0, res);
+    }
+    __syncthreads();  // run_p0 is reused by the next merge
+  };
 
   // Stream one partition's blocks (looking ahead into the next one).  At the end of a
   // segment, merge the four waves and write the output or the run's partial.
@@ -716,10 +801,26 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
           store_out4<DT>(a, row * D + d0, res);
         } else {
           const int64_t prow = row * a.max_parts + seg_p0;
-          *reinterpret_cast<f32x4_t*>(a.part_o + prow * D + d0) = res;
-          if (d0 == 0) *reinterpret_cast<f32x2_t*>(a.part_ml + prow * 2) = f32x2_t{mx, L};
+          // Device-scope stores: the run that merges this context may sit on another XCD.
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __hip_atomic_store(a.part_o + prow * D + d0 + e, res[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (d0 == 0) {
+            __hip_atomic_store(a.part_ml + prow * 2, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.part_ml + prow * 2 + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
       }
+    }
+    // Only a run's first and last segments can be part of a context; their partials are
+    // published once the run is done.
+    if (!(seg_p0 == 0 && cur.p == cur.np - 1)) {
+      if (npend == 0) {
+        pend0_s = cur.s, pend0_h = cur.h, pend0_c = cur.p - seg_p0 + 1, pend0_np = cur.np;
+      } else {
+        pend1_s = cur.s, pend1_h = cur.h, pend1_c = cur.p - seg_p0 + 1, pend1_np = cur.np;
+      }
+      ++npend;
     }
     ++wave_turn;
     __syncthreads();
@@ -775,6 +876,27 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     off += A.it.len;
     prepare_next(A.it, off, B);
   }
+
+  // Publish the run's partial segments: each adds its partitions to the count of its
+  // (sequence, KV head); the run that completes a context merges the partials of all its
+  // runs (its own included) and writes the output.  Every wave first waits until its
+  // device-scope partial stores are complete, so they are visible to any later device-scope
+  // load once the barrier has passed and thread 0 has counted them.
+  if (npend == 0) return;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t b0 = arrive(a.run_done + static_cast<int64_t>(pend0_s) * hkv + pend0_h, a.launch_tag, pend0_c);
+    merge_flag[0] = b0 + pend0_c == static_cast<uint32_t>(pend0_np);
+    merge_flag[1] = 0;
+    if (npend > 1) {
+      const uint32_t b1 = arrive(a.run_done + static_cast<int64_t>(pend1_s) * hkv + pend1_h, a.launch_tag, pend1_c);
+      merge_flag[1] = b1 + pend1_c == static_cast<uint32_t>(pend1_np);
+    }
+  }
+  __syncthreads();
+  if (merge_flag[0]) merge_ctx(pend0_s, pend0_h, pend0_np, nb_s[pend0_s]);
+  if (merge_flag[1]) merge_ctx(pend1_s, pend1_h, pend1_np, nb_s[pend1_s]);
 }
 
 // ------------------------------------------------------------------ generic VALU path
@@ -872,19 +994,15 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ partition merge
 
-constexpr int kMaxRuns = 1024;  // runs per context whose starts the merge keeps in LDS (more: recomputed)
-
 // One workgroup per (sequence, KV head, column slice) with more than one partition merges
-// the partials of that sequence's runs for its slice of the g query heads x D outputs:
-//   M = max_r m_r,  w_r = 2^(m_r - M) * l_r,  out = sum_r w_r * O_r / sum_r w_r
-// where O_r is run r's normalised output.  A run is one partition (run_grid == 0) or the
-// stretch of partitions one chunk of the split kernel streamed; its partial sits at the slot
-// of its first partition.  Threads form RG groups that take every RG-th run, merge online,
-// then combine in a fixed order: deterministic.  Zero-length and single-run sequences were
-// written by the main kernel.
+// the partials of that sequence's partitions for its slice of the g query heads x D outputs
+// (the per-partition kernels; the split kernel merges its runs itself):
+//   M = max_p m_p,  w_p = 2^(m_p - M) * l_p,  out = sum_p w_p * O_p / sum_p w_p
+// where O_p is partition p's normalised output.  Threads form RG groups that take every
+// RG-th partition, merge online, then combine in a fixed order: deterministic.  Zero-length
+// and single-partition sequences were written by the main kernel.
 template <int DT>
 __global__ __launch_bounds__(256) void reduce_partitions_kernel(DecodeArgs a) {
-  __shared__ int32_t ps[kMaxRuns + 1];  // run i covers partitions [ps[i], ps[i + 1])
   __shared__ float red_m[256];
   __shared__ float red_l[256];
   __shared__ __attribute__((aligned(16))) f32x4_t red_o[256];
@@ -900,31 +1018,6 @@ __global__ __launch_bounds__(256) void reduce_partitions_kernel(DecodeArgs a) {
   const int g = a.group;
   const int tid = threadIdx.x;
 
-  const bool split = a.run_grid > 0;
-  int64_t W = 0, A = 0, k0 = 0;
-  int R = 1, NR = 1, nruns = np;
-  if (split) {
-    W = a.run_pre[a.num_seqs];
-    A = a.run_pre[s] + static_cast<int64_t>(kvh) * nb;
-    NR = a.run_rounds;
-    R = a.run_grid / NR;
-    k0 = chunk_owner(A, W, R, NR);
-    const int64_t k1 = chunk_owner(A + static_cast<int64_t>(np - 1) * PB, W, R, NR);
-    if (k0 == k1) return;
-    nruns = static_cast<int>(k1 - k0 + 1);
-  }
-  // First partition of run i (i in 0..nruns; run nruns starts past the end).
-  auto run_start = [&](int i) -> int {
-    if (i >= nruns) return np;
-    if (!split) return i;
-    if (i == 0) return 0;
-    return static_cast<int>((chunk_lo(k0 + i, W, R, NR) - A + PB - 1) / PB);
-  };
-  const bool in_lds = nruns <= kMaxRuns;
-  if (in_lds)
-    for (int i = tid; i <= nruns; i += 256) ps[i] = run_start(i);
-  __syncthreads();
-
   const int nout4 = g * D / 4;
   const int C = (nout4 + gridDim.y - 1) / gridDim.y;  // columns per slice, <= 256
   const int c_begin = blockIdx.y * C;
@@ -937,11 +1030,8 @@ __global__ __launch_bounds__(256) void reduce_partitions_kernel(DecodeArgs a) {
   float M = -INFINITY, L = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (active) {
-    for (int i = rg; i < nruns; i += RG) {
-      const int p0 = in_lds ? ps[i] : run_start(i);
-      const int p1 = in_lds ? ps[i + 1] : run_start(i + 1);
-      if (p0 >= p1) continue;  // a chunk that starts no partition of this context
-      const int64_t prow = row * a.max_parts + p0;
+    for (int p = rg; p < np; p += RG) {
+      const int64_t prow = row * a.max_parts + p;
       const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(a.part_ml + prow * 2);
       const f32x4_t O = *reinterpret_cast<const f32x4_t*>(a.part_o + prow * D + d0);
       if (!(ml[1] > 0.f)) continue;
@@ -991,7 +1081,7 @@ struct Plan {
   int32_t part_blocks;
   int32_t ctx_limit;
   int32_t max_parts;
-  size_t prefix_offset;  // byte offset of the block prefix sums in the workspace
+  size_t counter_offset;  // byte offset of the arrival counters in the workspace
   size_t workspace;
 };
 
@@ -1020,8 +1110,9 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
   // Partials [S][H_q][parts][D] and [S][H_q][parts][2] (fp32), then the split kernel's
   // block prefix sums [S + 1] (int32).
   const size_t rows = static_cast<size_t>(p->num_seqs) * p->num_q_heads * parts;
-  out->prefix_offset = rows * (static_cast<size_t>(c.head_dim) + 2) * sizeof(float);
-  out->workspace = parts > 1 ? out->prefix_offset + (static_cast<size_t>(p->num_seqs) + 1) * sizeof(int32_t) : 0;
+  // then the per (sequence, KV head) arrival counters [S * H_kv] (uint64; the partials end 8-byte aligned)
+  out->counter_offset = rows * (static_cast<size_t>(c.head_dim) + 2) * sizeof(float);
+  out->workspace = parts > 1 ? out->counter_offset + static_cast<size_t>(p->num_seqs) * c.num_kv_heads * 8 : 0;
   return PA_OK;
 }
 
@@ -1069,7 +1160,7 @@ int32_t resident_workgroups(const void* kernel, int* out) {
 // out the finish times but add partials and workgroup start-up costs that outweigh that.
 constexpr int kSplitRounds = 1;
 
-// Launch the split kernel; sets args->run_grid / run_rounds for the merge kernel.
+// Launch the split kernel; sets args->run_grid / run_rounds.
 template <int DT, int D>
 int32_t launch_split(DecodeArgs* args, hipStream_t st) {
   const void* fn = reinterpret_cast<const void*>(&decode_split_kernel<DT, D, kPersistRing>);
@@ -1077,7 +1168,7 @@ int32_t launch_split(DecodeArgs* args, hipStream_t st) {
   const int32_t rc = resident_workgroups(fn, &resident);
   if (rc != PA_OK) return rc;
   args->run_rounds = kSplitRounds;
-  args->run_grid = kSplitRounds * resident;
+  args->run_grid = std::min(kSplitRounds * resident, kMaxSplitGrid / kSplitRounds * kSplitRounds);
   hipLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing>), dim3(static_cast<uint32_t>(args->run_grid)),
                      dim3(kWaves * kWave), 0, st, *args);
   return PA_OK;
@@ -1117,7 +1208,8 @@ int32_t launch_decode(DecodeArgs args, hipStream_t st, void* timing_event) {
     const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(timing_event), st);
     if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_decode: timing event", e);
   }
-  if (args.max_parts > 1) launch_reduce<DT>(args, st);
+  // The split kernel merges its runs in place; the per-partition kernels need the merge kernel.
+  if (args.max_parts > 1 && args.run_grid == 0) launch_reduce<DT>(args, st);
   return PA_OK;
 }
 
@@ -1163,9 +1255,15 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   a.max_parts = plan.max_parts;
   a.out_f32 = p->out_dtype == PA_F32 ? 1 : 0;
   a.num_blocks = p->cache.num_blocks;
-  a.run_pre = plan.workspace > 0
-                  ? reinterpret_cast<int32_t*>(static_cast<uint8_t*>(p->workspace) + plan.prefix_offset)
-                  : nullptr;
+  a.run_done = plan.workspace > 0
+                   ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(p->workspace) + plan.counter_offset)
+                   : nullptr;
+  // A tag no earlier call of this process used, seeded per process (a workspace may hold
+  // counters another process left): the arrival counters need no clearing.
+  static std::atomic<uint32_t> next_tag{static_cast<uint32_t>(
+      std::chrono::steady_clock::now().time_since_epoch().count() * 0x9e3779b97f4a7c15ull >> 32) ^
+      static_cast<uint32_t>(getpid())};
+  a.launch_tag = next_tag.fetch_add(1, std::memory_order_relaxed);
 
   hipStream_t stream = static_cast<hipStream_t>(p->stream);
   (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind

@@ -68,28 +68,27 @@ class PagedDecodeLayer:
         self.partition_size = partition_size
         self.device = device
         self.stream = torch.cuda.current_stream() if stream is None else stream
-        self._stage = [_Staging(max_seqs, max_blocks_per_seq, max_seqs, device) for _ in range(2)]
+        # Three staging buffers: the host fills one while the stream may still read the two
+        # before it, so host work on a step overlaps the GPU's previous steps.
+        self._stage = [_Staging(max_seqs, max_blocks_per_seq, max_seqs, device) for _ in range(3)]
         self._turn = 0
+        self._ones = np.ones(max_seqs, np.int32)
         probe_q = torch.empty(max_seqs, num_q_heads, head_dim, dtype=dtype, device=device)
         probe_t = torch.empty(max_seqs, max_blocks_per_seq, dtype=torch.int32, device=device)
         ws = paged_attention_workspace_bytes(probe_q, self.k_cache, self.v_cache, probe_t,
                                              torch.empty_like(probe_q, dtype=torch.float32),
                                              max_blocks_per_seq * 16, partition_size)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
-        self.max_len = {}  # host view of each sequence's length
 
     # ------------------------------------------------------------------ sequence management
     def add(self, seq: int):
         self.alloc.add(seq)
-        self.max_len[seq] = 0
 
     def fork(self, parent: int, child: int):
         self.alloc.fork(parent, child)
-        self.max_len[child] = self.max_len[parent]
 
     def free(self, seq: int):
         self.alloc.free(seq)
-        del self.max_len[seq]
 
     def prefill(self, seq: int, k, v):
         """Place a prompt's K/V [n, H_kv, D] (device tensors) into the cache."""
@@ -99,37 +98,30 @@ class PagedDecodeLayer:
             if len(pairs):
                 block_copy(self.k_cache, self.v_cache, torch.from_numpy(pairs).to(self.device), stream=self.stream)
             kv_append(k, v, torch.from_numpy(slots).to(self.device), self.k_cache, self.v_cache, stream=self.stream)
-        self.max_len[seq] += n
 
     # ------------------------------------------------------------------ one decode step
     def decode_step(self, seqs, q, k_new, v_new, out, scale: float, timing=None):
         """Each of ``seqs`` appends one token (k_new/v_new [S, H_kv, D]) and attends
         with q [S, H_q, D] over its whole context; writes out [S, H_q, D].
 
-        ``timing`` = (start, mid, end) torch.cuda.Events (already recorded once) are
-        recorded around the attention call: start..mid spans the main attention kernel,
-        mid..end the partition merge.  Returns the number of copy-on-write block copies."""
+        ``timing`` = (start, end) torch.cuda.Events (already recorded once) are recorded
+        right before and after the attention call.  Every event recorded between two
+        kernels costs the stream a few microseconds, so the step records one event
+        after the attention call (``end``, when given) and uses it to know when the
+        staging buffer may be rewritten.  Returns the number of copy-on-write block copies."""
         S = len(seqs)
         st = self._stage[self._turn]
-        self._turn ^= 1
+        self._turn = (self._turn + 1) % len(self._stage)
         if st.done is not None:
             st.done.synchronize()  # previous copies out of this pinned buffer have finished
-        slots, pairs = self.alloc.append_batch(seqs, np.ones(S, np.int32), st.h_slots, st.h_pairs)
-        t, l = self.alloc.build_batch(seqs, self.max_blocks)
-        np_tables = st.h_tables[:S]
-        np_lens = st.h_lens[:S]
-        np_tables[...] = t
-        np_lens[...] = l
-        max_ctx = 0
-        for s in seqs:
-            self.max_len[s] += 1
-            max_ctx = max(max_ctx, self.max_len[s])
+        ids = np.asarray(seqs, dtype=np.int64)
+        slots, pairs = self.alloc.append_batch(ids, self._ones[:S], st.h_slots, st.h_pairs)
+        np_tables, np_lens = self.alloc.build_batch(ids, self.max_blocks, st.h_tables, st.h_lens)
+        max_ctx = int(np_lens.max()) if S else 0
         npairs = len(pairs)
         used = st.o_tables + S * self.max_blocks  # lengths, slots, pairs and the first S table rows
         with torch.cuda.stream(self.stream):
             stage_copy(st.dev, st.host, used * 4, stream=self.stream)
-            st.done = torch.cuda.Event()
-            st.done.record(self.stream)
             if npairs:
                 block_copy(self.k_cache, self.v_cache, st.d_pairs(npairs), stream=self.stream)
             kv_append(k_new, v_new, st.d_slots(S), self.k_cache, self.v_cache, stream=self.stream)
@@ -137,10 +129,12 @@ class PagedDecodeLayer:
                 timing[0].record(self.stream)
             paged_attention_decode(q, self.k_cache, self.v_cache, st.d_tables(S), st.d_lens(S), scale, out,
                                    max_context_len=max_ctx, partition_size=self.partition_size,
-                                   workspace=self.workspace, stream=self.stream,
-                                   timing_event=None if timing is None else timing[1])
+                                   workspace=self.workspace, stream=self.stream)
             if timing is not None:
-                timing[2].record(self.stream)
+                st.done = timing[1]
+            else:
+                st.done = torch.cuda.Event()
+            st.done.record(self.stream)  # the staging copies (earlier in the stream) are done
         self.last_lens = np_lens.copy()
-        self.last_tables = np_tables  # view into the pinned staging buffer: valid until two steps later
+        self.last_tables = np_tables  # view into the pinned staging buffer: valid until three steps later
         return npairs

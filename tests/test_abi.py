@@ -51,10 +51,13 @@ def test_workspace_bytes():
     ws = pa.lib.paged_attention_workspace_bytes
     assert ws(ctypes.byref(_params())) == 0                      # one partition: no workspace
     p = _params(S=4, hq=64, hkv=8, d=128, maxb=8192, maxctx=131072, dtype=pa.PA_BF16, out=pa.PA_F32)
-    # partials (output row + max + sum per query head and partition), then S + 1 int32 prefix sums
-    assert ws(ctypes.byref(p)) == 4 * 64 * 256 * (128 + 2) * 4 + (4 + 1) * 4
+    # partials (output row + max + sum per query head and partition), then S * H_kv uint64
+    # arrival counters
+    def expect(S, hq, hkv, parts, d):
+        return S * hq * parts * (d + 2) * 4 + S * hkv * 8
+    assert ws(ctypes.byref(p)) == expect(4, 64, 8, 256, 128)
     p = _params(maxb=100, maxctx=1000, part=256)
-    assert ws(ctypes.byref(p)) == 4 * 4 * 4 * (64 + 2) * 4 + (4 + 1) * 4
+    assert ws(ctypes.byref(p)) == expect(4, 4, 4, 4, 64)
     assert ws(None) == 0
 
 

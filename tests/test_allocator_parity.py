@@ -165,6 +165,17 @@ def test_build_batch_matches_model():
     assert t_c.tolist() == t_m and l_c.tolist() == l_m
     with pytest.raises(pa.PagedAttnError):
         cpp.build_batch([4], 3)
+    # in place, into the leading rows of larger buffers (a staging area for several batch sizes)
+    tables = np.full((6, 8), 77, np.int32)
+    lens = np.full(6, 77, np.int32)
+    t_i, l_i = cpp.build_batch(np.array([4, 0, 2], np.int64), 8, tables, lens)
+    assert t_i.tolist() == t_m and l_i.tolist() == l_m
+    assert np.shares_memory(t_i, tables) and np.shares_memory(l_i, lens)
+    assert np.all(tables[3:] == 77) and np.all(lens[3:] == 77)
+    for bad_t, bad_l in ((np.empty((2, 8), np.int32), lens), (np.empty((6, 9), np.int32), lens),
+                         (np.empty((6, 8), np.int64), lens), (tables, np.empty(2, np.int32))):
+        with pytest.raises(ValueError):
+            cpp.build_batch([4, 0, 2], 8, bad_t, bad_l)
 
 
 def test_create_rejects_bad_pools():
