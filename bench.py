@@ -178,7 +178,8 @@ def main():
     print(f"[bench] {K} timed steps: {elapsed / K * 1e3:.3f} ms/step (host enqueue done after "
           f"{(t_enq - t0) / K * 1e3:.3f} ms/step)", file=sys.stderr, flush=True)
 
-    # The attention call is one launch of the split kernel (it merges split contexts itself).
+    # The events ride on the attention call's launch: start to end of the split kernel, which
+    # merges split contexts itself.
     main_ms = [a.elapsed_time(b) for a, b in events]
     block_bytes = hkv * D * 16 * eb
 

@@ -86,8 +86,12 @@ typedef struct pa_decode_params {
                                   NULL when that is 0 */
   size_t workspace_bytes;
   void* stream;                /* hipStream_t */
-  void* timing_event;          /* hipEvent_t or NULL: if set, recorded on the stream after the main attention
-                                  kernel and before the partition merge, so a caller can time the two apart */
+  void* start_event;           /* hipEvent_t or NULL: marks the start of the call's first kernel */
+  void* stop_event;            /* hipEvent_t or NULL: marks the end of the call's last kernel.  Both travel with
+                                  the kernel launches (no marker packets between kernels, which would delay the
+                                  stream); the events must already exist.  Elapsed time between them is the
+                                  call's GPU time; a caller can also wait on stop_event for the call's end.
+                                  With num_seqs = 0 nothing is launched and both are recorded on the stream. */
 } pa_decode_params;
 
 /* Human-readable name of a status code (static string). */

@@ -37,7 +37,8 @@ class CacheDesc(ctypes.Structure):
 class DecodeParams(ctypes.Structure):
     _fields_ = [("num_seqs", _i32), ("num_q_heads", _i32), ("max_blocks_per_seq", _i32), ("max_context_len", _i32),
                 ("partition_size", _i32), ("out_dtype", _i32), ("cache", CacheDesc), ("workspace", _vp),
-                ("workspace_bytes", _sz), ("stream", _vp), ("timing_event", _vp)]
+                ("workspace_bytes", _sz), ("stream", _vp), ("start_event", _vp),
+                ("stop_event", _vp)]
 
 
 _PAllocPtr = ctypes.POINTER(_vp)
@@ -152,7 +153,7 @@ def _event_ptr(ev):
     if ev is None:
         return None
     if ev.cuda_event == 0:
-        raise ValueError("record the timing event once before passing it (torch creates events lazily)")
+        raise ValueError("record the event once before passing it (torch creates events lazily)")
     return ev.cuda_event
 
 
@@ -170,7 +171,7 @@ def _require_device(*ts):
 
 # ----------------------------------------------------------------------------- kernels
 def decode_params(q, k_cache, v_cache, block_tables, out, max_context_len: int, partition_size: int = 0,
-                  workspace=None, stream=None, timing_event=None) -> DecodeParams:
+                  workspace=None, stream=None, start_event=None, stop_event=None) -> DecodeParams:
     c = cache_desc(k_cache, v_cache)
     S, hq, d = q.shape
     if d != c.head_dim:
@@ -178,7 +179,7 @@ def decode_params(q, k_cache, v_cache, block_tables, out, max_context_len: int, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return DecodeParams(S, hq, block_tables.shape[1], int(max_context_len), int(partition_size),
                         torch_dtype_code(out.dtype), c, _ptr(workspace).value, ws_bytes,
-                        _stream_ptr(stream).value, _event_ptr(timing_event))
+                        _stream_ptr(stream).value, _event_ptr(start_event), _event_ptr(stop_event))
 
 
 def paged_attention_workspace_bytes(q, k_cache, v_cache, block_tables, out, max_context_len: int,
@@ -189,13 +190,15 @@ def paged_attention_workspace_bytes(q, k_cache, v_cache, block_tables, out, max_
 
 def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
                            max_context_len: int, partition_size: int = 0, workspace=None, stream=None,
-                           timing_event=None):
+                           start_event=None, stop_event=None):
     """out[s, j] = softmax attention of q[s, j] over sequence s's cached tokens.
 
     q [S, H_q, D] and out [S, H_q, D] (fp32 or the cache dtype), block_tables int32
     [S, max_blocks], context_lens int32 [S]; ``max_context_len`` is a host-known upper
     bound of context_lens.  ``workspace`` (any device tensor of at least
     ``paged_attention_workspace_bytes`` bytes) is allocated here if omitted.
+    ``start_event`` / ``stop_event`` (torch.cuda.Events recorded once before) mark the
+    start of the call's first kernel and the end of its last one.
     """
     torch = _torch()
     _require_device(q, k_cache, v_cache, block_tables, context_lens, out)
@@ -211,7 +214,7 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     p = decode_params(q, k_cache, v_cache, block_tables, out, max_context_len, partition_size, workspace, stream,
-                      timing_event)
+                      start_event, stop_event)
     _check(lib.paged_attention_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
                                       float(scale), _ptr(out), ctypes.byref(p)), "paged_attention_decode")
     return out

@@ -46,6 +46,8 @@
 #include <mutex>
 #include <utility>
 
+#include <hip/hip_ext.h>
+
 #include "pa_device.h"
 #include "pa_status.h"
 
@@ -412,18 +414,25 @@ __device__ __forceinline__ int64_t chunk_owner(int64_t off, int64_t W, int R, in
 
 // Arrival count of one (sequence, KV head): the high 32 bits hold the tag of the launch
 // that last wrote it, the low 32 the partitions whose runs have published their partials.
-// A counter still holding another launch's tag counts as 0, so the workspace needs no
-// clearing between calls.  Returns the partitions published before this call's `add`.
-// Lock-free: each failed exchange means another run published, and every run publishes once.
+// The workspace is never cleared: a counter still holding another launch's tag counts as 0.
+// Returns the partitions published before this call's `add`.
+// Common case, one fetch-add: the counter already carries this launch's tag.  An add that
+// landed on a stale counter is redone: the first such run swaps in (tag, add), every later
+// one adds again.  Exactly one swap succeeds (the tag never changes back within a launch), so
+// the count of the launch is exact.  Runs of one context arrive together at the end of the
+// kernel; a swap loop there would retry once per competitor, a fetch-add never retries.
 __device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t tag, uint32_t add) {
-  uint64_t cur = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  while (true) {
-    const bool fresh = static_cast<uint32_t>(cur >> 32) == tag;
-    const uint64_t want = fresh ? cur + add : ((static_cast<uint64_t>(tag) << 32) | add);
-    if (__hip_atomic_compare_exchange_strong(ctr, &cur, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+  const uint64_t mine = static_cast<uint64_t>(tag) << 32;
+  uint64_t old = __hip_atomic_fetch_add(ctr, static_cast<uint64_t>(add), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((old >> 32) == tag) return static_cast<uint32_t>(old);
+  old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while ((old >> 32) != tag) {
+    if (__hip_atomic_compare_exchange_strong(ctr, &old, mine | add, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT))
-      return fresh ? static_cast<uint32_t>(cur) : 0u;
+      return 0u;
   }
+  old = __hip_atomic_fetch_add(ctr, static_cast<uint64_t>(add), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return static_cast<uint32_t>(old);
 }
 
 // One partition of one (sequence, KV head) as a workgroup sees it.
@@ -627,7 +636,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   // Merge the partials of all runs of (sequence s, KV head h) and write its g outputs, with
   // the whole workgroup: the runs' first partitions go to LDS (the partial of a run sits at
   // the slot of its first partition), then each thread takes 4 dims of one query head and
-  // loads the runs' partials 8 at a time.  Partials are read with device-scope loads: runs on
+  // loads the runs' partials 16 at a time.  Partials are read with device-scope loads: runs on
   // other XCDs wrote them through to memory.  Called by every thread, after the stream.
   int32_t* const run_p0 = reinterpret_cast<int32_t*>(&sm_o[0][0][0]);
   auto merge_ctx = [&](int s, int h, int np, int nb) {
@@ -639,7 +648,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
       run_p0[i] = i == 0 ? 0 : i == nr ? np : static_cast<int>((chunk_lo(k0 + i, W, R, NR) - A + PB - 1) / PB);
     __syncthreads();
     constexpr int kChunks = D / 4;
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 16;
     for (int c4 = tid; c4 < g * kChunks; c4 += kThreads) {
       const int cc = c4 / kChunks, d0 = (c4 % kChunks) * 4;
       const int64_t row = static_cast<int64_t>(s) * a.hq + h * g + cc;
@@ -1119,7 +1128,7 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <int DT>
-void launch_reduce(const DecodeArgs& args, hipStream_t st) {
+void launch_reduce(const DecodeArgs& args, hipStream_t st, hipEvent_t stop) {
   // Output columns (4 dims each) of one (sequence, KV head) are cut into slices so that each
   // workgroup has at most 256 columns and, for few sequences, enough workgroups overall.
   const int nout4 = args.group * args.head_dim / 4;
@@ -1127,8 +1136,8 @@ void launch_reduce(const DecodeArgs& args, hipStream_t st) {
   const int hi = std::max(lo, nout4 / 32);
   const int want = std::max(1, 2048 / std::max(1, args.num_seqs * args.hkv));
   const int nsl = std::min(hi, std::max(lo, want));
-  hipLaunchKernelGGL(reduce_partitions_kernel<DT>, dim3(static_cast<uint32_t>(args.num_seqs) * args.hkv, nsl),
-                     dim3(256), 0, st, args);
+  hipExtLaunchKernelGGL(reduce_partitions_kernel<DT>, dim3(static_cast<uint32_t>(args.num_seqs) * args.hkv, nsl),
+                        dim3(256), 0, st, nullptr, stop, 0, args);
 }
 
 // Workgroups of a kernel that fit on the current device at once
@@ -1162,20 +1171,20 @@ constexpr int kSplitRounds = 1;
 
 // Launch the split kernel; sets args->run_grid / run_rounds.
 template <int DT, int D>
-int32_t launch_split(DecodeArgs* args, hipStream_t st) {
+int32_t launch_split(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   const void* fn = reinterpret_cast<const void*>(&decode_split_kernel<DT, D, kPersistRing>);
   int resident = 0;
   const int32_t rc = resident_workgroups(fn, &resident);
   if (rc != PA_OK) return rc;
   args->run_rounds = kSplitRounds;
   args->run_grid = std::min(kSplitRounds * resident, kMaxSplitGrid / kSplitRounds * kSplitRounds);
-  hipLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing>), dim3(static_cast<uint32_t>(args->run_grid)),
-                     dim3(kWaves * kWave), 0, st, *args);
+  hipExtLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing>), dim3(static_cast<uint32_t>(args->run_grid)),
+                        dim3(kWaves * kWave), 0, st, start, stop, 0, *args);
   return PA_OK;
 }
 
 template <int DT>
-int32_t launch_decode(DecodeArgs args, hipStream_t st, void* timing_event) {
+int32_t launch_decode(DecodeArgs args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   const int64_t D = args.head_dim;
   const bool fast = DT != PA_F32 && (D == 64 || D == 128) && args.group <= 16;
   // The split kernel indexes blocks of all (sequence, KV head) pairs with int32.
@@ -1184,32 +1193,31 @@ int32_t launch_decode(DecodeArgs args, hipStream_t st, void* timing_event) {
   args.run_grid = 0;
   args.run_rounds = 0;
   if (split) {
-    if constexpr (DT != PA_F32) {
-      const int32_t rc = D == 64 ? launch_split<DT, 64>(&args, st) : launch_split<DT, 128>(&args, st);
-      if (rc != PA_OK) return rc;
-    }
-  } else if (fast) {
+    // One launch: the split kernel merges its runs in place.
+    if constexpr (DT != PA_F32) return D == 64 ? launch_split<DT, 64>(&args, st, start, stop)
+                                               : launch_split<DT, 128>(&args, st, start, stop);
+  }
+  // The per-partition kernels need the merge kernel when a context spans several partitions.
+  const bool merge = args.max_parts > 1;
+  hipEvent_t main_stop = merge ? nullptr : stop;
+  if (fast) {
     const int64_t nwg = int64_t{args.max_parts} * args.hkv * args.num_seqs;
     if (nwg > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
     if constexpr (DT != PA_F32) {
       if (D == 64)
-        hipLaunchKernelGGL((decode_mfma_kernel<DT, 64, kRing>), dim3(static_cast<uint32_t>(nwg)), dim3(kWaves * kWave), 0,
-                           st, args);
+        hipExtLaunchKernelGGL((decode_mfma_kernel<DT, 64, kRing>), dim3(static_cast<uint32_t>(nwg)),
+                              dim3(kWaves * kWave), 0, st, start, main_stop, 0, args);
       else
-        hipLaunchKernelGGL((decode_mfma_kernel<DT, 128, kRing>), dim3(static_cast<uint32_t>(nwg)), dim3(kWaves * kWave), 0,
-                           st, args);
+        hipExtLaunchKernelGGL((decode_mfma_kernel<DT, 128, kRing>), dim3(static_cast<uint32_t>(nwg)),
+                              dim3(kWaves * kWave), 0, st, start, main_stop, 0, args);
     }
   } else {
     const int64_t nwg = int64_t{args.max_parts} * args.hq * args.num_seqs;
     if (nwg > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(decode_generic_kernel<DT>, dim3(static_cast<uint32_t>(nwg)), dim3(kWave), 0, st, args);
+    hipExtLaunchKernelGGL(decode_generic_kernel<DT>, dim3(static_cast<uint32_t>(nwg)), dim3(kWave), 0, st, start,
+                          main_stop, 0, args);
   }
-  if (timing_event) {
-    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(timing_event), st);
-    if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_decode: timing event", e);
-  }
-  // The split kernel merges its runs in place; the per-partition kernels need the merge kernel.
-  if (args.max_parts > 1 && args.run_grid == 0) launch_reduce<DT>(args, st);
+  if (merge) launch_reduce<DT>(args, st, stop);
   return PA_OK;
 }
 
@@ -1226,7 +1234,15 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   Plan plan;
   const int32_t st = make_plan(p, &plan);
   if (st != PA_OK) return st;
-  if (p->num_seqs == 0) return PA_OK;
+  if (p->num_seqs == 0) {  // nothing to launch: the events are recorded on the stream directly
+    hipStream_t st = static_cast<hipStream_t>(p->stream);
+    for (void* ev : {p->start_event, p->stop_event}) {
+      if (!ev) continue;
+      const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev), st);
+      if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_decode: event", e);
+    }
+    return PA_OK;
+  }
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
@@ -1268,10 +1284,11 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   hipStream_t stream = static_cast<hipStream_t>(p->stream);
   (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind
   int32_t rc;
+  hipEvent_t start = static_cast<hipEvent_t>(p->start_event), stop = static_cast<hipEvent_t>(p->stop_event);
   switch (p->cache.dtype) {
-    case PA_F32: rc = launch_decode<PA_F32>(a, stream, p->timing_event); break;
-    case PA_BF16: rc = launch_decode<PA_BF16>(a, stream, p->timing_event); break;
-    default: rc = launch_decode<PA_F16>(a, stream, p->timing_event); break;
+    case PA_F32: rc = launch_decode<PA_F32>(a, stream, start, stop); break;
+    case PA_BF16: rc = launch_decode<PA_BF16>(a, stream, start, stop); break;
+    default: rc = launch_decode<PA_F16>(a, stream, start, stop); break;
   }
   if (rc != PA_OK) return rc;
   return PA_HIP_STATUS("paged_attention_decode", hipGetLastError());

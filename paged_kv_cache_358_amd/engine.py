@@ -38,7 +38,9 @@ class _Staging:
         self.h_slots = h[self.o_slots:self.o_pairs]
         self.h_pairs = h[self.o_pairs:self.o_tables].reshape(max_seqs, 2)
         self.h_tables = h[self.o_tables:].reshape(max_seqs, max_blocks)
-        self.done = None  # event recorded after this buffer's last host->device copy
+        self.done = None  # event that ends the step that last read this buffer
+        self.own_done = torch.cuda.Event()
+        self.own_done.record()  # create it now: kernel launches can only mark existing events
 
     def d_lens(self, n):
         return self.dev[self.o_lens:self.o_lens + n]
@@ -104,10 +106,10 @@ class PagedDecodeLayer:
         """Each of ``seqs`` appends one token (k_new/v_new [S, H_kv, D]) and attends
         with q [S, H_q, D] over its whole context; writes out [S, H_q, D].
 
-        ``timing`` = (start, end) torch.cuda.Events (already recorded once) are recorded
-        right before and after the attention call.  Every event recorded between two
-        kernels costs the stream a few microseconds, so the step records one event
-        after the attention call (``end``, when given) and uses it to know when the
+        ``timing`` = (start, end) timing-enabled torch.cuda.Events (already recorded once)
+        mark the start and end of the attention call's kernels.  No event is recorded
+        between kernels (a marker packet delays the stream by microseconds): the events
+        travel with the attention launch, and the end event also tells the host when the
         staging buffer may be rewritten.  Returns the number of copy-on-write block copies."""
         S = len(seqs)
         st = self._stage[self._turn]
@@ -125,16 +127,12 @@ class PagedDecodeLayer:
             if npairs:
                 block_copy(self.k_cache, self.v_cache, st.d_pairs(npairs), stream=self.stream)
             kv_append(k_new, v_new, st.d_slots(S), self.k_cache, self.v_cache, stream=self.stream)
-            if timing is not None:
-                timing[0].record(self.stream)
+            # the staging copies (earlier in the stream) are done when the attention kernels are
+            st.done = st.own_done if timing is None else timing[1]
             paged_attention_decode(q, self.k_cache, self.v_cache, st.d_tables(S), st.d_lens(S), scale, out,
                                    max_context_len=max_ctx, partition_size=self.partition_size,
-                                   workspace=self.workspace, stream=self.stream)
-            if timing is not None:
-                st.done = timing[1]
-            else:
-                st.done = torch.cuda.Event()
-            st.done.record(self.stream)  # the staging copies (earlier in the stream) are done
+                                   workspace=self.workspace, stream=self.stream,
+                                   start_event=None if timing is None else timing[0], stop_event=st.done)
         self.last_lens = np_lens.copy()
         self.last_tables = np_tables  # view into the pinned staging buffer: valid until three steps later
         return npairs

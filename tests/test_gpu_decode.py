@@ -236,3 +236,36 @@ def test_workspace_shared_by_calls_with_other_queries_and_partitions():
         for s in (0, 1, 3):
             ref = pd.oracle_sampled(s, heads)
             assert np.max(np.abs(o[s, heads] - ref)) <= 5e-3, (step, part, s)
+
+
+@pytest.mark.parametrize("part", [512, 16])
+def test_start_and_stop_events_bracket_the_kernels(part):
+    # The events travel with the launches; the per-partition path (more sequences than the
+    # split kernel indexes) ends with the merge kernel, which carries the stop event.
+    import paged_kv_cache_358_amd as pa
+    many = synth.DecodeConfig("many_seqs_ev", 43, 2050, 8, 2, 64, "bf16", "fixed", (40, 600) * 1025)
+    for cfg in (synth.scaled(synth.C2, lens=[700, 33, 2048]), many):
+        pd = PagedDecode(cfg, keep_truth=False)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        stop.record()
+        out = torch.empty(pd.q.shape, dtype=torch.float32, device=pd.q.device)
+        pa.paged_attention_decode(pd.q, pd.k_cache, pd.v_cache, pd.block_tables, pd.context_lens,
+                                  cfg.softmax_scale, out, max_context_len=pd.max_context_len,
+                                  partition_size=part, start_event=start, stop_event=stop)
+        stop.synchronize()
+        ms = start.elapsed_time(stop)
+        assert 0.0 < ms < 1000.0
+        for s in (0, 1):
+            ref = pd.oracle_sampled(s, [0, cfg.num_q_heads - 1])
+            assert np.max(np.abs(out[s, [0, cfg.num_q_heads - 1]].cpu().numpy() - ref)) <= 5e-3
+    # nothing to launch: both events are still recorded, in stream order
+    empty = torch.empty(0, 4, 128, dtype=torch.bfloat16, device="cuda")
+    kc, vc = pa.alloc_kv_cache(4, 4, 128, torch.bfloat16, "cuda")
+    start.record()
+    stop.record()
+    pa.paged_attention_decode(empty, kc, vc, torch.zeros(0, 1, dtype=torch.int32, device="cuda"),
+                              torch.zeros(0, dtype=torch.int32, device="cuda"), 0.1, empty.float(),
+                              max_context_len=0, start_event=start, stop_event=stop)
+    stop.synchronize()
+    assert start.elapsed_time(stop) >= 0.0
