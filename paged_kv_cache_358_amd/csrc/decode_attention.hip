@@ -76,6 +76,8 @@ struct DecodeArgs {
   int64_t num_blocks;
   int32_t run_grid;   // split: chunks (workgroups) of the main kernel; 0 = one run per partition
   int32_t run_rounds; // split: rounds of the chunk schedule
+  int32_t part_cost;  // split: balance weight of a partition beyond its blocks, in blocks
+  int32_t ctx_cost;   // split: balance weight of a (sequence, KV head) context's end, in blocks
   uint64_t* run_done; // split: per (sequence, KV head) arrival counters [S * H_kv] (workspace); tag << 32 | partitions
   uint32_t launch_tag; // split: this launch's counter tag
 };
@@ -387,11 +389,13 @@ constexpr int kXcds = 8;            // accelerator complex dies of an MI355X, ea
 constexpr int kMaxSplitGrid = 4095;  // chunks (workgroups) of the split kernel, at most
 
 // Work split.  The partitions of all (sequence, KV head) pairs are laid end to end in
-// (sequence, KV head, partition) order, each weighted by its block count; W is the total.
+// (sequence, KV head, partition) order, each weighted by its block count plus a fixed cost
+// per partition (its query and table loads, the ring's minimum depth, the segment's merge
+// and stores, which blocks alone do not account for); W is the total.
 // The split cuts [0, W) into chunks of decreasing size: NR rounds of R chunks (R = the
 // workgroups resident at once), round r covering [W - W/2^r, W - W/2^(r+1)) (the last round
 // runs to W), so the first chunks take half the work and the last ones fill the tail.  One
-// workgroup per chunk owns the partitions whose first block lies in the chunk: a contiguous
+// workgroup per chunk owns the partitions whose weighted start lies in the chunk: a contiguous
 // run.  Consecutive partitions of one (sequence, KV head) inside a run are merged on chip
 // (the online softmax simply continues); only where a run ends inside a sequence's context
 // is a partial (max, sum, output) written, to the slot of the run's first partition; the
@@ -459,7 +463,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   __shared__ __attribute__((aligned(16))) float sm_o[kWaves][16][D];
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
-  __shared__ int32_t blkpre[kMaxScanSeqs + 1];  // H_kv * (blocks of the sequences before s)
+  __shared__ int32_t blkpre[kMaxScanSeqs + 1];  // H_kv * (weight of the sequences before s)
   __shared__ int32_t nb_s[kMaxScanSeqs];        // blocks of sequence s
   __shared__ int32_t ctx_s[kMaxScanSeqs];       // clamped context length of s
   __shared__ int32_t scan[kThreads];
@@ -476,6 +480,12 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   const int hkv = a.hkv;
   const int g = a.group;
   const int J = gridDim.x;          // chunks = NR rounds of R
+  const int C = a.part_cost;        // fixed cost of a partition, in blocks of streaming
+  const int CE = a.ctx_cost;        // fixed cost of a context's end (merge and stores)
+  const int PW = PB + C;            // weighted stride of partitions within a context
+  // Weight of one (sequence, KV head) context with nb blocks: its blocks, C per partition
+  // and CE once, after its last partition.
+  auto wnb_of = [&](int nb) { return nb == 0 ? 0 : nb + C * ((nb + PB - 1) / PB) + CE; };
   const int NR = a.run_rounds;
   const int R = J / NR;
   // Chunk k of the split.  Workgroups are dealt to the 8 XCDs round-robin (workgroup i on XCD
@@ -488,12 +498,12 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     k = r * R + (t % kXcds) * (R / kXcds) + t / kXcds;
   }
 
-  // ---- prefix sums of blocks over sequences (every workgroup builds its own copy)
+  // ---- prefix sums of context weights over sequences (every workgroup builds its own copy)
   const int per = (S + kThreads - 1) / kThreads;
   int cnt = 0;
   for (int j = 0; j < per; ++j) {
     const int s = tid * per + j;
-    if (s < S) cnt += (clamp_ctx(a, s) + kBlockTokens - 1) / kBlockTokens;
+    if (s < S) cnt += wnb_of((clamp_ctx(a, s) + kBlockTokens - 1) / kBlockTokens);
   }
   scan[tid] = cnt;
   __syncthreads();
@@ -513,7 +523,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         blkpre[s] = base * hkv;
         nb_s[s] = nb;
         ctx_s[s] = n;
-        base += nb;
+        base += wnb_of(nb);
       }
     }
     if (tid == kThreads - 1) blkpre[S] = scan[kThreads - 1] * hkv;
@@ -532,7 +542,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   const int64_t hi = chunk_lo(k + 1, W, R, NR);
   if (lo >= hi) return;  // an empty chunk (small W): no partition starts in it
 
-  // Sequence holding global block offset off: the last s with blkpre[s] <= off (that skips
+  // Sequence holding weighted offset off: the last s with blkpre[s] <= off (that skips
   // zero-length sequences, which share their successor's prefix).
   auto seq_of = [&](int64_t off) {
     int lo_s = 0, hi_s = S - 1;
@@ -584,8 +594,8 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) sl.q[kk] = *reinterpret_cast<const u32x4_t*>(qp + qrow + (kk * 4 + grp) * 8);
   };
-  // The partition after `cur` in (sequence, KV head, partition) order, at global block
-  // offset off (= cur's offset + cur.len); empty when off reaches the end of the run.
+  // The partition after `cur` in (sequence, KV head, partition) order, at weighted offset
+  // off (= cur's offset + its weighted length); empty when off reaches the end of the run.
   auto prepare_next = [&](const Item& cur, int64_t off, Slot& sl) {
     int s = cur.s, h = cur.h, p = cur.p + 1;
     if (p >= cur.np) {
@@ -640,12 +650,12 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   // other XCDs wrote them through to memory.  Called by every thread, after the stream.
   int32_t* const run_p0 = reinterpret_cast<int32_t*>(&sm_o[0][0][0]);
   auto merge_ctx = [&](int s, int h, int np, int nb) {
-    const int64_t A = static_cast<int64_t>(blkpre[s]) + static_cast<int64_t>(h) * nb;
+    const int64_t A = static_cast<int64_t>(blkpre[s]) + static_cast<int64_t>(h) * wnb_of(nb);
     const int64_t k0 = chunk_owner(A, W, R, NR);
-    const int64_t k1 = chunk_owner(A + static_cast<int64_t>(np - 1) * PB, W, R, NR);
+    const int64_t k1 = chunk_owner(A + static_cast<int64_t>(np - 1) * PW, W, R, NR);
     const int nr = static_cast<int>(k1 - k0 + 1);
     for (int i = tid; i <= nr; i += kThreads)
-      run_p0[i] = i == 0 ? 0 : i == nr ? np : static_cast<int>((chunk_lo(k0 + i, W, R, NR) - A + PB - 1) / PB);
+      run_p0[i] = i == 0 ? 0 : i == nr ? np : static_cast<int>((chunk_lo(k0 + i, W, R, NR) - A + PW - 1) / PW);
     __syncthreads();
     constexpr int kChunks = D / 4;
     constexpr int kBatch = 16;
@@ -840,19 +850,19 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     seg_p0 = nxi.p;
   };
 
-  // First partition: the first one whose first block is at or after lo.
+  // First partition: the first one that starts at or after lo (in weighted offsets).
   int64_t off;
   {
     const int s = seq_of(lo);
     const int nb = __builtin_amdgcn_readfirstlane(nb_s[s]);
+    const int wn = wnb_of(nb);
     const int r = static_cast<int>(lo - __builtin_amdgcn_readfirstlane(blkpre[s]));
-    int h = r / nb, b = r % nb;
-    b = (b + PB - 1) / PB * PB;
-    if (b >= nb) {
-      b = 0;
+    int h = r / wn, p = (r % wn + PW - 1) / PW;
+    if (p >= (nb + PB - 1) / PB) {
+      p = 0;
       ++h;
     }
-    off = __builtin_amdgcn_readfirstlane(blkpre[s]) + static_cast<int64_t>(h) * nb + b;
+    off = __builtin_amdgcn_readfirstlane(blkpre[s]) + static_cast<int64_t>(h) * wn + static_cast<int64_t>(p) * PW;
   }
   Slot A, B;
   {
@@ -860,10 +870,10 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     int s0 = 0, h0 = 0, p0 = 0;
     if (ok) {
       s0 = seq_of(off);
-      const int nb = __builtin_amdgcn_readfirstlane(nb_s[s0]);
+      const int wn = wnb_of(__builtin_amdgcn_readfirstlane(nb_s[s0]));
       const int r = static_cast<int>(off - __builtin_amdgcn_readfirstlane(blkpre[s0]));
-      h0 = r / nb;
-      p0 = (r % nb) / PB;
+      h0 = r / wn;
+      p0 = (r % wn) / PW;
     }
     fill(A, ok, s0, h0, p0);
   }
@@ -873,16 +883,18 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   seg_p0 = A.it.p;
 #pragma unroll
   for (int j = 0; j < NBUF - 1; ++j) load_tile(ring[j], __builtin_amdgcn_readlane(A.ids, j), j, A.it.my_n, A.it.h);
-  off += A.it.len;
+  // Weighted length of a partition: its blocks, C, and CE if it ends its context.
+  auto wlen = [&](const Item& it) { return it.len + C + (it.p == it.np - 1 ? CE : 0); };
+  off += wlen(A.it);
   prepare_next(A.it, off, B);
   while (true) {
     run(A.it, A.ids, A.q, B.it, B.ok, B.ids);
     if (!B.ok) break;
-    off += B.it.len;
+    off += wlen(B.it);
     prepare_next(B.it, off, A);
     run(B.it, B.ids, B.q, A.it, A.ok, A.ids);
     if (!A.ok) break;
-    off += A.it.len;
+    off += wlen(A.it);
     prepare_next(A.it, off, B);
   }
 
@@ -1169,6 +1181,13 @@ int32_t resident_workgroups(const void* kernel, int* out) {
 // out the finish times but add partials and workgroup start-up costs that outweigh that.
 constexpr int kSplitRounds = 1;
 
+// Balance weights beyond the blocks, in blocks of streaming time: per partition its query and
+// table loads and the ring's minimum depth; per context the merge through LDS and the output
+// stores at its end.  Without them, a workgroup whose chunk holds many short contexts
+// finishes last by tens of microseconds.
+constexpr int kPartCost = 5;
+constexpr int kCtxCost = 5;
+
 // Launch the split kernel; sets args->run_grid / run_rounds.
 template <int DT, int D>
 int32_t launch_split(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
@@ -1187,9 +1206,13 @@ template <int DT>
 int32_t launch_decode(DecodeArgs args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   const int64_t D = args.head_dim;
   const bool fast = DT != PA_F32 && (D == 64 || D == 128) && args.group <= 16;
-  // The split kernel indexes blocks of all (sequence, KV head) pairs with int32.
+  args.part_cost = kPartCost;
+  args.ctx_cost = kCtxCost;
+  // The split kernel indexes the weighted blocks of all (sequence, KV head) pairs with int32.
   const bool split = fast && args.num_seqs <= kMaxScanSeqs &&
-                     int64_t{args.num_seqs} * args.hkv * args.max_blocks < 0x7fffffffLL;
+                     int64_t{args.num_seqs} * args.hkv *
+                             (int64_t{args.max_blocks} + int64_t{args.part_cost} * args.max_parts + args.ctx_cost) <
+                         0x7fffffffLL;
   args.run_grid = 0;
   args.run_rounds = 0;
   if (split) {
