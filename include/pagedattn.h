@@ -173,6 +173,23 @@ int32_t block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n
  */
 int32_t pa_stage_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/*
+ * pa_stage_append: pa_stage_copy and kv_append in one kernel launch, for a decode step whose
+ * allocator output needs no block copies first.  One part of the grid copies `bytes` from pinned
+ * host `src` to device `dst`; the other writes k_new / v_new into the cache slots, as kv_append
+ * does (the append of each new token: "Stop Wasting GPU Memory" page, Technical Details,
+ * "Single Sequence Generation").  The append does not read `dst`: `slot_mapping` may be device
+ * memory or pinned host memory (the staging buffer itself), read over the bus.  One launch fewer
+ * per step than the two calls; the copy and the append run side by side.
+ *   src, dst, bytes     as for pa_stage_copy (bytes may be 0)
+ *   other arguments     as for kv_append (num_tokens may be 0)
+ * Errors as for the two calls; PA_ERR_INVALID_ARG if slot_mapping is neither device nor pinned host
+ * memory.
+ */
+int32_t pa_stage_append(void* dst, const void* src, size_t bytes, const void* k_new, const void* v_new,
+                        const int32_t* slot_mapping, int32_t num_tokens, void* k_cache, void* v_cache,
+                        const pa_cache_desc* cache, void* stream);
+
 /* ----------------------------------------------------------------------- host block allocator */
 
 typedef struct pa_allocator pa_allocator;

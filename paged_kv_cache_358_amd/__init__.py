@@ -51,6 +51,7 @@ SIGNATURES = {
     "kv_append": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc), _vp]),
     "block_copy": (_i32, [_vp, _vp, _vp, _i32, ctypes.POINTER(CacheDesc), _vp]),
     "pa_stage_copy": (_i32, [_vp, _vp, _sz, _vp]),
+    "pa_stage_append": (_i32, [_vp, _vp, _sz, _vp, _vp, _vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc), _vp]),
     "pa_alloc_create": (_i32, [_i32, _i32, _P32, _PAllocPtr]),
     "pa_alloc_destroy": (None, [_vp]),
     "pa_seq_add": (_i32, [_vp, _i64]),
@@ -257,6 +258,27 @@ def stage_copy(dst, src, nbytes: int, *, stream=None):
     _check(lib.pa_stage_copy(_ptr(dst), _ptr(src), int(nbytes), _stream_ptr(stream)), "pa_stage_copy")
 
 
+def stage_append(dst, src, nbytes: int, k_new, v_new, slot_mapping, k_cache, v_cache, *, stream=None):
+    """stage_copy(dst, src, nbytes) and kv_append(k_new, v_new, slot_mapping, ...) in one launch.
+    slot_mapping (int32 [T]) may be a device tensor or a pinned host tensor (read over the bus)."""
+    torch = _torch()
+    if not dst.is_cuda or src.is_cuda or not src.is_pinned():
+        raise ValueError("stage_append copies a pinned host tensor into a device tensor")
+    if nbytes > min(dst.numel() * dst.element_size(), src.numel() * src.element_size()):
+        raise ValueError("nbytes exceeds a buffer")
+    _require_device(k_new, v_new, k_cache, v_cache)
+    T = slot_mapping.numel()
+    if slot_mapping.dtype != torch.int32 or (T and not (slot_mapping.is_cuda or slot_mapping.is_pinned())):
+        raise ValueError("slot_mapping must be int32, on the device or in pinned host memory")
+    c = cache_desc(k_cache, v_cache)
+    if tuple(k_new.shape) != (T, c.num_kv_heads, c.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new / v_new must be [T, H_kv, D]")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise ValueError("k_new / v_new must have the cache dtype")
+    _check(lib.pa_stage_append(_ptr(dst), _ptr(src), int(nbytes), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T,
+                               _ptr(k_cache), _ptr(v_cache), ctypes.byref(c), _stream_ptr(stream)), "pa_stage_append")
+
+
 # ----------------------------------------------------------------------------- allocator
 def _as_i32(a):
     a = np.ascontiguousarray(a, dtype=np.int32)
@@ -362,6 +384,7 @@ class BlockAllocator:
 
 
 __all__ = ["paged_attention_decode", "paged_attention_workspace_bytes", "kv_append", "block_copy", "stage_copy",
+           "stage_append",
            "BlockAllocator",
            "alloc_kv_cache", "cache_shapes", "cache_desc", "PagedAttnError", "lib", "LIB_PATH", "SIGNATURES",
            "PA_F32", "PA_BF16", "PA_F16", "BLOCK_SIZE"]

@@ -17,13 +17,11 @@ namespace pa {
 // chunk [blk][h][chunk][off][0..X) as one vector store; V goes to [blk][h][d][off]
 // element by element (V is stored with tokens fastest).
 template <int EB>
-__global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restrict__ k_new,
-                                                        const uint8_t* __restrict__ v_new,
-                                                        const int32_t* __restrict__ slots, int64_t total,
-                                                        uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
-                                                        int64_t num_slots, int H, int D, int B) {
+__device__ __forceinline__ void kv_append_one(const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+                                              const int32_t* __restrict__ slots, int64_t gid, int64_t total,
+                                              uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                              int64_t num_slots, int H, int D, int B) {
   constexpr int X = 16 / EB;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (gid >= total) return;
   const int chunks = D / X;
   const int c = static_cast<int>(gid % chunks);
@@ -51,6 +49,16 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restric
   }
 }
 
+template <int EB>
+__global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restrict__ k_new,
+                                                        const uint8_t* __restrict__ v_new,
+                                                        const int32_t* __restrict__ slots, int64_t total,
+                                                        uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                                        int64_t num_slots, int H, int D, int B) {
+  kv_append_one<EB>(k_new, v_new, slots, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x, total, k_cache,
+                    v_cache, num_slots, H, D, B);
+}
+
 // Grid x = pair * chunks_per_block + chunk (4 KiB per workgroup), y = 0 for K, 1 for V.
 __global__ __launch_bounds__(256) void block_copy_kernel(uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
                                                          const int32_t* __restrict__ pairs, int64_t num_blocks,
@@ -70,14 +78,36 @@ __global__ __launch_bounds__(256) void block_copy_kernel(uint8_t* __restrict__ k
 
 // Copy bytes (a multiple of 4) from pinned host memory the device can address into device
 // memory, 16 bytes per thread and a tail of 4-byte words: one kernel on the caller's stream.
-__global__ __launch_bounds__(256) void stage_copy_kernel(uint32_t* __restrict__ dst, const uint32_t* __restrict__ src,
-                                                         int64_t words) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void stage_copy_one(uint32_t* __restrict__ dst, const uint32_t* __restrict__ src,
+                                               int64_t words, int64_t i) {
   const int64_t v = i * 4;
   if (v + 3 < words) {
     *reinterpret_cast<u32x4_t*>(dst + v) = *reinterpret_cast<const u32x4_t*>(src + v);
   } else {
     for (int64_t w = v; w < words; ++w) dst[w] = src[w];
+  }
+}
+
+__global__ __launch_bounds__(256) void stage_copy_kernel(uint32_t* __restrict__ dst, const uint32_t* __restrict__ src,
+                                                         int64_t words) {
+  stage_copy_one(dst, src, words, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x);
+}
+
+// Both at once: workgroups [0, copy_wgs) copy, the rest append.  The two parts share no memory.
+template <int EB>
+__global__ __launch_bounds__(256) void stage_append_kernel(uint32_t* __restrict__ dst, const uint32_t* __restrict__ src,
+                                                           int64_t words, int64_t copy_wgs,
+                                                           const uint8_t* __restrict__ k_new,
+                                                           const uint8_t* __restrict__ v_new,
+                                                           const int32_t* __restrict__ slots, int64_t total,
+                                                           uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                                           int64_t num_slots, int H, int D, int B) {
+  const int64_t wg = blockIdx.x;
+  if (wg < copy_wgs) {
+    stage_copy_one(dst, src, words, wg * blockDim.x + threadIdx.x);
+  } else {
+    kv_append_one<EB>(k_new, v_new, slots, (wg - copy_wgs) * blockDim.x + threadIdx.x, total, k_cache, v_cache,
+                      num_slots, H, D, B);
   }
 }
 
@@ -89,6 +119,19 @@ static bool cache_desc_ok(const pa_cache_desc* c) {
 }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The address a kernel uses for p: pinned host memory goes through the device pointer HIP
+// reports for it; device memory is used as is.  nullptr if p is neither.
+static const void* device_view(const void* p, bool host_only) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type == hipMemoryTypeHost) return attr.devicePointer;
+  if (host_only) return nullptr;
+  return (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) ? p : nullptr;
+}
 
 }  // namespace pa
 
@@ -147,15 +190,52 @@ extern "C" int32_t pa_stage_copy(void* dst, const void* src, size_t bytes, void*
   if ((threads + 255) / 256 > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
   (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind
   // src must be pinned host memory the device can address; use the address HIP reports for it.
-  hipPointerAttribute_t attr;
-  if (hipPointerGetAttributes(&attr, src) != hipSuccess || attr.type != hipMemoryTypeHost ||
-      attr.devicePointer == nullptr) {
-    (void)hipGetLastError();
-    return PA_ERR_INVALID_ARG;
-  }
-  const uint32_t* dsrc = static_cast<const uint32_t*>(attr.devicePointer);
-  if (!aligned16(dsrc)) return PA_ERR_INVALID_ARG;
+  const uint32_t* dsrc = static_cast<const uint32_t*>(device_view(src, true));
+  if (!dsrc || !aligned16(dsrc)) return PA_ERR_INVALID_ARG;
   hipLaunchKernelGGL(stage_copy_kernel, dim3(static_cast<uint32_t>((threads + 255) / 256)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint32_t*>(dst), dsrc, words);
   return PA_HIP_STATUS("pa_stage_copy", hipGetLastError());
+}
+
+extern "C" int32_t pa_stage_append(void* dst, const void* src, size_t bytes, const void* k_new, const void* v_new,
+                                   const int32_t* slot_mapping, int32_t num_tokens, void* k_cache, void* v_cache,
+                                   const pa_cache_desc* cache, void* stream) {
+  if (!cache_desc_ok(cache) || num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (bytes % 4 != 0 || (bytes > 0 && (!dst || !src || !aligned16(dst) || !aligned16(src)))) return PA_ERR_INVALID_ARG;
+  if (num_tokens > 0 && (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)) return PA_ERR_INVALID_ARG;
+  if (num_tokens > 0 && (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)))
+    return PA_ERR_INVALID_ARG;
+  if (bytes == 0 && num_tokens == 0) return PA_OK;
+  (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind
+  const uint32_t* dsrc = nullptr;
+  if (bytes > 0) {
+    dsrc = static_cast<const uint32_t*>(device_view(src, true));
+    if (!dsrc || !aligned16(dsrc)) return PA_ERR_INVALID_ARG;
+  }
+  const int32_t* dslots = nullptr;
+  if (num_tokens > 0) {
+    dslots = static_cast<const int32_t*>(device_view(slot_mapping, false));
+    if (!dslots) return PA_ERR_INVALID_ARG;
+  }
+  const int64_t words = static_cast<int64_t>(bytes / 4);
+  const int64_t copy_wgs = ((words + 3) / 4 + 255) / 256;
+  const int eb = elem_bytes(cache->dtype);
+  const int64_t total = static_cast<int64_t>(num_tokens) * cache->num_kv_heads * (cache->head_dim / (16 / eb));
+  const int64_t append_wgs = (total + 255) / 256;
+  if (copy_wgs + append_wgs > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  const int64_t num_slots = cache->num_blocks * cache->block_size;
+  const dim3 grid(static_cast<uint32_t>(copy_wgs + append_wgs));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (eb == 4) {
+    hipLaunchKernelGGL(stage_append_kernel<4>, grid, dim3(256), 0, st, static_cast<uint32_t*>(dst), dsrc, words,
+                       copy_wgs, static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new), dslots, total,
+                       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), num_slots, cache->num_kv_heads,
+                       cache->head_dim, cache->block_size);
+  } else {
+    hipLaunchKernelGGL(stage_append_kernel<2>, grid, dim3(256), 0, st, static_cast<uint32_t*>(dst), dsrc, words,
+                       copy_wgs, static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new), dslots, total,
+                       static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), num_slots, cache->num_kv_heads,
+                       cache->head_dim, cache->block_size);
+  }
+  return PA_HIP_STATUS("pa_stage_append", hipGetLastError());
 }

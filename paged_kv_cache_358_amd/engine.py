@@ -15,7 +15,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (BlockAllocator, alloc_kv_cache, block_copy, kv_append, paged_attention_decode,
+from . import (BlockAllocator, alloc_kv_cache, block_copy, kv_append, paged_attention_decode, stage_append,
                paged_attention_workspace_bytes, stage_copy)
 
 
@@ -38,6 +38,7 @@ class _Staging:
         self.h_slots = h[self.o_slots:self.o_pairs]
         self.h_pairs = h[self.o_pairs:self.o_tables].reshape(max_seqs, 2)
         self.h_tables = h[self.o_tables:].reshape(max_seqs, max_blocks)
+        self.h_slots_t = self.host[self.o_slots:self.o_pairs]  # the slots as a pinned tensor
         self.done = None  # event that ends the step that last read this buffer
         self.own_done = torch.cuda.Event()
         self.own_done.record()  # create it now: kernel launches can only mark existing events
@@ -123,10 +124,15 @@ class PagedDecodeLayer:
         npairs = len(pairs)
         used = st.o_tables + S * self.max_blocks  # lengths, slots, pairs and the first S table rows
         with torch.cuda.stream(self.stream):
-            stage_copy(st.dev, st.host, used * 4, stream=self.stream)
             if npairs:
+                # copy-on-write blocks are copied before the append writes into them
+                stage_copy(st.dev, st.host, used * 4, stream=self.stream)
                 block_copy(self.k_cache, self.v_cache, st.d_pairs(npairs), stream=self.stream)
-            kv_append(k_new, v_new, st.d_slots(S), self.k_cache, self.v_cache, stream=self.stream)
+                kv_append(k_new, v_new, st.d_slots(S), self.k_cache, self.v_cache, stream=self.stream)
+            else:
+                # one launch: the metadata copy, and the append reading its slots from the staging buffer
+                stage_append(st.dev, st.host, used * 4, k_new, v_new, st.h_slots_t[:S], self.k_cache, self.v_cache,
+                             stream=self.stream)
             # the staging copies (earlier in the stream) are done when the attention kernels are
             st.done = st.own_done if timing is None else timing[1]
             paged_attention_decode(q, self.k_cache, self.v_cache, st.d_tables(S), st.d_lens(S), scale, out,

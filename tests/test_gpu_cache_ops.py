@@ -98,3 +98,59 @@ def test_stage_copy_rejects_pageable_source():
         pa.stage_copy(dev, host, 256)
     rc = pa.lib.pa_stage_copy(ctypes.c_void_p(dev.data_ptr()), ctypes.c_void_p(host.data_ptr()), 256, None)
     assert rc == pa.PA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("dtype,H,D,slots_on", [("bf16", 8, 128, "host"), ("f32", 4, 64, "device"),
+                                                 ("f16", 32, 128, "host")])
+def test_stage_append_copies_and_appends_in_one_launch(dtype, H, D, slots_on):
+    # The copy part moves the staging words; the append part writes the cache exactly as
+    # kv_append does, with the slot mapping read from pinned host memory or the device.
+    B, N = 16, 40
+    k_cache, v_cache, kh, vh = random_cache(N, H, D, dtype, 4)
+    rng = np.random.default_rng(5)
+    T = 200
+    slots = rng.choice(N * B, size=T, replace=False).astype(np.int32)
+    slots[::9] = -1
+    slots[5] = N * B + 3
+    k_new = synth.encode(rng.standard_normal((T, H, D), dtype=np.float32), dtype)
+    v_new = synth.encode(rng.standard_normal((T, H, D), dtype=np.float32), dtype)
+    host = torch.arange(7, 7 + 10003, dtype=torch.int32).pin_memory()
+    dev = torch.full((10004,), -3, dtype=torch.int32, device="cuda")
+    slot_t = torch.from_numpy(slots).pin_memory() if slots_on == "host" else torch.from_numpy(slots).cuda()
+    pa.stage_append(dev, host, 10003 * 4, to_torch(k_new, dtype), to_torch(v_new, dtype), slot_t, k_cache, v_cache)
+    torch.cuda.synchronize()
+    got = dev.cpu()
+    assert torch.equal(got[:10003], host) and got[10003].item() == -3
+    valid = [s if 0 <= s < N * B else -1 for s in slots]
+    ek, ev = pl.apply_kv_append(storage_raw(kh, dtype), storage_raw(vh, dtype), valid,
+                                storage_raw(k_new, dtype), storage_raw(v_new, dtype), H, D, B, synth.ELEM_BYTES[dtype])
+    assert np.array_equal(raw_view(k_cache), ek)
+    assert np.array_equal(raw_view(v_cache), ev)
+
+
+def test_stage_append_either_part_empty_and_bad_slots():
+    k_cache, v_cache, kh, vh = random_cache(4, 2, 64, "bf16", 6)
+    host = torch.arange(64, dtype=torch.int32).pin_memory()
+    dev = torch.zeros(64, dtype=torch.int32, device="cuda")
+    empty = torch.empty(0, 2, 64, dtype=torch.bfloat16, device="cuda")
+    pa.stage_append(dev, host, 64 * 4, empty, empty, torch.empty(0, dtype=torch.int32).pin_memory(), k_cache, v_cache)
+    torch.cuda.synchronize()
+    assert torch.equal(dev.cpu(), host) and np.array_equal(raw_view(k_cache), storage_raw(kh, "bf16"))
+    one = synth.encode(np.arange(128, dtype=np.float32).reshape(1, 2, 64), "bf16")
+    pa.stage_append(dev, host, 0, to_torch(one, "bf16"), to_torch(one, "bf16"),
+                    torch.tensor([63], dtype=torch.int32).pin_memory(), k_cache, v_cache)
+    torch.cuda.synchronize()
+    k, v = pl.gather_sequence(raw_view(k_cache), raw_view(v_cache), [3], 16, 2, 64, 16, 2)
+    assert np.array_equal(k[15], storage_raw(one[0], "bf16")) and np.array_equal(v[15], storage_raw(one[0], "bf16"))
+    # pageable host slots: not addressable by the device, refused before any launch
+    with pytest.raises(ValueError):
+        pa.stage_append(dev, host, 0, to_torch(one, "bf16"), to_torch(one, "bf16"),
+                        torch.tensor([1], dtype=torch.int32), k_cache, v_cache)
+    c = pa.cache_desc(k_cache, v_cache)
+    pageable = torch.tensor([1], dtype=torch.int32)
+    kt = to_torch(one, "bf16")
+    rc = pa.lib.pa_stage_append(ctypes.c_void_p(dev.data_ptr()), ctypes.c_void_p(host.data_ptr()), 0,
+                                ctypes.c_void_p(kt.data_ptr()), ctypes.c_void_p(kt.data_ptr()),
+                                ctypes.c_void_p(pageable.data_ptr()), 1, ctypes.c_void_p(k_cache.data_ptr()),
+                                ctypes.c_void_p(v_cache.data_ptr()), ctypes.byref(c), None)
+    assert rc == pa.PA_ERR_INVALID_ARG
