@@ -236,9 +236,63 @@ def main():
         result["logical_attention_bytes_per_launch"] = int(np.mean(logical))
         result["effective_logical_gbs"] = round(float(np.mean(logical)) / mean_main_s / 1e9, 1)
 
+    result["cache_ops"] = cache_ops_probe(layer, step_inputs[-1], step_tables[-1] if shared else layer.last_tables,
+                                          block_bytes)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, cfg, lens0, kvbpt)
     print(json.dumps(result), flush=True)
+
+
+def cache_ops_probe(layer, step_input, tables, block_bytes, reps=20, max_pairs=448):
+    """Bandwidth of block_copy and kv_append on their own, after the timed steps: `reps`
+    back-to-back launches between two events.  Both write only blocks on the allocator's free
+    list, so no live cache content changes.  block_copy copies up to 448 live blocks (the
+    copy-on-write count of the first sampling step) into free ones; kv_append writes the last
+    step's new K/V (one token per sequence) into free slots."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_358_amd import block_copy, kv_append
+
+    free = layer.alloc.free_list()
+    live = np.unique(np.asarray(tables)[np.asarray(tables) >= 0])
+    out = {}
+    n = min(max_pairs, len(free), len(live))
+    if n > 0:
+        pairs = torch.tensor(np.stack([live[:n], np.asarray(free[:n])], axis=1).astype(np.int32), device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(layer.stream):
+            block_copy(layer.k_cache, layer.v_cache, pairs, stream=layer.stream)  # warm
+            e0.record(layer.stream)
+            for _ in range(reps):
+                block_copy(layer.k_cache, layer.v_cache, pairs, stream=layer.stream)
+            e1.record(layer.stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps / 1e3
+        moved = n * block_bytes * 2 * 2  # K and V blocks, read and written
+        out["block_copy"] = {"pairs": n, "us_per_launch": round(t * 1e6, 2), "bytes_per_launch": moved,
+                             "achieved_gbs": round(moved / t / 1e9, 1),
+                             "frac": round(moved / t / 1e9 / PEAK_HBM_GBS, 4)}
+    _, k_new, v_new = step_input
+    T = k_new.shape[0]
+    if T > 0 and len(free) * 16 >= T:
+        blocks = np.asarray(free[:(T + 15) // 16], dtype=np.int64)
+        slots = torch.tensor((np.repeat(blocks, 16)[:T] * 16 + np.tile(np.arange(16), len(blocks))[:T]).astype(np.int32),
+                             device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(layer.stream):
+            kv_append(k_new, v_new, slots, layer.k_cache, layer.v_cache, stream=layer.stream)  # warm
+            e0.record(layer.stream)
+            for _ in range(reps):
+                kv_append(k_new, v_new, slots, layer.k_cache, layer.v_cache, stream=layer.stream)
+            e1.record(layer.stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps / 1e3
+        moved = k_new.numel() * k_new.element_size() * 2 * 2 + T * 4  # K and V read and written, slots
+        out["kv_append"] = {"tokens": T, "us_per_launch": round(t * 1e6, 2), "bytes_per_launch": int(moved),
+                            "achieved_gbs": round(moved / t / 1e9, 1),
+                            "frac": round(moved / t / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
 
 
 def main_kernel_name(dtype, head_dim, group, num_seqs):
