@@ -1,0 +1,76 @@
+// MFMA building blocks shared by the gfx950 attention kernels: the S^T = K Q^T and
+// O^T += V^T P^T tiles over one 16-token block, and the buffer loads that feed them.
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw (unstructured) buffer, 32-bit data format
+constexpr int kLoadNT = 2;              // buffer-load cache policy: non-temporal (streamed once)
+
+// P (4 probabilities of one head for tokens 4j..4j+3) split as P = hi + lo, both in the
+// cache's 16-bit type; each half is the B operand of one PV MFMA, so the probabilities
+// enter the product with ~16 significant bits while the accumulation stays fp32.
+template <int DT> struct PSplit;
+template <> struct PSplit<PA_BF16> {
+  __device__ static void split(const float p[4], u32x2_t& hi_out, u32x2_t& lo_out) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t u = __float_as_uint(p[r]) & 0xffff0000u;  // truncation: exact bf16
+      const float rest = p[r] - __uint_as_float(u);               // exact in fp32
+      const uint32_t ru = __float_as_uint(rest);
+      hi[r] = u;
+      lo[r] = (ru + 0x7fffu + ((ru >> 16) & 1u)) & 0xffff0000u;    // bf16, round to nearest even
+    }
+    hi_out = u32x2_t{(hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3]};
+    lo_out = u32x2_t{(lo[0] >> 16) | lo[1], (lo[2] >> 16) | lo[3]};
+  }
+};
+template <> struct PSplit<PA_F16> {
+  __device__ static void split(const float p[4], u32x2_t& hi_out, u32x2_t& lo_out) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const _Float16 h = static_cast<_Float16>(p[r]);
+      const _Float16 l = static_cast<_Float16>(p[r] - static_cast<float>(h));
+      hi[r] = __builtin_bit_cast(uint16_t, h);
+      lo[r] = __builtin_bit_cast(uint16_t, l);
+    }
+    hi_out = u32x2_t{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+    lo_out = u32x2_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+  }
+};
+
+// S^T tile: v_mfma_f32_16x16x32 (8 elements of the contraction per lane).
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_qk(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  if constexpr (DT == PA_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+  }
+}
+
+// O^T tile: v_mfma_f32_16x16x16 (4 tokens per lane), V straight from its load registers.
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_pv(const u32x2_t& a, const u32x2_t& b, const f32x4_t& c) {
+  if constexpr (DT == PA_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, b),
+                                                     c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0,
+                                                 0, 0);
+  }
+}
+
+template <int D>
+struct KVRegs {
+  u32x4_t k[D / 32];  // K operand, one 16-byte chunk per QK MFMA
+  u32x2_t v[D / 16];  // V^T operand, 4 tokens of one dim per PV MFMA
+};
+
+}  // namespace pa
