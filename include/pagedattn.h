@@ -162,6 +162,41 @@ int32_t kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapp
 int32_t block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                    const pa_cache_desc* cache, void* stream);
 
+/* Parameters of one paged_attention_prefill call. */
+typedef struct pa_prefill_params {
+  int32_t num_seqs;            /* S >= 0 */
+  int32_t num_tokens;          /* T = rows of q and out (query_start[S]) */
+  int32_t num_q_heads;         /* H_q, a multiple of num_kv_heads */
+  int32_t max_blocks_per_seq;  /* row stride (in int32) of block_tables, >= 1 */
+  int32_t max_query_len;       /* host-known upper bound of the chunk lengths; sizes the grid */
+  int32_t out_dtype;           /* PA_F32, or the cache dtype */
+  pa_cache_desc cache;
+  void* stream;                /* hipStream_t */
+  void* start_event;           /* hipEvent_t or NULL, as for paged_attention_decode */
+  void* stop_event;            /* hipEvent_t or NULL, as for paged_attention_decode */
+} pa_prefill_params;
+
+/*
+ * paged_attention_prefill: causal attention of each sequence's newest tokens (a chunk whose K/V
+ * kv_append has already written) over the sequence's cached tokens, through its block table.
+ * The prefill phase fills a sequence's blocks ("Stop Wasting GPU Memory" page, Technical
+ * Details, "Single Sequence Generation"); the attention math is unchanged by paging
+ * ("PagedAttention: How Virtual Memory Paging Solved LLM KV Cache Waste" page, Key points).
+ * Chunk row i of sequence s (q row query_start[s] + i), with n = context_lens[s] tokens of
+ * which c = query_start[s+1] - query_start[s] are the chunk, is position n - c + i and attends to
+ * tokens 0 .. n - c + i:
+ *   out[row, j, :] = sum_t softmax_t(scale * q[row, j, :] . K[t, j / g, :]) V[t, j / g, :]
+ *   q            [T][H_q][D] (the cache dtype), device
+ *   block_tables [S][max_blocks_per_seq] int32; context_lens [S] int32 (tokens including the chunk)
+ *   query_start  [S + 1] int32, non-decreasing, query_start[0] = 0, query_start[S] = T, device
+ *   out          [T][H_q][D] fp32 or the cache dtype
+ * Rows whose position would be negative (a chunk longer than its context) are left unwritten.
+ * bf16 / fp16 caches with head_dim 64 or 128 (else PA_ERR_UNSUPPORTED); asynchronous on the stream.
+ */
+int32_t paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start, float scale, void* out,
+                                const pa_prefill_params* p);
+
 /*
  * pa_stage_copy: copy `bytes` (a multiple of 4) from src to dst with one kernel on `stream`.  It moves
  * the host allocator's per-step output (block tables, context lengths, slot mapping, copy pairs) to

@@ -41,6 +41,12 @@ class DecodeParams(ctypes.Structure):
                 ("stop_event", _vp)]
 
 
+class PrefillParams(ctypes.Structure):
+    _fields_ = [("num_seqs", _i32), ("num_tokens", _i32), ("num_q_heads", _i32), ("max_blocks_per_seq", _i32),
+                ("max_query_len", _i32), ("out_dtype", _i32), ("cache", CacheDesc), ("stream", _vp),
+                ("start_event", _vp), ("stop_event", _vp)]
+
+
 _PAllocPtr = ctypes.POINTER(_vp)
 SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [_i32]),
@@ -51,6 +57,8 @@ SIGNATURES = {
     "kv_append": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc), _vp]),
     "block_copy": (_i32, [_vp, _vp, _vp, _i32, ctypes.POINTER(CacheDesc), _vp]),
     "pa_stage_copy": (_i32, [_vp, _vp, _sz, _vp]),
+    "paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                                       ctypes.POINTER(PrefillParams)]),
     "pa_stage_append": (_i32, [_vp, _vp, _sz, _vp, _vp, _vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc), _vp]),
     "pa_alloc_create": (_i32, [_i32, _i32, _P32, _PAllocPtr]),
     "pa_alloc_destroy": (None, [_vp]),
@@ -221,6 +229,38 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     return out
 
 
+def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float, out, *,
+                            max_query_len: int, stream=None, start_event=None, stop_event=None):
+    """out[row, j] = causal attention of chunk row `row` over its sequence's cached tokens.
+
+    q / out [T, H_q, D]; query_start int32 [S + 1] (device) gives each sequence's first row;
+    context_lens int32 [S] counts the sequence's tokens including its chunk (already appended);
+    ``max_query_len`` is a host-known upper bound of the chunk lengths.
+    """
+    torch = _torch()
+    _require_device(q, k_cache, v_cache, block_tables, context_lens, query_start, out)
+    for t in (block_tables, context_lens, query_start):
+        if t.dtype != torch.int32:
+            raise ValueError("block_tables, context_lens and query_start must be int32")
+    if q.dtype != k_cache.dtype:
+        raise ValueError("q must have the cache dtype")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    c = cache_desc(k_cache, v_cache)
+    T, hq, d = q.shape
+    if d != c.head_dim:
+        raise ValueError("q head_dim does not match the cache")
+    S = block_tables.shape[0]
+    if query_start.numel() != S + 1 or context_lens.numel() != S:
+        raise ValueError("query_start must have S + 1 entries and context_lens S")
+    p = PrefillParams(S, T, hq, block_tables.shape[1], int(max_query_len), torch_dtype_code(out.dtype), c,
+                      _stream_ptr(stream).value, _event_ptr(start_event), _event_ptr(stop_event))
+    _check(lib.paged_attention_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+                                       _ptr(query_start), float(scale), _ptr(out), ctypes.byref(p)),
+           "paged_attention_prefill")
+    return out
+
+
 def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, *, stream=None):
     """Write k_new/v_new [T, H_kv, D] into the cache slots slot_mapping[T] (int32, -1 = skip)."""
     torch = _torch()
@@ -383,7 +423,7 @@ class BlockAllocator:
         return tables_out[:n, :max_blocks], lens_out[:n]
 
 
-__all__ = ["paged_attention_decode", "paged_attention_workspace_bytes", "kv_append", "block_copy", "stage_copy",
+__all__ = ["paged_attention_decode", "paged_attention_workspace_bytes", "paged_attention_prefill", "kv_append", "block_copy", "stage_copy",
            "stage_append",
            "BlockAllocator",
            "alloc_kv_cache", "cache_shapes", "cache_desc", "PagedAttnError", "lib", "LIB_PATH", "SIGNATURES",

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-HIP_SOURCES = ["cache_ops.hip", "decode_attention.hip"]
+HIP_SOURCES = ["cache_ops.hip", "decode_attention.hip", "prefill_attention.hip"]
 CXX_SOURCES = ["allocator.cpp", "status.cpp"]
 ARCH = "gfx950"
 

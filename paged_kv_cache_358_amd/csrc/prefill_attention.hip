@@ -1,0 +1,274 @@
+// Paged prefill attention (gfx950): the newest tokens of each sequence, a chunk already
+// written into its blocks, attend causally to the sequence's cached tokens.
+//
+// The prefill phase writes a sequence's tokens into blocks ("Stop Wasting GPU Memory" page,
+// Technical Details, "Single Sequence Generation"); the attention itself is the unchanged
+// transformer math ("PagedAttention: How Virtual Memory Paging Solved LLM KV Cache Waste"
+// page, Key points), gathered through the block table.  Chunk row i of a sequence with n
+// cached tokens, c of them in the chunk, is position p = n - c + i and sees tokens 0..p.
+//
+// One workgroup per (64-row tile of a chunk, query head, sequence); each wave owns 16 chunk
+// rows, the 16 columns of the MFMA tiles, and streams the K/V blocks its last row can see
+// through a ring of two register sets (block b+1 loads while block b computes).  The four
+// waves of a workgroup read the same blocks, so the caches serve the repeats.  Per block:
+// S^T = K Q^T with v_mfma_f32_16x16x32, an online softmax per column (query row) with the
+// causal bound applied per (token, column), and O^T += V^T (P_hi + P_lo) with two
+// v_mfma_f32_16x16x16 as in the decode kernels.  Each wave writes its own rows.
+#include <hip/hip_ext.h>
+
+#include <cmath>
+
+#include "pa_device.h"
+#include "pa_mfma.h"
+#include "pa_status.h"
+
+namespace pa {
+
+struct PrefillArgs {
+  const void* q;  // [T][H_q][D]
+  const void* k;
+  const void* v;
+  const int32_t* block_tables;  // [S][max_blocks]
+  const int32_t* context_lens;  // [S], tokens including the chunk
+  const int32_t* query_start;   // [S + 1], first row of each sequence's chunk in q / out
+  void* out;                    // [T][H_q][D]
+  float scale_log2;
+  int32_t num_tokens;  // T
+  int32_t hq;
+  int32_t hkv;
+  int32_t max_blocks;
+  int32_t out_f32;
+  int64_t num_blocks;
+};
+
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRows = kPrefillWaves * 16;  // chunk rows per workgroup
+
+template <int DT>
+__device__ __forceinline__ void prefill_store4(const PrefillArgs& a, int64_t idx, const f32x4_t& v) {
+  if (a.out_f32) {
+    *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + idx) = v;
+  } else {
+    uint32_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = Elem<DT>::from_float(v[e]);
+    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + idx) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  }
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int KK = D / 32;
+  constexpr int NV = D / 16;
+  constexpr int kTileBytes = D * kBlockTokens * 2;
+
+  const int s = blockIdx.z;
+  const int j = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int g = a.hq / a.hkv;
+  const int h = j / g;
+
+  const int q0 = a.query_start[s];
+  const int c = a.query_start[s + 1] - q0;                  // chunk rows of this sequence
+  int n = a.context_lens[s];
+  n = n < 0 ? 0 : (n > a.max_blocks * kBlockTokens ? a.max_blocks * kBlockTokens : n);
+  const int r0 = blockIdx.x * kPrefillRows + w * 16;       // this wave's first chunk row
+  if (c <= 0 || r0 >= c) return;
+  const int r_last = min(c, r0 + 16) - 1;
+  const int p_last = n - c + r_last;                       // position of the wave's last row
+  if (p_last < 0) return;                                  // n < c: no row of this wave has a position
+
+  // This lane's column: chunk row r = r0 + col at position p (-1 = no row / no position).
+  const int r = r0 + col;
+  const int64_t row = static_cast<int64_t>(q0) + r;
+  const bool real = r < c && n - c + r >= 0 && row >= 0 && row < a.num_tokens;
+  const int p = real ? n - c + r : -1;
+
+  // Q^T operand: lane (column col, k-group grp) holds dims (kk*4 + grp)*8 .. +8 of its row.
+  using st = uint16_t;
+  const st* qp = static_cast<const st*>(a.q);
+  u32x4_t qop[KK];
+  {
+    const int64_t qrow = ((real ? row : 0) * a.hq + j) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qp + qrow + (kk * 4 + grp) * 8);
+      qop[kk] = real ? x : u32x4_t{0, 0, 0, 0};
+    }
+  }
+
+  const int nblk = p_last / kBlockTokens + 1;  // blocks holding tokens 0 .. p_last
+  const int32_t* tab = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
+  // Block ids, 64 per register: lane i holds block base + i (clamped into the row).
+  auto load_ids = [&](int base) { return tab[min(base + lane, a.max_blocks - 1)]; };
+
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + static_cast<int64_t>(h) * kTileBytes;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + static_cast<int64_t>(h) * kTileBytes;
+  const int64_t blk_stride = static_cast<int64_t>(a.hkv) * kTileBytes;
+  const int k_off = lane * 16;
+  const int v_off = col * 32 + grp * 8;
+  // A block past the wave's last one, or an id outside the pool, gets an empty resource:
+  // its loads return zeros and touch no memory.
+  auto load = [&](KVRegs<D>& rg, int32_t phys, bool ok) {
+    ok = ok && phys >= 0 && phys < a.num_blocks;
+    const int64_t off = ok ? static_cast<int64_t>(phys) * blk_stride : 0;
+    const int nrec = ok ? kTileBytes : 0;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kbase + off), 0, nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vbase + off), 0, nrec, kRsrcWord3);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      rg.k[kk] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, kk * 1024, 0));
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn)
+      rg.v[nn] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, nn * 512, 0));
+  };
+
+  f32x4_t o[NV];
+#pragma unroll
+  for (int nn = 0; nn < NV; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  auto compute = [&](const KVRegs<D>& rg, int b, int32_t phys) {
+    int nv = n - b * kBlockTokens;  // tokens of the block in the context
+    nv = nv > kBlockTokens ? kBlockTokens : nv;
+    if (phys < 0 || phys >= a.num_blocks) nv = 0;
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) sacc = mfma_qk<DT>(rg.k[kk], qop[kk], sacc);
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = grp * 4 + e;
+      x[e] = (t < nv && b * kBlockTokens + t <= p) ? sacc[e] * a.scale_log2 : -INFINITY;
+    }
+    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float m_new = fmaxf(m, bm);
+    const float alpha = (m == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m_new);
+    l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m = m_new;
+    u32x2_t p_hi, p_lo;
+    PSplit<DT>::split(pr, p_hi, p_lo);
+    // Tokens past the context may hold anything, even NaN: select them out of V.
+    uint32_t keep[2];
+#pragma unroll
+    for (int wd = 0; wd < 2; ++wd) {
+      const int t0 = grp * 4 + 2 * wd;
+      keep[wd] = (t0 < nv ? 0x0000ffffu : 0u) | (t0 + 1 < nv ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn) {
+      const u32x2_t vv = {rg.v[nn][0] & keep[0], rg.v[nn][1] & keep[1]};
+      o[nn] *= alpha;
+      o[nn] = mfma_pv<DT>(vv, p_hi, o[nn]);
+      o[nn] = mfma_pv<DT>(vv, p_lo, o[nn]);
+    }
+  };
+
+  // Blocks in pairs over a ring of two: the block after the current one is always loading.
+  int32_t ids = load_ids(0);
+  int32_t ids_next = load_ids(64);
+  KVRegs<D> ring0, ring1;
+  int32_t ph0 = __builtin_amdgcn_readlane(ids, 0);
+  load(ring0, ph0, true);
+  for (int b = 0; b < nblk; b += 2) {
+    // b is even, so b and b + 1 share a 64-block id register unless b + 1 == base + 64 (never:
+    // 64 is even); b + 2 may start the next one.
+    const int i1 = (b + 1) & 63;
+    const int32_t ph1 = __builtin_amdgcn_readlane(ids, i1);
+    load(ring1, ph1, b + 1 < nblk);
+    compute(ring0, b, ph0);
+    if (b + 1 >= nblk) break;
+    const int b2 = b + 2;
+    if ((b2 & 63) == 0) {
+      ids = ids_next;
+      ids_next = load_ids(b2 + 64);
+    }
+    ph0 = __builtin_amdgcn_readlane(ids, b2 & 63);
+    load(ring0, ph0, b2 < nblk);
+    compute(ring1, b + 1, ph1);
+  }
+
+  if (!real) return;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  const int64_t orow = (row * a.hq + j) * D;
+#pragma unroll
+  for (int nn = 0; nn < NV; ++nn) prefill_store4<DT>(a, orow + nn * 16 + grp * 4, o[nn] * inv);
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" int32_t paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache,
+                                           const int32_t* block_tables, const int32_t* context_lens,
+                                           const int32_t* query_start, float scale, void* out,
+                                           const pa_prefill_params* p) {
+  if (!p) return PA_ERR_INVALID_ARG;
+  const pa_cache_desc& c = p->cache;
+  if (p->num_seqs < 0 || p->num_tokens < 0 || p->num_q_heads <= 0 || p->max_blocks_per_seq <= 0 ||
+      p->max_query_len < 0 || c.num_blocks <= 0 || c.num_kv_heads <= 0 || c.head_dim <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (p->num_q_heads % c.num_kv_heads != 0 || !valid_dtype(c.dtype)) return PA_ERR_INVALID_ARG;
+  if (p->out_dtype != PA_F32 && p->out_dtype != c.dtype) return PA_ERR_INVALID_ARG;
+  if (c.block_size != kBlockTokens || c.dtype == PA_F32 || (c.head_dim != 64 && c.head_dim != 128))
+    return PA_ERR_UNSUPPORTED;
+  if (p->num_seqs > 65535 || p->num_q_heads > 65535) return PA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(p->stream);
+  hipEvent_t start = static_cast<hipEvent_t>(p->start_event), stop = static_cast<hipEvent_t>(p->stop_event);
+  (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind
+  if (p->num_seqs == 0 || p->num_tokens == 0 || p->max_query_len == 0) {
+    for (hipEvent_t ev : {start, stop}) {
+      if (!ev) continue;
+      const hipError_t e = hipEventRecord(ev, st);
+      if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_prefill: event", e);
+    }
+    return PA_OK;
+  }
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out) return PA_ERR_INVALID_ARG;
+  auto a16 = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; };
+  if (!a16(q) || !a16(k_cache) || !a16(v_cache) || !a16(out)) return PA_ERR_INVALID_ARG;
+
+  PrefillArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.out = out;
+  a.scale_log2 = scale * kLog2e;
+  a.num_tokens = p->num_tokens;
+  a.hq = p->num_q_heads;
+  a.hkv = c.num_kv_heads;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.out_f32 = p->out_dtype == PA_F32 ? 1 : 0;
+  a.num_blocks = c.num_blocks;
+  const dim3 grid(static_cast<uint32_t>((p->max_query_len + kPrefillRows - 1) / kPrefillRows),
+                  static_cast<uint32_t>(p->num_q_heads), static_cast<uint32_t>(p->num_seqs));
+  const dim3 block(kPrefillWaves * kWave);
+  if (c.dtype == PA_BF16) {
+    if (c.head_dim == 64)
+      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_BF16, 64>), grid, block, 0, st, start, stop, 0, a);
+    else
+      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_BF16, 128>), grid, block, 0, st, start, stop, 0, a);
+  } else {
+    if (c.head_dim == 64)
+      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_F16, 64>), grid, block, 0, st, start, stop, 0, a);
+    else
+      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_F16, 128>), grid, block, 0, st, start, stop, 0, a);
+  }
+  return PA_HIP_STATUS("paged_attention_prefill", hipGetLastError());
+}

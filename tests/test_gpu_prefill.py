@@ -1,0 +1,141 @@
+"""Paged prefill attention on the GPU against the fp64 causal oracle.
+
+The cache is laid out by the library (NaN in every slot that must not be read); each
+sequence's last c tokens are the chunk, with their own queries.  Tolerance: max-abs 5e-3
+for bf16/fp16 inputs with fp32 accumulation, as for decode.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_358_amd as pa
+import synth
+from oracle.prefill import prefill_attention_seq
+from paged_setup import PagedDecode, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _chunk_queries(cfg, chunks, seed):
+    T = int(sum(chunks))
+    q = synth.rng(cfg.cfg_id, 9000 + seed).standard_normal((T, cfg.num_q_heads, cfg.head_dim), dtype=np.float32)
+    return synth.encode(q, cfg.dtype)
+
+
+def _run(pd, chunks, q_np, out_dtype=torch.float32, max_query_len=None):
+    cfg = pd.cfg
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = to_torch(q_np, cfg.dtype, "cuda")
+    out = torch.full(q.shape, float("nan"), dtype=out_dtype, device="cuda")
+    pa.paged_attention_prefill(q, pd.k_cache, pd.v_cache, pd.block_tables, pd.context_lens,
+                               torch.from_numpy(qs).cuda(), cfg.softmax_scale, out,
+                               max_query_len=int(max(chunks)) if max_query_len is None else max_query_len)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), qs
+
+
+def _check(pd, chunks, q_np, got, qs, rows_per_seq=None, tol=5e-3):
+    cfg = pd.cfg
+    worst = 0.0
+    for s, c in enumerate(chunks):
+        if c == 0:
+            continue
+        k, v = pd.truth[s]
+        rows = list(range(c)) if rows_per_seq is None else sorted({0, c - 1, *[i % c for i in rows_per_seq]})
+        ref = prefill_attention_seq(synth.decode_f64(q_np[qs[s]:qs[s + 1]], cfg.dtype), synth.decode_f64(k, cfg.dtype),
+                                    synth.decode_f64(v, cfg.dtype), cfg.softmax_scale, rows=rows)
+        g = got[qs[s]:qs[s + 1]][rows]
+        assert np.all(np.isfinite(g)), s
+        worst = max(worst, float(np.max(np.abs(g - ref))))
+    assert worst <= tol, worst
+    return worst
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_mha_chunks_of_every_shape(dtype):
+    # chunk lengths around the 16-row wave tile and the 64-row workgroup tile, chunks that are
+    # the whole sequence and chunks at the end of a longer context
+    lens = [1, 16, 17, 64, 65, 200, 300, 530, 16, 100]
+    chunks = [1, 16, 17, 64, 65, 200, 1, 130, 5, 100]
+    cfg = synth.scaled(synth.C2, lens=lens, dtype=dtype)
+    pd = PagedDecode(cfg)
+    q_np = _chunk_queries(cfg, chunks, 1)
+    got, qs = _run(pd, chunks, q_np)
+    _check(pd, chunks, q_np, got, qs)
+
+
+def test_gqa_and_head_dim_64():
+    for cfg, lens, chunks in ((synth.scaled(synth.C3, lens=[40, 700, 129, 1000]), [40, 700, 129, 1000], [40, 77, 129, 3]),
+                              (synth.DecodeConfig("pf_d64", 51, 3, 16, 4, 64, "bf16", "fixed", (33, 250, 96)),
+                               [33, 250, 96], [33, 64, 95])):
+        pd = PagedDecode(cfg)
+        q_np = _chunk_queries(cfg, chunks, 2)
+        got, qs = _run(pd, chunks, q_np)
+        _check(pd, chunks, q_np, got, qs)
+
+
+def test_first_position_of_a_whole_sequence_chunk_is_its_value():
+    cfg = synth.scaled(synth.C3, lens=[48, 20])
+    pd = PagedDecode(cfg)
+    chunks = [48, 20]
+    q_np = _chunk_queries(cfg, chunks, 3)
+    got, qs = _run(pd, chunks, q_np)
+    for s in range(2):
+        _, v = pd.truth[s]
+        expect = np.repeat(synth.decode_f64(v[0], cfg.dtype), cfg.group, axis=0)   # [H_q, D]
+        assert np.array_equal(got[qs[s]], expect.astype(np.float32))
+
+
+def test_last_chunk_row_equals_decode():
+    # the last row of a chunk is the decode query of the same context
+    lens = [300, 1025, 64]
+    cfg = synth.scaled(synth.C2, lens=lens)
+    pd = PagedDecode(cfg)
+    chunks = [7, 1, 64]
+    q_np = _chunk_queries(cfg, chunks, 4)
+    got, qs = _run(pd, chunks, q_np)
+    q_dec = np.stack([q_np[qs[s + 1] - 1] for s in range(3)])
+    out = torch.empty((3, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    pa.paged_attention_decode(to_torch(q_dec, cfg.dtype, "cuda"), pd.k_cache, pd.v_cache, pd.block_tables,
+                              pd.context_lens, cfg.softmax_scale, out, max_context_len=int(max(lens)))
+    torch.cuda.synchronize()
+    dec = out.cpu().numpy()
+    for s in range(3):
+        assert np.max(np.abs(got[qs[s + 1] - 1] - dec[s])) <= 2e-3
+
+
+def test_bf16_output_empty_chunks_and_a_loose_bound():
+    lens = [90, 0, 33, 5]
+    chunks = [20, 0, 0, 5]
+    cfg = synth.scaled(synth.C3, lens=lens)
+    pd = PagedDecode(cfg)
+    q_np = _chunk_queries(cfg, chunks, 5)
+    got, qs = _run(pd, chunks, q_np, out_dtype=torch.bfloat16, max_query_len=200)   # bound above the real max
+    _check(pd, chunks, q_np, got, qs, tol=5e-3 + 2 ** -8)
+
+
+def test_long_context_chunk_sampled_rows():
+    lens = [6000, 2500]
+    chunks = [512, 256]
+    cfg = synth.scaled(synth.C5, lens=lens)
+    pd = PagedDecode(cfg)
+    q_np = _chunk_queries(cfg, chunks, 6)
+    got, qs = _run(pd, chunks, q_np)
+    _check(pd, chunks, q_np, got, qs, rows_per_seq=[0, 1, 63, 64, 200, 255, 511])
+
+
+def test_rejects_what_it_does_not_cover():
+    cfg = synth.scaled(synth.C3, lens=[16])
+    pd = PagedDecode(cfg)
+    q = to_torch(_chunk_queries(cfg, [16], 7), cfg.dtype, "cuda")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):       # query_start must have S + 1 entries
+        pa.paged_attention_prefill(q, pd.k_cache, pd.v_cache, pd.block_tables, pd.context_lens,
+                                   torch.zeros(1, dtype=torch.int32, device="cuda"), 0.1, out, max_query_len=16)
+    kc, vc = pa.alloc_kv_cache(4, 2, 128, torch.float32)
+    q32 = torch.zeros(1, 2, 128, dtype=torch.float32, device="cuda")
+    with pytest.raises(pa.PagedAttnError):
+        pa.paged_attention_prefill(q32, kc, vc, torch.zeros(1, 1, dtype=torch.int32, device="cuda"),
+                                   torch.ones(1, dtype=torch.int32, device="cuda"),
+                                   torch.tensor([0, 1], dtype=torch.int32, device="cuda"), 0.1,
+                                   torch.zeros_like(q32), max_query_len=1)
