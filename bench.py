@@ -28,6 +28,7 @@ import time
 
 METRIC = "decode attention achieved HBM GB/s (% of peak) + seq-tokens/sec per layer"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 FOREIGN = -1
 
 
@@ -36,7 +37,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=55)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5", "prefill"],
+                    help="decode workloads c2..c5; 'prefill' times chunked prefill attention on c2's sequences")
+    ap.add_argument("--chunk", type=int, default=512, help="prefill: chunk rows per sequence (at most its length)")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-context partition in tokens (0 = the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -53,6 +56,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "the paged decode path has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "prefill":
+        run_prefill(args)
+        return
 
     import numpy as np
     import torch
@@ -293,6 +299,78 @@ def cache_ops_probe(layer, step_input, tables, block_bytes, reps=20, max_pairs=4
                             "achieved_gbs": round(moved / t / 1e9, 1),
                             "frac": round(moved / t / 1e9 / PEAK_HBM_GBS, 4)}
     return out
+
+
+def run_prefill(args):
+    """Chunked prefill attention on the MHA decode workload's sequences: the last
+    min(chunk, n) tokens of each sequence are the chunk (their K/V already in the cache).
+    Algorithmic work per query head and chunk row at position p: 2 D (p + 1) multiply-adds
+    (scores and weighted sum), 4 D (p + 1) flops."""
+    import numpy as np
+    import torch
+
+    import synth
+    import paged_kv_cache_358_amd as pa
+
+    W, K = args.warmup, args.steps
+    dev = torch.device("cuda:0")
+    cfg = synth.C2
+    lens = synth.context_lens(cfg).astype(np.int64)
+    chunks = np.minimum(lens, args.chunk)
+    S, hq, hkv, D = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    plan = synth.pool_plan(cfg, lens)
+    torch.manual_seed(cfg.cfg_id)
+    k_cache, v_cache = pa.alloc_kv_cache(plan.num_blocks, hkv, D, torch.bfloat16, dev)
+    k_cache.normal_()
+    v_cache.normal_()
+    alloc = pa.BlockAllocator(plan.num_blocks, 16, plan.free_order)
+    for s_ in range(S):
+        alloc.add(s_)
+        alloc.append(s_, int(lens[s_]))
+    max_blocks = int(synth.blocks_for(lens.max()))
+    tables, lens_np = alloc.build_batch(list(range(S)), max_blocks)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    T = int(qs[-1])
+    q = torch.randn(T, hq, D, device=dev).to(torch.bfloat16)
+    out = torch.empty(T, hq, D, device=dev, dtype=torch.float32)
+    bt, cl, qst = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (tables, lens_np, qs))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in ev:
+        a.record()
+        b.record()
+
+    def launch(events=None):
+        pa.paged_attention_prefill(q, k_cache, v_cache, bt, cl, qst, cfg.softmax_scale, out,
+                                   max_query_len=int(chunks.max()),
+                                   start_event=None if events is None else events[0],
+                                   stop_event=None if events is None else events[1])
+
+    for _ in range(W):
+        launch()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        launch(ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    pos_sum = sum(int(n) * int(c) - int(c) * (int(c) - 1) // 2 for n, c in zip(lens, chunks))  # sum of p + 1
+    flops = 4.0 * D * hq * pos_sum
+    kv_bytes = int(lens.sum()) * cfg.kv_bytes_per_token() + 2 * T * hq * D * 2
+    tflops = flops / kern_s / 1e12
+    print(json.dumps({
+        "metric": "prefill attention TFLOP/s (algorithmic)", "value": round(flops / (elapsed / K) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (torch-seeded N(0,1) q/K/V, seeded context lengths and shuffled block pool)",
+        "config": {"workload": "c2_mha_bf16 chunked prefill", "num_seqs": S, "chunk": args.chunk,
+                   "rows": T, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D, "block_size": 16},
+        "kernel_ms": round(kern_s * 1e3, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_mfma_kernel", "flops_per_launch": flops},
+        "kv_bytes_per_launch": kv_bytes, "kv_gbs_if_read_once": round(kv_bytes / kern_s / 1e9, 1),
+    }), flush=True)
 
 
 def main_kernel_name(dtype, head_dim, group, num_seqs):

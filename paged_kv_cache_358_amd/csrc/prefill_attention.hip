@@ -7,9 +7,10 @@
 // page, Key points), gathered through the block table.  Chunk row i of a sequence with n
 // cached tokens, c of them in the chunk, is position p = n - c + i and sees tokens 0..p.
 //
-// One workgroup per (64-row tile of a chunk, query head, sequence); each wave owns 16 chunk
+// One workgroup per (64-row tile of a chunk, query head, sequence), the tiles of one
+// (sequence, query head) placed on one XCD so they share its L2; each wave owns 16 chunk
 // rows, the 16 columns of the MFMA tiles, and streams the K/V blocks its last row can see
-// through a ring of two register sets (block b+1 loads while block b computes).  The four
+// through a ring of register sets (the next blocks load while one computes).  The four
 // waves of a workgroup read the same blocks, so the caches serve the repeats.  Per block:
 // S^T = K Q^T with v_mfma_f32_16x16x32, an online softmax per column (query row) with the
 // causal bound applied per (token, column), and O^T += V^T (P_hi + P_lo) with two
@@ -38,11 +39,16 @@ struct PrefillArgs {
   int32_t hkv;
   int32_t max_blocks;
   int32_t out_f32;
+  int32_t tiles;      // 64-row tiles per chunk (ceil(max_query_len / 64))
+  int32_t per_xcd;    // workgroups per XCD
+  int64_t items;      // sequences x query heads x tiles
   int64_t num_blocks;
 };
 
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRows = kPrefillWaves * 16;  // chunk rows per workgroup
+constexpr int kXcdCount = 8;  // accelerator complex dies of an MI355X, one L2 each
+constexpr int kPrefillRing = 2;  // K/V register sets per wave: blocks in flight + 1 (divides 64)
 
 template <int DT>
 __device__ __forceinline__ void prefill_store4(const PrefillArgs& a, int64_t idx, const f32x4_t& v) {
@@ -56,14 +62,23 @@ __device__ __forceinline__ void prefill_store4(const PrefillArgs& a, int64_t idx
   }
 }
 
-template <int DT, int D>
+template <int DT, int D, int NBUF>
 __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int KK = D / 32;
   constexpr int NV = D / 16;
   constexpr int kTileBytes = D * kBlockTokens * 2;
 
-  const int s = blockIdx.z;
-  const int j = blockIdx.y;
+  // Workgroups go to the 8 XCDs round-robin (workgroup i on XCD i % 8).  The (sequence,
+  // query head) groups are dealt to the XCDs round-robin too, and the k-th workgroup of XCD x
+  // takes tile k % tiles of its (k / tiles)-th group: the tiles of one group run back to back
+  // on one XCD and read the sequence's blocks through its L2 instead of fetching them from HBM
+  // once per tile, while every XCD gets an even share of long and short sequences.
+  const int64_t kx = blockIdx.x / kXcdCount;
+  const int64_t sj = static_cast<int64_t>(blockIdx.x % kXcdCount) + kXcdCount * (kx / a.tiles);
+  if (sj >= a.items / a.tiles) return;
+  const int tile = static_cast<int>(kx % a.tiles);
+  const int j = static_cast<int>(sj % a.hq);
+  const int s = static_cast<int>(sj / a.hq);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;
@@ -75,7 +90,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_mfma_kernel(Pre
   const int c = a.query_start[s + 1] - q0;                  // chunk rows of this sequence
   int n = a.context_lens[s];
   n = n < 0 ? 0 : (n > a.max_blocks * kBlockTokens ? a.max_blocks * kBlockTokens : n);
-  const int r0 = blockIdx.x * kPrefillRows + w * 16;       // this wave's first chunk row
+  const int r0 = tile * kPrefillRows + w * 16;             // this wave's first chunk row
   if (c <= 0 || r0 >= c) return;
   const int r_last = min(c, r0 + 16) - 1;
   const int p_last = n - c + r_last;                       // position of the wave's last row
@@ -174,28 +189,30 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_mfma_kernel(Pre
     }
   };
 
-  // Blocks in pairs over a ring of two: the block after the current one is always loading.
+  // A ring of NBUF register sets: blocks b+1 .. b+NBUF-1 are loading while block b computes.
+  // Block ids come 64 to a register; the lookahead reaches at most NBUF-1 < 64 blocks into
+  // the next register, which is loaded 64 blocks ahead of its first use.
+  int base = 0;
   int32_t ids = load_ids(0);
   int32_t ids_next = load_ids(64);
-  KVRegs<D> ring0, ring1;
-  int32_t ph0 = __builtin_amdgcn_readlane(ids, 0);
-  load(ring0, ph0, true);
-  for (int b = 0; b < nblk; b += 2) {
-    // b is even, so b and b + 1 share a 64-block id register unless b + 1 == base + 64 (never:
-    // 64 is even); b + 2 may start the next one.
-    const int i1 = (b + 1) & 63;
-    const int32_t ph1 = __builtin_amdgcn_readlane(ids, i1);
-    load(ring1, ph1, b + 1 < nblk);
-    compute(ring0, b, ph0);
-    if (b + 1 >= nblk) break;
-    const int b2 = b + 2;
-    if ((b2 & 63) == 0) {
-      ids = ids_next;
-      ids_next = load_ids(b2 + 64);
+  auto phys_at = [&](int pos) {
+    return pos < base + 64 ? __builtin_amdgcn_readlane(ids, pos - base) : __builtin_amdgcn_readlane(ids_next, pos - base - 64);
+  };
+  KVRegs<D> ring[NBUF];
+#pragma unroll
+  for (int jj = 0; jj < NBUF - 1; ++jj) load(ring[jj], phys_at(jj), jj < nblk);
+  for (int b = 0; b < nblk; b += NBUF) {
+#pragma unroll
+    for (int jj = 0; jj < NBUF; ++jj) {
+      const int la = b + jj + NBUF - 1;
+      load(ring[(jj + NBUF - 1) % NBUF], phys_at(la), la < nblk);
+      if (b + jj < nblk) compute(ring[jj], b + jj, phys_at(b + jj));
     }
-    ph0 = __builtin_amdgcn_readlane(ids, b2 & 63);
-    load(ring0, ph0, b2 < nblk);
-    compute(ring1, b + 1, ph1);
+    if (((b + NBUF) & 63) == 0) {
+      base += 64;
+      ids = ids_next;
+      ids_next = load_ids(base + 64);
+    }
   }
 
   if (!real) return;
@@ -224,7 +241,6 @@ extern "C" int32_t paged_attention_prefill(const void* q, const void* k_cache, c
   if (p->out_dtype != PA_F32 && p->out_dtype != c.dtype) return PA_ERR_INVALID_ARG;
   if (c.block_size != kBlockTokens || c.dtype == PA_F32 || (c.head_dim != 64 && c.head_dim != 128))
     return PA_ERR_UNSUPPORTED;
-  if (p->num_seqs > 65535 || p->num_q_heads > 65535) return PA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(p->stream);
   hipEvent_t start = static_cast<hipEvent_t>(p->start_event), stop = static_cast<hipEvent_t>(p->stop_event);
@@ -256,19 +272,24 @@ extern "C" int32_t paged_attention_prefill(const void* q, const void* k_cache, c
   a.max_blocks = p->max_blocks_per_seq;
   a.out_f32 = p->out_dtype == PA_F32 ? 1 : 0;
   a.num_blocks = c.num_blocks;
-  const dim3 grid(static_cast<uint32_t>((p->max_query_len + kPrefillRows - 1) / kPrefillRows),
-                  static_cast<uint32_t>(p->num_q_heads), static_cast<uint32_t>(p->num_seqs));
+  a.tiles = (p->max_query_len + kPrefillRows - 1) / kPrefillRows;
+  a.items = static_cast<int64_t>(p->num_seqs) * p->num_q_heads * a.tiles;
+  const int64_t groups = static_cast<int64_t>(p->num_seqs) * p->num_q_heads;
+  const int64_t per_xcd = (groups + kXcdCount - 1) / kXcdCount * a.tiles;
+  if (per_xcd * kXcdCount > 0x7fffffffLL || per_xcd > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  a.per_xcd = static_cast<int32_t>(per_xcd);
+  const dim3 grid(static_cast<uint32_t>(per_xcd * kXcdCount));
   const dim3 block(kPrefillWaves * kWave);
   if (c.dtype == PA_BF16) {
     if (c.head_dim == 64)
-      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_BF16, 64>), grid, block, 0, st, start, stop, 0, a);
+      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_BF16, 64, kPrefillRing>), grid, block, 0, st, start, stop, 0, a);
     else
-      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_BF16, 128>), grid, block, 0, st, start, stop, 0, a);
+      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_BF16, 128, kPrefillRing>), grid, block, 0, st, start, stop, 0, a);
   } else {
     if (c.head_dim == 64)
-      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_F16, 64>), grid, block, 0, st, start, stop, 0, a);
+      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_F16, 64, kPrefillRing>), grid, block, 0, st, start, stop, 0, a);
     else
-      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_F16, 128>), grid, block, 0, st, start, stop, 0, a);
+      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_F16, 128, kPrefillRing>), grid, block, 0, st, start, stop, 0, a);
   }
   return PA_HIP_STATUS("paged_attention_prefill", hipGetLastError());
 }
