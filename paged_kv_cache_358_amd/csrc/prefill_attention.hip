@@ -63,7 +63,8 @@ __device__ __forceinline__ void prefill_store4(const PrefillArgs& a, int64_t idx
 }
 
 template <int DT, int D, int NBUF>
-__global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_per_eu(3))) void prefill_mfma_kernel(
+    PrefillArgs a) {
   constexpr int KK = D / 32;
   constexpr int NV = D / 16;
   constexpr int kTileBytes = D * kBlockTokens * 2;
@@ -148,29 +149,46 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_mfma_kernel(Pre
   for (int nn = 0; nn < NV; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
+  // A block whose 16 tokens all lie in the context and before the wave's first row is seen
+  // whole by every row: no token needs masking (rows past the chunk are never written).
+  const int p_first = n - c + r0;
   auto compute = [&](const KVRegs<D>& rg, int b, int32_t phys) {
     int nv = n - b * kBlockTokens;  // tokens of the block in the context
     nv = nv > kBlockTokens ? kBlockTokens : nv;
     if (phys < 0 || phys >= a.num_blocks) nv = 0;
+    const bool whole = nv == kBlockTokens && b * kBlockTokens + kBlockTokens - 1 <= p_first;
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) sacc = mfma_qk<DT>(rg.k[kk], qop[kk], sacc);
     float x[4];
+    if (whole) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = grp * 4 + e;
-      x[e] = (t < nv && b * kBlockTokens + t <= p) ? sacc[e] * a.scale_log2 : -INFINITY;
+      for (int e = 0; e < 4; ++e) x[e] = sacc[e] * a.scale_log2;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = grp * 4 + e;
+        x[e] = (t < nv && b * kBlockTokens + t <= p) ? sacc[e] * a.scale_log2 : -INFINITY;
+      }
     }
     float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
     const float m_new = fmaxf(m, bm);
+    // Once the rows' running maxima settle, most blocks raise none of them: then every
+    // correction factor is 1 and the rescale of O (32 accumulators a lane) is skipped for the
+    // whole wave.
+    const bool rescale = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
     const float alpha = (m == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
     float pr[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) pr[e] = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m_new);
     l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m = m_new;
+    if (rescale) {
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) o[nn] *= alpha;
+    }
     u32x2_t p_hi, p_lo;
     PSplit<DT>::split(pr, p_hi, p_lo);
     // Tokens past the context may hold anything, even NaN: select them out of V.
@@ -183,7 +201,6 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) void prefill_mfma_kernel(Pre
 #pragma unroll
     for (int nn = 0; nn < NV; ++nn) {
       const u32x2_t vv = {rg.v[nn][0] & keep[0], rg.v[nn][1] & keep[1]};
-      o[nn] *= alpha;
       o[nn] = mfma_pv<DT>(vv, p_hi, o[nn]);
       o[nn] = mfma_pv<DT>(vv, p_lo, o[nn]);
     }
