@@ -69,7 +69,8 @@ typedef struct pa_cache_desc {
   int64_t num_blocks;    /* physical blocks in the pool, > 0 */
   int32_t num_kv_heads;  /* H_kv, > 0 */
   int32_t head_dim;      /* D, a multiple of X; the decode fast path covers 64 and 128 */
-  int32_t block_size;    /* tokens per block; 16 */
+  int32_t block_size;    /* tokens per block: 16 on the MFMA paths; other sizes (<= 1024) take the VALU decode
+                            kernel, and prefill takes 16 only */
   int32_t dtype;         /* pa_dtype of K and V */
 } pa_cache_desc;
 
@@ -79,7 +80,8 @@ typedef struct pa_decode_params {
   int32_t num_q_heads;         /* H_q, a multiple of num_kv_heads; query head j reads KV head j / (H_q / H_kv) */
   int32_t max_blocks_per_seq;  /* row stride (in int32) of block_tables, >= 1 */
   int32_t max_context_len;     /* host-known upper bound of context_lens[]; sizes the grid without a device->host copy */
-  int32_t partition_size;      /* tokens per split-context partition, a multiple of block_size in [16, 1024]; 0 = 512 */
+  int32_t partition_size;      /* tokens per split-context partition, a multiple of block_size, at most 1024;
+                                  0 = 512 rounded down to whole blocks */
   int32_t out_dtype;           /* PA_F32, or the cache dtype */
   pa_cache_desc cache;
   void* workspace;             /* device scratch for partition partials, >= paged_attention_workspace_bytes(); may be

@@ -130,10 +130,11 @@ def cache_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype_code: 
     return (num_blocks, num_kv_heads, head_dim // x, block_size, x), (num_blocks, num_kv_heads, head_dim, block_size)
 
 
-def alloc_kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda"):
+def alloc_kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda",
+                   block_size: int = BLOCK_SIZE):
     """Allocate an (uninitialised) K and V cache pair with torch."""
     torch = _torch()
-    ks, vs = cache_shapes(num_blocks, num_kv_heads, head_dim, torch_dtype_code(dtype))
+    ks, vs = cache_shapes(num_blocks, num_kv_heads, head_dim, torch_dtype_code(dtype), block_size)
     return torch.empty(ks, dtype=dtype, device=device), torch.empty(vs, dtype=dtype, device=device)
 
 

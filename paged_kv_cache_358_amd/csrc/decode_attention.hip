@@ -72,6 +72,7 @@ struct DecodeArgs {
   int32_t max_blocks;   // block-table row stride
   int32_t ctx_limit;    // min(max_context_len, max_blocks * 16)
   int32_t part_blocks;  // blocks per partition
+  int32_t block_tokens; // tokens per block (16 on the MFMA paths)
   int32_t max_parts;
   int32_t out_f32;
   int64_t num_blocks;
@@ -88,8 +89,8 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s) {
   return n < 0 ? 0 : (n > a.ctx_limit ? a.ctx_limit : n);
 }
 
-__device__ __forceinline__ int num_parts(int n, int part_blocks) {
-  const int pt = part_blocks * kBlockTokens;
+__device__ __forceinline__ int num_parts(int n, int part_blocks, int block_tokens) {
+  const int pt = part_blocks * block_tokens;
   const int p = (n + pt - 1) / pt;
   return p < 1 ? 1 : p;
 }
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
   const int h = rest % a.hkv;
   const int s = rest / a.hkv;
   const int n = clamp_ctx(a, s);
-  const int nparts = num_parts(n, a.part_blocks);
+  const int nparts = num_parts(n, a.part_blocks, kBlockTokens);
   if (p >= nparts) return;
 
   const int tid = threadIdx.x;
@@ -866,7 +867,7 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
   constexpr int X = 16 / sizeof(st);
   __shared__ float q_s[kMaxGenericD];
   __shared__ float sc[kMaxPartTokens];
-  __shared__ int32_t ids[kMaxPartTokens / kBlockTokens];
+  __shared__ int32_t ids[kMaxPartTokens];  // one per block of the partition (blocks of >= 1 token)
 
   const int wg = blockIdx.x;
   const int p = wg % a.max_parts;
@@ -874,7 +875,8 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
   const int j = rest % a.hq;
   const int s = rest / a.hq;
   const int n = clamp_ctx(a, s);
-  const int nparts = num_parts(n, a.part_blocks);
+  const int B = a.block_tokens;
+  const int nparts = num_parts(n, a.part_blocks, B);
   if (p >= nparts) return;
   const int lane = threadIdx.x;
   const int D = a.head_dim;
@@ -887,11 +889,11 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
   }
   const st* q = static_cast<const st*>(a.q);
   for (int d = lane; d < D; d += kWave) q_s[d] = Elem<DT>::to_float(q[row * D + d]);
-  const int pt = a.part_blocks * kBlockTokens;
+  const int pt = a.part_blocks * B;
   const int t0 = p * pt;
   const int t1 = min(n, t0 + pt);
-  const int bl0 = t0 / kBlockTokens;
-  const int nb = (t1 - t0 + kBlockTokens - 1) / kBlockTokens;
+  const int bl0 = t0 / B;
+  const int nb = (t1 - t0 + B - 1) / B;
   for (int b = lane; b < nb; b += kWave) {
     const int32_t id = a.block_tables[static_cast<int64_t>(s) * a.max_blocks + bl0 + b];
     ids[b] = (id >= 0 && id < a.num_blocks) ? id : -1;
@@ -900,16 +902,16 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
 
   const st* kc = static_cast<const st*>(a.k);
   const st* vc = static_cast<const st*>(a.v);
-  const int64_t head_stride = static_cast<int64_t>(D) * kBlockTokens;
+  const int64_t head_stride = static_cast<int64_t>(D) * B;
   float mx = -INFINITY;
   for (int t = t0 + lane; t < t1; t += kWave) {
-    const int id = ids[(t - t0) / kBlockTokens];
+    const int id = ids[(t - t0) / B];
     float x = -INFINITY;
     if (id >= 0) {
       const st* kb = kc + (static_cast<int64_t>(id) * a.hkv + h) * head_stride;
-      const int off = t % kBlockTokens;
+      const int off = t % B;
       float dot = 0.f;
-      for (int d = 0; d < D; ++d) dot = fmaf(q_s[d], Elem<DT>::to_float(kb[((d / X) * kBlockTokens + off) * X + d % X]), dot);
+      for (int d = 0; d < D; ++d) dot = fmaf(q_s[d], Elem<DT>::to_float(kb[((d / X) * B + off) * X + d % X]), dot);
       x = dot * a.scale_log2;
     }
     sc[t - t0] = x;
@@ -929,10 +931,10 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
   for (int d = lane; d < D; d += kWave) {
     float acc = 0.f;
     for (int t = t0; t < t1; ++t) {
-      const int id = ids[(t - t0) / kBlockTokens];
+      const int id = ids[(t - t0) / B];
       if (id < 0) continue;
       const st* vb = vc + (static_cast<int64_t>(id) * a.hkv + h) * head_stride;
-      acc = fmaf(sc[t - t0], Elem<DT>::to_float(vb[d * kBlockTokens + t % kBlockTokens]), acc);
+      acc = fmaf(sc[t - t0], Elem<DT>::to_float(vb[d * B + t % B]), acc);
     }
     const float res = L > 0.f ? acc / L : 0.f;
     if (single) {
@@ -967,7 +969,7 @@ __global__ __launch_bounds__(256) void reduce_partitions_kernel(DecodeArgs a) {
   const int n = clamp_ctx(a, s);
   if (n == 0) return;
   const int PB = a.part_blocks;
-  const int nb = (n + kBlockTokens - 1) / kBlockTokens;
+  const int nb = (n + a.block_tokens - 1) / a.block_tokens;
   const int np = (nb + PB - 1) / PB;
   if (np <= 1) return;
   const int D = a.head_dim;
@@ -1051,20 +1053,20 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
   if (!valid_dtype(c.dtype)) return PA_ERR_INVALID_ARG;
   if (p->out_dtype != PA_F32 && p->out_dtype != c.dtype) return PA_ERR_INVALID_ARG;
   if (c.head_dim % (16 / elem_bytes(c.dtype)) != 0) return PA_ERR_INVALID_ARG;
-  if (c.block_size != kBlockTokens) return PA_ERR_UNSUPPORTED;
-  if (c.head_dim > kMaxGenericD) return PA_ERR_UNSUPPORTED;
-  const int32_t pt = p->partition_size == 0 ? 512 : p->partition_size;
-  if (pt < kBlockTokens || pt > kMaxPartTokens || pt % kBlockTokens != 0) return PA_ERR_INVALID_ARG;
-  const int64_t limit64 = std::min<int64_t>(p->max_context_len, int64_t{p->max_blocks_per_seq} * kBlockTokens);
+  if (c.head_dim > kMaxGenericD || c.block_size > kMaxPartTokens) return PA_ERR_UNSUPPORTED;
+  const int32_t B = c.block_size;
+  // 0: 512 tokens, rounded down to whole blocks (at least one block)
+  const int32_t pt = p->partition_size == 0 ? std::max(B, 512 / B * B) : p->partition_size;
+  if (pt < B || pt > kMaxPartTokens || pt % B != 0) return PA_ERR_INVALID_ARG;
+  const int64_t limit64 = std::min<int64_t>(p->max_context_len, int64_t{p->max_blocks_per_seq} * B);
   const int32_t limit = static_cast<int32_t>(std::min<int64_t>(limit64, INT32_MAX));
   const int32_t parts = std::max<int32_t>(1, static_cast<int32_t>((int64_t{limit} + pt - 1) / pt));
   if (parts > 8192) return PA_ERR_UNSUPPORTED;
   out->part_tokens = pt;
-  out->part_blocks = pt / kBlockTokens;
+  out->part_blocks = pt / B;
   out->ctx_limit = limit;
   out->max_parts = parts;
-  // Partials [S][H_q][parts][D] and [S][H_q][parts][2] (fp32), then the split kernel's
-  // block prefix sums [S + 1] (int32).
+  // Partials [S][H_q][parts][D] and [S][H_q][parts][2] (fp32),
   const size_t rows = static_cast<size_t>(p->num_seqs) * p->num_q_heads * parts;
   // then the per (sequence, KV head) arrival counters [S * H_kv] (uint64; the partials end 8-byte aligned)
   out->counter_offset = rows * (static_cast<size_t>(c.head_dim) + 2) * sizeof(float);
@@ -1140,7 +1142,8 @@ int32_t launch_split(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEven
 template <int DT>
 int32_t launch_decode(DecodeArgs args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   const int64_t D = args.head_dim;
-  const bool fast = DT != PA_F32 && (D == 64 || D == 128) && args.group <= 16;
+  // The MFMA kernels take 16-token blocks; other block sizes take the VALU kernel.
+  const bool fast = DT != PA_F32 && (D == 64 || D == 128) && args.group <= 16 && args.block_tokens == kBlockTokens;
   args.part_cost = kPartCost;
   args.ctx_cost = kCtxCost;
   // The split kernel indexes the weighted blocks of all (sequence, KV head) pairs with int32.
@@ -1226,6 +1229,7 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   a.max_blocks = p->max_blocks_per_seq;
   a.ctx_limit = plan.ctx_limit;
   a.part_blocks = plan.part_blocks;
+  a.block_tokens = p->cache.block_size;
   a.max_parts = plan.max_parts;
   a.out_f32 = p->out_dtype == PA_F32 ? 1 : 0;
   a.num_blocks = p->cache.num_blocks;

@@ -54,7 +54,8 @@ class PagedDecode:
             self.alloc.add(FOREIGN)
             self.alloc.append(FOREIGN, plan.preoccupy_blocks * cfg.block_size)
         tdt = TORCH_DTYPE[cfg.dtype]
-        self.k_cache, self.v_cache = pa.alloc_kv_cache(plan.num_blocks, cfg.num_kv_heads, cfg.head_dim, tdt, device)
+        self.k_cache, self.v_cache = pa.alloc_kv_cache(plan.num_blocks, cfg.num_kv_heads, cfg.head_dim, tdt, device,
+                                                       cfg.block_size)
         if poison:  # every slot not written below holds NaN and must never be read
             self.k_cache.fill_(float("nan"))
             self.v_cache.fill_(float("nan"))
@@ -74,7 +75,7 @@ class PagedDecode:
                 self.truth[s] = (k, v)
             pa.kv_append(to_torch(k, cfg.dtype, device), to_torch(v, cfg.dtype, device),
                          torch.from_numpy(slots).to(device), self.k_cache, self.v_cache)
-        self.max_blocks = max(1, int(synth.blocks_for(self.lens.max() if self.lens.size else 0).max()))
+        self.max_blocks = max(1, int(synth.blocks_for(self.lens.max() if self.lens.size else 0, cfg.block_size).max()))
         tables, lens_ = self.alloc.build_batch(list(range(cfg.num_seqs)), self.max_blocks)
         assert np.array_equal(lens_, self.lens)
         self.tables_np = tables

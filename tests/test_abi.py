@@ -58,12 +58,19 @@ def test_workspace_bytes():
     assert ws(ctypes.byref(p)) == expect(4, 64, 8, 256, 128)
     p = _params(maxb=100, maxctx=1000, part=256)
     assert ws(ctypes.byref(p)) == expect(4, 4, 4, 4, 64)
+    # 32-token blocks: the table covers 100 * 32 tokens; default partitions of 512 tokens
+    p = _params(maxb=100, maxctx=5000, bs=32)
+    assert ws(ctypes.byref(p)) == expect(4, 4, 4, 7, 64)          # min(5000, 3200) / 512 -> 7
+    # 48-token blocks: the default partition rounds 512 down to 480
+    p = _params(maxb=100, maxctx=1000, bs=48)
+    assert ws(ctypes.byref(p)) == expect(4, 4, 4, 3, 64)
     assert ws(None) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(hq=6, hkv=4), pa.PA_ERR_INVALID_ARG),          # H_q not a multiple of H_kv
-    (dict(bs=8), pa.PA_ERR_UNSUPPORTED),                 # block size other than 16
+    (dict(bs=2048), pa.PA_ERR_UNSUPPORTED),              # a block larger than any partition
+    (dict(bs=32, part=48), pa.PA_ERR_INVALID_ARG),       # partition not a multiple of the block size
     (dict(part=100), pa.PA_ERR_INVALID_ARG),             # partition not a multiple of 16
     (dict(part=2048), pa.PA_ERR_INVALID_ARG),
     (dict(d=66), pa.PA_ERR_INVALID_ARG),                 # head_dim not a multiple of 16 bytes

@@ -14,8 +14,8 @@ from paged_setup import TORCH_DTYPE, raw_view, storage_raw, to_torch
 pytestmark = pytest.mark.gpu
 
 
-def random_cache(num_blocks, H, D, dtype, seed):
-    k_cache, v_cache = pa.alloc_kv_cache(num_blocks, H, D, TORCH_DTYPE[dtype])
+def random_cache(num_blocks, H, D, dtype, seed, block_size=16):
+    k_cache, v_cache = pa.alloc_kv_cache(num_blocks, H, D, TORCH_DTYPE[dtype], block_size=block_size)
     rng = synth.rng(100, seed)
     kh = synth.encode(rng.standard_normal(k_cache.numel(), dtype=np.float32), dtype)
     vh = synth.encode(rng.standard_normal(v_cache.numel(), dtype=np.float32), dtype)
@@ -24,10 +24,11 @@ def random_cache(num_blocks, H, D, dtype, seed):
     return k_cache, v_cache, kh, vh
 
 
-@pytest.mark.parametrize("dtype,H,D", [("f32", 4, 64), ("bf16", 8, 128), ("f16", 3, 64), ("bf16", 32, 128)])
-def test_kv_append_bitwise(dtype, H, D):
-    B, N = 16, 40
-    k_cache, v_cache, kh, vh = random_cache(N, H, D, dtype, 1)
+@pytest.mark.parametrize("dtype,H,D,B", [("f32", 4, 64, 16), ("bf16", 8, 128, 16), ("f16", 3, 64, 16),
+                                          ("bf16", 32, 128, 16), ("bf16", 8, 128, 32), ("f32", 2, 64, 8)])
+def test_kv_append_bitwise(dtype, H, D, B):
+    N = 40
+    k_cache, v_cache, kh, vh = random_cache(N, H, D, dtype, 1, B)
     rng = np.random.default_rng(2)
     T = 300
     slots = rng.choice(N * B, size=T, replace=False).astype(np.int32)

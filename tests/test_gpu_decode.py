@@ -269,3 +269,17 @@ def test_start_and_stop_events_bracket_the_kernels(part):
                               max_context_len=0, start_event=start, stop_event=stop)
     stop.synchronize()
     assert start.elapsed_time(stop) >= 0.0
+
+
+@pytest.mark.parametrize("dtype,B", [("bf16", 8), ("bf16", 32), ("f32", 32), ("f16", 64)])
+def test_other_block_sizes(dtype, B):
+    # Blocks of other than 16 tokens take the VALU kernel (and the partition merge); lengths
+    # around the block size, several blocks and several partitions.
+    lens = [1, B - 1, B, B + 1, 2 * B + 3, 300, 1000]
+    cfg = synth.scaled(synth.C3, lens=lens, dtype=dtype, block_size=B)
+    pd = PagedDecode(cfg)
+    assert pd.k_cache.shape[3] == B
+    out = pd.run()
+    assert max_err(out, pd) <= tol_for(dtype)
+    out2 = pd.run(partition_size=4 * B)
+    assert max_err(out2, pd) <= tol_for(dtype)
