@@ -11,6 +11,9 @@ The pages' comparison:
   forks share blocks until they diverge ("Copy-on-Write for Parallel Sampling").
 * Less waste means more requests in the same memory, the source of the pages' 2-4x
   throughput (ml-canon page, "where the x2-4 comes from").
+* Beam search and shared system prompts: beams and requests with a common prefix hold its
+  blocks once ("Stop Wasting GPU Memory" page, "Beam Search Optimization"; ml-canon page,
+  prefix sharing).
 
 The paged side is counted by running the library's own block allocator over the lengths
 (``BlockAllocator``), so forks and copy-on-write are the real ones; the contiguous side is
@@ -20,6 +23,7 @@ the plain arithmetic of a max-length reservation.
 """
 from __future__ import annotations
 
+import hashlib
 import json
 
 import numpy as np
@@ -74,6 +78,89 @@ def sampling_footprint(prompts: int, samples: int, prefix_len: int, new_tokens: 
             "saved_frac": round(1.0 - shared / unshared, 4)}
 
 
+def beam_search_footprint(width: int, prompt_len: int, steps: int, block_size: int = 16, seed: int = 0,
+                          skew: float = 1.5, alloc_factory=None) -> dict:
+    """Beam search as a process tree ("Stop Wasting GPU Memory" page, Technical Details, "Beam
+    Search Optimization"): each step every new beam forks the beam it extends, the old beams
+    are freed (a pruned beam's blocks go back to the pool when no beam holds them), and every
+    beam appends its token (copying a shared partial block on the first write).  Parents are
+    drawn from a seeded generator, beam r with weight r^-skew (skew 0: uniform; larger: a few
+    beams take most of the children, as a search that keeps extending its best paths).
+    Returns peak and mean blocks with sharing and without (every beam holding its whole
+    history).  `alloc_factory(num_blocks, block_size)` builds the allocator (the library's by
+    default)."""
+    rng = np.random.default_rng(seed)
+    worst = width * -(-(prompt_len + steps) // block_size)
+    alloc = (alloc_factory or BlockAllocator)(worst + width + 1, block_size)
+    next_id = 0
+    alloc.add(next_id)
+    alloc.append(next_id, prompt_len)
+    beams = [next_id] * width
+    live = {next_id}
+    shared, unshared = [], []
+    weights = 1.0 / np.arange(1, width + 1) ** skew
+    weights /= weights.sum()
+    for t in range(steps):
+        parents = rng.choice(np.arange(width), size=width, p=weights) if t else np.zeros(width, int)
+        children = []
+        for par in parents:
+            next_id += 1
+            alloc.fork(beams[par], next_id)
+            children.append(next_id)
+        for old in sorted(live):
+            alloc.free(old)
+        live = set(children)
+        beams = children
+        alloc.append_batch(children, np.ones(len(children), np.int32))
+        shared.append(alloc.num_blocks - alloc.num_free())
+        unshared.append(width * -(-(prompt_len + t + 1) // block_size))
+    return {"width": width, "prompt_len": prompt_len, "steps": steps, "skew": skew,
+            "peak_blocks": int(max(shared)), "peak_blocks_without_sharing": int(max(unshared)),
+            "mean_saved_frac": round(1.0 - float(np.mean(shared)) / float(np.mean(unshared)), 4),
+            "peak_saved_frac": round(1.0 - max(shared) / max(unshared), 4)}
+
+
+class PrefixIndex:
+    """Shared prompts held once: the index maps a prompt's tokens to a sequence that holds its
+    blocks, and a request with that prompt forks from it (ml-canon page, "prefix sharing":
+    a long system prompt stored once and referenced from every request, copy-on-write)."""
+
+    def __init__(self, alloc, first_id: int):
+        self.alloc = alloc
+        self._holders = {}
+        self._next = first_id
+
+    def holder(self, prompt) -> int:
+        """The sequence holding `prompt` (tokens), allocated on first use."""
+        key = hashlib.sha256(np.asarray(prompt, dtype=np.int64).tobytes()).hexdigest()
+        if key not in self._holders:
+            h = self._next
+            self._next += 1
+            self.alloc.add(h)
+            self.alloc.append(h, len(prompt))
+            self._holders[key] = h
+        return self._holders[key]
+
+
+def shared_prompt_footprint(prompt_len: int, suffix_lens, block_size: int = 16, seed: int = 0,
+                            alloc_factory=None) -> dict:
+    """Requests that share one system prompt of `prompt_len` tokens, each followed by its own
+    suffix: through a PrefixIndex (one holder, every request forks from it) and without."""
+    suffix_lens = [int(x) for x in suffix_lens]
+    prompt = np.random.default_rng(seed).integers(0, 32000, size=prompt_len)
+    need = -(-prompt_len // block_size) + sum(-(-(prompt_len + s) // block_size) for s in suffix_lens)
+    alloc = (alloc_factory or BlockAllocator)(need + 1, block_size)
+    index = PrefixIndex(alloc, first_id=len(suffix_lens))
+    for r, s in enumerate(suffix_lens):
+        alloc.fork(index.holder(prompt), r)
+        if s:
+            alloc.append(r, s)
+    shared = alloc.num_blocks - alloc.num_free()
+    unshared = sum(-(-(prompt_len + s) // block_size) for s in suffix_lens)
+    return {"requests": len(suffix_lens), "prompt_len": prompt_len, "blocks": shared,
+            "blocks_without_sharing": unshared, "saved_frac": round(1.0 - shared / unshared, 4)}
+
+
 def max_batch(budget_slots: int, lens, block_size: int, reserve: int) -> dict:
     """Requests (taken in order) that fit in `budget_slots` token slots, paged and contiguous."""
     used, paged = 0, 0
@@ -111,6 +198,11 @@ def study() -> list[dict]:
     c4 = synth.C4
     rows.append({"workload": c4.name, "prompts": c4.num_prompts, "samples": c4.samples,
                  "paged_after_all_steps": sampling_footprint(c4.num_prompts, c4.samples, c4.prefix_len, c4.steps)})
+    for width, prompt, steps in ((4, 512, 256), (8, 1000, 200)):
+        for skew in (0.0, 1.5):
+            rows.append({"workload": "beam_search", **beam_search_footprint(width, prompt, steps, skew=skew)})
+    suffixes = np.random.default_rng(7).integers(16, 512, size=256).tolist()
+    rows.append({"workload": "shared_system_prompt", **shared_prompt_footprint(2000, suffixes)})
     return rows
 
 

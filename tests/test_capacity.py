@@ -48,3 +48,90 @@ def test_study_rows_follow_the_pages_claims():
         assert all(b["paged"] >= b["contiguous"] for b in r["max_batch"])
     assert rows["c3_gqa_bf16"]["contiguous"]["waste_frac"] > 0.6   # lognormal lengths under an 8192 reservation
     assert np.isclose(rows["c4_cow_sampling_bf16"]["paged_after_all_steps"]["saved_frac"], 0.7233, atol=1e-4)
+
+
+class _ModelAllocator:
+    """The oracle's allocator model behind the library allocator's method names, so the same
+    beam and prefix traces run through both and their block counts can be compared."""
+
+    def __init__(self, num_blocks, block_size):
+        from oracle.allocator_model import BlockAllocatorModel
+        self.m = BlockAllocatorModel(num_blocks, block_size)
+        self.num_blocks = num_blocks
+        self.log = []
+
+    def add(self, seq):
+        self.m.add(seq)
+
+    def fork(self, parent, child):
+        self.m.fork(parent, child)
+
+    def append(self, seq, n=1):
+        self.log.append(self.m.append(seq, n))
+
+    def append_batch(self, seqs, counts):
+        for s, n in zip(seqs, counts):
+            self.append(int(s), int(n))
+
+    def free(self, seq):
+        self.m.free_seq(seq)
+
+    def num_free(self):
+        return self.m.num_free()
+
+
+def test_beam_of_width_one_shares_nothing():
+    out = capacity.beam_search_footprint(1, 100, 60)
+    assert out["peak_blocks"] == out["peak_blocks_without_sharing"] == -(-160 // 16)
+    assert out["mean_saved_frac"] == 0.0
+
+
+@pytest.mark.parametrize("width,prompt,steps,skew", [(4, 40, 50, 0.0), (6, 33, 70, 1.5), (3, 16, 33, 3.0)])
+def test_beam_counts_match_the_allocator_model(width, prompt, steps, skew):
+    lib = capacity.beam_search_footprint(width, prompt, steps, skew=skew, seed=5)
+    model = capacity.beam_search_footprint(width, prompt, steps, skew=skew, seed=5, alloc_factory=_ModelAllocator)
+    assert lib == model
+    # every beam holds at least its own last block and all of them the shared prompt
+    assert lib["peak_blocks"] >= -(-(prompt + steps) // 16) + width - 1
+
+
+def test_beam_with_one_surviving_parent_is_a_tree_of_the_last_blocks():
+    # skew so large that every child extends beam 0: after each step all beams share the
+    # whole history except the partial block each one copied (or, at a block boundary, opened)
+    out = capacity.beam_search_footprint(4, 32, 20, skew=60.0)
+    n = 32 + 20
+    assert out["peak_blocks"] <= n // 16 + 4
+
+
+@pytest.mark.parametrize("prompt,suffixes", [(2000, [0, 1, 16, 17, 500]), (64, [16, 5, 0]), (7, [1, 9, 30])])
+def test_shared_prompt_closed_form(prompt, suffixes):
+    # the holder keeps ceil(P/B) blocks; a request with a suffix copies the shared partial
+    # block (if any) and owns ceil((P+s)/B) - floor(P/B) blocks; one without owns nothing
+    B = 16
+    out = capacity.shared_prompt_footprint(prompt, suffixes)
+    own = sum(-(-(prompt + s) // B) - prompt // B for s in suffixes if s)
+    assert out["blocks"] == -(-prompt // B) + own
+    assert out["blocks_without_sharing"] == sum(-(-(prompt + s) // B) for s in suffixes)
+    model = capacity.shared_prompt_footprint(prompt, suffixes, alloc_factory=_ModelAllocator)
+    assert model == out
+
+
+def test_prefix_index_holds_each_prompt_once():
+    alloc = _ModelAllocator(64, 16)
+    index = capacity.PrefixIndex(alloc, first_id=100)
+    a, b = np.arange(40), np.arange(40) + 1
+    ha = index.holder(a)
+    assert index.holder(a.copy()) == ha and index.holder(list(a)) == ha
+    hb = index.holder(b)
+    assert hb != ha
+    assert alloc.num_free() == 64 - 2 * 3          # two prompts of 40 tokens, 3 blocks each
+    assert alloc.m.table(ha) != alloc.m.table(hb)
+
+
+def test_study_reports_the_sharing_rows():
+    rows = capacity.study()
+    beams = [r for r in rows if r["workload"] == "beam_search"]
+    assert {(r["width"], r["skew"]) for r in beams} == {(4, 0.0), (4, 1.5), (8, 0.0), (8, 1.5)}
+    assert all(r["mean_saved_frac"] > 0.5 for r in beams)
+    (sp,) = [r for r in rows if r["workload"] == "shared_system_prompt"]
+    assert sp["saved_frac"] > 0.8
