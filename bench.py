@@ -242,8 +242,11 @@ def main():
         result["logical_attention_bytes_per_launch"] = int(np.mean(logical))
         result["effective_logical_gbs"] = round(float(np.mean(logical)) / mean_main_s / 1e9, 1)
 
-    result["cache_ops"] = cache_ops_probe(layer, step_inputs[-1], step_tables[-1] if shared else layer.last_tables,
-                                          block_bytes)
+    last_tables = (step_tables[-1] if shared else layer.last_tables).copy()
+    result["cache_ops"] = cache_ops_probe(layer, step_inputs[-1], last_tables, block_bytes)
+    if not shared:
+        result["decode_probes"] = decode_probes(layer, step_inputs[-1][0], out, scale, last_tables,
+                                                step_lens[-1], part, attn[-1])
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, cfg, lens0, kvbpt)
@@ -299,6 +302,71 @@ def cache_ops_probe(layer, step_input, tables, block_bytes, reps=20, max_pairs=4
                             "achieved_gbs": round(moved / t / 1e9, 1),
                             "frac": round(moved / t / 1e9 / PEAK_HBM_GBS, 4)}
     return out
+
+
+def decode_probes(layer, q, out, scale, tables, lens, part, nbytes, reps=20, flush_mib=1024):
+    """The attention call alone, after the timed steps, on the last step's batch: with the
+    step's (shuffled) block tables and with identity tables (each sequence's blocks contiguous
+    in the pool, so the table lookup gathers nothing), each warm (launches back to back) and
+    cold (a 1 GiB buffer written between launches evicts L2 and the 256 MiB last-level cache).
+    The identity tables point at other blocks' data: only the timing is meaningful.  Last, a
+    STREAM-style copy as a reference for the achievable HBM rate: block_copy of the pool's
+    first half onto its second half (this overwrites cache contents; nothing reads them after)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_358_amd import block_copy, paged_attention_decode
+
+    S = len(lens)
+    lens = np.asarray(lens, dtype=np.int64)
+    nb = -(-lens // 16)
+    num_blocks = layer.k_cache.shape[0]
+    if int(nb.sum()) > num_blocks:
+        return None
+    ident = np.full_like(np.asarray(tables), -1)
+    off = np.concatenate([[0], np.cumsum(nb)])
+    for s_ in range(S):
+        ident[s_, :nb[s_]] = np.arange(off[s_], off[s_ + 1])
+    dev_lens = torch.from_numpy(lens.astype(np.int32)).cuda()
+    flush = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
+    res = {}
+    with torch.cuda.stream(layer.stream):
+        for name, tb in (("shuffled", tables), ("identity", ident)):
+            dev_t = torch.from_numpy(np.ascontiguousarray(tb, dtype=np.int32)).cuda()
+            for mode in ("warm", "cold"):
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+                for a, b in ev:
+                    a.record(layer.stream)
+                    b.record(layer.stream)
+                for i in range(reps + 1):
+                    if mode == "cold":
+                        flush.fill_(i & 0xFF)
+                    e = ev[i - 1] if i else (None, None)          # launch 0 is a warm-up
+                    paged_attention_decode(q, layer.k_cache, layer.v_cache, dev_t, dev_lens, scale, out,
+                                           max_context_len=int(lens.max()), partition_size=part,
+                                           workspace=layer.workspace, stream=layer.stream,
+                                           start_event=e[0], stop_event=e[1])
+                torch.cuda.synchronize()
+                ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+                res[f"{name}_{mode}_ms"] = round(ms, 4)
+                res[f"{name}_{mode}_gbs"] = round(nbytes / (ms / 1e3) / 1e9, 1)
+    res["table_indirection_cost_cold"] = round(res["shuffled_cold_ms"] / res["identity_cold_ms"] - 1.0, 4)
+    del flush
+    half = num_blocks // 2
+    pairs = torch.from_numpy(np.stack([np.arange(half), np.arange(half) + half], axis=1).astype(np.int32)).cuda()
+    moved = 2 * half * layer.k_cache[0].numel() * layer.k_cache.element_size() * 2   # K and V, read and written
+    with torch.cuda.stream(layer.stream):
+        block_copy(layer.k_cache, layer.v_cache, pairs, stream=layer.stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(layer.stream)
+        for _ in range(10):
+            block_copy(layer.k_cache, layer.v_cache, pairs, stream=layer.stream)
+        e1.record(layer.stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 10 / 1e3
+    res["copy_probe_bytes"] = int(moved)
+    res["copy_probe_gbs"] = round(moved / t / 1e9, 1)
+    res["shuffled_cold_frac_of_copy_probe"] = round(res["shuffled_cold_gbs"] / res["copy_probe_gbs"], 4)
+    return res
 
 
 def run_prefill(args):
