@@ -34,11 +34,15 @@ class CacheDesc(ctypes.Structure):
                 ("dtype", _i32)]
 
 
+class SharedPrefix(ctypes.Structure):
+    _fields_ = [("groups", _vp), ("seq_prefix", _vp), ("num_groups", _i32)]
+
+
 class DecodeParams(ctypes.Structure):
     _fields_ = [("num_seqs", _i32), ("num_q_heads", _i32), ("max_blocks_per_seq", _i32), ("max_context_len", _i32),
                 ("partition_size", _i32), ("out_dtype", _i32), ("cache", CacheDesc), ("workspace", _vp),
                 ("workspace_bytes", _sz), ("stream", _vp), ("start_event", _vp),
-                ("stop_event", _vp)]
+                ("stop_event", _vp), ("shared", ctypes.POINTER(SharedPrefix))]
 
 
 class PrefillParams(ctypes.Structure):
@@ -73,6 +77,7 @@ SIGNATURES = {
     "pa_refcount": (_i32, [_vp, _i32]),
     "pa_free_list": (_i32, [_vp, _P32, _i32, _P32]),
     "pa_build_batch": (_i32, [_vp, _P64, _i32, _i32, _P32, _P32]),
+    "pa_shared_prefixes": (_i32, [_P32, _P32, _i32, _i32, _i32, _i32, _i32, _P32, _P32, _i32, _P32]),
 }
 
 
@@ -181,7 +186,8 @@ def _require_device(*ts):
 
 # ----------------------------------------------------------------------------- kernels
 def decode_params(q, k_cache, v_cache, block_tables, out, max_context_len: int, partition_size: int = 0,
-                  workspace=None, stream=None, start_event=None, stop_event=None) -> DecodeParams:
+                  workspace=None, stream=None, start_event=None, stop_event=None, shared=None) -> DecodeParams:
+    """``shared`` is a SharedPrefix (kept alive by the caller for the call) or None."""
     c = cache_desc(k_cache, v_cache)
     S, hq, d = q.shape
     if d != c.head_dim:
@@ -189,18 +195,47 @@ def decode_params(q, k_cache, v_cache, block_tables, out, max_context_len: int, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return DecodeParams(S, hq, block_tables.shape[1], int(max_context_len), int(partition_size),
                         torch_dtype_code(out.dtype), c, _ptr(workspace).value, ws_bytes,
-                        _stream_ptr(stream).value, _event_ptr(start_event), _event_ptr(stop_event))
+                        _stream_ptr(stream).value, _event_ptr(start_event), _event_ptr(stop_event),
+                        None if shared is None else ctypes.pointer(shared))
 
 
 def paged_attention_workspace_bytes(q, k_cache, v_cache, block_tables, out, max_context_len: int,
-                                    partition_size: int = 0) -> int:
-    p = decode_params(q, k_cache, v_cache, block_tables, out, max_context_len, partition_size)
+                                    partition_size: int = 0, shared: bool = False) -> int:
+    """Workspace bytes of a decode call; ``shared=True`` includes the prefix partials that calls with
+    shared prefixes need."""
+    sh = SharedPrefix(None, None, 0) if shared else None
+    p = decode_params(q, k_cache, v_cache, block_tables, out, max_context_len, partition_size, shared=sh)
     return int(lib.paged_attention_workspace_bytes(ctypes.byref(p)))
+
+
+def shared_prefixes(tables, lens, max_members: int, min_blocks: int = 1, block_size: int = BLOCK_SIZE,
+                    seq_prefix_out=None, groups_out=None):
+    """Groups of consecutive sequences whose host block tables (int32 [S, max_blocks]) share leading
+    full blocks: returns (seq_prefix int32[S], groups int32[G, 3] of (first, members, prefix blocks)).
+    ``max_members`` is at most 16 // (H_q / H_kv) for paged_attention_decode.  Optional C-contiguous
+    int32 outputs of at least [S] and [S // 2, 3] receive the result in place."""
+    t, tptr = _as_i32(tables)
+    ln, lptr = _as_i32(lens)
+    S = int(ln.size)
+    width = int(t.shape[1]) if t.ndim == 2 else 1
+    if t.ndim != 2 or t.shape[0] < S:
+        raise ValueError("tables must be int32 [S, max_blocks]")
+    sp = np.empty(max(S, 1), np.int32) if seq_prefix_out is None else seq_prefix_out
+    cap = max(S // 2, 1)
+    gr = np.empty((cap, 3), np.int32) if groups_out is None else groups_out
+    for arr, n in ((sp, S), (gr, 3 * cap)):
+        if arr.dtype != np.int32 or not arr.flags.c_contiguous or arr.size < n:
+            raise ValueError("shared_prefixes: outputs must be C-contiguous int32 of sufficient size")
+    ng = ctypes.c_int32(0)
+    _check(lib.pa_shared_prefixes(tptr, lptr, S, width, int(block_size), int(max_members), int(min_blocks),
+                                  sp.ctypes.data_as(_P32), gr.ctypes.data_as(_P32), gr.shape[0] if gr.ndim == 2
+                                  else gr.size // 3, ctypes.byref(ng)), "pa_shared_prefixes")
+    return sp[:S], gr.reshape(-1, 3)[:ng.value]
 
 
 def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
                            max_context_len: int, partition_size: int = 0, workspace=None, stream=None,
-                           start_event=None, stop_event=None):
+                           start_event=None, stop_event=None, shared=None):
     """out[s, j] = softmax attention of q[s, j] over sequence s's cached tokens.
 
     q [S, H_q, D] and out [S, H_q, D] (fp32 or the cache dtype), block_tables int32
@@ -209,6 +244,8 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     ``paged_attention_workspace_bytes`` bytes) is allocated here if omitted.
     ``start_event`` / ``stop_event`` (torch.cuda.Events recorded once before) mark the
     start of the call's first kernel and the end of its last one.
+    ``shared`` = (groups int32 [G, 3], seq_prefix int32 [S]) device tensors from
+    ``shared_prefixes``: the groups' leading blocks are read once for all members.
     """
     torch = _torch()
     _require_device(q, k_cache, v_cache, block_tables, context_lens, out)
@@ -218,13 +255,22 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         raise ValueError("q must have the cache dtype")
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
+    sh = None
+    if shared is not None:
+        groups, seq_prefix = shared
+        _require_device(groups, seq_prefix)
+        if groups.dtype != torch.int32 or seq_prefix.dtype != torch.int32:
+            raise ValueError("shared groups and seq_prefix must be int32")
+        if (groups.numel() and (groups.dim() != 2 or groups.shape[1] != 3)) or seq_prefix.numel() != q.shape[0]:
+            raise ValueError("shared = (groups [G, 3], seq_prefix [S])")
+        sh = SharedPrefix(_ptr(groups).value, _ptr(seq_prefix).value, groups.shape[0] if groups.numel() else 0)
     if workspace is None:
         need = paged_attention_workspace_bytes(q, k_cache, v_cache, block_tables, out, max_context_len,
-                                               partition_size)
+                                               partition_size, shared=sh is not None)
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     p = decode_params(q, k_cache, v_cache, block_tables, out, max_context_len, partition_size, workspace, stream,
-                      start_event, stop_event)
+                      start_event, stop_event, sh)
     _check(lib.paged_attention_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
                                       float(scale), _ptr(out), ctypes.byref(p)), "paged_attention_decode")
     return out
@@ -424,7 +470,7 @@ class BlockAllocator:
         return tables_out[:n, :max_blocks], lens_out[:n]
 
 
-__all__ = ["paged_attention_decode", "paged_attention_workspace_bytes", "paged_attention_prefill", "kv_append", "block_copy", "stage_copy",
+__all__ = ["paged_attention_decode", "paged_attention_workspace_bytes", "shared_prefixes", "SharedPrefix", "paged_attention_prefill", "kv_append", "block_copy", "stage_copy",
            "stage_append",
            "BlockAllocator",
            "alloc_kv_cache", "cache_shapes", "cache_desc", "PagedAttnError", "lib", "LIB_PATH", "SIGNATURES",

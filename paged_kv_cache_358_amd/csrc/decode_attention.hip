@@ -82,6 +82,13 @@ struct DecodeArgs {
   int32_t ctx_cost;   // split: balance weight of a (sequence, KV head) context's end, in blocks
   uint64_t* run_done; // split: per (sequence, KV head) arrival counters [S * H_kv] (workspace); tag << 32 | partitions
   uint32_t launch_tag; // split: this launch's counter tag
+  // Shared leading blocks (split kernel only).  The prefix pass walks the groups; the rest pass
+  // skips each sequence's prefix blocks and merges the prefix pass's partial into its output.
+  const int32_t* share_groups;  // [num_groups][3]: first sequence, members, prefix blocks
+  const int32_t* share_skip;    // [S]: prefix blocks of sequence s covered by its group, 0 if none
+  float* pre_o;                 // [S][H_q][D] prefix partial outputs (normalised)
+  float* pre_ml;                // [S][H_q][2] prefix partial (max in log2 units, sum)
+  int32_t num_groups;
 };
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s) {
@@ -324,6 +331,15 @@ constexpr int kPersistRing = 2;     // ring depth of the split kernel
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X, each with its own L2
 constexpr int kMaxSplitGrid = 4095;  // chunks (workgroups) of the split kernel, at most
 
+// Modes of the split kernel.  kPlain: every sequence's whole context.  kPrefix: the contexts are
+// the groups of sequences that share leading blocks; a group's context is its prefix blocks, read
+// through its first member's table, and its query columns are (member, query head of the KV
+// head) pairs; results go to the prefix partials.  kRest: every sequence's context minus the
+// blocks its group covered; the output merges the prefix partial in.
+constexpr int kPlain = 0;
+constexpr int kPrefix = 1;
+constexpr int kRest = 2;
+
 // Work split.  The partitions of all (sequence, KV head) pairs are laid end to end in
 // (sequence, KV head, partition) order, each weighted by its block count plus a fixed cost
 // per partition (its query and table loads, the ring's minimum depth, the segment's merge
@@ -389,7 +405,7 @@ struct Item {
 // loaded one partition ahead into the other of two slots (A/B), so no loaded value is copied
 // before it is used.  Per-block arithmetic is that of decode_mfma_kernel.
 // At least two waves per SIMD: the compiler keeps the kernel within 256 VGPRs.
-template <int DT, int D, int NBUF>
+template <int DT, int D, int NBUF, int MODE>
 __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(
     DecodeArgs a) {
   constexpr int KK = D / 32;
@@ -402,6 +418,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   __shared__ int32_t blkpre[kMaxScanSeqs + 1];  // H_kv * (weight of the sequences before s)
   __shared__ int32_t nb_s[kMaxScanSeqs];        // blocks of sequence s
   __shared__ int32_t ctx_s[kMaxScanSeqs];       // clamped context length of s
+  __shared__ int32_t skip_s[MODE == kRest ? kMaxScanSeqs : 1];  // kRest: leading blocks of s already covered
   __shared__ int32_t scan[kThreads];
   __shared__ int32_t merge_flag[2];  // thread 0's arrivals completed these contexts
   static_assert(kWaves * 16 * D > kMaxSplitGrid, "run starts of one context fit in sm_o");
@@ -411,7 +428,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int S = a.num_seqs;
+  const int S = MODE == kPrefix ? a.num_groups : a.num_seqs;  // contexts are groups in the prefix pass
   const int PB = a.part_blocks;
   const int hkv = a.hkv;
   const int g = a.group;
@@ -434,12 +451,43 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     k = r * R + (t % kXcds) * (R / kXcds) + t / kXcds;
   }
 
+  // kPrefix: group v's first sequence and members, clamped so that every row stays inside the
+  // batch and the columns inside one 16-wide tile.
+  auto group_first = [&](int v) {
+    const int f = a.share_groups[3 * v];
+    return f < 0 ? 0 : (f >= a.num_seqs ? a.num_seqs - 1 : f);
+  };
+  auto group_members = [&](int v, int first) {
+    const int mm = a.share_groups[3 * v + 1];
+    return max(0, min(min(mm, a.num_seqs - first), 16 / g));
+  };
+  // Context length, blocks to stream and blocks skipped of context s.
+  auto shape_of = [&](int s, int& n, int& nb, int& skip) {
+    skip = 0;
+    if constexpr (MODE == kPrefix) {
+      const int kb = max(0, min(a.share_groups[3 * s + 2], min(a.max_blocks, a.ctx_limit / kBlockTokens)));
+      n = kb * kBlockTokens;
+      nb = kb;
+    } else {
+      n = clamp_ctx(a, s);
+      nb = (n + kBlockTokens - 1) / kBlockTokens;
+      if constexpr (MODE == kRest) {
+        skip = max(0, min(a.share_skip[s], nb));
+        nb -= skip;
+      }
+    }
+  };
+
   // ---- prefix sums of context weights over sequences (every workgroup builds its own copy)
   const int per = (S + kThreads - 1) / kThreads;
   int cnt = 0;
   for (int j = 0; j < per; ++j) {
     const int s = tid * per + j;
-    if (s < S) cnt += wnb_of((clamp_ctx(a, s) + kBlockTokens - 1) / kBlockTokens);
+    if (s < S) {
+      int n, nb, skip;
+      shape_of(s, n, nb, skip);
+      cnt += wnb_of(nb);
+    }
   }
   scan[tid] = cnt;
   __syncthreads();
@@ -454,11 +502,12 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     for (int j = 0; j < per; ++j) {
       const int s = tid * per + j;
       if (s < S) {
-        const int n = clamp_ctx(a, s);
-        const int nb = (n + kBlockTokens - 1) / kBlockTokens;
+        int n, nb, skip;
+        shape_of(s, n, nb, skip);
         blkpre[s] = base * hkv;
         nb_s[s] = nb;
         ctx_s[s] = n;
+        if constexpr (MODE == kRest) skip_s[s] = skip;
         base += wnb_of(nb);
       }
     }
@@ -467,10 +516,17 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   __syncthreads();
   const int W = __builtin_amdgcn_readfirstlane(blkpre[S]);
 
-  // Zero-length sequences own no partition: their output is 0.
-  for (int s = blockIdx.x; s < S; s += J) {
-    if (ctx_s[s] == 0)
-      for (int i = tid; i < a.hq * D; i += kThreads) store_out<DT>(a, static_cast<int64_t>(s) * a.hq * D + i, 0.0f);
+  // Zero-length sequences own no partition: their output is 0.  In the rest pass a sequence whose
+  // prefix covers its whole context has the prefix partial (normalised) as its output.
+  if constexpr (MODE != kPrefix) {
+    for (int s = blockIdx.x; s < S; s += J) {
+      if (ctx_s[s] == 0) {
+        for (int i = tid; i < a.hq * D; i += kThreads) store_out<DT>(a, static_cast<int64_t>(s) * a.hq * D + i, 0.0f);
+      } else if (MODE == kRest && nb_s[s] == 0) {
+        for (int i = tid; i < a.hq * D; i += kThreads)
+          store_out<DT>(a, static_cast<int64_t>(s) * a.hq * D + i, a.pre_o[static_cast<int64_t>(s) * a.hq * D + i]);
+      }
+    }
   }
   if (W == 0) return;
 
@@ -517,16 +573,28 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
       it.p = p;
       it.n = __builtin_amdgcn_readfirstlane(ctx_s[s]);
       it.np = (nb + PB - 1) / PB;
+      it.len = min(PB, nb - p * PB);
       it.b0 = p * PB;
-      it.len = min(PB, nb - it.b0);
+      if constexpr (MODE == kRest) it.b0 += __builtin_amdgcn_readfirstlane(skip_s[s]);
       it.my_n = (it.len > w) ? (it.len - w + kWaves - 1) / kWaves : 0;
     }
+    // The table row and the query row of column col.
+    int64_t trow = it.s;
+    int64_t qrow;
+    if constexpr (MODE == kPrefix) {
+      const int first = __builtin_amdgcn_readfirstlane(group_first(it.s));
+      const int ncol = group_members(it.s, first) * g;
+      trow = first;
+      const int c = col < ncol ? col : 0;
+      qrow = (static_cast<int64_t>(first + c / g) * a.hq + it.h * g + c % g) * D;
+    } else {
+      qrow = (static_cast<int64_t>(it.s) * a.hq + it.h * g + (col < g ? col : 0)) * D;
+    }
     const int b = min(it.b0 + w + kWaves * lane, a.max_blocks - 1);
-    sl.ids = a.block_tables[static_cast<int64_t>(it.s) * a.max_blocks + b];
+    sl.ids = a.block_tables[trow * a.max_blocks + b];
     // Keep the id load ahead of the query loads: the lookahead waits for it while the
     // query loads may still be in flight.
     __builtin_amdgcn_sched_barrier(0);
-    const int64_t qrow = (static_cast<int64_t>(it.s) * a.hq + it.h * g + (col < g ? col : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) sl.q[kk] = *reinterpret_cast<const u32x4_t*>(qp + qrow + (kk * 4 + grp) * 8);
   };
@@ -585,6 +653,46 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   // loads the runs' partials 16 at a time.  Partials are read with device-scope loads: runs on
   // other XCDs wrote them through to memory.  Called by every thread, after the stream.
   int32_t* const run_p0 = reinterpret_cast<int32_t*>(&sm_o[0][0][0]);
+  // Query columns of context s (first = its group's first sequence in the prefix pass), and the
+  // q / out row of column cc with KV head h.
+  auto ncols = [&](int s, int first) {
+    if constexpr (MODE == kPrefix) return group_members(s, first) * g;
+    else return g;
+  };
+  auto out_row = [&](int s, int h, int cc, int first) -> int64_t {
+    if constexpr (MODE == kPrefix) return static_cast<int64_t>(first + cc / g) * a.hq + h * g + cc % g;
+    else return static_cast<int64_t>(s) * a.hq + h * g + cc;
+  };
+  // Final result of 4 dims of one row from its merged (max, sum, unnormalised output).  The rest
+  // pass merges the row's prefix partial in first; the prefix pass writes the prefix partial.
+  auto emit = [&](int64_t row, int d0, float mx, float L, f32x4_t O, bool with_prefix) {
+    if constexpr (MODE == kRest) {
+      if (with_prefix) {
+        const float pm = a.pre_ml[row * 2], pl = a.pre_ml[row * 2 + 1];
+        const f32x4_t po = *reinterpret_cast<const f32x4_t*>(a.pre_o + row * D + d0);
+        if (pl > 0.f) {
+          const float Mn = fmaxf(mx, pm);
+          const float sc = (mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mx - Mn);
+          const float wr = __builtin_amdgcn_exp2f(pm - Mn) * pl;
+          O = O * sc + po * wr;
+          L = L * sc + wr;
+          mx = Mn;
+        }
+      }
+    }
+    f32x4_t res;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) res[e] = L > 0.f ? O[e] / L : 0.f;
+    if constexpr (MODE == kPrefix) {
+      *reinterpret_cast<f32x4_t*>(a.pre_o + row * D + d0) = res;
+      if (d0 == 0) {
+        a.pre_ml[row * 2] = mx;
+        a.pre_ml[row * 2 + 1] = L;
+      }
+    } else {
+      store_out4<DT>(a, row * D + d0, res);
+    }
+  };
   auto merge_ctx = [&](int s, int h, int np, int nb) {
     const int64_t A = static_cast<int64_t>(blkpre[s]) + static_cast<int64_t>(h) * wnb_of(nb);
     const int64_t k0 = chunk_owner(A, W, R, NR);
@@ -595,9 +703,11 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
     constexpr int kChunks = D / 4;
     constexpr int kBatch = 16;
-    for (int c4 = tid; c4 < g * kChunks; c4 += kThreads) {
+    const int first = MODE == kPrefix ? group_first(s) : s;
+    const bool with_prefix = MODE == kRest && skip_s[MODE == kRest ? s : 0] > 0;
+    for (int c4 = tid; c4 < ncols(s, first) * kChunks; c4 += kThreads) {
       const int cc = c4 / kChunks, d0 = (c4 % kChunks) * 4;
-      const int64_t row = static_cast<int64_t>(s) * a.hq + h * g + cc;
+      const int64_t row = out_row(s, h, cc, first);
       float M = -INFINITY, Lsum = 0.f;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       for (int r0 = 0; r0 < nr; r0 += kBatch) {
@@ -632,10 +742,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
           }
         }
       }
-      f32x4_t res;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) res[e] = Lsum > 0.f ? acc[e] / Lsum : 0.f;
-      store_out4<DT>(a, row * D + d0, res);
+      emit(row, d0, M, Lsum, acc, with_prefix);
     }
     __syncthreads();  // run_p0 is reused by the next merge
   };
@@ -733,7 +840,9 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     if (w == (wave_turn & (kWaves - 1))) {
       const bool final = seg_p0 == 0 && cur.p == cur.np - 1;  // the segment is the whole context
       constexpr int kChunks = D / 4;                            // 4 consecutive dims per lane and store
-      for (int c4 = lane; c4 < g * kChunks; c4 += kWave) {
+      const int first = MODE == kPrefix ? __builtin_amdgcn_readfirstlane(group_first(cur.s)) : cur.s;
+      const bool with_prefix = MODE == kRest && skip_s[MODE == kRest ? cur.s : 0] > 0;
+      for (int c4 = lane; c4 < ncols(cur.s, first) * kChunks; c4 += kWave) {
         const int cc = c4 / kChunks, d0 = (c4 % kChunks) * 4;
         float mx = sm_m[0][cc];
 #pragma unroll
@@ -748,13 +857,13 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
             O += e * *reinterpret_cast<const f32x4_t*>(&sm_o[ww][cc][d0]);
           }
         }
-        f32x4_t res;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) res[e] = L > 0.f ? O[e] / L : 0.f;
-        const int64_t row = static_cast<int64_t>(cur.s) * a.hq + cur.h * g + cc;
+        const int64_t row = out_row(cur.s, cur.h, cc, first);
         if (final) {
-          store_out4<DT>(a, row * D + d0, res);
+          emit(row, d0, mx, L, O, with_prefix);
         } else {
+          f32x4_t res;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) res[e] = L > 0.f ? O[e] / L : 0.f;
           const int64_t prow = row * a.max_parts + seg_p0;
           // Device-scope stores: the run that merges this context may sit on another XCD.
 #pragma unroll
@@ -1040,6 +1149,7 @@ struct Plan {
   int32_t ctx_limit;
   int32_t max_parts;
   size_t counter_offset;  // byte offset of the arrival counters in the workspace
+  size_t pre_offset;      // byte offset of the prefix partials (with shared prefixes)
   size_t workspace;
 };
 
@@ -1071,6 +1181,15 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
   // then the per (sequence, KV head) arrival counters [S * H_kv] (uint64; the partials end 8-byte aligned)
   out->counter_offset = rows * (static_cast<size_t>(c.head_dim) + 2) * sizeof(float);
   out->workspace = parts > 1 ? out->counter_offset + static_cast<size_t>(p->num_seqs) * c.num_kv_heads * 8 : 0;
+  // then, with shared prefixes, the prefix partials [S][H_q][D] and [S][H_q][2] (fp32), 16-byte aligned
+  out->pre_offset = (out->workspace + 15) / 16 * 16;
+  if (p->shared) {
+    const pa_shared_prefix& sh = *p->shared;
+    if (sh.num_groups < 0 || sh.num_groups > p->num_seqs / 2) return PA_ERR_INVALID_ARG;
+    if (sh.num_groups > 0 && (!sh.groups || !sh.seq_prefix)) return PA_ERR_INVALID_ARG;
+    out->workspace = out->pre_offset + static_cast<size_t>(p->num_seqs) * p->num_q_heads *
+                                           (static_cast<size_t>(c.head_dim) + 2) * sizeof(float);
+  }
   return PA_OK;
 }
 
@@ -1126,17 +1245,28 @@ constexpr int kPartCost = 5;
 constexpr int kCtxCost = 5;
 
 // Launch the split kernel; sets args->run_grid / run_rounds.
-template <int DT, int D>
+template <int DT, int D, int MODE>
 int32_t launch_split(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  const void* fn = reinterpret_cast<const void*>(&decode_split_kernel<DT, D, kPersistRing>);
+  const void* fn = reinterpret_cast<const void*>(&decode_split_kernel<DT, D, kPersistRing, MODE>);
   int resident = 0;
   const int32_t rc = resident_workgroups(fn, &resident);
   if (rc != PA_OK) return rc;
   args->run_rounds = kSplitRounds;
   args->run_grid = std::min(kSplitRounds * resident, kMaxSplitGrid / kSplitRounds * kSplitRounds);
-  hipExtLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing>), dim3(static_cast<uint32_t>(args->run_grid)),
+  hipExtLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing, MODE>), dim3(static_cast<uint32_t>(args->run_grid)),
                         dim3(kWaves * kWave), 0, st, start, stop, 0, *args);
   return PA_OK;
+}
+
+// Shared prefixes: the prefix pass (groups) then the rest pass, each with its own counter tag.
+// Otherwise one plain launch.
+template <int DT, int D>
+int32_t launch_split_all(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  if (args->num_groups <= 0) return launch_split<DT, D, kPlain>(args, st, start, stop);
+  const int32_t rc = launch_split<DT, D, kPrefix>(args, st, start, nullptr);
+  if (rc != PA_OK) return rc;
+  args->launch_tag += 1;
+  return launch_split<DT, D, kRest>(args, st, nullptr, stop);
 }
 
 template <int DT>
@@ -1155,8 +1285,8 @@ int32_t launch_decode(DecodeArgs args, hipStream_t st, hipEvent_t start, hipEven
   args.run_rounds = 0;
   if (split) {
     // One launch: the split kernel merges its runs in place.
-    if constexpr (DT != PA_F32) return D == 64 ? launch_split<DT, 64>(&args, st, start, stop)
-                                               : launch_split<DT, 128>(&args, st, start, stop);
+    if constexpr (DT != PA_F32) return D == 64 ? launch_split_all<DT, 64>(&args, st, start, stop)
+                                               : launch_split_all<DT, 128>(&args, st, start, stop);
   }
   // The per-partition kernels need the merge kernel when a context spans several partitions.
   const bool merge = args.max_parts > 1;
@@ -1233,15 +1363,22 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   a.max_parts = plan.max_parts;
   a.out_f32 = p->out_dtype == PA_F32 ? 1 : 0;
   a.num_blocks = p->cache.num_blocks;
-  a.run_done = plan.workspace > 0
+  a.run_done = plan.max_parts > 1
                    ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(p->workspace) + plan.counter_offset)
                    : nullptr;
+  if (p->shared && p->shared->num_groups > 0) {
+    a.share_groups = p->shared->groups;
+    a.share_skip = p->shared->seq_prefix;
+    a.num_groups = p->shared->num_groups;
+    a.pre_o = reinterpret_cast<float*>(static_cast<uint8_t*>(p->workspace) + plan.pre_offset);
+    a.pre_ml = a.pre_o + static_cast<size_t>(p->num_seqs) * p->num_q_heads * p->cache.head_dim;
+  }
   // A tag no earlier call of this process used, seeded per process (a workspace may hold
   // counters another process left): the arrival counters need no clearing.
   static std::atomic<uint32_t> next_tag{static_cast<uint32_t>(
       std::chrono::steady_clock::now().time_since_epoch().count() * 0x9e3779b97f4a7c15ull >> 32) ^
       static_cast<uint32_t>(getpid())};
-  a.launch_tag = next_tag.fetch_add(1, std::memory_order_relaxed);
+  a.launch_tag = next_tag.fetch_add(2, std::memory_order_relaxed);  // the rest pass takes the second
 
   hipStream_t stream = static_cast<hipStream_t>(p->stream);
   (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind

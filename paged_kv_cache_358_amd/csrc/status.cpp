@@ -27,7 +27,7 @@ const char* pa_status_string(int32_t status) {
   }
 }
 
-int32_t pa_version(void) { return 100; }
+int32_t pa_version(void) { return 200; }
 
 const char* pa_last_error(void) { return pa::g_last_error; }
 

@@ -9,6 +9,11 @@ pinned host memory and copied to the device on the compute stream, then
 ``block_copy`` -> ``kv_append`` -> ``paged_attention_decode`` run on that stream
 in that order.  Nothing in a step waits for the device, except when a pinned
 staging buffer is about to be reused while its previous copy is still pending.
+
+Forked sequences keep the blocks they inherited until they write into one, so
+consecutive samples or beams of one prompt share their leading blocks; each step
+groups them (``shared_prefixes``) and the attention call reads a group's shared
+blocks once for all members.
 """
 from __future__ import annotations
 
@@ -16,19 +21,22 @@ import numpy as np
 import torch
 
 from . import (BlockAllocator, alloc_kv_cache, block_copy, kv_append, paged_attention_decode, stage_append,
-               paged_attention_workspace_bytes, stage_copy)
+               paged_attention_workspace_bytes, shared_prefixes, stage_copy)
 
 
 class _Staging:
     """One pinned host buffer and one device buffer holding a step's metadata, int32:
-    context lengths [max_seqs] | slots [max_tokens] | copy pairs [max_seqs, 2] | block
-    tables [max_seqs, max_blocks].  A step moves the used prefix in one host->device copy."""
+    context lengths [max_seqs] | slots [max_tokens] | copy pairs [max_seqs, 2] | shared
+    prefix blocks [max_seqs] | shared-prefix groups [max_seqs // 2, 3] | block tables
+    [max_seqs, max_blocks].  A step moves the used prefix in one host->device copy."""
 
     def __init__(self, max_seqs: int, max_blocks: int, max_tokens: int, device):
         self.o_lens = 0
         self.o_slots = max_seqs
         self.o_pairs = self.o_slots + max_tokens
-        self.o_tables = self.o_pairs + 2 * max_seqs
+        self.o_prefix = self.o_pairs + 2 * max_seqs
+        self.o_groups = self.o_prefix + max_seqs
+        self.o_tables = self.o_groups + 3 * max(max_seqs // 2, 1)
         total = (self.o_tables + max_seqs * max_blocks + 3) // 4 * 4
         self.max_blocks = max_blocks
         self.host = torch.empty(total, dtype=torch.int32, pin_memory=True)
@@ -36,7 +44,9 @@ class _Staging:
         h = self.host.numpy()
         self.h_lens = h[self.o_lens:self.o_slots]
         self.h_slots = h[self.o_slots:self.o_pairs]
-        self.h_pairs = h[self.o_pairs:self.o_tables].reshape(max_seqs, 2)
+        self.h_pairs = h[self.o_pairs:self.o_prefix].reshape(max_seqs, 2)
+        self.h_prefix = h[self.o_prefix:self.o_groups]
+        self.h_groups = h[self.o_groups:self.o_tables].reshape(-1, 3)
         self.h_tables = h[self.o_tables:].reshape(max_seqs, max_blocks)
         self.h_slots_t = self.host[self.o_slots:self.o_pairs]  # the slots as a pinned tensor
         self.done = None  # event that ends the step that last read this buffer
@@ -52,6 +62,12 @@ class _Staging:
     def d_pairs(self, n):
         return self.dev[self.o_pairs:self.o_pairs + 2 * n].view(n, 2)
 
+    def d_prefix(self, n):
+        return self.dev[self.o_prefix:self.o_prefix + n]
+
+    def d_groups(self, n):
+        return self.dev[self.o_groups:self.o_groups + 3 * n].view(n, 3)
+
     def d_tables(self, n):
         return self.dev[self.o_tables:self.o_tables + n * self.max_blocks].view(n, self.max_blocks)
 
@@ -59,7 +75,7 @@ class _Staging:
 class PagedDecodeLayer:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, num_q_heads: int, dtype,
                  max_seqs: int, max_blocks_per_seq: int, free_order=None, partition_size: int = 512,
-                 device="cuda", stream=None):
+                 device="cuda", stream=None, share_prefixes: bool = True, share_min_blocks: int = 4):
         self.alloc = BlockAllocator(num_blocks, 16, free_order)
         self.k_cache, self.v_cache = alloc_kv_cache(num_blocks, num_kv_heads, head_dim, dtype, device)
         self.num_q_heads = num_q_heads
@@ -69,6 +85,10 @@ class PagedDecodeLayer:
         self.max_seqs = max_seqs
         self.max_blocks = max_blocks_per_seq
         self.partition_size = partition_size
+        # Shared leading blocks are read once per group when at least share_min_blocks are shared.
+        self.share_prefixes = share_prefixes
+        self.share_min_blocks = share_min_blocks
+        self.share_max_members = 16 // (num_q_heads // num_kv_heads)
         self.device = device
         self.stream = torch.cuda.current_stream() if stream is None else stream
         # Three staging buffers: the host fills one while the stream may still read the two
@@ -80,7 +100,7 @@ class PagedDecodeLayer:
         probe_t = torch.empty(max_seqs, max_blocks_per_seq, dtype=torch.int32, device=device)
         ws = paged_attention_workspace_bytes(probe_q, self.k_cache, self.v_cache, probe_t,
                                              torch.empty_like(probe_q, dtype=torch.float32),
-                                             max_blocks_per_seq * 16, partition_size)
+                                             max_blocks_per_seq * 16, partition_size, shared=share_prefixes)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
 
     # ------------------------------------------------------------------ sequence management
@@ -122,7 +142,12 @@ class PagedDecodeLayer:
         np_tables, np_lens = self.alloc.build_batch(ids, self.max_blocks, st.h_tables, st.h_lens)
         max_ctx = int(np_lens.max()) if S else 0
         npairs = len(pairs)
-        used = st.o_tables + S * self.max_blocks  # lengths, slots, pairs and the first S table rows
+        ngroups = 0
+        if self.share_prefixes and S >= 2 and self.share_max_members >= 2:
+            _, groups = shared_prefixes(np_tables, np_lens, self.share_max_members, self.share_min_blocks,
+                                        seq_prefix_out=st.h_prefix, groups_out=st.h_groups)
+            ngroups = len(groups)
+        used = st.o_tables + S * self.max_blocks  # lengths, slots, pairs, sharing and the first S table rows
         with torch.cuda.stream(self.stream):
             if npairs:
                 # copy-on-write blocks are copied before the append writes into them
@@ -138,7 +163,9 @@ class PagedDecodeLayer:
             paged_attention_decode(q, self.k_cache, self.v_cache, st.d_tables(S), st.d_lens(S), scale, out,
                                    max_context_len=max_ctx, partition_size=self.partition_size,
                                    workspace=self.workspace, stream=self.stream,
-                                   start_event=None if timing is None else timing[0], stop_event=st.done)
+                                   start_event=None if timing is None else timing[0], stop_event=st.done,
+                                   shared=(st.d_groups(ngroups), st.d_prefix(S)) if ngroups else None)
+        self.last_groups = ngroups
         self.last_lens = np_lens.copy()
         self.last_tables = np_tables  # view into the pinned staging buffer: valid until three steps later
         return npairs

@@ -120,3 +120,39 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(pa, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(ImportError):
         pa._load()
+
+
+def test_workspace_bytes_with_shared_prefixes():
+    ws = pa.lib.paged_attention_workspace_bytes
+    sh = pa.SharedPrefix(None, None, 0)
+    # one partition: only the prefix partials, S * H_q rows of D + 2 floats
+    p = _params(S=4, hq=8, hkv=2, d=64)
+    p.shared = ctypes.pointer(sh)
+    assert ws(ctypes.byref(p)) == 4 * 8 * (64 + 2) * 4
+    # several partitions: partials, counters, then the prefix partials at a 16-byte boundary
+    p = _params(S=3, hq=4, hkv=4, d=64, maxb=100, maxctx=1000, part=256)
+    base = 3 * 4 * 4 * (64 + 2) * 4 + 3 * 4 * 8
+    p.shared = ctypes.pointer(sh)
+    assert ws(ctypes.byref(p)) == (base + 15) // 16 * 16 + 3 * 4 * (64 + 2) * 4
+    # more groups than half the batch, or groups without arrays: rejected
+    for bad in (pa.SharedPrefix(None, None, 3), pa.SharedPrefix(None, None, -1), pa.SharedPrefix(None, None, 1)):
+        p = _params(S=4)
+        p.shared = ctypes.pointer(bad)
+        assert ws(ctypes.byref(p)) == 0
+        assert pa.lib.paged_attention_decode(None, None, None, None, None, 1.0, None, ctypes.byref(p)) == \
+            pa.PA_ERR_INVALID_ARG
+
+
+def test_shared_prefixes_rejects_bad_arguments():
+    t = (ctypes.c_int32 * 8)()
+    out = (ctypes.c_int32 * 8)()
+    n = ctypes.c_int32(0)
+    f = pa.lib.pa_shared_prefixes
+    P = ctypes.POINTER(ctypes.c_int32)
+    tp, op = ctypes.cast(t, P), ctypes.cast(out, P)
+    assert f(tp, tp, 4, 2, 16, 2, 1, op, op, 2, ctypes.byref(n)) == pa.PA_OK
+    assert f(tp, tp, 4, 2, 16, 2, 1, op, op, 1, ctypes.byref(n)) == pa.PA_ERR_INVALID_ARG  # groups_cap < S / 2
+    assert f(tp, tp, 4, 2, 16, 0, 1, op, op, 2, ctypes.byref(n)) == pa.PA_ERR_INVALID_ARG  # max_members
+    assert f(tp, tp, 4, 2, 16, 2, 0, op, op, 2, ctypes.byref(n)) == pa.PA_ERR_INVALID_ARG  # min_blocks
+    assert f(None, tp, 4, 2, 16, 2, 1, op, op, 2, ctypes.byref(n)) == pa.PA_ERR_INVALID_ARG
+    assert f(None, None, 0, 2, 16, 2, 1, None, None, 0, ctypes.byref(n)) == pa.PA_OK and n.value == 0
