@@ -77,23 +77,23 @@ typedef struct pa_cache_desc {
 /*
  * Sequences of a decode batch that read the same leading blocks (forked samples or beams of one
  * prompt: "Stop Wasting GPU Memory" page, Technical Details, "Copy-on-Write for Parallel Sampling" and
- * "Beam Search Optimization").  A group is a run of consecutive sequences first .. first + members - 1
- * whose block tables hold the same physical ids in entries [0, prefix_blocks), each of which every
- * member fills completely (prefix_blocks * block_size <= context_lens[s]).  paged_attention_decode
- * then reads those blocks once for all members' queries (one extra kernel launch) and each member's
- * remaining blocks on their own, merging the two by the log-sum-exp rule: the result is the same
- * softmax attention, within rounding.  pa_shared_prefixes builds this description from host copies of
+ * "Beam Search Optimization").  The batch is cut into groups of consecutive sequences, in order: group i
+ * is sequences first .. first + members - 1, whose block tables hold the same physical ids in entries
+ * [0, prefix_blocks), each of which every member fills completely (prefix_blocks * block_size <=
+ * context_lens[s]); a sequence that shares nothing is a group of one with prefix_blocks 0.
+ * paged_attention_decode then treats a group as one context: its shared blocks followed by each member's
+ * own blocks, with a block's scores counted only for the query heads of the sequences that hold it.
+ * Each shared block is read once for all members; every output is the same softmax attention as
+ * without the description, within rounding.  pa_shared_prefixes builds the groups from host copies of
  * the tables and lengths.
- *   groups      device int32 [num_groups][3]: first sequence, members, prefix_blocks
- *   seq_prefix  device int32 [num_seqs]: prefix_blocks of the group holding sequence s, 0 if none
- * members * (H_q / H_kv) must not exceed 16 (the query columns of one matrix-core tile).  A
- * description that does not match the tables gives undefined results (never out-of-bounds accesses).
- * Used by the bf16/fp16, head_dim 64/128, up-to-2048-sequence path; the other paths ignore it.
+ *   groups   device int32 [num_groups][3]: first sequence, members, prefix_blocks
+ * members * (H_q / H_kv) must not exceed 16 (the query columns of one matrix-core tile).  A description
+ * that does not match the tables gives undefined results (never out-of-bounds accesses).  Used by the
+ * bf16/fp16, head_dim 64/128, up-to-2048-sequence path; the other paths ignore it.
  */
 typedef struct pa_shared_prefix {
   const int32_t* groups;
-  const int32_t* seq_prefix;
-  int32_t num_groups;  /* 0 <= num_groups <= num_seqs / 2 */
+  int32_t num_groups;  /* 0 (= no sharing) or the number of groups covering the batch, <= num_seqs */
 } pa_shared_prefix;
 
 /* Parameters of one paged_attention_decode call. */
@@ -117,7 +117,7 @@ typedef struct pa_decode_params {
                                   call's GPU time; a caller can also wait on stop_event for the call's end.
                                   With num_seqs = 0 nothing is launched and both are recorded on the stream. */
   const pa_shared_prefix* shared; /* host pointer or NULL: shared leading blocks (see above).  When not NULL
-                                  the workspace also holds num_seqs * H_q * (head_dim + 2) fp32 prefix partials */
+                                  the workspace holds partials for whole groups (see the workspace size) */
 } pa_decode_params;
 
 /* Human-readable name of a status code (static string). */
@@ -133,10 +133,10 @@ const char* pa_last_error(void);
 /* ----------------------------------------------------------------------- decode attention */
 
 /* Device workspace bytes paged_attention_decode needs for these parameters: when more than one partition
- * can occur, P = num_seqs * H_q * ceil(max_context_len / partition_size) fp32 partial rows of head_dim + 2
- * values (P * (head_dim + 2) * 4 bytes), then num_seqs * H_kv uint64 arrival counters; with p->shared set,
- * then num_seqs * H_q prefix partial rows of head_dim + 2 fp32 values.  Returns 0 for invalid parameters
- * (the decode call then reports the error).  The contents need no initialisation (the counters carry a per-call tag)
+ * can occur, P = num_seqs * H_q * n fp32 partial rows of head_dim + 2 values (P * (head_dim + 2) * 4 bytes),
+ * then num_seqs * H_kv uint64 arrival counters; else 0.  n = ceil(max_context_len / partition_size), or with
+ * p->shared set the partitions of a group of min(16 / (H_q / H_kv), num_seqs) members of ceil(max_context_len
+ * / 16) blocks each.  Returns 0 for invalid parameters (the decode call then reports the error).  The contents need no initialisation (the counters carry a per-call tag)
  * and are scratch between calls; two calls in flight at once must not share a workspace. */
 size_t paged_attention_workspace_bytes(const pa_decode_params* p);
 
@@ -312,19 +312,19 @@ int32_t pa_build_batch(const pa_allocator* a, const int64_t* ids, int32_t n, int
                        int32_t* tables_out, int32_t* lens_out);
 
 /*
- * Groups of consecutive sequences that share leading full blocks, for pa_shared_prefix (host arrays).
- * full(s) = min(lens[s] / block_size, max_blocks).  A run starts at the first sequence i not yet grouped
- * with k = full(i); the next sequence j joins while the run has fewer than max_members members and
- * k' = min(k, full(j), leading entries where rows i and j agree) >= min_blocks (then k = k').  A run of
- * two or more is a group (i, members, k) and its members get seq_prefix = k; other sequences get 0.
- *   tables      host int32 [num_seqs][max_blocks];  lens  host int32 [num_seqs]
- *   seq_prefix  host int32 [num_seqs] (out);  groups  host int32 [groups_cap][3] (out);  *num_groups (out)
+ * The groups of pa_shared_prefix for a batch (host arrays).  full(s) = min(lens[s] / block_size,
+ * max_blocks).  A run starts at the first sequence i not yet grouped with k = full(i); the next sequence j
+ * joins while the run has fewer than max_members members and k' = min(k, full(j), leading entries where
+ * rows i and j agree) >= min_blocks (then k = k').  A run of two or more is a group (i, members, k); every
+ * other sequence is a group (i, 1, 0) of its own.  The groups cover the batch in order.
+ *   tables  host int32 [num_seqs][max_blocks];  lens  host int32 [num_seqs]
+ *   groups  host int32 [groups_cap][3] (out);  *num_groups (out)
  * PA_ERR_INVALID_ARG for null pointers, num_seqs < 0, block_size, max_blocks, max_members or min_blocks < 1,
- * or groups_cap < num_seqs / 2 (the most groups a batch can form).
+ * or groups_cap < num_seqs.
  */
 int32_t pa_shared_prefixes(const int32_t* tables, const int32_t* lens, int32_t num_seqs, int32_t max_blocks,
-                           int32_t block_size, int32_t max_members, int32_t min_blocks, int32_t* seq_prefix,
-                           int32_t* groups, int32_t groups_cap, int32_t* num_groups);
+                           int32_t block_size, int32_t max_members, int32_t min_blocks, int32_t* groups,
+                           int32_t groups_cap, int32_t* num_groups);
 
 #ifdef __cplusplus
 }

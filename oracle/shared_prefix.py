@@ -64,3 +64,19 @@ def shared_prefix_groups(tables, lens, block_size: int, max_members: int, min_bl
         else:
             i += 1
     return prefix, groups
+
+
+def shared_prefix_cover(tables, lens, block_size: int, max_members: int, min_blocks: int):
+    """The batch cut into runs, in order: the groups above and every other sequence as a run of one
+    with no shared blocks.  Returns [(first, members, prefix_blocks)]."""
+    _, groups = shared_prefix_groups(tables, lens, block_size, max_members, min_blocks)
+    runs = []
+    s = 0
+    for first, members, k in groups + [(len(lens), 0, 0)]:
+        while s < first:
+            runs.append((s, 1, 0))
+            s += 1
+        if members:
+            runs.append((first, members, k))
+            s = first + members
+    return runs

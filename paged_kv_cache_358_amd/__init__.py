@@ -35,7 +35,7 @@ class CacheDesc(ctypes.Structure):
 
 
 class SharedPrefix(ctypes.Structure):
-    _fields_ = [("groups", _vp), ("seq_prefix", _vp), ("num_groups", _i32)]
+    _fields_ = [("groups", _vp), ("num_groups", _i32)]
 
 
 class DecodeParams(ctypes.Structure):
@@ -77,7 +77,7 @@ SIGNATURES = {
     "pa_refcount": (_i32, [_vp, _i32]),
     "pa_free_list": (_i32, [_vp, _P32, _i32, _P32]),
     "pa_build_batch": (_i32, [_vp, _P64, _i32, _i32, _P32, _P32]),
-    "pa_shared_prefixes": (_i32, [_P32, _P32, _i32, _i32, _i32, _i32, _i32, _P32, _P32, _i32, _P32]),
+    "pa_shared_prefixes": (_i32, [_P32, _P32, _i32, _i32, _i32, _i32, _i32, _P32, _i32, _P32]),
 }
 
 
@@ -201,36 +201,31 @@ def decode_params(q, k_cache, v_cache, block_tables, out, max_context_len: int, 
 
 def paged_attention_workspace_bytes(q, k_cache, v_cache, block_tables, out, max_context_len: int,
                                     partition_size: int = 0, shared: bool = False) -> int:
-    """Workspace bytes of a decode call; ``shared=True`` includes the prefix partials that calls with
-    shared prefixes need."""
-    sh = SharedPrefix(None, None, 0) if shared else None
+    """Workspace bytes of a decode call; ``shared=True`` sizes it for calls with shared prefixes."""
+    sh = SharedPrefix(None, 0) if shared else None
     p = decode_params(q, k_cache, v_cache, block_tables, out, max_context_len, partition_size, shared=sh)
     return int(lib.paged_attention_workspace_bytes(ctypes.byref(p)))
 
 
 def shared_prefixes(tables, lens, max_members: int, min_blocks: int = 1, block_size: int = BLOCK_SIZE,
-                    seq_prefix_out=None, groups_out=None):
-    """Groups of consecutive sequences whose host block tables (int32 [S, max_blocks]) share leading
-    full blocks: returns (seq_prefix int32[S], groups int32[G, 3] of (first, members, prefix blocks)).
-    ``max_members`` is at most 16 // (H_q / H_kv) for paged_attention_decode.  Optional C-contiguous
-    int32 outputs of at least [S] and [S // 2, 3] receive the result in place."""
+                    groups_out=None):
+    """The batch (host block tables int32 [S, max_blocks], lengths int32 [S]) cut into groups of
+    consecutive sequences that share leading full blocks: int32 [G, 3] rows of (first sequence,
+    members, shared blocks), covering the batch in order (a sequence that shares nothing is a group
+    of one with 0 shared blocks).  ``max_members`` is at most 16 // (H_q / H_kv) for
+    paged_attention_decode.  ``groups_out`` (C-contiguous int32 [>= S, 3]) receives it in place."""
     t, tptr = _as_i32(tables)
     ln, lptr = _as_i32(lens)
     S = int(ln.size)
-    width = int(t.shape[1]) if t.ndim == 2 else 1
     if t.ndim != 2 or t.shape[0] < S:
         raise ValueError("tables must be int32 [S, max_blocks]")
-    sp = np.empty(max(S, 1), np.int32) if seq_prefix_out is None else seq_prefix_out
-    cap = max(S // 2, 1)
-    gr = np.empty((cap, 3), np.int32) if groups_out is None else groups_out
-    for arr, n in ((sp, S), (gr, 3 * cap)):
-        if arr.dtype != np.int32 or not arr.flags.c_contiguous or arr.size < n:
-            raise ValueError("shared_prefixes: outputs must be C-contiguous int32 of sufficient size")
+    gr = np.empty((max(S, 1), 3), np.int32) if groups_out is None else groups_out
+    if gr.dtype != np.int32 or not gr.flags.c_contiguous or gr.ndim != 2 or gr.shape[1] != 3 or gr.shape[0] < S:
+        raise ValueError("shared_prefixes: groups_out must be C-contiguous int32 [>= S, 3]")
     ng = ctypes.c_int32(0)
-    _check(lib.pa_shared_prefixes(tptr, lptr, S, width, int(block_size), int(max_members), int(min_blocks),
-                                  sp.ctypes.data_as(_P32), gr.ctypes.data_as(_P32), gr.shape[0] if gr.ndim == 2
-                                  else gr.size // 3, ctypes.byref(ng)), "pa_shared_prefixes")
-    return sp[:S], gr.reshape(-1, 3)[:ng.value]
+    _check(lib.pa_shared_prefixes(tptr, lptr, S, int(t.shape[1]), int(block_size), int(max_members), int(min_blocks),
+                                  gr.ctypes.data_as(_P32), gr.shape[0], ctypes.byref(ng)), "pa_shared_prefixes")
+    return gr[:ng.value]
 
 
 def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
@@ -244,8 +239,8 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     ``paged_attention_workspace_bytes`` bytes) is allocated here if omitted.
     ``start_event`` / ``stop_event`` (torch.cuda.Events recorded once before) mark the
     start of the call's first kernel and the end of its last one.
-    ``shared`` = (groups int32 [G, 3], seq_prefix int32 [S]) device tensors from
-    ``shared_prefixes``: the groups' leading blocks are read once for all members.
+    ``shared`` = device int32 [G, 3] groups from ``shared_prefixes`` (covering the batch): each
+    group's shared leading blocks are read once for all its members.
     """
     torch = _torch()
     _require_device(q, k_cache, v_cache, block_tables, context_lens, out)
@@ -257,13 +252,10 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         raise ValueError("out must have q's shape")
     sh = None
     if shared is not None:
-        groups, seq_prefix = shared
-        _require_device(groups, seq_prefix)
-        if groups.dtype != torch.int32 or seq_prefix.dtype != torch.int32:
-            raise ValueError("shared groups and seq_prefix must be int32")
-        if (groups.numel() and (groups.dim() != 2 or groups.shape[1] != 3)) or seq_prefix.numel() != q.shape[0]:
-            raise ValueError("shared = (groups [G, 3], seq_prefix [S])")
-        sh = SharedPrefix(_ptr(groups).value, _ptr(seq_prefix).value, groups.shape[0] if groups.numel() else 0)
+        _require_device(shared)
+        if shared.dtype != torch.int32 or (shared.numel() and (shared.dim() != 2 or shared.shape[1] != 3)):
+            raise ValueError("shared must be int32 [G, 3]")
+        sh = SharedPrefix(_ptr(shared).value, shared.shape[0] if shared.numel() else 0)
     if workspace is None:
         need = paged_attention_workspace_bytes(q, k_cache, v_cache, block_tables, out, max_context_len,
                                                partition_size, shared=sh is not None)

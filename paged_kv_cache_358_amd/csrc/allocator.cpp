@@ -255,16 +255,15 @@ int32_t pa_build_batch(const pa_allocator* a, const int64_t* ids, int32_t n, int
   return PA_OK;
 }
 
-// Groups of forked sequences for the decode's prefix pass: runs of consecutive sequences whose
-// block tables name the same physical blocks for their first full blocks.  Forks keep the blocks
-// they inherit until they write into one, so samples and beams of one prompt form such runs.
+// Groups of forked sequences for the decode: runs of consecutive sequences whose block tables name
+// the same physical blocks for their first full blocks, every other sequence alone.  Forks keep the
+// blocks they inherit until they write into one, so samples and beams of one prompt form such runs.
 int32_t pa_shared_prefixes(const int32_t* tables, const int32_t* lens, int32_t num_seqs, int32_t max_blocks,
-                           int32_t block_size, int32_t max_members, int32_t min_blocks, int32_t* seq_prefix,
-                           int32_t* groups, int32_t groups_cap, int32_t* num_groups) {
+                           int32_t block_size, int32_t max_members, int32_t min_blocks, int32_t* groups,
+                           int32_t groups_cap, int32_t* num_groups) {
   if (num_seqs < 0 || max_blocks < 1 || block_size < 1 || max_members < 1 || min_blocks < 1 || !num_groups)
     return PA_ERR_INVALID_ARG;
-  if (num_seqs > 0 && (!tables || !lens || !seq_prefix || (num_seqs >= 2 && (!groups || groups_cap < num_seqs / 2))))
-    return PA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!tables || !lens || !groups || groups_cap < num_seqs)) return PA_ERR_INVALID_ARG;
   auto full = [&](int32_t s) {
     const int32_t n = lens[s];
     return n <= 0 ? 0 : std::min(n / block_size, max_blocks);
@@ -284,17 +283,15 @@ int32_t pa_shared_prefixes(const int32_t* tables, const int32_t* lens, int32_t n
       k = common;
       ++j;
     }
-    if (j - i >= 2) {
-      groups[3 * ng + 0] = i;
-      groups[3 * ng + 1] = j - i;
-      groups[3 * ng + 2] = k;
-      ++ng;
-      for (int32_t s = i; s < j; ++s) seq_prefix[s] = k;
-      i = j;
-    } else {
-      seq_prefix[i] = 0;
-      ++i;
+    if (j - i < 2) {  // nobody to share with
+      j = i + 1;
+      k = 0;
     }
+    groups[3 * ng + 0] = i;
+    groups[3 * ng + 1] = j - i;
+    groups[3 * ng + 2] = k;
+    ++ng;
+    i = j;
   }
   *num_groups = ng;
   return PA_OK;

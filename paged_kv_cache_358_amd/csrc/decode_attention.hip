@@ -82,13 +82,11 @@ struct DecodeArgs {
   int32_t ctx_cost;   // split: balance weight of a (sequence, KV head) context's end, in blocks
   uint64_t* run_done; // split: per (sequence, KV head) arrival counters [S * H_kv] (workspace); tag << 32 | partitions
   uint32_t launch_tag; // split: this launch's counter tag
-  // Shared leading blocks (split kernel only).  The prefix pass walks the groups; the rest pass
-  // skips each sequence's prefix blocks and merges the prefix pass's partial into its output.
-  const int32_t* share_groups;  // [num_groups][3]: first sequence, members, prefix blocks
-  const int32_t* share_skip;    // [S]: prefix blocks of sequence s covered by its group, 0 if none
-  float* pre_o;                 // [S][H_q][D] prefix partial outputs (normalised)
-  float* pre_ml;                // [S][H_q][2] prefix partial (max in log2 units, sum)
+  // Groups of sequences sharing leading blocks (split kernel only): [num_groups][3] = first
+  // sequence, members, prefix blocks; the groups cover the batch in order.
+  const int32_t* share_groups;
   int32_t num_groups;
+  int32_t slot_parts;  // partial slots per query row in the workspace (>= max_parts)
 };
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s) {
@@ -331,14 +329,15 @@ constexpr int kPersistRing = 2;     // ring depth of the split kernel
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X, each with its own L2
 constexpr int kMaxSplitGrid = 4095;  // chunks (workgroups) of the split kernel, at most
 
-// Modes of the split kernel.  kPlain: every sequence's whole context.  kPrefix: the contexts are
-// the groups of sequences that share leading blocks; a group's context is its prefix blocks, read
-// through its first member's table, and its query columns are (member, query head of the KV
-// head) pairs; results go to the prefix partials.  kRest: every sequence's context minus the
-// blocks its group covered; the output merges the prefix partial in.
+// Modes of the split kernel.  kPlain: one context per sequence.  kGroup: one context per group of
+// consecutive sequences whose block tables share their first k blocks (forked samples or beams of
+// one prompt).  A group's query columns are its (member, query head of the KV head) pairs, and its
+// context is the shared blocks (read through the first member's table) followed by each member's
+// own blocks k .. in member order.  Scores of a member's own block count only in that member's
+// columns (the others see -inf there), so every column's online softmax runs over exactly its
+// sequence's tokens, and each shared block is read once for all members.
 constexpr int kPlain = 0;
-constexpr int kPrefix = 1;
-constexpr int kRest = 2;
+constexpr int kGroup = 1;
 
 // Work split.  The partitions of all (sequence, KV head) pairs are laid end to end in
 // (sequence, KV head, partition) order, each weighted by its block count plus a fixed cost
@@ -418,7 +417,6 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   __shared__ int32_t blkpre[kMaxScanSeqs + 1];  // H_kv * (weight of the sequences before s)
   __shared__ int32_t nb_s[kMaxScanSeqs];        // blocks of sequence s
   __shared__ int32_t ctx_s[kMaxScanSeqs];       // clamped context length of s
-  __shared__ int32_t skip_s[MODE == kRest ? kMaxScanSeqs : 1];  // kRest: leading blocks of s already covered
   __shared__ int32_t scan[kThreads];
   __shared__ int32_t merge_flag[2];  // thread 0's arrivals completed these contexts
   static_assert(kWaves * 16 * D > kMaxSplitGrid, "run starts of one context fit in sm_o");
@@ -428,7 +426,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int S = MODE == kPrefix ? a.num_groups : a.num_seqs;  // contexts are groups in the prefix pass
+  const int S = MODE == kGroup ? a.num_groups : a.num_seqs;  // contexts: groups or sequences
   const int PB = a.part_blocks;
   const int hkv = a.hkv;
   const int g = a.group;
@@ -451,30 +449,31 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     k = r * R + (t % kXcds) * (R / kXcds) + t / kXcds;
   }
 
-  // kPrefix: group v's first sequence and members, clamped so that every row stays inside the
-  // batch and the columns inside one 16-wide tile.
+  // kGroup: group v's first sequence, members and shared blocks, clamped so that every row stays
+  // inside the batch, the columns inside one 16-wide tile and the shared blocks inside a table row.
   auto group_first = [&](int v) {
     const int f = a.share_groups[3 * v];
     return f < 0 ? 0 : (f >= a.num_seqs ? a.num_seqs - 1 : f);
   };
   auto group_members = [&](int v, int first) {
     const int mm = a.share_groups[3 * v + 1];
-    return max(0, min(min(mm, a.num_seqs - first), 16 / g));
+    return max(1, min(min(mm, a.num_seqs - first), 16 / g));
   };
-  // Context length, blocks to stream and blocks skipped of context s.
-  auto shape_of = [&](int s, int& n, int& nb, int& skip) {
-    skip = 0;
-    if constexpr (MODE == kPrefix) {
-      const int kb = max(0, min(a.share_groups[3 * s + 2], min(a.max_blocks, a.ctx_limit / kBlockTokens)));
-      n = kb * kBlockTokens;
-      nb = kb;
+  auto group_shared = [&](int v) {
+    return max(0, min(a.share_groups[3 * v + 2], min(a.max_blocks, a.ctx_limit / kBlockTokens)));
+  };
+  // Blocks of a member with n tokens beyond the k shared ones.
+  auto own_blocks = [&](int n, int k) { return max(0, (n + kBlockTokens - 1) / kBlockTokens - k); };
+  // Context length (kPlain) and blocks to stream of context s.
+  auto shape_of = [&](int s, int& n, int& nb) {
+    if constexpr (MODE == kGroup) {
+      const int f = group_first(s), mm = group_members(s, f), k = group_shared(s);
+      nb = k;
+      for (int j = 0; j < mm; ++j) nb += own_blocks(clamp_ctx(a, f + j), k);
+      n = nb * kBlockTokens;
     } else {
       n = clamp_ctx(a, s);
       nb = (n + kBlockTokens - 1) / kBlockTokens;
-      if constexpr (MODE == kRest) {
-        skip = max(0, min(a.share_skip[s], nb));
-        nb -= skip;
-      }
     }
   };
 
@@ -484,8 +483,8 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   for (int j = 0; j < per; ++j) {
     const int s = tid * per + j;
     if (s < S) {
-      int n, nb, skip;
-      shape_of(s, n, nb, skip);
+      int n, nb;
+      shape_of(s, n, nb);
       cnt += wnb_of(nb);
     }
   }
@@ -502,12 +501,11 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     for (int j = 0; j < per; ++j) {
       const int s = tid * per + j;
       if (s < S) {
-        int n, nb, skip;
-        shape_of(s, n, nb, skip);
+        int n, nb;
+        shape_of(s, n, nb);
         blkpre[s] = base * hkv;
         nb_s[s] = nb;
         ctx_s[s] = n;
-        if constexpr (MODE == kRest) skip_s[s] = skip;
         base += wnb_of(nb);
       }
     }
@@ -516,16 +514,16 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   __syncthreads();
   const int W = __builtin_amdgcn_readfirstlane(blkpre[S]);
 
-  // Zero-length sequences own no partition: their output is 0.  In the rest pass a sequence whose
-  // prefix covers its whole context has the prefix partial (normalised) as its output.
-  if constexpr (MODE != kPrefix) {
-    for (int s = blockIdx.x; s < S; s += J) {
-      if (ctx_s[s] == 0) {
-        for (int i = tid; i < a.hq * D; i += kThreads) store_out<DT>(a, static_cast<int64_t>(s) * a.hq * D + i, 0.0f);
-      } else if (MODE == kRest && nb_s[s] == 0) {
-        for (int i = tid; i < a.hq * D; i += kThreads)
-          store_out<DT>(a, static_cast<int64_t>(s) * a.hq * D + i, a.pre_o[static_cast<int64_t>(s) * a.hq * D + i]);
+  // Zero-length contexts own no partition: their output is 0 (all members' rows for a group).
+  for (int s = blockIdx.x; s < S; s += J) {
+    if (ctx_s[s] == 0) {
+      int f = s, mm = 1;
+      if constexpr (MODE == kGroup) {
+        f = group_first(s);
+        mm = group_members(s, f);
       }
+      for (int i = tid; i < mm * a.hq * D; i += kThreads)
+        store_out<DT>(a, static_cast<int64_t>(f) * a.hq * D + i, 0.0f);
     }
   }
   if (W == 0) return;
@@ -551,6 +549,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     Item it;
     bool ok;
     int32_t ids;    // this wave's block ids, one per lane; lanes >= my_n are never used
+    int32_t meta;   // kGroup: per lane, (owning member + 1) << 8 | tokens of the block (owner 0 = shared)
     u32x4_t q[KK];  // Q^T operand
   };
   using st = uint16_t;
@@ -575,23 +574,42 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
       it.np = (nb + PB - 1) / PB;
       it.len = min(PB, nb - p * PB);
       it.b0 = p * PB;
-      if constexpr (MODE == kRest) it.b0 += __builtin_amdgcn_readfirstlane(skip_s[s]);
       it.my_n = (it.len > w) ? (it.len - w + kWaves - 1) / kWaves : 0;
     }
-    // The table row and the query row of column col.
-    int64_t trow = it.s;
     int64_t qrow;
-    if constexpr (MODE == kPrefix) {
+    if constexpr (MODE == kGroup) {
+      // This lane's block b of the group's context: shared block b (first member's row) while
+      // b < k, else block k + r of the member whose own blocks hold position r = b - k.
       const int first = __builtin_amdgcn_readfirstlane(group_first(it.s));
-      const int ncol = group_members(it.s, first) * g;
-      trow = first;
-      const int c = col < ncol ? col : 0;
+      const int mm = __builtin_amdgcn_readfirstlane(group_members(it.s, first));
+      const int k = __builtin_amdgcn_readfirstlane(group_shared(it.s));
+      const int c = col < mm * g ? col : 0;
       qrow = (static_cast<int64_t>(first + c / g) * a.hq + it.h * g + c % g) * D;
+      const int b = it.b0 + w + kWaves * lane;
+      int row = first, pos = b, owner = 0, nv = kBlockTokens;
+      if (b >= k) {
+        int r = b - k;
+        for (int j = 0; j < mm; ++j) {
+          const int nj = clamp_ctx(a, first + j);
+          const int oj = own_blocks(nj, k);
+          if (r < oj || j == mm - 1) {
+            row = first + j;
+            pos = k + r;
+            owner = j + 1;
+            nv = min(kBlockTokens, max(0, nj - pos * kBlockTokens));
+            break;
+          }
+          r -= oj;
+        }
+      }
+      sl.meta = (owner << 8) | nv;
+      sl.ids = a.block_tables[static_cast<int64_t>(row) * a.max_blocks + min(max(pos, 0), a.max_blocks - 1)];
     } else {
       qrow = (static_cast<int64_t>(it.s) * a.hq + it.h * g + (col < g ? col : 0)) * D;
+      const int b = min(it.b0 + w + kWaves * lane, a.max_blocks - 1);
+      sl.meta = 0;
+      sl.ids = a.block_tables[static_cast<int64_t>(it.s) * a.max_blocks + b];
     }
-    const int b = min(it.b0 + w + kWaves * lane, a.max_blocks - 1);
-    sl.ids = a.block_tables[trow * a.max_blocks + b];
     // Keep the id load ahead of the query loads: the lookahead waits for it while the
     // query loads may still be in flight.
     __builtin_amdgcn_sched_barrier(0);
@@ -656,42 +674,12 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   // Query columns of context s (first = its group's first sequence in the prefix pass), and the
   // q / out row of column cc with KV head h.
   auto ncols = [&](int s, int first) {
-    if constexpr (MODE == kPrefix) return group_members(s, first) * g;
+    if constexpr (MODE == kGroup) return group_members(s, first) * g;
     else return g;
   };
   auto out_row = [&](int s, int h, int cc, int first) -> int64_t {
-    if constexpr (MODE == kPrefix) return static_cast<int64_t>(first + cc / g) * a.hq + h * g + cc % g;
+    if constexpr (MODE == kGroup) return static_cast<int64_t>(first + cc / g) * a.hq + h * g + cc % g;
     else return static_cast<int64_t>(s) * a.hq + h * g + cc;
-  };
-  // Final result of 4 dims of one row from its merged (max, sum, unnormalised output).  The rest
-  // pass merges the row's prefix partial in first; the prefix pass writes the prefix partial.
-  auto emit = [&](int64_t row, int d0, float mx, float L, f32x4_t O, bool with_prefix) {
-    if constexpr (MODE == kRest) {
-      if (with_prefix) {
-        const float pm = a.pre_ml[row * 2], pl = a.pre_ml[row * 2 + 1];
-        const f32x4_t po = *reinterpret_cast<const f32x4_t*>(a.pre_o + row * D + d0);
-        if (pl > 0.f) {
-          const float Mn = fmaxf(mx, pm);
-          const float sc = (mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mx - Mn);
-          const float wr = __builtin_amdgcn_exp2f(pm - Mn) * pl;
-          O = O * sc + po * wr;
-          L = L * sc + wr;
-          mx = Mn;
-        }
-      }
-    }
-    f32x4_t res;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) res[e] = L > 0.f ? O[e] / L : 0.f;
-    if constexpr (MODE == kPrefix) {
-      *reinterpret_cast<f32x4_t*>(a.pre_o + row * D + d0) = res;
-      if (d0 == 0) {
-        a.pre_ml[row * 2] = mx;
-        a.pre_ml[row * 2 + 1] = L;
-      }
-    } else {
-      store_out4<DT>(a, row * D + d0, res);
-    }
   };
   auto merge_ctx = [&](int s, int h, int np, int nb) {
     const int64_t A = static_cast<int64_t>(blkpre[s]) + static_cast<int64_t>(h) * wnb_of(nb);
@@ -703,8 +691,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
     constexpr int kChunks = D / 4;
     constexpr int kBatch = 16;
-    const int first = MODE == kPrefix ? group_first(s) : s;
-    const bool with_prefix = MODE == kRest && skip_s[MODE == kRest ? s : 0] > 0;
+    const int first = MODE == kGroup ? group_first(s) : s;
     for (int c4 = tid; c4 < ncols(s, first) * kChunks; c4 += kThreads) {
       const int cc = c4 / kChunks, d0 = (c4 % kChunks) * 4;
       const int64_t row = out_row(s, h, cc, first);
@@ -742,21 +729,35 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
           }
         }
       }
-      emit(row, d0, M, Lsum, acc, with_prefix);
+      f32x4_t res;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) res[e] = Lsum > 0.f ? acc[e] / Lsum : 0.f;
+      store_out4<DT>(a, row * D + d0, res);
     }
     __syncthreads();  // run_p0 is reused by the next merge
   };
 
   // Stream one partition's blocks (looking ahead into the next one).  At the end of a
   // segment, merge the four waves and write the output or the run's partial.
-  auto run = [&](const Item cur, const int32_t cur_ids, const u32x4_t (&qc)[KK], const Item nxi, const bool nx_ok,
-                 const int32_t nx_ids) {
+  auto run = [&](const Item cur, const int32_t cur_ids, const int32_t cur_meta, const u32x4_t (&qc)[KK],
+                 const Item nxi, const bool nx_ok, const int32_t nx_ids) {
     auto compute = [&](const KVRegs<D>& r, int i) {
-      const int bl = cur.b0 + w + kWaves * i;
       const int32_t phys = __builtin_amdgcn_readlane(cur_ids, i < 63 ? i : 63);
-      int nv = cur.n - bl * kBlockTokens;
-      nv = nv > kBlockTokens ? kBlockTokens : nv;
-      if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
+      int nv;      // tokens of the block
+      int nv_col;  // tokens of the block this lane's query column sees
+      if constexpr (MODE == kGroup) {
+        const int meta = __builtin_amdgcn_readlane(cur_meta, i < 63 ? i : 63);
+        nv = meta & 0xff;
+        const int owner = meta >> 8;
+        if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
+        nv_col = (owner == 0 || owner - 1 == col / g) ? nv : 0;
+      } else {
+        const int bl = cur.b0 + w + kWaves * i;
+        nv = cur.n - bl * kBlockTokens;
+        nv = nv > kBlockTokens ? kBlockTokens : nv;
+        if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
+        nv_col = nv;
+      }
 
       f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -764,7 +765,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
 
       float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (grp * 4 + e < nv) ? sacc[e] * a.scale_log2 : -INFINITY;
+      for (int e = 0; e < 4; ++e) x[e] = (grp * 4 + e < nv_col) ? sacc[e] * a.scale_log2 : -INFINITY;
       float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
@@ -840,8 +841,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     if (w == (wave_turn & (kWaves - 1))) {
       const bool final = seg_p0 == 0 && cur.p == cur.np - 1;  // the segment is the whole context
       constexpr int kChunks = D / 4;                            // 4 consecutive dims per lane and store
-      const int first = MODE == kPrefix ? __builtin_amdgcn_readfirstlane(group_first(cur.s)) : cur.s;
-      const bool with_prefix = MODE == kRest && skip_s[MODE == kRest ? cur.s : 0] > 0;
+      const int first = MODE == kGroup ? __builtin_amdgcn_readfirstlane(group_first(cur.s)) : cur.s;
       for (int c4 = lane; c4 < ncols(cur.s, first) * kChunks; c4 += kWave) {
         const int cc = c4 / kChunks, d0 = (c4 % kChunks) * 4;
         float mx = sm_m[0][cc];
@@ -857,13 +857,13 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
             O += e * *reinterpret_cast<const f32x4_t*>(&sm_o[ww][cc][d0]);
           }
         }
+        f32x4_t res;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[e] = L > 0.f ? O[e] / L : 0.f;
         const int64_t row = out_row(cur.s, cur.h, cc, first);
         if (final) {
-          emit(row, d0, mx, L, O, with_prefix);
+          store_out4<DT>(a, row * D + d0, res);
         } else {
-          f32x4_t res;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) res[e] = L > 0.f ? O[e] / L : 0.f;
           const int64_t prow = row * a.max_parts + seg_p0;
           // Device-scope stores: the run that merges this context may sit on another XCD.
 #pragma unroll
@@ -933,11 +933,11 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   off += wlen(A.it);
   prepare_next(A.it, off, B);
   while (true) {
-    run(A.it, A.ids, A.q, B.it, B.ok, B.ids);
+    run(A.it, A.ids, A.meta, A.q, B.it, B.ok, B.ids);
     if (!B.ok) break;
     off += wlen(B.it);
     prepare_next(B.it, off, A);
-    run(B.it, B.ids, B.q, A.it, A.ok, A.ids);
+    run(B.it, B.ids, B.meta, B.q, A.it, A.ok, A.ids);
     if (!A.ok) break;
     off += wlen(A.it);
     prepare_next(A.it, off, B);
@@ -1147,9 +1147,9 @@ struct Plan {
   int32_t part_tokens;
   int32_t part_blocks;
   int32_t ctx_limit;
-  int32_t max_parts;
+  int32_t max_parts;   // partitions of the longest context
+  int32_t slot_parts;  // partial slots per query row: max_parts, or a whole group's partitions with sharing
   size_t counter_offset;  // byte offset of the arrival counters in the workspace
-  size_t pre_offset;      // byte offset of the prefix partials (with shared prefixes)
   size_t workspace;
 };
 
@@ -1176,20 +1176,24 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
   out->part_blocks = pt / B;
   out->ctx_limit = limit;
   out->max_parts = parts;
-  // Partials [S][H_q][parts][D] and [S][H_q][parts][2] (fp32),
-  const size_t rows = static_cast<size_t>(p->num_seqs) * p->num_q_heads * parts;
-  // then the per (sequence, KV head) arrival counters [S * H_kv] (uint64; the partials end 8-byte aligned)
-  out->counter_offset = rows * (static_cast<size_t>(c.head_dim) + 2) * sizeof(float);
-  out->workspace = parts > 1 ? out->counter_offset + static_cast<size_t>(p->num_seqs) * c.num_kv_heads * 8 : 0;
-  // then, with shared prefixes, the prefix partials [S][H_q][D] and [S][H_q][2] (fp32), 16-byte aligned
-  out->pre_offset = (out->workspace + 15) / 16 * 16;
+  out->slot_parts = parts;
   if (p->shared) {
     const pa_shared_prefix& sh = *p->shared;
-    if (sh.num_groups < 0 || sh.num_groups > p->num_seqs / 2) return PA_ERR_INVALID_ARG;
-    if (sh.num_groups > 0 && (!sh.groups || !sh.seq_prefix)) return PA_ERR_INVALID_ARG;
-    out->workspace = out->pre_offset + static_cast<size_t>(p->num_seqs) * p->num_q_heads *
-                                           (static_cast<size_t>(c.head_dim) + 2) * sizeof(float);
+    if (sh.num_groups < 0 || sh.num_groups > p->num_seqs) return PA_ERR_INVALID_ARG;
+    if (sh.num_groups > 0 && !sh.groups) return PA_ERR_INVALID_ARG;
+    // A group's context holds at most 16 / g members' blocks (each at most ceil(limit / B)).
+    const int64_t members = std::max(1, std::min(16 / (p->num_q_heads / c.num_kv_heads), std::max(1, p->num_seqs)));
+    const int64_t gblocks = members * ((int64_t{limit} + B - 1) / B);
+    const int64_t gparts = std::max<int64_t>(1, (gblocks + out->part_blocks - 1) / out->part_blocks);
+    if (gparts > 8192) return PA_ERR_UNSUPPORTED;
+    out->slot_parts = std::max(parts, static_cast<int32_t>(gparts));
   }
+  // Partials [S][H_q][slot_parts][D] and [S][H_q][slot_parts][2] (fp32),
+  const size_t rows = static_cast<size_t>(p->num_seqs) * p->num_q_heads * out->slot_parts;
+  // then the per (sequence, KV head) arrival counters [S * H_kv] (uint64; the partials end 8-byte aligned)
+  out->counter_offset = rows * (static_cast<size_t>(c.head_dim) + 2) * sizeof(float);
+  out->workspace =
+      out->slot_parts > 1 ? out->counter_offset + static_cast<size_t>(p->num_seqs) * c.num_kv_heads * 8 : 0;
   return PA_OK;
 }
 
@@ -1258,15 +1262,11 @@ int32_t launch_split(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEven
   return PA_OK;
 }
 
-// Shared prefixes: the prefix pass (groups) then the rest pass, each with its own counter tag.
-// Otherwise one plain launch.
+// One launch: over groups when the batch comes with shared prefixes, else over sequences.
 template <int DT, int D>
 int32_t launch_split_all(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  if (args->num_groups <= 0) return launch_split<DT, D, kPlain>(args, st, start, stop);
-  const int32_t rc = launch_split<DT, D, kPrefix>(args, st, start, nullptr);
-  if (rc != PA_OK) return rc;
-  args->launch_tag += 1;
-  return launch_split<DT, D, kRest>(args, st, nullptr, stop);
+  if (args->num_groups > 0) return launch_split<DT, D, kGroup>(args, st, start, stop);
+  return launch_split<DT, D, kPlain>(args, st, start, stop);
 }
 
 template <int DT>
@@ -1279,10 +1279,17 @@ int32_t launch_decode(DecodeArgs args, hipStream_t st, hipEvent_t start, hipEven
   // The split kernel indexes the weighted blocks of all (sequence, KV head) pairs with int32.
   const bool split = fast && args.num_seqs <= kMaxScanSeqs &&
                      int64_t{args.num_seqs} * args.hkv *
-                             (int64_t{args.max_blocks} + int64_t{args.part_cost} * args.max_parts + args.ctx_cost) <
+                             (int64_t{args.max_blocks} + int64_t{args.part_cost} * (args.max_parts + 1) +
+                              args.ctx_cost) <
                          0x7fffffffLL;
   args.run_grid = 0;
   args.run_rounds = 0;
+  if (split && args.num_groups > 0) {
+    // Group contexts span several members' blocks: their partitions index the larger slot range.
+    args.max_parts = args.slot_parts;
+  } else {
+    args.num_groups = 0;  // the other kernels take every sequence on its own
+  }
   if (split) {
     // One launch: the split kernel merges its runs in place.
     if constexpr (DT != PA_F32) return D == 64 ? launch_split_all<DT, 64>(&args, st, start, stop)
@@ -1347,7 +1354,7 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   a.context_lens = context_lens;
   a.out = out;
   a.part_o = static_cast<float*>(p->workspace);
-  a.part_ml = a.part_o ? a.part_o + static_cast<size_t>(p->num_seqs) * p->num_q_heads * plan.max_parts *
+  a.part_ml = a.part_o ? a.part_o + static_cast<size_t>(p->num_seqs) * p->num_q_heads * plan.slot_parts *
                                         p->cache.head_dim
                        : nullptr;
   a.scale_log2 = scale * kLog2e;
@@ -1361,24 +1368,22 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   a.part_blocks = plan.part_blocks;
   a.block_tokens = p->cache.block_size;
   a.max_parts = plan.max_parts;
+  a.slot_parts = plan.slot_parts;
   a.out_f32 = p->out_dtype == PA_F32 ? 1 : 0;
   a.num_blocks = p->cache.num_blocks;
-  a.run_done = plan.max_parts > 1
+  a.run_done = plan.slot_parts > 1
                    ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(p->workspace) + plan.counter_offset)
                    : nullptr;
   if (p->shared && p->shared->num_groups > 0) {
     a.share_groups = p->shared->groups;
-    a.share_skip = p->shared->seq_prefix;
     a.num_groups = p->shared->num_groups;
-    a.pre_o = reinterpret_cast<float*>(static_cast<uint8_t*>(p->workspace) + plan.pre_offset);
-    a.pre_ml = a.pre_o + static_cast<size_t>(p->num_seqs) * p->num_q_heads * p->cache.head_dim;
   }
   // A tag no earlier call of this process used, seeded per process (a workspace may hold
   // counters another process left): the arrival counters need no clearing.
   static std::atomic<uint32_t> next_tag{static_cast<uint32_t>(
       std::chrono::steady_clock::now().time_since_epoch().count() * 0x9e3779b97f4a7c15ull >> 32) ^
       static_cast<uint32_t>(getpid())};
-  a.launch_tag = next_tag.fetch_add(2, std::memory_order_relaxed);  // the rest pass takes the second
+  a.launch_tag = next_tag.fetch_add(1, std::memory_order_relaxed);
 
   hipStream_t stream = static_cast<hipStream_t>(p->stream);
   (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind

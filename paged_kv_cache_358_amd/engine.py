@@ -26,17 +26,16 @@ from . import (BlockAllocator, alloc_kv_cache, block_copy, kv_append, paged_atte
 
 class _Staging:
     """One pinned host buffer and one device buffer holding a step's metadata, int32:
-    context lengths [max_seqs] | slots [max_tokens] | copy pairs [max_seqs, 2] | shared
-    prefix blocks [max_seqs] | shared-prefix groups [max_seqs // 2, 3] | block tables
-    [max_seqs, max_blocks].  A step moves the used prefix in one host->device copy."""
+    context lengths [max_seqs] | slots [max_tokens] | copy pairs [max_seqs, 2] | groups of
+    sequences sharing leading blocks [max_seqs, 3] | block tables [max_seqs, max_blocks].
+    A step moves the used prefix in one host->device copy."""
 
     def __init__(self, max_seqs: int, max_blocks: int, max_tokens: int, device):
         self.o_lens = 0
         self.o_slots = max_seqs
         self.o_pairs = self.o_slots + max_tokens
-        self.o_prefix = self.o_pairs + 2 * max_seqs
-        self.o_groups = self.o_prefix + max_seqs
-        self.o_tables = self.o_groups + 3 * max(max_seqs // 2, 1)
+        self.o_groups = self.o_pairs + 2 * max_seqs
+        self.o_tables = self.o_groups + 3 * max_seqs
         total = (self.o_tables + max_seqs * max_blocks + 3) // 4 * 4
         self.max_blocks = max_blocks
         self.host = torch.empty(total, dtype=torch.int32, pin_memory=True)
@@ -44,9 +43,8 @@ class _Staging:
         h = self.host.numpy()
         self.h_lens = h[self.o_lens:self.o_slots]
         self.h_slots = h[self.o_slots:self.o_pairs]
-        self.h_pairs = h[self.o_pairs:self.o_prefix].reshape(max_seqs, 2)
-        self.h_prefix = h[self.o_prefix:self.o_groups]
-        self.h_groups = h[self.o_groups:self.o_tables].reshape(-1, 3)
+        self.h_pairs = h[self.o_pairs:self.o_groups].reshape(max_seqs, 2)
+        self.h_groups = h[self.o_groups:self.o_tables].reshape(max_seqs, 3)
         self.h_tables = h[self.o_tables:].reshape(max_seqs, max_blocks)
         self.h_slots_t = self.host[self.o_slots:self.o_pairs]  # the slots as a pinned tensor
         self.done = None  # event that ends the step that last read this buffer
@@ -61,9 +59,6 @@ class _Staging:
 
     def d_pairs(self, n):
         return self.dev[self.o_pairs:self.o_pairs + 2 * n].view(n, 2)
-
-    def d_prefix(self, n):
-        return self.dev[self.o_prefix:self.o_prefix + n]
 
     def d_groups(self, n):
         return self.dev[self.o_groups:self.o_groups + 3 * n].view(n, 3)
@@ -142,11 +137,11 @@ class PagedDecodeLayer:
         np_tables, np_lens = self.alloc.build_batch(ids, self.max_blocks, st.h_tables, st.h_lens)
         max_ctx = int(np_lens.max()) if S else 0
         npairs = len(pairs)
-        ngroups = 0
+        ngroups = 0  # groups covering the batch; 0 when no two sequences share a block
         if self.share_prefixes and S >= 2 and self.share_max_members >= 2:
-            _, groups = shared_prefixes(np_tables, np_lens, self.share_max_members, self.share_min_blocks,
-                                        seq_prefix_out=st.h_prefix, groups_out=st.h_groups)
-            ngroups = len(groups)
+            groups = shared_prefixes(np_tables, np_lens, self.share_max_members, self.share_min_blocks,
+                                     groups_out=st.h_groups)
+            ngroups = len(groups) if len(groups) < S else 0
         used = st.o_tables + S * self.max_blocks  # lengths, slots, pairs, sharing and the first S table rows
         with torch.cuda.stream(self.stream):
             if npairs:
@@ -164,7 +159,7 @@ class PagedDecodeLayer:
                                    max_context_len=max_ctx, partition_size=self.partition_size,
                                    workspace=self.workspace, stream=self.stream,
                                    start_event=None if timing is None else timing[0], stop_event=st.done,
-                                   shared=(st.d_groups(ngroups), st.d_prefix(S)) if ngroups else None)
+                                   shared=st.d_groups(ngroups) if ngroups else None)
         self.last_groups = ngroups
         self.last_lens = np_lens.copy()
         self.last_tables = np_tables  # view into the pinned staging buffer: valid until three steps later

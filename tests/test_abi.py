@@ -124,18 +124,25 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 def test_workspace_bytes_with_shared_prefixes():
     ws = pa.lib.paged_attention_workspace_bytes
-    sh = pa.SharedPrefix(None, None, 0)
-    # one partition: only the prefix partials, S * H_q rows of D + 2 floats
-    p = _params(S=4, hq=8, hkv=2, d=64)
+    sh = pa.SharedPrefix(None, 0)
+
+    def expect(S, hq, hkv, parts, d):
+        return S * hq * parts * (d + 2) * 4 + S * hkv * 8
+
+    # a group holds min(16 / g, S) members' blocks: 4 members (g = 4) of 4 blocks = 1 partition of 512
+    p = _params(S=8, hq=8, hkv=2, d=64)
     p.shared = ctypes.pointer(sh)
-    assert ws(ctypes.byref(p)) == 4 * 8 * (64 + 2) * 4
-    # several partitions: partials, counters, then the prefix partials at a 16-byte boundary
+    assert ws(ctypes.byref(p)) == 0
+    # 4 members of 32 blocks = 4 partitions of 512 tokens
+    p = _params(S=8, hq=8, hkv=2, d=64, maxb=32, maxctx=512)
+    p.shared = ctypes.pointer(sh)
+    assert ws(ctypes.byref(p)) == expect(8, 8, 2, 4, 64)
+    # MHA: at most the batch's 3 sequences per group, 63 blocks each -> ceil(189 / 16) partitions of 256
     p = _params(S=3, hq=4, hkv=4, d=64, maxb=100, maxctx=1000, part=256)
-    base = 3 * 4 * 4 * (64 + 2) * 4 + 3 * 4 * 8
     p.shared = ctypes.pointer(sh)
-    assert ws(ctypes.byref(p)) == (base + 15) // 16 * 16 + 3 * 4 * (64 + 2) * 4
-    # more groups than half the batch, or groups without arrays: rejected
-    for bad in (pa.SharedPrefix(None, None, 3), pa.SharedPrefix(None, None, -1), pa.SharedPrefix(None, None, 1)):
+    assert ws(ctypes.byref(p)) == expect(3, 4, 4, 12, 64)
+    # more groups than sequences, a negative count, or groups without an array: rejected
+    for bad in (pa.SharedPrefix(None, 5), pa.SharedPrefix(None, -1), pa.SharedPrefix(None, 1)):
         p = _params(S=4)
         p.shared = ctypes.pointer(bad)
         assert ws(ctypes.byref(p)) == 0
@@ -144,15 +151,15 @@ def test_workspace_bytes_with_shared_prefixes():
 
 
 def test_shared_prefixes_rejects_bad_arguments():
-    t = (ctypes.c_int32 * 8)()
-    out = (ctypes.c_int32 * 8)()
+    t = (ctypes.c_int32 * 16)()
+    out = (ctypes.c_int32 * 16)()
     n = ctypes.c_int32(0)
     f = pa.lib.pa_shared_prefixes
     P = ctypes.POINTER(ctypes.c_int32)
     tp, op = ctypes.cast(t, P), ctypes.cast(out, P)
-    assert f(tp, tp, 4, 2, 16, 2, 1, op, op, 2, ctypes.byref(n)) == pa.PA_OK
-    assert f(tp, tp, 4, 2, 16, 2, 1, op, op, 1, ctypes.byref(n)) == pa.PA_ERR_INVALID_ARG  # groups_cap < S / 2
-    assert f(tp, tp, 4, 2, 16, 0, 1, op, op, 2, ctypes.byref(n)) == pa.PA_ERR_INVALID_ARG  # max_members
-    assert f(tp, tp, 4, 2, 16, 2, 0, op, op, 2, ctypes.byref(n)) == pa.PA_ERR_INVALID_ARG  # min_blocks
-    assert f(None, tp, 4, 2, 16, 2, 1, op, op, 2, ctypes.byref(n)) == pa.PA_ERR_INVALID_ARG
-    assert f(None, None, 0, 2, 16, 2, 1, None, None, 0, ctypes.byref(n)) == pa.PA_OK and n.value == 0
+    assert f(tp, tp, 4, 2, 16, 2, 1, op, 4, ctypes.byref(n)) == pa.PA_OK and n.value == 4  # all alone
+    assert f(tp, tp, 4, 2, 16, 2, 1, op, 3, ctypes.byref(n)) == pa.PA_ERR_INVALID_ARG  # groups_cap < S
+    assert f(tp, tp, 4, 2, 16, 0, 1, op, 4, ctypes.byref(n)) == pa.PA_ERR_INVALID_ARG  # max_members
+    assert f(tp, tp, 4, 2, 16, 2, 0, op, 4, ctypes.byref(n)) == pa.PA_ERR_INVALID_ARG  # min_blocks
+    assert f(None, tp, 4, 2, 16, 2, 1, op, 4, ctypes.byref(n)) == pa.PA_ERR_INVALID_ARG
+    assert f(None, None, 0, 2, 16, 2, 1, None, 0, ctypes.byref(n)) == pa.PA_OK and n.value == 0

@@ -4,8 +4,9 @@ Prompts are written once, forked into samples that keep the prompt's blocks
 ("Stop Wasting GPU Memory" page, Technical Details, "Copy-on-Write for Parallel
 Sampling"), and each sample appends its own tokens (the first write into the
 shared partial block copies it).  The batch is laid out prompt by prompt, with
-lone sequences in between; pa_shared_prefixes groups the samples and
-paged_attention_decode reads each group's full prefix blocks once.  The oracle
+lone sequences in between; pa_shared_prefixes cuts the batch into groups and
+paged_attention_decode reads each group's shared blocks once, with each
+member's own blocks scored only for that member's query heads.  The oracle
 sees only each sequence's contiguous truth (prefix + own tokens).
 
 Tolerance: max abs error 5e-3 (bf16/fp16 inputs, fp32 accumulation) against the
@@ -90,15 +91,11 @@ class ForkedBatch:
 
     def groups(self, max_members=None, min_blocks=1):
         mm = 16 // (self.hq // self.hkv) if max_members is None else max_members
-        sp, gr = pa.shared_prefixes(self.tables_np, self.lens_np, mm, min_blocks)
-        return sp, gr
+        return pa.shared_prefixes(self.tables_np, self.lens_np, mm, min_blocks)
 
     def run(self, shared=None, out_dtype=torch.float32):
         out = torch.empty(self.q.shape, dtype=out_dtype, device="cuda")
-        sh = None
-        if shared is not None:
-            sp, gr = shared
-            sh = (torch.from_numpy(np.ascontiguousarray(gr)).cuda(), torch.from_numpy(sp.copy()).cuda())
+        sh = None if shared is None else torch.from_numpy(np.ascontiguousarray(shared)).cuda()
         pa.paged_attention_decode(self.q, self.k_cache, self.v_cache, self.tables, self.lens, self.scale, out,
                                   max_context_len=int(self.lens_np.max()), partition_size=self.part, shared=sh)
         torch.cuda.synchronize()
@@ -116,14 +113,14 @@ class ForkedBatch:
 
 
 def check(fb, **kw):
-    sp, gr = fb.groups(**kw)
-    assert len(gr) > 0
-    o_sh = fb.run((sp, gr))
+    gr = fb.groups(**kw)
+    assert np.any(gr[:, 1] > 1)
+    o_sh = fb.run(gr)
     o_plain = fb.run()
     assert fb.max_err(o_sh) <= 5e-3
     assert fb.max_err(o_plain) <= 5e-3
     assert float(np.max(np.abs(o_sh - o_plain))) <= 5e-3
-    return sp, gr, o_sh
+    return gr, o_sh
 
 
 def test_gqa_samples_ragged_suffixes():
@@ -131,9 +128,11 @@ def test_gqa_samples_ragged_suffixes():
     # 512-token prompt, so its whole context is the group's prefix.
     prompts = [(1000, [200, 1, 17, 0, 64, 300, 5, 16]), (37, [3, 40, 100]), (512, [0, 15, 16, 600, 1, 2])]
     fb = ForkedBatch(1, 32, 8, 128, "bf16", prompts, lone=[700, 1])
-    sp, gr, _ = check(fb)
-    # prompt 0: samples 0..3, 4..7 (62 blocks; sample 3 appended nothing and fills 62 blocks too)
-    assert gr[:2].tolist() == [[0, 4, 62], [4, 4, 62]]
+    gr, _ = check(fb)
+    # prompt 0: samples 0..3, 4..7 (62 blocks; sample 3 appended nothing and fills 62 blocks too),
+    # then the lone sequence, prompt 1's three samples (2 shared blocks), the other lone one,
+    # prompt 2's samples in runs of four and two (32 blocks)
+    assert gr.tolist() == [[0, 4, 62], [4, 4, 62], [8, 1, 0], [9, 3, 2], [12, 1, 0], [13, 4, 32], [17, 2, 32]]
 
 
 def test_mha_sixteen_members_multi_partition_prefix_and_rest():
@@ -142,8 +141,8 @@ def test_mha_sixteen_members_multi_partition_prefix_and_rest():
     rng = np.random.default_rng(5)
     prompts = [(1500, rng.integers(0, 1100, 20).tolist()), (800, rng.integers(1, 40, 3).tolist())]
     fb = ForkedBatch(2, 8, 8, 128, "f16", prompts, lone=[2000, 33])
-    sp, gr, _ = check(fb)
-    assert gr[0].tolist() == [0, 16, 1500 // B]
+    gr, _ = check(fb)
+    assert gr[:2].tolist() == [[0, 16, 1500 // B], [16, 4, 1500 // B]]
 
 
 @pytest.mark.parametrize("part", [16, 48, 1024])
@@ -157,14 +156,14 @@ def test_bf16_output_and_min_blocks():
     prompts = [(640, [10, 20, 30, 40]), (100, [1, 1, 1, 1])]
     fb = ForkedBatch(4, 32, 8, 128, "bf16", prompts)
     # min_blocks 8: prompt 1's 6 full blocks are not shared
-    sp, gr = fb.groups(min_blocks=8)
-    assert gr.tolist() == [[0, 4, 40]] and sp.tolist() == [40] * 4 + [0] * 4
+    gr = fb.groups(min_blocks=8)
+    assert gr.tolist() == [[0, 4, 40], [4, 1, 0], [5, 1, 0], [6, 1, 0], [7, 1, 0]]
     o = torch.empty(fb.q.shape, dtype=torch.bfloat16, device="cuda")
-    sh = (torch.from_numpy(gr.copy()).cuda(), torch.from_numpy(sp.copy()).cuda())
+    sh = torch.from_numpy(gr.copy()).cuda()
     pa.paged_attention_decode(fb.q, fb.k_cache, fb.v_cache, fb.tables, fb.lens, fb.scale, o,
                               max_context_len=int(fb.lens_np.max()), shared=sh)
     torch.cuda.synchronize()
-    o32 = fb.run((sp, gr))
+    o32 = fb.run(gr)
     ob = o.float().cpu().numpy()
     # bf16 output is the fp32 result rounded once: within half a bf16 ulp of it
     assert np.all(np.abs(ob - o32) <= np.abs(o32) * 2.0 ** -8 + 1e-30)
@@ -173,11 +172,11 @@ def test_bf16_output_and_min_blocks():
 def test_workspace_reuse_between_shared_and_plain_calls():
     prompts = [(700, [5, 300, 9, 900]), (1200, [1, 2, 3, 4, 5, 6, 7, 8])]
     fb = ForkedBatch(6, 32, 8, 128, "bf16", prompts, lone=[1300])
-    sp, gr = fb.groups()
+    gr = fb.groups()
     need = pa.paged_attention_workspace_bytes(fb.q, fb.k_cache, fb.v_cache, fb.tables,
                                               torch.empty(1, device="cuda"), int(fb.lens_np.max()), 512, shared=True)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    sh = (torch.from_numpy(gr.copy()).cuda(), torch.from_numpy(sp.copy()).cuda())
+    sh = torch.from_numpy(gr.copy()).cuda()
     outs = []
     for use in (True, False, True, True):
         o = torch.empty(fb.q.shape, dtype=torch.float32, device="cuda")
@@ -189,3 +188,26 @@ def test_workspace_reuse_between_shared_and_plain_calls():
     # the same call gives the same bits every time
     assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[0], outs[3])
     assert fb.max_err(outs[0]) <= 5e-3 and fb.max_err(outs[1]) <= 5e-3
+
+
+def test_groups_of_one_and_an_empty_context():
+    # every sequence alone (the cover without sharing) gives the plain call's bits; samples that
+    # own one or two tokens beyond the shared blocks; an empty sequence alone gives 0
+    prompts = [(48, [0, 1, 2, 16, 17, 100])]
+    fb = ForkedBatch(7, 32, 8, 128, "bf16", prompts, lone=[0])
+    alone = np.array([[s, 1, 0] for s in range(len(fb.order))], np.int32)
+    o_alone, o_plain = fb.run(alone), fb.run()
+    assert np.array_equal(o_alone, o_plain)
+    gr = fb.groups()
+    assert gr.tolist()[:2] == [[0, 4, 3], [4, 2, 3]] and gr.tolist()[2] == [6, 1, 0]
+    o = fb.run(gr)
+    errs = []
+    for i, s in enumerate(fb.order):
+        k, v = fb.truth[s]
+        if k.shape[0] == 0:
+            assert np.all(o[i] == 0)
+            continue
+        ref = decode_attention_seq(synth.decode_f64(fb.q_np[i], "bf16"), synth.decode_f64(k, "bf16"),
+                                   synth.decode_f64(v, "bf16"), fb.scale)
+        errs.append(float(np.max(np.abs(o[i] - ref))))
+    assert max(errs) <= 5e-3

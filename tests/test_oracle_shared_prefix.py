@@ -183,3 +183,22 @@ def test_prefix_and_rest_merge_to_the_whole_attention():
         merged = (a1 * o1 + a2 * o2) / (a1 + a2)
         ref = decode_attention_seq(q[None, :], K[:, None, :], V[:, None, :], scale)[0]
         assert np.max(np.abs(merged - ref)) < 1e-13
+
+
+def test_cover_cuts_the_batch_into_runs_in_order():
+    from oracle.shared_prefix import shared_prefix_cover
+    tables = [[7, 8, 9, 10, -1], [7, 8, 9, 11, -1], [7, 8, 9, 12, -1], [7, 20, 21, -1, -1],
+              [30, 31, -1, -1, -1], [30, 31, -1, -1, -1], [40, -1, -1, -1, -1]]
+    lens = [64, 60, 40, 40, 31, 32, 16]
+    assert shared_prefix_cover(tables, lens, B, 8, 2) == [(0, 3, 2), (3, 1, 0), (4, 1, 0), (5, 1, 0), (6, 1, 0)]
+    assert shared_prefix_cover(tables, lens, B, 2, 1) == [(0, 2, 3), (2, 2, 1), (4, 2, 1), (6, 1, 0)]
+    assert shared_prefix_cover([], [], B, 4, 1) == []
+    rng = np.random.default_rng(2)
+    for _ in range(30):
+        S = int(rng.integers(1, 12))
+        tables = rng.integers(0, 3, (S, 4)).tolist()
+        lens = rng.integers(0, 70, S).tolist()
+        runs = shared_prefix_cover(tables, lens, B, int(rng.integers(1, 5)), 1)
+        assert [r[0] for r in runs] == list(np.cumsum([0] + [r[1] for r in runs[:-1]]))
+        assert sum(r[1] for r in runs) == S
+        assert all(r[2] == 0 for r in runs if r[1] == 1)
