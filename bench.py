@@ -170,14 +170,16 @@ def main():
     step_lens, step_pairs = [], []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step_tables, step_groups = [], []
+    step_groups, step_group_rows = [], []
+    first_tables = None
     for i in range(K):
         q, kn, vn = step_inputs[W + i]
         step_pairs.append(layer.decode_step(seqs, q, kn, vn, out, scale, timing=events[i]))
         step_lens.append(layer.last_lens)
         step_groups.append(layer.last_groups)
-        if shared:
-            step_tables.append(layer.last_tables.copy())
+        step_group_rows.append(layer.last_group_rows)
+        if shared and i == 0:
+            first_tables = layer.last_tables.copy()
     t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -206,8 +208,23 @@ def main():
                 used[phys] = max(used.get(phys, 0), min(16, n - 16 * b))
         return int(sum(used.values()) * kvbpt) + fixed
 
+    # With groups, a group's k shared (full) blocks are one set of physical blocks and every other block
+    # is held by one sequence: each member beyond the first re-reads 16 k tokens.  The first timed step
+    # checks that against the count over its physical blocks.
+    def group_bytes(lens, rows):
+        if rows is None:
+            return attn_bytes(lens)
+        dup = int(sum((m - 1) * 16 * k for _, m, k in rows.tolist()))
+        return attn_bytes(lens) - dup * kvbpt
+
     logical = [attn_bytes(l) for l in step_lens]
-    attn = [attn_bytes(l, t) for l, t in zip(step_lens, step_tables)] if shared else logical
+    if shared:
+        attn = [group_bytes(l, r) for l, r in zip(step_lens, step_group_rows)]
+        exact = attn_bytes(step_lens[0], first_tables)
+        if attn[0] != exact:
+            sys.exit(f"bench: unique bytes from the groups ({attn[0]}) differ from the block count ({exact})")
+    else:
+        attn = logical
     append_b = S * hkv * D * eb * 2 * 2 + S * 4
     copy_b = [p * block_bytes * 2 * 2 for p in step_pairs]
     total_bytes = sum(attn) + K * append_b + sum(copy_b)
@@ -246,7 +263,7 @@ def main():
         result["logical_attention_bytes_per_launch"] = int(np.mean(logical))
         result["effective_logical_gbs"] = round(float(np.mean(logical)) / mean_main_s / 1e9, 1)
 
-    last_tables = (step_tables[-1] if shared else layer.last_tables).copy()
+    last_tables = layer.last_tables.copy()
     result["cache_ops"] = cache_ops_probe(layer, step_inputs[-1], last_tables, block_bytes)
     if not shared:
         result["decode_probes"] = decode_probes(layer, step_inputs[-1][0], out, scale, last_tables,

@@ -87,7 +87,7 @@ typedef struct pa_cache_desc {
  * without the description, within rounding.  pa_shared_prefixes builds the groups from host copies of
  * the tables and lengths.
  *   groups   device int32 [num_groups][3]: first sequence, members, prefix_blocks
- * members * (H_q / H_kv) must not exceed 16 (the query columns of one matrix-core tile).  A description
+ * members * (H_q / H_kv) must not exceed 32 (the query columns of two matrix-core tiles).  A description
  * that does not match the tables gives undefined results (never out-of-bounds accesses).  Used by the
  * bf16/fp16, head_dim 64/128, up-to-2048-sequence path; the other paths ignore it.
  */
@@ -135,7 +135,7 @@ const char* pa_last_error(void);
 /* Device workspace bytes paged_attention_decode needs for these parameters: when more than one partition
  * can occur, P = num_seqs * H_q * n fp32 partial rows of head_dim + 2 values (P * (head_dim + 2) * 4 bytes),
  * then num_seqs * H_kv uint64 arrival counters; else 0.  n = ceil(max_context_len / partition_size), or with
- * p->shared set the partitions of a group of min(16 / (H_q / H_kv), num_seqs) members of ceil(max_context_len
+ * p->shared set the partitions of a group of min(32 / (H_q / H_kv), num_seqs) members of ceil(max_context_len
  * / 16) blocks each.  Returns 0 for invalid parameters (the decode call then reports the error).  The contents need no initialisation (the counters carry a per-call tag)
  * and are scratch between calls; two calls in flight at once must not share a workspace. */
 size_t paged_attention_workspace_bytes(const pa_decode_params* p);

@@ -212,7 +212,7 @@ def shared_prefixes(tables, lens, max_members: int, min_blocks: int = 1, block_s
     """The batch (host block tables int32 [S, max_blocks], lengths int32 [S]) cut into groups of
     consecutive sequences that share leading full blocks: int32 [G, 3] rows of (first sequence,
     members, shared blocks), covering the batch in order (a sequence that shares nothing is a group
-    of one with 0 shared blocks).  ``max_members`` is at most 16 // (H_q / H_kv) for
+    of one with 0 shared blocks).  ``max_members`` is at most 32 // (H_q / H_kv) for
     paged_attention_decode.  ``groups_out`` (C-contiguous int32 [>= S, 3]) receives it in place."""
     t, tptr = _as_i32(tables)
     ln, lptr = _as_i32(lens)

@@ -26,12 +26,22 @@ struct pa_allocator {
   struct Seq {
     std::vector<int32_t> table;
     int64_t len = 0;
+    // Dry-run state of a batched append (valid while stamp equals the allocator's gen).
+    uint64_t stamp = 0;
+    int64_t len_after = 0;
+    int32_t last_after = -1;  // current last block after earlier copy-on-write, -1 = private fresh block
   };
   int32_t num_blocks = 0;
   int32_t block_size = 0;
   std::vector<int32_t> free_stack;  // back() is handed out next
   std::vector<int32_t> refcnt;
   std::unordered_map<int64_t, Seq> seqs;
+  // Scratch of batched appends: a generation counter, per-block count changes of the dry run
+  // (valid while delta_stamp equals gen) and the batch's sequences.
+  uint64_t gen = 0;
+  std::vector<int32_t> delta;
+  std::vector<uint64_t> delta_stamp;
+  std::vector<Seq*> batch;
 
   int32_t take() {
     int32_t b = free_stack.back();
@@ -144,39 +154,51 @@ int32_t pa_seq_append_batch(pa_allocator* a, const int64_t* ids, int32_t n_seqs,
     return PA_ERR_INVALID_ARG;
   // Dry run: replay the batch on lengths and last-block counts only, so the whole
   // batch is admitted or refused before any state changes.  Sequences that appear
-  // more than once, and siblings sharing a last block, are replayed in order.
-  std::unordered_map<int64_t, int64_t> len_after;
-  std::unordered_map<int64_t, int32_t> last_after;      // seq -> current last block (after earlier CoW)
-  std::unordered_map<int32_t, int32_t> count_delta;     // block -> change of its count
+  // more than once, and siblings sharing a last block, are replayed in order.  The
+  // replay state lives in the sequences and a per-block array, stamped with this call's
+  // generation, so nothing is allocated per call once the scratch has grown.
+  const uint64_t gen = ++a->gen;
+  if (a->delta.size() != static_cast<size_t>(a->num_blocks)) {
+    a->delta.assign(a->num_blocks, 0);
+    a->delta_stamp.assign(a->num_blocks, 0);
+  }
+  if (a->batch.size() < static_cast<size_t>(n_seqs)) a->batch.resize(n_seqs);
   int64_t need_total = 0, pairs_total = 0, tokens_total = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
     auto it = a->seqs.find(ids[i]);
     if (it == a->seqs.end() || counts[i] < 0) return PA_ERR_INVALID_ARG;
-    const pa_allocator::Seq& s = it->second;
-    auto li = len_after.find(ids[i]);
-    const int64_t len = li == len_after.end() ? s.len : li->second;
+    pa_allocator::Seq& s = it->second;
+    a->batch[i] = &s;
+    if (s.stamp != gen) {
+      s.stamp = gen;
+      s.len_after = s.len;
+      s.last_after = s.table.empty() ? -1 : s.table.back();
+    }
+    const int64_t len = s.len_after;
     const int32_t n = counts[i];
     tokens_total += n;
     if (n == 0) continue;
     const int64_t fresh = a->blocks_of(len + n, a->block_size) - a->blocks_of(len, a->block_size);
     need_total += fresh;
     if (len % a->block_size != 0) {
-      auto lb = last_after.find(ids[i]);
-      const int32_t last = lb == last_after.end() ? s.table.back() : lb->second;
+      const int32_t last = s.last_after;
       if (last >= 0) {
-        auto cd = count_delta.find(last);
-        const int32_t cnt = a->refcnt[last] + (cd == count_delta.end() ? 0 : cd->second);
+        const int32_t cnt = a->refcnt[last] + (a->delta_stamp[last] == gen ? a->delta[last] : 0);
         if (cnt > 1) {
           need_total += 1;
           pairs_total += 1;
-          count_delta[last] -= 1;
-          last_after[ids[i]] = -1;  // now a private fresh block (count 1)
+          if (a->delta_stamp[last] != gen) {
+            a->delta_stamp[last] = gen;
+            a->delta[last] = 0;
+          }
+          a->delta[last] -= 1;
+          s.last_after = -1;  // now a private fresh block (count 1)
         }
       }
     }
     if (len + n > static_cast<int64_t>(INT32_MAX)) return PA_ERR_INVALID_ARG;
-    len_after[ids[i]] = len + n;
-    if (fresh > 0) last_after[ids[i]] = -1;  // the last block is freshly taken
+    s.len_after = len + n;
+    if (fresh > 0) s.last_after = -1;  // the last block is freshly taken
   }
   if (tokens_total > 0 && !slots_out) return PA_ERR_INVALID_ARG;
   if (pairs_total > pairs_cap || (pairs_total > 0 && !pairs_out)) return PA_ERR_INVALID_ARG;
@@ -184,8 +206,7 @@ int32_t pa_seq_append_batch(pa_allocator* a, const int64_t* ids, int32_t n_seqs,
   *n_pairs = 0;
   int64_t off = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
-    pa_allocator::Seq& s = a->seqs.find(ids[i])->second;
-    a->do_append(s, counts[i], slots_out + off, pairs_out, n_pairs);
+    a->do_append(*a->batch[i], counts[i], slots_out + off, pairs_out, n_pairs);
     off += counts[i];
   }
   return PA_OK;
@@ -239,17 +260,20 @@ int32_t pa_build_batch(const pa_allocator* a, const int64_t* ids, int32_t n, int
                        int32_t* tables_out, int32_t* lens_out) {
   if (!a || n < 0 || max_blocks < 0) return PA_ERR_INVALID_ARG;
   if (n > 0 && (!ids || !lens_out || (max_blocks > 0 && !tables_out))) return PA_ERR_INVALID_ARG;
+  std::vector<const pa_allocator::Seq*> rows(n);
   for (int32_t i = 0; i < n; ++i) {
     auto it = a->seqs.find(ids[i]);
     if (it == a->seqs.end()) return PA_ERR_INVALID_ARG;
     if (static_cast<int64_t>(it->second.table.size()) > max_blocks) return PA_ERR_INVALID_ARG;
     if (it->second.len > INT32_MAX) return PA_ERR_INVALID_ARG;
+    rows[i] = &it->second;
   }
   for (int32_t i = 0; i < n; ++i) {
-    const auto& s = a->seqs.find(ids[i])->second;
+    const auto& s = *rows[i];
     int32_t* row = tables_out + static_cast<int64_t>(i) * max_blocks;
-    std::fill(row, row + max_blocks, -1);
-    if (!s.table.empty()) std::memcpy(row, s.table.data(), s.table.size() * sizeof(int32_t));
+    const size_t used = s.table.size();
+    if (used) std::memcpy(row, s.table.data(), used * sizeof(int32_t));
+    std::fill(row + used, row + max_blocks, -1);
     lens_out[i] = static_cast<int32_t>(s.len);
   }
   return PA_OK;
@@ -277,8 +301,9 @@ int32_t pa_shared_prefixes(const int32_t* tables, const int32_t* lens, int32_t n
     while (j < num_seqs && j - i < max_members) {
       const int32_t* row_j = tables + static_cast<int64_t>(j) * max_blocks;
       const int32_t lim = std::min(k, full(j));
-      int32_t common = 0;
-      while (common < lim && row_i[common] == row_j[common]) ++common;
+      int32_t common = lim;
+      if (std::memcmp(row_i, row_j, static_cast<size_t>(lim) * sizeof(int32_t)) != 0)
+        common = static_cast<int32_t>(std::mismatch(row_i, row_i + lim, row_j).first - row_i);
       if (common < min_blocks) break;
       k = common;
       ++j;

@@ -335,7 +335,8 @@ constexpr int kMaxSplitGrid = 4095;  // chunks (workgroups) of the split kernel,
 // context is the shared blocks (read through the first member's table) followed by each member's
 // own blocks k .. in member order.  Scores of a member's own block count only in that member's
 // columns (the others see -inf there), so every column's online softmax runs over exactly its
-// sequence's tokens, and each shared block is read once for all members.
+// sequence's tokens, and each shared block is read once for all members.  A group has up to 32
+// query columns: two 16-column MFMA tiles that share every K/V block's registers.
 constexpr int kPlain = 0;
 constexpr int kGroup = 1;
 
@@ -411,6 +412,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   constexpr int NV = D / 16;
   constexpr int kTileBytes = D * kBlockTokens * 2;
   constexpr int kThreads = kWaves * kWave;
+  constexpr int NT = MODE == kGroup ? 2 : 1;  // 16-column MFMA tiles of query columns
   __shared__ __attribute__((aligned(16))) float sm_o[kWaves][16][D];
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
@@ -450,14 +452,14 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   }
 
   // kGroup: group v's first sequence, members and shared blocks, clamped so that every row stays
-  // inside the batch, the columns inside one 16-wide tile and the shared blocks inside a table row.
+  // inside the batch, the columns inside the NT 16-wide tiles and the shared blocks inside a table row.
   auto group_first = [&](int v) {
     const int f = a.share_groups[3 * v];
     return f < 0 ? 0 : (f >= a.num_seqs ? a.num_seqs - 1 : f);
   };
   auto group_members = [&](int v, int first) {
     const int mm = a.share_groups[3 * v + 1];
-    return max(1, min(min(mm, a.num_seqs - first), 16 / g));
+    return max(1, min(min(mm, a.num_seqs - first), 16 * NT / g));
   };
   auto group_shared = [&](int v) {
     return max(0, min(a.share_groups[3 * v + 2], min(a.max_blocks, a.ctx_limit / kBlockTokens)));
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     bool ok;
     int32_t ids;    // this wave's block ids, one per lane; lanes >= my_n are never used
     int32_t meta;   // kGroup: per lane, (owning member + 1) << 8 | tokens of the block (owner 0 = shared)
-    u32x4_t q[KK];  // Q^T operand
+    u32x4_t q[NT][KK];  // Q^T operand of each column tile
   };
   using st = uint16_t;
   const st* qp = static_cast<const st*>(a.q);
@@ -576,15 +578,18 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
       it.b0 = p * PB;
       it.my_n = (it.len > w) ? (it.len - w + kWaves - 1) / kWaves : 0;
     }
-    int64_t qrow;
+    int64_t qrow[NT];
     if constexpr (MODE == kGroup) {
       // This lane's block b of the group's context: shared block b (first member's row) while
       // b < k, else block k + r of the member whose own blocks hold position r = b - k.
       const int first = __builtin_amdgcn_readfirstlane(group_first(it.s));
       const int mm = __builtin_amdgcn_readfirstlane(group_members(it.s, first));
       const int k = __builtin_amdgcn_readfirstlane(group_shared(it.s));
-      const int c = col < mm * g ? col : 0;
-      qrow = (static_cast<int64_t>(first + c / g) * a.hq + it.h * g + c % g) * D;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int c = t * 16 + col < mm * g ? t * 16 + col : 0;
+        qrow[t] = (static_cast<int64_t>(first + c / g) * a.hq + it.h * g + c % g) * D;
+      }
       const int b = it.b0 + w + kWaves * lane;
       int row = first, pos = b, owner = 0, nv = kBlockTokens;
       if (b >= k) {
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
       sl.meta = (owner << 8) | nv;
       sl.ids = a.block_tables[static_cast<int64_t>(row) * a.max_blocks + min(max(pos, 0), a.max_blocks - 1)];
     } else {
-      qrow = (static_cast<int64_t>(it.s) * a.hq + it.h * g + (col < g ? col : 0)) * D;
+      qrow[0] = (static_cast<int64_t>(it.s) * a.hq + it.h * g + (col < g ? col : 0)) * D;
       const int b = min(it.b0 + w + kWaves * lane, a.max_blocks - 1);
       sl.meta = 0;
       sl.ids = a.block_tables[static_cast<int64_t>(it.s) * a.max_blocks + b];
@@ -614,7 +619,10 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     // query loads may still be in flight.
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) sl.q[kk] = *reinterpret_cast<const u32x4_t*>(qp + qrow + (kk * 4 + grp) * 8);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        sl.q[t][kk] = *reinterpret_cast<const u32x4_t*>(qp + qrow[t] + (kk * 4 + grp) * 8);
   };
   // The partition after `cur` in (sequence, KV head, partition) order, at weighted offset
   // off (= cur's offset + its weighted length); empty when off reaches the end of the run.
@@ -657,8 +665,13 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   auto steps_of = [&](const Item& it) { return max(NBUF, (it.my_n + NBUF - 1) / NBUF * NBUF); };
 
   KVRegs<D> ring[NBUF];
-  f32x4_t o[NV];
-  float m = -INFINITY, l = 0.f;
+  f32x4_t o[NT][NV];
+  float m[NT], l[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    m[t] = -INFINITY;
+    l[t] = 0.f;
+  }
   int seg_p0 = 0;     // first partition of the current (sequence, KV head) segment
   int wave_turn = 0;  // which wave writes the next segment's results
   int npend = 0;      // partial segments written (at most 2: the run's first and last)
@@ -739,45 +752,50 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
 
   // Stream one partition's blocks (looking ahead into the next one).  At the end of a
   // segment, merge the four waves and write the output or the run's partial.
-  auto run = [&](const Item cur, const int32_t cur_ids, const int32_t cur_meta, const u32x4_t (&qc)[KK],
+  auto run = [&](const Item cur, const int32_t cur_ids, const int32_t cur_meta, const u32x4_t (&qc)[NT][KK],
                  const Item nxi, const bool nx_ok, const int32_t nx_ids) {
     auto compute = [&](const KVRegs<D>& r, int i) {
       const int32_t phys = __builtin_amdgcn_readlane(cur_ids, i < 63 ? i : 63);
-      int nv;      // tokens of the block
-      int nv_col;  // tokens of the block this lane's query column sees
+      int nv;          // tokens of the block
+      int nv_col[NT];  // tokens of the block this lane's query column sees, per column tile
       if constexpr (MODE == kGroup) {
         const int meta = __builtin_amdgcn_readlane(cur_meta, i < 63 ? i : 63);
         nv = meta & 0xff;
         const int owner = meta >> 8;
         if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
-        nv_col = (owner == 0 || owner - 1 == col / g) ? nv : 0;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) nv_col[t] = (owner == 0 || owner - 1 == (t * 16 + col) / g) ? nv : 0;
       } else {
         const int bl = cur.b0 + w + kWaves * i;
         nv = cur.n - bl * kBlockTokens;
         nv = nv > kBlockTokens ? kBlockTokens : nv;
         if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
-        nv_col = nv;
+        nv_col[0] = nv;
       }
 
-      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+      float alpha[NT];
+      u32x2_t p_hi[NT], p_lo[NT];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) sacc = mfma_qk<DT>(r.k[kk], qc[kk], sacc);
+      for (int t = 0; t < NT; ++t) {
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) sacc = mfma_qk<DT>(r.k[kk], qc[t][kk], sacc);
 
-      float x[4];
+        float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (grp * 4 + e < nv_col) ? sacc[e] * a.scale_log2 : -INFINITY;
-      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float m_new = fmaxf(m, bm);
-      const float alpha = (m == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
-      float pr[4];
+        for (int e = 0; e < 4; ++e) x[e] = (grp * 4 + e < nv_col[t]) ? sacc[e] * a.scale_log2 : -INFINITY;
+        float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float m_new = fmaxf(m[t], bm);
+        alpha[t] = (m[t] == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m[t] - m_new);
+        float pr[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pr[e] = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m_new);
-      l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-      m = m_new;
-      u32x2_t p_hi, p_lo;
-      PSplit<DT>::split(pr, p_hi, p_lo);
+        for (int e = 0; e < 4; ++e) pr[e] = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m_new);
+        l[t] = l[t] * alpha[t] + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        m[t] = m_new;
+        PSplit<DT>::split(pr, p_hi[t], p_lo[t]);
+      }
       uint32_t keep[2];
 #pragma unroll
       for (int wd = 0; wd < 2; ++wd) {
@@ -787,9 +805,12 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int nn = 0; nn < NV; ++nn) {
         const u32x2_t vv = {r.v[nn][0] & keep[0], r.v[nn][1] & keep[1]};
-        o[nn] *= alpha;
-        o[nn] = mfma_pv<DT>(vv, p_hi, o[nn]);
-        o[nn] = mfma_pv<DT>(vv, p_lo, o[nn]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          o[t][nn] *= alpha[t];
+          o[t][nn] = mfma_pv<DT>(vv, p_hi[t], o[t][nn]);
+          o[t][nn] = mfma_pv<DT>(vv, p_lo[t], o[t][nn]);
+        }
       }
     };
 
@@ -822,56 +843,62 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
 
     if (nx_ok && nxi.s == cur.s && nxi.h == cur.h) return;  // the segment goes on
 
-    // ---- end of segment: merge the four waves through LDS
-    float lt = l;
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    if (grp == 0) {
-      sm_m[w][col] = m;
-      sm_l[w][col] = lt;
-    }
+    // ---- end of segment: merge the four waves through LDS, one column tile at a time
+    const bool final = seg_p0 == 0 && cur.p == cur.np - 1;  // the segment is the whole context
+    const int first = MODE == kGroup ? __builtin_amdgcn_readfirstlane(group_first(cur.s)) : cur.s;
+    const int ncol = ncols(cur.s, first);
 #pragma unroll
-    for (int nn = 0; nn < NV; ++nn)
+    for (int t = 0; t < NT; ++t) {
+      if (t > 0) __syncthreads();  // the previous tile's merge has read the LDS
+      float lt = l[t];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+      if (grp == 0) {
+        sm_m[w][col] = m[t];
+        sm_l[w][col] = lt;
+      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm_o[w][col][nn * 16 + grp * 4 + e] = o[nn][e];
-    __syncthreads();
-    // One wave, rotating per segment, merges and writes; the others go straight on.  The
-    // counter of outstanding vector-memory operations also counts stores, so a wave that
-    // stores cannot use its later loads before the stores complete.
-    if (w == (wave_turn & (kWaves - 1))) {
-      const bool final = seg_p0 == 0 && cur.p == cur.np - 1;  // the segment is the whole context
-      constexpr int kChunks = D / 4;                            // 4 consecutive dims per lane and store
-      const int first = MODE == kGroup ? __builtin_amdgcn_readfirstlane(group_first(cur.s)) : cur.s;
-      for (int c4 = lane; c4 < ncols(cur.s, first) * kChunks; c4 += kWave) {
-        const int cc = c4 / kChunks, d0 = (c4 % kChunks) * 4;
-        float mx = sm_m[0][cc];
+      for (int nn = 0; nn < NV; ++nn)
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, sm_m[ww][cc]);
-        float L = 0.f;
-        f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-        if (mx != -INFINITY) {
+        for (int e = 0; e < 4; ++e) sm_o[w][col][nn * 16 + grp * 4 + e] = o[t][nn][e];
+      __syncthreads();
+      // One wave, rotating per segment, merges and writes; the others go straight on.  The
+      // counter of outstanding vector-memory operations also counts stores, so a wave that
+      // stores cannot use its later loads before the stores complete.
+      if (w == (wave_turn & (kWaves - 1))) {
+        constexpr int kChunks = D / 4;  // 4 consecutive dims per lane and store
+        const int tcols = min(16, ncol - t * 16);
+        for (int c4 = lane; c4 < tcols * kChunks; c4 += kWave) {
+          const int cc = c4 / kChunks, d0 = (c4 % kChunks) * 4;
+          float mx = sm_m[0][cc];
 #pragma unroll
-          for (int ww = 0; ww < kWaves; ++ww) {
-            const float e = __builtin_amdgcn_exp2f(sm_m[ww][cc] - mx);
-            L += e * sm_l[ww][cc];
-            O += e * *reinterpret_cast<const f32x4_t*>(&sm_o[ww][cc][d0]);
+          for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, sm_m[ww][cc]);
+          float L = 0.f;
+          f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+          if (mx != -INFINITY) {
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) {
+              const float e = __builtin_amdgcn_exp2f(sm_m[ww][cc] - mx);
+              L += e * sm_l[ww][cc];
+              O += e * *reinterpret_cast<const f32x4_t*>(&sm_o[ww][cc][d0]);
+            }
           }
-        }
-        f32x4_t res;
+          f32x4_t res;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) res[e] = L > 0.f ? O[e] / L : 0.f;
-        const int64_t row = out_row(cur.s, cur.h, cc, first);
-        if (final) {
-          store_out4<DT>(a, row * D + d0, res);
-        } else {
-          const int64_t prow = row * a.max_parts + seg_p0;
-          // Device-scope stores: the run that merges this context may sit on another XCD.
+          for (int e = 0; e < 4; ++e) res[e] = L > 0.f ? O[e] / L : 0.f;
+          const int64_t row = out_row(cur.s, cur.h, t * 16 + cc, first);
+          if (final) {
+            store_out4<DT>(a, row * D + d0, res);
+          } else {
+            const int64_t prow = row * a.max_parts + seg_p0;
+            // Device-scope stores: the run that merges this context may sit on another XCD.
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            __hip_atomic_store(a.part_o + prow * D + d0 + e, res[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (d0 == 0) {
-            __hip_atomic_store(a.part_ml + prow * 2, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.part_ml + prow * 2 + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int e = 0; e < 4; ++e)
+              __hip_atomic_store(a.part_o + prow * D + d0 + e, res[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d0 == 0) {
+              __hip_atomic_store(a.part_ml + prow * 2, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(a.part_ml + prow * 2 + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
         }
       }
@@ -889,9 +916,12 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     ++wave_turn;
     __syncthreads();
 #pragma unroll
-    for (int nn = 0; nn < NV; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m = -INFINITY;
-    l = 0.f;
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) o[t][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m[t] = -INFINITY;
+      l[t] = 0.f;
+    }
     seg_p0 = nxi.p;
   };
 
@@ -924,7 +954,9 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   }
   if (!A.ok) return;  // the run holds no partition start
 #pragma unroll
-  for (int nn = 0; nn < NV; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn) o[t][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   seg_p0 = A.it.p;
 #pragma unroll
   for (int j = 0; j < NBUF - 1; ++j) load_tile(ring[j], __builtin_amdgcn_readlane(A.ids, j), j, A.it.my_n, A.it.h);
@@ -1181,8 +1213,8 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
     const pa_shared_prefix& sh = *p->shared;
     if (sh.num_groups < 0 || sh.num_groups > p->num_seqs) return PA_ERR_INVALID_ARG;
     if (sh.num_groups > 0 && !sh.groups) return PA_ERR_INVALID_ARG;
-    // A group's context holds at most 16 / g members' blocks (each at most ceil(limit / B)).
-    const int64_t members = std::max(1, std::min(16 / (p->num_q_heads / c.num_kv_heads), std::max(1, p->num_seqs)));
+    // A group's context holds at most 32 / g members' blocks (each at most ceil(limit / B)).
+    const int64_t members = std::max(1, std::min(32 / (p->num_q_heads / c.num_kv_heads), std::max(1, p->num_seqs)));
     const int64_t gblocks = members * ((int64_t{limit} + B - 1) / B);
     const int64_t gparts = std::max<int64_t>(1, (gblocks + out->part_blocks - 1) / out->part_blocks);
     if (gparts > 8192) return PA_ERR_UNSUPPORTED;

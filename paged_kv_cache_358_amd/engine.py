@@ -17,11 +17,14 @@ blocks once for all members.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import torch
 
-from . import (BlockAllocator, alloc_kv_cache, block_copy, kv_append, paged_attention_decode, stage_append,
-               paged_attention_workspace_bytes, shared_prefixes, stage_copy)
+from . import (PA_OK, BlockAllocator, DecodeParams, PagedAttnError, SharedPrefix, alloc_kv_cache, block_copy,
+               cache_desc, kv_append, lib, paged_attention_workspace_bytes, shared_prefixes, stage_copy,
+               torch_dtype_code)
 
 
 class _Staging:
@@ -46,13 +49,11 @@ class _Staging:
         self.h_pairs = h[self.o_pairs:self.o_groups].reshape(max_seqs, 2)
         self.h_groups = h[self.o_groups:self.o_tables].reshape(max_seqs, 3)
         self.h_tables = h[self.o_tables:].reshape(max_seqs, max_blocks)
-        self.h_slots_t = self.host[self.o_slots:self.o_pairs]  # the slots as a pinned tensor
+        self.host_ptr = self.host.data_ptr()
+        self.dev_ptr = self.dev.data_ptr()
         self.done = None  # event that ends the step that last read this buffer
         self.own_done = torch.cuda.Event()
         self.own_done.record()  # create it now: kernel launches can only mark existing events
-
-    def d_lens(self, n):
-        return self.dev[self.o_lens:self.o_lens + n]
 
     def d_slots(self, n):
         return self.dev[self.o_slots:self.o_slots + n]
@@ -60,11 +61,6 @@ class _Staging:
     def d_pairs(self, n):
         return self.dev[self.o_pairs:self.o_pairs + 2 * n].view(n, 2)
 
-    def d_groups(self, n):
-        return self.dev[self.o_groups:self.o_groups + 3 * n].view(n, 3)
-
-    def d_tables(self, n):
-        return self.dev[self.o_tables:self.o_tables + n * self.max_blocks].view(n, self.max_blocks)
 
 
 class PagedDecodeLayer:
@@ -83,7 +79,7 @@ class PagedDecodeLayer:
         # Shared leading blocks are read once per group when at least share_min_blocks are shared.
         self.share_prefixes = share_prefixes
         self.share_min_blocks = share_min_blocks
-        self.share_max_members = 16 // (num_q_heads // num_kv_heads)
+        self.share_max_members = 32 // (num_q_heads // num_kv_heads)  # two 16-column tiles of query heads
         self.device = device
         self.stream = torch.cuda.current_stream() if stream is None else stream
         # Three staging buffers: the host fills one while the stream may still read the two
@@ -97,6 +93,17 @@ class PagedDecodeLayer:
                                              torch.empty_like(probe_q, dtype=torch.float32),
                                              max_blocks_per_seq * 16, partition_size, shared=share_prefixes)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
+        # The per-step library calls go straight to the C ABI with argument blocks built here once:
+        # the layer owns the caches, staging buffers and workspace, so only the step's tensors,
+        # sizes and events change between calls.
+        self._cdesc = cache_desc(self.k_cache, self.v_cache)
+        self._k_ptr = self.k_cache.data_ptr()
+        self._v_ptr = self.v_cache.data_ptr()
+        self._stream_ptr = self.stream.cuda_stream
+        self._shared = SharedPrefix(None, 0)
+        self._params = DecodeParams(0, num_q_heads, max_blocks_per_seq, 0, partition_size, 0, self._cdesc,
+                                    self.workspace.data_ptr(), self.workspace.numel(), self._stream_ptr, None, None,
+                                    None)
 
     # ------------------------------------------------------------------ sequence management
     def add(self, seq: int):
@@ -128,6 +135,12 @@ class PagedDecodeLayer:
         travel with the attention launch, and the end event also tells the host when the
         staging buffer may be rewritten.  Returns the number of copy-on-write block copies."""
         S = len(seqs)
+        hq, hkv, D = self.num_q_heads, self.num_kv_heads, self.head_dim
+        for t, shape in ((q, (S, hq, D)), (out, (S, hq, D)), (k_new, (S, hkv, D)), (v_new, (S, hkv, D))):
+            if tuple(t.shape) != shape or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"decode_step: expected a contiguous device tensor of shape {shape}")
+        if q.dtype != self.dtype or k_new.dtype != self.dtype or v_new.dtype != self.dtype:
+            raise ValueError("decode_step: q, k_new and v_new must have the cache dtype")
         st = self._stage[self._turn]
         self._turn = (self._turn + 1) % len(self._stage)
         if st.done is not None:
@@ -143,24 +156,38 @@ class PagedDecodeLayer:
                                      groups_out=st.h_groups)
             ngroups = len(groups) if len(groups) < S else 0
         used = st.o_tables + S * self.max_blocks  # lengths, slots, pairs, sharing and the first S table rows
-        with torch.cuda.stream(self.stream):
-            if npairs:
-                # copy-on-write blocks are copied before the append writes into them
-                stage_copy(st.dev, st.host, used * 4, stream=self.stream)
-                block_copy(self.k_cache, self.v_cache, st.d_pairs(npairs), stream=self.stream)
-                kv_append(k_new, v_new, st.d_slots(S), self.k_cache, self.v_cache, stream=self.stream)
-            else:
-                # one launch: the metadata copy, and the append reading its slots from the staging buffer
-                stage_append(st.dev, st.host, used * 4, k_new, v_new, st.h_slots_t[:S], self.k_cache, self.v_cache,
-                             stream=self.stream)
-            # the staging copies (earlier in the stream) are done when the attention kernels are
-            st.done = st.own_done if timing is None else timing[1]
-            paged_attention_decode(q, self.k_cache, self.v_cache, st.d_tables(S), st.d_lens(S), scale, out,
-                                   max_context_len=max_ctx, partition_size=self.partition_size,
-                                   workspace=self.workspace, stream=self.stream,
-                                   start_event=None if timing is None else timing[0], stop_event=st.done,
-                                   shared=st.d_groups(ngroups) if ngroups else None)
+        if npairs:
+            # copy-on-write blocks are copied before the append writes into them
+            stage_copy(st.dev, st.host, used * 4, stream=self.stream)
+            block_copy(self.k_cache, self.v_cache, st.d_pairs(npairs), stream=self.stream)
+            kv_append(k_new, v_new, st.d_slots(S), self.k_cache, self.v_cache, stream=self.stream)
+        else:
+            # one launch: the metadata copy, and the append reading its slots from the staging buffer
+            rc = lib.pa_stage_append(st.dev_ptr, st.host_ptr, used * 4, k_new.data_ptr(), v_new.data_ptr(),
+                                     st.host_ptr + 4 * st.o_slots, S, self._k_ptr, self._v_ptr,
+                                     ctypes.byref(self._cdesc), self._stream_ptr)
+            if rc != PA_OK:
+                raise PagedAttnError(rc, "pa_stage_append")
+        # the staging copies (earlier in the stream) are done when the attention kernels are
+        st.done = st.own_done if timing is None else timing[1]
+        p = self._params
+        p.num_seqs = S
+        p.max_context_len = max_ctx
+        p.out_dtype = torch_dtype_code(out.dtype)
+        p.start_event = None if timing is None else timing[0].cuda_event
+        p.stop_event = st.done.cuda_event
+        if ngroups:
+            self._shared.groups = st.dev_ptr + 4 * st.o_groups
+            self._shared.num_groups = ngroups
+            p.shared = ctypes.pointer(self._shared)
+        else:
+            p.shared = None
+        rc = lib.paged_attention_decode(q.data_ptr(), self._k_ptr, self._v_ptr, st.dev_ptr + 4 * st.o_tables,
+                                        st.dev_ptr + 4 * st.o_lens, float(scale), out.data_ptr(), ctypes.byref(p))
+        if rc != PA_OK:
+            raise PagedAttnError(rc, "paged_attention_decode")
         self.last_groups = ngroups
+        self.last_group_rows = st.h_groups[:ngroups].copy() if ngroups else None
         self.last_lens = np_lens.copy()
         self.last_tables = np_tables  # view into the pinned staging buffer: valid until three steps later
         return npairs

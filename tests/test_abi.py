@@ -129,14 +129,14 @@ def test_workspace_bytes_with_shared_prefixes():
     def expect(S, hq, hkv, parts, d):
         return S * hq * parts * (d + 2) * 4 + S * hkv * 8
 
-    # a group holds min(16 / g, S) members' blocks: 4 members (g = 4) of 4 blocks = 1 partition of 512
+    # a group holds min(32 / g, S) members' blocks: 8 members (g = 4) of 4 blocks = 1 partition of 512
     p = _params(S=8, hq=8, hkv=2, d=64)
     p.shared = ctypes.pointer(sh)
     assert ws(ctypes.byref(p)) == 0
-    # 4 members of 32 blocks = 4 partitions of 512 tokens
+    # 8 members of 32 blocks = 8 partitions of 512 tokens
     p = _params(S=8, hq=8, hkv=2, d=64, maxb=32, maxctx=512)
     p.shared = ctypes.pointer(sh)
-    assert ws(ctypes.byref(p)) == expect(8, 8, 2, 4, 64)
+    assert ws(ctypes.byref(p)) == expect(8, 8, 2, 8, 64)
     # MHA: at most the batch's 3 sequences per group, 63 blocks each -> ceil(189 / 16) partitions of 256
     p = _params(S=3, hq=4, hkv=4, d=64, maxb=100, maxctx=1000, part=256)
     p.shared = ctypes.pointer(sh)

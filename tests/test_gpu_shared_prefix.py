@@ -90,7 +90,7 @@ class ForkedBatch:
         self.scale = float(np.float32(1.0 / np.sqrt(D)))
 
     def groups(self, max_members=None, min_blocks=1):
-        mm = 16 // (self.hq // self.hkv) if max_members is None else max_members
+        mm = 32 // (self.hq // self.hkv) if max_members is None else max_members
         return pa.shared_prefixes(self.tables_np, self.lens_np, mm, min_blocks)
 
     def run(self, shared=None, out_dtype=torch.float32):
@@ -124,24 +124,28 @@ def check(fb, **kw):
 
 
 def test_gqa_samples_ragged_suffixes():
-    # 32 query / 8 KV heads: four samples per group.  Prompt 2's sample 0 appends nothing to a
-    # 512-token prompt, so its whole context is the group's prefix.
+    # 32 query / 8 KV heads: up to eight samples per group.  Prompt 2's sample 0 appends nothing to a
+    # 512-token prompt, so its whole context is the group's shared blocks.
     prompts = [(1000, [200, 1, 17, 0, 64, 300, 5, 16]), (37, [3, 40, 100]), (512, [0, 15, 16, 600, 1, 2])]
     fb = ForkedBatch(1, 32, 8, 128, "bf16", prompts, lone=[700, 1])
     gr, _ = check(fb)
-    # prompt 0: samples 0..3, 4..7 (62 blocks; sample 3 appended nothing and fills 62 blocks too),
-    # then the lone sequence, prompt 1's three samples (2 shared blocks), the other lone one,
-    # prompt 2's samples in runs of four and two (32 blocks)
-    assert gr.tolist() == [[0, 4, 62], [4, 4, 62], [8, 1, 0], [9, 3, 2], [12, 1, 0], [13, 4, 32], [17, 2, 32]]
+    # prompt 0: samples 0..7 (62 blocks; sample 3 appended nothing and fills 62 blocks too), then the
+    # lone sequence, prompt 1's three samples (2 shared blocks), the other lone one, prompt 2's six
+    # samples (32 blocks)
+    assert gr.tolist() == [[0, 8, 62], [8, 1, 0], [9, 3, 2], [12, 1, 0], [13, 6, 32]]
+    # groups of at most four: one column tile per group
+    check(fb, max_members=4)
 
 
 def test_mha_sixteen_members_multi_partition_prefix_and_rest():
-    # g = 1: sixteen members per group; a 1500-token prefix spans three 512-token partitions,
-    # suffixes up to 1100 tokens span three more.
+    # g = 1: up to 32 members per group (here 20, then 16 and 4); a 1500-token prefix spans three
+    # 512-token partitions, suffixes up to 1100 tokens span three more.
     rng = np.random.default_rng(5)
     prompts = [(1500, rng.integers(0, 1100, 20).tolist()), (800, rng.integers(1, 40, 3).tolist())]
     fb = ForkedBatch(2, 8, 8, 128, "f16", prompts, lone=[2000, 33])
     gr, _ = check(fb)
+    assert gr[0].tolist() == [0, 20, 1500 // B]
+    gr, _ = check(fb, max_members=16)
     assert gr[:2].tolist() == [[0, 16, 1500 // B], [16, 4, 1500 // B]]
 
 
@@ -199,7 +203,7 @@ def test_groups_of_one_and_an_empty_context():
     o_alone, o_plain = fb.run(alone), fb.run()
     assert np.array_equal(o_alone, o_plain)
     gr = fb.groups()
-    assert gr.tolist()[:2] == [[0, 4, 3], [4, 2, 3]] and gr.tolist()[2] == [6, 1, 0]
+    assert gr.tolist() == [[0, 6, 3], [6, 1, 0]]
     o = fb.run(gr)
     errs = []
     for i, s in enumerate(fb.order):

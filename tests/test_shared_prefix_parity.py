@@ -35,9 +35,11 @@ def test_parallel_sampling_workload(step):
             a.append(s, 1)
     width = -(-(cfg.prefix_len + cfg.steps) // B)
     tables, lens = a.build_batch(seqs, width)
-    groups = same(tables, lens, 16 // cfg.group, 1)
-    # 8 samples in runs of 4 query-head groups of 4 heads: two groups per prompt over its 62 full blocks
-    assert len(groups) == 2 * cfg.num_prompts and {g[2] for g in groups} == {cfg.prefix_len // B}
+    groups = same(tables, lens, 32 // cfg.group, 1)
+    # 8 samples x 4 query heads per KV head = 32 columns: one group per prompt over its 62 full blocks
+    assert len(groups) == cfg.num_prompts and {g[2] for g in groups} == {cfg.prefix_len // B}
+    groups = same(tables, lens, 4, 1)
+    assert len(groups) == 2 * cfg.num_prompts
     same(tables, lens, 8, 16)
     same(tables, lens, 3, 63)  # no member fills 63 shared blocks: no groups
 
