@@ -381,10 +381,12 @@ class BlockAllocator:
         self.num_blocks = num_blocks
         self.block_size = block_size
 
-    def __del__(self):
+    def __del__(self, _destroy=lib.pa_alloc_destroy):
+        # _destroy is bound when the class is made: at interpreter exit the module's globals may
+        # already be gone when the last allocators are collected.
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            lib.pa_alloc_destroy(h)
+            _destroy(h)
             self._h = None
 
     def add(self, seq: int):

@@ -418,7 +418,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   __shared__ float sm_l[kWaves][16];
   __shared__ int32_t blkpre[kMaxScanSeqs + 1];  // H_kv * (weight of the sequences before s)
   __shared__ int32_t nb_s[kMaxScanSeqs];        // blocks of sequence s
-  __shared__ int32_t ctx_s[kMaxScanSeqs];       // clamped context length of s
+  __shared__ int32_t ctx_s[kMaxScanSeqs];       // clamped context length of sequence s (both modes)
   __shared__ int32_t scan[kThreads];
   __shared__ int32_t merge_flag[2];  // thread 0's arrivals completed these contexts
   static_assert(kWaves * 16 * D > kMaxSplitGrid, "run starts of one context fit in sm_o");
@@ -507,18 +507,21 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         shape_of(s, n, nb);
         blkpre[s] = base * hkv;
         nb_s[s] = nb;
-        ctx_s[s] = n;
+        if constexpr (MODE != kGroup) ctx_s[s] = n;
         base += wnb_of(nb);
       }
     }
     if (tid == kThreads - 1) blkpre[S] = scan[kThreads - 1] * hkv;
+  }
+  if constexpr (MODE == kGroup) {
+    for (int s = tid; s < a.num_seqs; s += kThreads) ctx_s[s] = clamp_ctx(a, s);
   }
   __syncthreads();
   const int W = __builtin_amdgcn_readfirstlane(blkpre[S]);
 
   // Zero-length contexts own no partition: their output is 0 (all members' rows for a group).
   for (int s = blockIdx.x; s < S; s += J) {
-    if (ctx_s[s] == 0) {
+    if (nb_s[s] == 0) {
       int f = s, mm = 1;
       if constexpr (MODE == kGroup) {
         f = group_first(s);
@@ -572,7 +575,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
       it.s = s;
       it.h = h;
       it.p = p;
-      it.n = __builtin_amdgcn_readfirstlane(ctx_s[s]);
+      it.n = MODE == kGroup ? 0 : __builtin_amdgcn_readfirstlane(ctx_s[s]);  // group: per member
       it.np = (nb + PB - 1) / PB;
       it.len = min(PB, nb - p * PB);
       it.b0 = p * PB;
@@ -595,7 +598,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
       if (b >= k) {
         int r = b - k;
         for (int j = 0; j < mm; ++j) {
-          const int nj = clamp_ctx(a, first + j);
+          const int nj = ctx_s[first + j];
           const int oj = own_blocks(nj, k);
           if (r < oj || j == mm - 1) {
             row = first + j;
