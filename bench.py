@@ -255,7 +255,7 @@ def main():
         "shared_prefix_groups": int(max(step_groups)),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(kernel, workload["workload"]),
+                     "traffic": measured_traffic(kernel, workload["workload"], workload.get("timed_steps")),
                      "kernel": kernel, "bytes_per_launch": int(np.mean(attn))},
         "copy_on_write_blocks": int(sum(step_pairs)),
     }
@@ -469,9 +469,10 @@ def main_kernel_name(dtype, head_dim, group, num_seqs):
     return "decode_split_kernel" if num_seqs <= 2048 else "decode_mfma_kernel"
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, workload, steps=None):
     """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
-    profiles/hbm_traffic.txt, if they were taken on the current kernel source; else None."""
+    profiles/hbm_traffic.txt, if they were taken on the current kernel source (and, for a record
+    that names the decode steps it measured, on the steps timed here); else None."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     src = os.path.join(root, "paged_kv_cache_358_amd", "csrc", "decode_attention.hip")
@@ -482,6 +483,8 @@ def measured_traffic(kernel, workload):
     for line in open(table):
         f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
         if f.get("kernel") == kernel and f.get("workload") == workload and f.get("source_sha256") == sha:
+            if "steps" in f and f["steps"] != steps:
+                continue
             return int(f["traffic_bytes"])
     return None
 
