@@ -144,7 +144,7 @@ def main():
                     "mean_context": float(lens0.mean()), "pool_blocks": plan.num_blocks}
     torch.cuda.synchronize()
     print(f"[bench] {workload['workload']}: workload resident on the GPU", file=sys.stderr, flush=True)
-    seqs = list(range(S))
+    seqs = np.arange(S, dtype=np.int64)
     eb = synth.ELEM_BYTES[dtype]
     out = torch.empty(S, hq, D, dtype=tdt[dtype], device=dev)
 

@@ -22,9 +22,8 @@ import ctypes
 import numpy as np
 import torch
 
-from . import (PA_OK, BlockAllocator, DecodeParams, PagedAttnError, SharedPrefix, alloc_kv_cache, block_copy,
-               cache_desc, kv_append, lib, paged_attention_workspace_bytes, shared_prefixes, stage_copy,
-               torch_dtype_code)
+from . import (PA_OK, BlockAllocator, DecodeParams, PagedAttnError, SharedPrefix, _P32, _P64, alloc_kv_cache,
+               block_copy, cache_desc, kv_append, lib, paged_attention_workspace_bytes, stage_copy, torch_dtype_code)
 
 
 class _Staging:
@@ -51,6 +50,12 @@ class _Staging:
         self.h_tables = h[self.o_tables:].reshape(max_seqs, max_blocks)
         self.host_ptr = self.host.data_ptr()
         self.dev_ptr = self.dev.data_ptr()
+        # ctypes views of the host regions for the allocator calls
+        self.c_slots = self.h_slots.ctypes.data_as(_P32)
+        self.c_pairs = self.h_pairs.ctypes.data_as(_P32)
+        self.c_groups = self.h_groups.ctypes.data_as(_P32)
+        self.c_tables = self.h_tables.ctypes.data_as(_P32)
+        self.c_lens = self.h_lens.ctypes.data_as(_P32)
         self.done = None  # event that ends the step that last read this buffer
         self.own_done = torch.cuda.Event()
         self.own_done.record()  # create it now: kernel launches can only mark existing events
@@ -87,6 +92,9 @@ class PagedDecodeLayer:
         self._stage = [_Staging(max_seqs, max_blocks_per_seq, max_seqs, device) for _ in range(3)]
         self._turn = 0
         self._ones = np.ones(max_seqs, np.int32)
+        self._c_ones = self._ones.ctypes.data_as(_P32)
+        self._npairs = ctypes.c_int32(0)
+        self._ngroups = ctypes.c_int32(0)
         probe_q = torch.empty(max_seqs, num_q_heads, head_dim, dtype=dtype, device=device)
         probe_t = torch.empty(max_seqs, max_blocks_per_seq, dtype=torch.int32, device=device)
         ws = paged_attention_workspace_bytes(probe_q, self.k_cache, self.v_cache, probe_t,
@@ -126,7 +134,8 @@ class PagedDecodeLayer:
 
     # ------------------------------------------------------------------ one decode step
     def decode_step(self, seqs, q, k_new, v_new, out, scale: float, timing=None):
-        """Each of ``seqs`` appends one token (k_new/v_new [S, H_kv, D]) and attends
+        """Each of ``seqs`` (sequence ids: a list, or an int64 array, which is used without a copy)
+        appends one token (k_new/v_new [S, H_kv, D]) and attends
         with q [S, H_q, D] over its whole context; writes out [S, H_q, D].
 
         ``timing`` = (start, end) timing-enabled torch.cuda.Events (already recorded once)
@@ -145,16 +154,30 @@ class PagedDecodeLayer:
         self._turn = (self._turn + 1) % len(self._stage)
         if st.done is not None:
             st.done.synchronize()  # previous copies out of this pinned buffer have finished
-        ids = np.asarray(seqs, dtype=np.int64)
-        slots, pairs = self.alloc.append_batch(ids, self._ones[:S], st.h_slots, st.h_pairs)
-        np_tables, np_lens = self.alloc.build_batch(ids, self.max_blocks, st.h_tables, st.h_lens)
+        if S > self.max_seqs:
+            raise ValueError("decode_step: more sequences than the layer was sized for")
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)  # no copy for a contiguous int64 array
+        c_ids = ids.ctypes.data_as(_P64)
+        # The allocator's step, straight through the C ABI into the staging buffer: one token per
+        # sequence (slots, copy-on-write pairs), the block tables and lengths, and the groups of
+        # sequences that share leading blocks.
+        rc = lib.pa_seq_append_batch(self.alloc._h, c_ids, S, self._c_ones, st.c_slots, st.c_pairs, self.max_seqs,
+                                     ctypes.byref(self._npairs))
+        if rc != PA_OK:
+            raise PagedAttnError(rc, "pa_seq_append_batch")
+        rc = lib.pa_build_batch(self.alloc._h, c_ids, S, self.max_blocks, st.c_tables, st.c_lens)
+        if rc != PA_OK:
+            raise PagedAttnError(rc, "pa_build_batch")
+        np_tables, np_lens = st.h_tables[:S], st.h_lens[:S]
         max_ctx = int(np_lens.max()) if S else 0
-        npairs = len(pairs)
+        npairs = self._npairs.value
         ngroups = 0  # groups covering the batch; 0 when no two sequences share a block
         if self.share_prefixes and S >= 2 and self.share_max_members >= 2:
-            groups = shared_prefixes(np_tables, np_lens, self.share_max_members, self.share_min_blocks,
-                                     groups_out=st.h_groups)
-            ngroups = len(groups) if len(groups) < S else 0
+            rc = lib.pa_shared_prefixes(st.c_tables, st.c_lens, S, self.max_blocks, 16, self.share_max_members,
+                                        self.share_min_blocks, st.c_groups, self.max_seqs, ctypes.byref(self._ngroups))
+            if rc != PA_OK:
+                raise PagedAttnError(rc, "pa_shared_prefixes")
+            ngroups = self._ngroups.value if self._ngroups.value < S else 0
         used = st.o_tables + S * self.max_blocks  # lengths, slots, pairs, sharing and the first S table rows
         if npairs:
             # copy-on-write blocks are copied before the append writes into them
