@@ -757,7 +757,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   // segment, merge the four waves and write the output or the run's partial.
   auto run = [&](const Item cur, const int32_t cur_ids, const int32_t cur_meta, const u32x4_t (&qc)[NT][KK],
                  const Item nxi, const bool nx_ok, const int32_t nx_ids) {
-    auto compute = [&](const KVRegs<D>& r, int i) {
+    auto compute = [&](KVRegs<D>& r, int i) {
       const int32_t phys = __builtin_amdgcn_readlane(cur_ids, i < 63 ? i : 63);
       int nv;          // tokens of the block
       int nv_col[NT];  // tokens of the block this lane's query column sees, per column tile
@@ -799,20 +799,26 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         m[t] = m_new;
         PSplit<DT>::split(pr, p_hi[t], p_lo[t]);
       }
-      uint32_t keep[2];
+      // O^T += V^T P^T.  Tokens past the context may hold anything, even NaN: a block that is
+      // not full has them selected out of its V registers (in place: the ring reloads them next);
+      // a full block (all but a context's last) needs no mask.
+      if (nv < kBlockTokens) {
+        uint32_t keep[2];
 #pragma unroll
-      for (int wd = 0; wd < 2; ++wd) {
-        const int t0 = grp * 4 + 2 * wd;
-        keep[wd] = (t0 < nv ? 0x0000ffffu : 0u) | (t0 + 1 < nv ? 0xffff0000u : 0u);
+        for (int wd = 0; wd < 2; ++wd) {
+          const int t0 = grp * 4 + 2 * wd;
+          keep[wd] = (t0 < nv ? 0x0000ffffu : 0u) | (t0 + 1 < nv ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int nn = 0; nn < NV; ++nn) r.v[nn] = u32x2_t{r.v[nn][0] & keep[0], r.v[nn][1] & keep[1]};
       }
 #pragma unroll
       for (int nn = 0; nn < NV; ++nn) {
-        const u32x2_t vv = {r.v[nn][0] & keep[0], r.v[nn][1] & keep[1]};
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           o[t][nn] *= alpha[t];
-          o[t][nn] = mfma_pv<DT>(vv, p_hi[t], o[t][nn]);
-          o[t][nn] = mfma_pv<DT>(vv, p_lo[t], o[t][nn]);
+          o[t][nn] = mfma_pv<DT>(r.v[nn], p_hi[t], o[t][nn]);
+          o[t][nn] = mfma_pv<DT>(r.v[nn], p_lo[t], o[t][nn]);
         }
       }
     };

@@ -14,18 +14,17 @@ constexpr int kLoadNT = 2;              // buffer-load cache policy: non-tempora
 // enter the product with ~16 significant bits while the accumulation stays fp32.
 template <int DT> struct PSplit;
 template <> struct PSplit<PA_BF16> {
+  // Two probabilities to a packed bf16 pair, rounded to nearest even (v_cvt_pk_bf16_f32).
+  __device__ static uint32_t pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+  }
   __device__ static void split(const float p[4], u32x2_t& hi_out, u32x2_t& lo_out) {
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t u = __float_as_uint(p[r]) & 0xffff0000u;  // truncation: exact bf16
-      const float rest = p[r] - __uint_as_float(u);               // exact in fp32
-      const uint32_t ru = __float_as_uint(rest);
-      hi[r] = u;
-      lo[r] = (ru + 0x7fffu + ((ru >> 16) & 1u)) & 0xffff0000u;    // bf16, round to nearest even
-    }
-    hi_out = u32x2_t{(hi[0] >> 16) | hi[1], (hi[2] >> 16) | hi[3]};
-    lo_out = u32x2_t{(lo[0] >> 16) | lo[1], (lo[2] >> 16) | lo[3]};
+    // hi = bf16(p); the remainder p - hi is exact in fp32; lo = bf16(remainder).
+    const uint32_t h01 = pack(p[0], p[1]), h23 = pack(p[2], p[3]);
+    const float r0 = p[0] - __uint_as_float(h01 << 16), r1 = p[1] - __uint_as_float(h01 & 0xffff0000u);
+    const float r2 = p[2] - __uint_as_float(h23 << 16), r3 = p[3] - __uint_as_float(h23 & 0xffff0000u);
+    hi_out = u32x2_t{h01, h23};
+    lo_out = u32x2_t{pack(r0, r1), pack(r2, r3)};
   }
 };
 template <> struct PSplit<PA_F16> {

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
   // A block whose 16 tokens all lie in the context and before the wave's first row is seen
   // whole by every row: no token needs masking (rows past the chunk are never written).
   const int p_first = n - c + r0;
-  auto compute = [&](const KVRegs<D>& rg, int b, int32_t phys) {
+  auto compute = [&](KVRegs<D>& rg, int b, int32_t phys) {
     int nv = n - b * kBlockTokens;  // tokens of the block in the context
     nv = nv > kBlockTokens ? kBlockTokens : nv;
     if (phys < 0 || phys >= a.num_blocks) nv = 0;
@@ -191,18 +191,23 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
     }
     u32x2_t p_hi, p_lo;
     PSplit<DT>::split(pr, p_hi, p_lo);
-    // Tokens past the context may hold anything, even NaN: select them out of V.
-    uint32_t keep[2];
+    // Tokens past the context may hold anything, even NaN: a block that is not full has them
+    // selected out of its V registers (in place: the ring reloads them next); a full block needs
+    // no mask.
+    if (nv < kBlockTokens) {
+      uint32_t keep[2];
 #pragma unroll
-    for (int wd = 0; wd < 2; ++wd) {
-      const int t0 = grp * 4 + 2 * wd;
-      keep[wd] = (t0 < nv ? 0x0000ffffu : 0u) | (t0 + 1 < nv ? 0xffff0000u : 0u);
+      for (int wd = 0; wd < 2; ++wd) {
+        const int t0 = grp * 4 + 2 * wd;
+        keep[wd] = (t0 < nv ? 0x0000ffffu : 0u) | (t0 + 1 < nv ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) rg.v[nn] = u32x2_t{rg.v[nn][0] & keep[0], rg.v[nn][1] & keep[1]};
     }
 #pragma unroll
     for (int nn = 0; nn < NV; ++nn) {
-      const u32x2_t vv = {rg.v[nn][0] & keep[0], rg.v[nn][1] & keep[1]};
-      o[nn] = mfma_pv<DT>(vv, p_hi, o[nn]);
-      o[nn] = mfma_pv<DT>(vv, p_lo, o[nn]);
+      o[nn] = mfma_pv<DT>(rg.v[nn], p_hi, o[nn]);
+      o[nn] = mfma_pv<DT>(rg.v[nn], p_lo, o[nn]);
     }
   };
 
