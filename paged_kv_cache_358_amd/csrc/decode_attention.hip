@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   __shared__ int32_t blkpre[kMaxScanSeqs + 1];  // H_kv * (weight of the sequences before s)
   __shared__ int32_t nb_s[kMaxScanSeqs];        // blocks of sequence s
   __shared__ int32_t ctx_s[kMaxScanSeqs];       // clamped context length of sequence s (both modes)
-  __shared__ int32_t scan[kThreads];
+  __shared__ int32_t scan[kWaves];  // per-wave totals of the prologue's scan
   __shared__ int32_t merge_flag[2];  // thread 0's arrivals completed these contexts
   static_assert(kWaves * 16 * D > kMaxSplitGrid, "run starts of one context fit in sm_o");
 
@@ -466,55 +466,60 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   };
   // Blocks of a member with n tokens beyond the k shared ones.
   auto own_blocks = [&](int n, int k) { return max(0, (n + kBlockTokens - 1) / kBlockTokens - k); };
-  // Context length (kPlain) and blocks to stream of context s.
-  auto shape_of = [&](int s, int& n, int& nb) {
+  // Blocks to stream of context s; a group reads its members' lengths from ctx_s.
+  auto blocks_of = [&](int s) {
     if constexpr (MODE == kGroup) {
       const int f = group_first(s), mm = group_members(s, f), k = group_shared(s);
-      nb = k;
-      for (int j = 0; j < mm; ++j) nb += own_blocks(clamp_ctx(a, f + j), k);
-      n = nb * kBlockTokens;
+      int nb = k;
+      for (int j = 0; j < mm; ++j) nb += own_blocks(ctx_s[f + j], k);
+      return nb;
     } else {
-      n = clamp_ctx(a, s);
-      nb = (n + kBlockTokens - 1) / kBlockTokens;
+      return (ctx_s[s] + kBlockTokens - 1) / kBlockTokens;
     }
   };
 
-  // ---- prefix sums of context weights over sequences (every workgroup builds its own copy)
+  // ---- prefix sums of context weights over sequences (every workgroup builds its own copy).
+  // Every sequence's clamped length goes to LDS first (one round of global loads), then each
+  // thread sizes its contexts once (nb_s) and the second pass reads only LDS.
+  for (int s = tid; s < a.num_seqs; s += kThreads) ctx_s[s] = clamp_ctx(a, s);
+  __syncthreads();
   const int per = (S + kThreads - 1) / kThreads;
   int cnt = 0;
   for (int j = 0; j < per; ++j) {
     const int s = tid * per + j;
     if (s < S) {
-      int n, nb;
-      shape_of(s, n, nb);
+      const int nb = blocks_of(s);
+      nb_s[s] = nb;
       cnt += wnb_of(nb);
     }
   }
-  scan[tid] = cnt;
+  // Inclusive scan of the per-thread counts: within each wave by shuffles, then across the
+  // four waves through their totals in LDS.
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  if (lane == kWave - 1) scan[w] = incl;
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int ww = 0; ww < kWaves; ++ww) {
+    const int t = scan[ww];
+    before += ww < w ? t : 0;
+    total += t;
   }
   {
-    int base = scan[tid] - cnt;
+    int base = before + incl - cnt;
     for (int j = 0; j < per; ++j) {
       const int s = tid * per + j;
       if (s < S) {
-        int n, nb;
-        shape_of(s, n, nb);
         blkpre[s] = base * hkv;
-        nb_s[s] = nb;
-        if constexpr (MODE != kGroup) ctx_s[s] = n;
-        base += wnb_of(nb);
+        base += wnb_of(nb_s[s]);
       }
     }
-    if (tid == kThreads - 1) blkpre[S] = scan[kThreads - 1] * hkv;
-  }
-  if constexpr (MODE == kGroup) {
-    for (int s = tid; s < a.num_seqs; s += kThreads) ctx_s[s] = clamp_ctx(a, s);
+    if (tid == kThreads - 1) blkpre[S] = total * hkv;
   }
   __syncthreads();
   const int W = __builtin_amdgcn_readfirstlane(blkpre[S]);
