@@ -187,9 +187,8 @@ def main():
     print(f"[bench] {K} timed steps: {elapsed / K * 1e3:.3f} ms/step (host enqueue done after "
           f"{(t_enq - t0) / K * 1e3:.3f} ms/step)", file=sys.stderr, flush=True)
 
-    # The events ride on the attention call's launches: start to end of the split kernel, which
-    # merges split contexts itself; with shared prefixes, start of the prefix pass to the end of
-    # the rest pass (both launches and the gap between them).
+    # The events ride on the attention call's launch: start to end of the split kernel, which
+    # merges split contexts itself (over groups of forked samples when they share blocks).
     main_ms = [a.elapsed_time(b) for a, b in events]
     block_bytes = hkv * D * 16 * eb
 
@@ -250,8 +249,7 @@ def main():
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
         "seq_tokens_per_s_per_layer": round(S / (elapsed / K), 1),
         "context_tokens_per_s_per_layer": round(float(np.mean([np.sum(l) for l in step_lens])) / (elapsed / K), 1),
-        "attention_ms": {("prefix_and_rest_passes" if any(step_groups) else "main_kernel"):
-                         round(float(np.mean(main_ms)), 4)},
+        "attention_ms": {"main_kernel": round(float(np.mean(main_ms)), 4)},
         "shared_prefix_groups": int(max(step_groups)),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
