@@ -7,10 +7,11 @@
 // page, Key points), gathered through the block table.  Chunk row i of a sequence with n
 // cached tokens, c of them in the chunk, is position p = n - c + i and sees tokens 0..p.
 //
-// One workgroup per (64-row tile of a chunk, query head, sequence), the tiles of one
-// (sequence, query head) placed on one XCD so they share its L2; each wave owns 16 chunk
-// rows, the 16 columns of the MFMA tiles, and streams the K/V blocks its last row can see
-// through a ring of register sets (the next blocks load while one computes).  The four
+// One workgroup per (128-row tile of a chunk, query head, sequence), the tiles of one
+// (sequence, query head) placed on one XCD so they share its L2; each wave owns 32 chunk
+// rows, the columns of two 16-column MFMA tiles that share every K/V block's registers, and
+// streams the K/V blocks its last row can see through a ring of register sets (the next
+// blocks load while one computes).  The four
 // waves of a workgroup read the same blocks, so the caches serve the repeats.  Per block:
 // S^T = K Q^T with v_mfma_f32_16x16x32, an online softmax per column (query row) with the
 // causal bound applied per (token, column), and O^T += V^T (P_hi + P_lo) with two
@@ -39,14 +40,16 @@ struct PrefillArgs {
   int32_t hkv;
   int32_t max_blocks;
   int32_t out_f32;
-  int32_t tiles;      // 64-row tiles per chunk (ceil(max_query_len / 64))
+  int32_t tiles;      // row tiles per chunk (ceil(max_query_len / rows per workgroup))
   int32_t per_xcd;    // workgroups per XCD
   int64_t items;      // sequences x query heads x tiles
   int64_t num_blocks;
 };
 
 constexpr int kPrefillWaves = 4;
-constexpr int kPrefillRows = kPrefillWaves * 16;  // chunk rows per workgroup
+constexpr int kPrefillTiles = 2;                                 // 16-row MFMA column tiles per wave
+constexpr int kPrefillWaveRows = 16 * kPrefillTiles;             // chunk rows per wave
+constexpr int kPrefillRows = kPrefillWaves * kPrefillWaveRows;  // chunk rows per workgroup
 constexpr int kXcdCount = 8;  // accelerator complex dies of an MI355X, one L2 each
 constexpr int kPrefillRing = 2;  // K/V register sets per wave: blocks in flight + 1 (divides 64)
 
@@ -63,10 +66,11 @@ __device__ __forceinline__ void prefill_store4(const PrefillArgs& a, int64_t idx
 }
 
 template <int DT, int D, int NBUF>
-__global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_per_eu(3))) void prefill_mfma_kernel(
+__global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     PrefillArgs a) {
   constexpr int KK = D / 32;
   constexpr int NV = D / 16;
+  constexpr int NT = kPrefillTiles;
   constexpr int kTileBytes = D * kBlockTokens * 2;
 
   // Workgroups go to the 8 XCDs round-robin (workgroup i on XCD i % 8).  The (sequence,
@@ -91,28 +95,36 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
   const int c = a.query_start[s + 1] - q0;                  // chunk rows of this sequence
   int n = a.context_lens[s];
   n = n < 0 ? 0 : (n > a.max_blocks * kBlockTokens ? a.max_blocks * kBlockTokens : n);
-  const int r0 = tile * kPrefillRows + w * 16;             // this wave's first chunk row
+  const int r0 = tile * kPrefillRows + w * kPrefillWaveRows;  // this wave's first chunk row
   if (c <= 0 || r0 >= c) return;
-  const int r_last = min(c, r0 + 16) - 1;
+  const int r_last = min(c, r0 + kPrefillWaveRows) - 1;
   const int p_last = n - c + r_last;                       // position of the wave's last row
   if (p_last < 0) return;                                  // n < c: no row of this wave has a position
 
-  // This lane's column: chunk row r = r0 + col at position p (-1 = no row / no position).
-  const int r = r0 + col;
-  const int64_t row = static_cast<int64_t>(q0) + r;
-  const bool real = r < c && n - c + r >= 0 && row >= 0 && row < a.num_tokens;
-  const int p = real ? n - c + r : -1;
+  // This lane's columns: chunk row r0 + 16 t + col of tile t at position p[t] (-1 = no row /
+  // no position).
+  int64_t row[NT];
+  bool real[NT];
+  int p[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int r = r0 + 16 * t + col;
+    row[t] = static_cast<int64_t>(q0) + r;
+    real[t] = r < c && n - c + r >= 0 && row[t] >= 0 && row[t] < a.num_tokens;
+    p[t] = real[t] ? n - c + r : -1;
+  }
 
-  // Q^T operand: lane (column col, k-group grp) holds dims (kk*4 + grp)*8 .. +8 of its row.
+  // Q^T operands: lane (column col, k-group grp) holds dims (kk*4 + grp)*8 .. +8 of its rows.
   using st = uint16_t;
   const st* qp = static_cast<const st*>(a.q);
-  u32x4_t qop[KK];
-  {
-    const int64_t qrow = ((real ? row : 0) * a.hq + j) * D;
+  u32x4_t qop[NT][KK];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int64_t qrow = ((real[t] ? row[t] : 0) * a.hq + j) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qp + qrow + (kk * 4 + grp) * 8);
-      qop[kk] = real ? x : u32x4_t{0, 0, 0, 0};
+      qop[t][kk] = real[t] ? x : u32x4_t{0, 0, 0, 0};
     }
   }
 
@@ -144,10 +156,15 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
       rg.v[nn] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, nn * 512, 0));
   };
 
-  f32x4_t o[NV];
+  f32x4_t o[NT][NV];
+  float m[NT], l[NT];
 #pragma unroll
-  for (int nn = 0; nn < NV; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn) o[t][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m[t] = -INFINITY;
+    l[t] = 0.f;
+  }
 
   // A block whose 16 tokens all lie in the context and before the wave's first row is seen
   // whole by every row: no token needs masking (rows past the chunk are never written).
@@ -157,40 +174,43 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
     nv = nv > kBlockTokens ? kBlockTokens : nv;
     if (phys < 0 || phys >= a.num_blocks) nv = 0;
     const bool whole = nv == kBlockTokens && b * kBlockTokens + kBlockTokens - 1 <= p_first;
-    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+    u32x2_t p_hi[NT], p_lo[NT];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) sacc = mfma_qk<DT>(rg.k[kk], qop[kk], sacc);
-    float x[4];
-    if (whole) {
+    for (int t = 0; t < NT; ++t) {
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = sacc[e] * a.scale_log2;
-    } else {
+      for (int kk = 0; kk < KK; ++kk) sacc = mfma_qk<DT>(rg.k[kk], qop[t][kk], sacc);
+      float x[4];
+      if (whole) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = grp * 4 + e;
-        x[e] = (t < nv && b * kBlockTokens + t <= p) ? sacc[e] * a.scale_log2 : -INFINITY;
+        for (int e = 0; e < 4; ++e) x[e] = sacc[e] * a.scale_log2;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tok = grp * 4 + e;
+          x[e] = (tok < nv && b * kBlockTokens + tok <= p[t]) ? sacc[e] * a.scale_log2 : -INFINITY;
+        }
       }
-    }
-    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m, bm);
-    // Once the rows' running maxima settle, most blocks raise none of them: then every
-    // correction factor is 1 and the rescale of O (32 accumulators a lane) is skipped for the
-    // whole wave.
-    const bool rescale = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
-    const float alpha = (m == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
-    float pr[4];
+      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float m_new = fmaxf(m[t], bm);
+      // Once the rows' running maxima settle, most blocks raise none of them: then every
+      // correction factor is 1 and the rescale of the tile's O (32 accumulators a lane) is
+      // skipped for the whole wave.
+      const bool rescale = __builtin_amdgcn_ballot_w64(m_new != m[t]) != 0;
+      const float alpha = (m[t] == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m[t] - m_new);
+      float pr[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pr[e] = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m_new);
-    l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m = m_new;
-    if (rescale) {
+      for (int e = 0; e < 4; ++e) pr[e] = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m_new);
+      l[t] = l[t] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      m[t] = m_new;
+      if (rescale) {
 #pragma unroll
-      for (int nn = 0; nn < NV; ++nn) o[nn] *= alpha;
+        for (int nn = 0; nn < NV; ++nn) o[t][nn] *= alpha;
+      }
+      PSplit<DT>::split(pr, p_hi[t], p_lo[t]);
     }
-    u32x2_t p_hi, p_lo;
-    PSplit<DT>::split(pr, p_hi, p_lo);
     // Tokens past the context may hold anything, even NaN: a block that is not full has them
     // selected out of its V registers (in place: the ring reloads them next); a full block needs
     // no mask.
@@ -204,10 +224,14 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
 #pragma unroll
       for (int nn = 0; nn < NV; ++nn) rg.v[nn] = u32x2_t{rg.v[nn][0] & keep[0], rg.v[nn][1] & keep[1]};
     }
+    // Both tiles use each V register of the block.
 #pragma unroll
     for (int nn = 0; nn < NV; ++nn) {
-      o[nn] = mfma_pv<DT>(rg.v[nn], p_hi, o[nn]);
-      o[nn] = mfma_pv<DT>(rg.v[nn], p_lo, o[nn]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        o[t][nn] = mfma_pv<DT>(rg.v[nn], p_hi[t], o[t][nn]);
+        o[t][nn] = mfma_pv<DT>(rg.v[nn], p_lo[t], o[t][nn]);
+      }
     }
   };
 
@@ -237,13 +261,17 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
     }
   }
 
-  if (!real) return;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-  const int64_t orow = (row * a.hq + j) * D;
 #pragma unroll
-  for (int nn = 0; nn < NV; ++nn) prefill_store4<DT>(a, orow + nn * 16 + grp * 4, o[nn] * inv);
+  for (int t = 0; t < NT; ++t) {
+    float lt = l[t];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (!real[t]) continue;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int64_t orow = (row[t] * a.hq + j) * D;
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn) prefill_store4<DT>(a, orow + nn * 16 + grp * 4, o[t][nn] * inv);
+  }
 }
 
 }  // namespace pa
