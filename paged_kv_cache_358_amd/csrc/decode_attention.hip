@@ -405,23 +405,23 @@ struct Item {
 // loaded one partition ahead into the other of two slots (A/B), so no loaded value is copied
 // before it is used.  Per-block arithmetic is that of decode_mfma_kernel.
 // At least two waves per SIMD: the compiler keeps the kernel within 256 VGPRs.
-template <int DT, int D, int NBUF, int MODE>
-__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(
+template <int DT, int D, int NBUF, int MODE, int WV>
+__global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(
     DecodeArgs a) {
   constexpr int KK = D / 32;
   constexpr int NV = D / 16;
   constexpr int kTileBytes = D * kBlockTokens * 2;
-  constexpr int kThreads = kWaves * kWave;
+  constexpr int kThreads = WV * kWave;
   constexpr int NT = MODE == kGroup ? 2 : 1;  // 16-column MFMA tiles of query columns
-  __shared__ __attribute__((aligned(16))) float sm_o[kWaves][16][D];
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
+  __shared__ __attribute__((aligned(16))) float sm_o[WV][16][D];
+  __shared__ float sm_m[WV][16];
+  __shared__ float sm_l[WV][16];
   __shared__ int32_t blkpre[kMaxScanSeqs + 1];  // H_kv * (weight of the sequences before s)
   __shared__ int32_t nb_s[kMaxScanSeqs];        // blocks of sequence s
   __shared__ int32_t ctx_s[kMaxScanSeqs];       // clamped context length of sequence s (both modes)
-  __shared__ int32_t scan[kWaves];  // per-wave totals of the prologue's scan
+  __shared__ int32_t scan[WV];  // per-wave totals of the prologue's scan
   __shared__ int32_t merge_flag[2];  // thread 0's arrivals completed these contexts
-  static_assert(kWaves * 16 * D > kMaxSplitGrid, "run starts of one context fit in sm_o");
+  static_assert(WV * 16 * D > kMaxSplitGrid, "run starts of one context fit in sm_o");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
   __syncthreads();
   int before = 0, total = 0;
 #pragma unroll
-  for (int ww = 0; ww < kWaves; ++ww) {
+  for (int ww = 0; ww < WV; ++ww) {
     const int t = scan[ww];
     before += ww < w ? t : 0;
     total += t;
@@ -584,7 +584,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
       it.np = (nb + PB - 1) / PB;
       it.len = min(PB, nb - p * PB);
       it.b0 = p * PB;
-      it.my_n = (it.len > w) ? (it.len - w + kWaves - 1) / kWaves : 0;
+      it.my_n = (it.len > w) ? (it.len - w + WV - 1) / WV : 0;
     }
     int64_t qrow[NT];
     if constexpr (MODE == kGroup) {
@@ -598,7 +598,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         const int c = t * 16 + col < mm * g ? t * 16 + col : 0;
         qrow[t] = (static_cast<int64_t>(first + c / g) * a.hq + it.h * g + c % g) * D;
       }
-      const int b = it.b0 + w + kWaves * lane;
+      const int b = it.b0 + w + WV * lane;
       int row = first, pos = b, owner = 0, nv = kBlockTokens;
       if (b >= k) {
         int r = b - k;
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
       sl.ids = a.block_tables[static_cast<int64_t>(row) * a.max_blocks + min(max(pos, 0), a.max_blocks - 1)];
     } else {
       qrow[0] = (static_cast<int64_t>(it.s) * a.hq + it.h * g + (col < g ? col : 0)) * D;
-      const int b = min(it.b0 + w + kWaves * lane, a.max_blocks - 1);
+      const int b = min(it.b0 + w + WV * lane, a.max_blocks - 1);
       sl.meta = 0;
       sl.ids = a.block_tables[static_cast<int64_t>(it.s) * a.max_blocks + b];
     }
@@ -774,7 +774,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int t = 0; t < NT; ++t) nv_col[t] = (owner == 0 || owner - 1 == (t * 16 + col) / g) ? nv : 0;
       } else {
-        const int bl = cur.b0 + w + kWaves * i;
+        const int bl = cur.b0 + w + WV * i;
         nv = cur.n - bl * kBlockTokens;
         nv = nv > kBlockTokens ? kBlockTokens : nv;
         if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
@@ -879,19 +879,19 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
       // One wave, rotating per segment, merges and writes; the others go straight on.  The
       // counter of outstanding vector-memory operations also counts stores, so a wave that
       // stores cannot use its later loads before the stores complete.
-      if (w == (wave_turn & (kWaves - 1))) {
+      if (w == (wave_turn & (WV - 1))) {
         constexpr int kChunks = D / 4;  // 4 consecutive dims per lane and store
         const int tcols = min(16, ncol - t * 16);
         for (int c4 = lane; c4 < tcols * kChunks; c4 += kWave) {
           const int cc = c4 / kChunks, d0 = (c4 % kChunks) * 4;
           float mx = sm_m[0][cc];
 #pragma unroll
-          for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, sm_m[ww][cc]);
+          for (int ww = 1; ww < WV; ++ww) mx = fmaxf(mx, sm_m[ww][cc]);
           float L = 0.f;
           f32x4_t O = {0.f, 0.f, 0.f, 0.f};
           if (mx != -INFINITY) {
 #pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) {
+            for (int ww = 0; ww < WV; ++ww) {
               const float e = __builtin_amdgcn_exp2f(sm_m[ww][cc] - mx);
               L += e * sm_l[ww][cc];
               O += e * *reinterpret_cast<const f32x4_t*>(&sm_o[ww][cc][d0]);
@@ -1260,7 +1260,7 @@ void launch_reduce(const DecodeArgs& args, hipStream_t st, hipEvent_t stop) {
 
 // Workgroups of a kernel that fit on the current device at once
 // (compute units x resident workgroups per CU), looked up once per (device, kernel).
-int32_t resident_workgroups(const void* kernel, int* out) {
+int32_t resident_workgroups(const void* kernel, int threads, int* out) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, int> cache;
   int dev = 0;
@@ -1275,7 +1275,7 @@ int32_t resident_workgroups(const void* kernel, int* out) {
   int cus = 0, per_cu = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_decode: CU count", e);
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWaves * kWave, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
   if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_decode: occupancy", e);
   *out = std::max(1, cus) * std::max(1, per_cu);
   cache[{dev, kernel}] = *out;
@@ -1294,18 +1294,52 @@ constexpr int kSplitRounds = 1;
 constexpr int kPartCost = 5;
 constexpr int kCtxCost = 5;
 
-// Launch the split kernel; sets args->run_grid / run_rounds.
-template <int DT, int D, int MODE>
-int32_t launch_split(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  const void* fn = reinterpret_cast<const void*>(&decode_split_kernel<DT, D, kPersistRing, MODE>);
+// Compute units of the current device, looked up once per device.
+int32_t device_cus(int* out) {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_decode: hipGetDevice", e);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_decode: CU count", e);
+    it = cache.emplace(dev, std::max(1, cus)).first;
+  }
+  *out = it->second;
+  return PA_OK;
+}
+
+// Launch the split kernel with WV wavefronts per workgroup; sets args->run_grid / run_rounds.
+template <int DT, int D, int MODE, int WV>
+int32_t launch_split_waves(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  const void* fn = reinterpret_cast<const void*>(&decode_split_kernel<DT, D, kPersistRing, MODE, WV>);
   int resident = 0;
-  const int32_t rc = resident_workgroups(fn, &resident);
+  const int32_t rc = resident_workgroups(fn, WV * kWave, &resident);
   if (rc != PA_OK) return rc;
   args->run_rounds = kSplitRounds;
   args->run_grid = std::min(kSplitRounds * resident, kMaxSplitGrid / kSplitRounds * kSplitRounds);
-  hipExtLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing, MODE>), dim3(static_cast<uint32_t>(args->run_grid)),
-                        dim3(kWaves * kWave), 0, st, start, stop, 0, *args);
+  hipExtLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing, MODE, WV>), dim3(static_cast<uint32_t>(args->run_grid)),
+                        dim3(WV * kWave), 0, st, start, stop, 0, *args);
   return PA_OK;
+}
+
+// Workgroups of 4 wavefronts, two per CU, by default.  With fewer (sequence or group, KV head)
+// contexts than CUs, every context is cut into runs for several workgroups anyway; one workgroup
+// of 8 wavefronts per CU then halves the runs, partials and merges of each context.  Measured on
+// MI355X: 4 sequences of 131072 tokens, 8 KV heads: 356 -> 339 us; with 512 to 2048 contexts the
+// 8-wavefront form was 2-21% slower.
+template <int DT, int D, int MODE>
+int32_t launch_split(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  int cus = 0;
+  const int32_t rc = device_cus(&cus);
+  if (rc != PA_OK) return rc;
+  const int64_t contexts = int64_t{MODE == kGroup ? args->num_groups : args->num_seqs} * args->hkv;
+  if (contexts < cus) return launch_split_waves<DT, D, MODE, 8>(args, st, start, stop);
+  return launch_split_waves<DT, D, MODE, 4>(args, st, start, stop);
 }
 
 // One launch: over groups when the batch comes with shared prefixes, else over sequences.

@@ -25,13 +25,13 @@ from paged_setup import raw_view, storage_raw, to_torch
 pytestmark = pytest.mark.gpu
 
 
-def run_sampling(cfg: synth.SamplingConfig, check_steps, check_seqs):
+def run_sampling(cfg: synth.SamplingConfig, check_steps, check_seqs, share_prefixes=True):
     B = cfg.block_size
     max_blocks = -(-(cfg.prefix_len + cfg.steps) // B)
     order = cfg.free_order()
     layer = PagedDecodeLayer(cfg.pool_blocks(), cfg.num_kv_heads, cfg.head_dim, cfg.num_q_heads, torch.bfloat16,
                              max_seqs=cfg.num_seqs, max_blocks_per_seq=max_blocks, free_order=order,
-                             partition_size=cfg.partition_size)
+                             partition_size=cfg.partition_size, share_prefixes=share_prefixes)
     layer.k_cache.fill_(float("nan"))
     layer.v_cache.fill_(float("nan"))
     model = BlockAllocatorModel(cfg.pool_blocks(), B, order.tolist())
@@ -57,6 +57,8 @@ def run_sampling(cfg: synth.SamplingConfig, check_steps, check_seqs):
         kn, vn = cfg.step_kv(step)
         npairs = layer.decode_step(seqs, to_torch(q, "bf16"), to_torch(kn, "bf16"), to_torch(vn, "bf16"), out,
                                    cfg.softmax_scale)
+        # with sharing on, every prompt's samples form one group over its full prompt blocks
+        assert layer.last_groups == (cfg.num_prompts if share_prefixes else 0)
         model_pairs = []
         for s in seqs:
             model_pairs += model.append(s, 1)[1]
@@ -90,9 +92,10 @@ def run_sampling(cfg: synth.SamplingConfig, check_steps, check_seqs):
     return layer
 
 
-def test_cow_sampling_small_all_sequences():
+@pytest.mark.parametrize("share_prefixes", [True, False])
+def test_cow_sampling_small_all_sequences(share_prefixes):
     cfg = dataclasses.replace(synth.C4, num_prompts=3, steps=24, slack_blocks=16)
-    run_sampling(cfg, {1, 2, 17, 24}, list(range(cfg.num_seqs)))
+    run_sampling(cfg, {1, 2, 17, 24}, list(range(cfg.num_seqs)), share_prefixes)
 
 
 def test_cow_sampling_full_sampled():
