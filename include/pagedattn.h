@@ -148,7 +148,8 @@ size_t paged_attention_workspace_bytes(const pa_decode_params* p);
  *     out[s, j, :] = sum_t softmax_t(scale * q[s, j, :] . K_s[t, h, :]) * V_s[t, h, :],   t < n
  * where K_s[t] / V_s[t] are read from block block_tables[s * max_blocks_per_seq + t / B], slot t % B.
  * A sequence with n == 0 gets out = 0.  Contexts longer than one partition are split into partitions whose
- * softmax partials (max, sum, normalised output) go to the workspace and are merged by a second kernel.
+ * softmax partials (max, sum, normalised output) go to the workspace; the bf16/fp16 path merges them in the
+ * same kernel launch, the other paths with a second kernel.
  *
  *   q             device [num_seqs][H_q][head_dim], cache dtype
  *   k_cache/v_cache  device, layout above

@@ -8,13 +8,14 @@
 // Details, "Core Architecture").  Softmax is taken online, block by block, as in the
 // FlashAttention kernels the ml-canon page's "Connections" section says vLLM uses.
 //
-// Work decomposition.  A context is split into partitions of P tokens.  One
-// workgroup (4 wavefronts) handles one (partition, KV head, sequence); its waves
-// take the partition's blocks round-robin.  Each wave keeps a running max, sum and
-// unnormalised output per query head; the four waves merge through LDS.  A sequence
-// with one partition writes its output directly; otherwise each partition writes
-// (max, sum, normalised output) to the workspace and a second kernel merges them
-// with the log-sum-exp rule.
+// Work decomposition.  A context is split into partitions of P tokens; a workgroup's
+// waves take a partition's blocks round-robin.  Each wave keeps a running max, sum and
+// unnormalised output per query head; the waves merge through LDS.  The main (split)
+// kernel runs one workgroup per resident slot over a balanced run of partitions and
+// merges contexts that span several runs in the same launch (the last run to finish
+// merges them with the log-sum-exp rule).  The per-partition kernels for the other
+// shapes write each partition's (max, sum, normalised output) to the workspace and a
+// second kernel merges them.
 //
 // bf16/fp16 fast path (MFMA).  All g = H_q / H_kv query heads of a KV head share
 // each K/V block, so a block is one dense contraction, done on the matrix cores with
@@ -692,7 +693,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   // loads the runs' partials 16 at a time.  Partials are read with device-scope loads: runs on
   // other XCDs wrote them through to memory.  Called by every thread, after the stream.
   int32_t* const run_p0 = reinterpret_cast<int32_t*>(&sm_o[0][0][0]);
-  // Query columns of context s (first = its group's first sequence in the prefix pass), and the
+  // Query columns of context s (first = its group's first sequence in group mode), and the
   // q / out row of column cc with KV head h.
   auto ncols = [&](int s, int first) {
     if constexpr (MODE == kGroup) return group_members(s, first) * g;

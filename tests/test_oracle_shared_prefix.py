@@ -11,7 +11,7 @@ What fixes it, beyond restating the rule:
   forked into M samples, group into P * ceil(M / max_members) groups covering
   floor(L / B) blocks;
 * the invariants every grouping must satisfy, on random fork trees;
-* the attention identity the prefix pass relies on: attention over a prefix and
+* the attention identity that reading shared blocks once relies on: attention over a prefix and
   over the rest, merged by the log-sum-exp rule, equals attention over the
   whole context (fp64, against the oracle's plain attention).
 """
