@@ -467,20 +467,29 @@ def main_kernel_name(dtype, head_dim, group, num_seqs):
     return "decode_split_kernel" if num_seqs <= 2048 else "decode_mfma_kernel"
 
 
+def kernel_code_hash(path):
+    """sha256[:16] of a source file's code: comments and blank lines removed, so that edits to
+    comments alone leave measurements taken on the file valid."""
+    import hashlib
+    import re
+    text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+    lines = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
+    return hashlib.sha256("\n".join(line for line in lines if line.strip()).encode()).hexdigest()[:16]
+
+
 def measured_traffic(kernel, workload, steps=None):
     """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
-    profiles/hbm_traffic.txt, if they were taken on the current kernel source (and, for a record
+    profiles/hbm_traffic.txt, if they were taken on the current kernel code (and, for a record
     that names the decode steps it measured, on the steps timed here); else None."""
-    import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     src = os.path.join(root, "paged_kv_cache_358_amd", "csrc", "decode_attention.hip")
     table = os.path.join(root, "profiles", "hbm_traffic.txt")
     if not os.path.exists(table):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    sha = kernel_code_hash(src)
     for line in open(table):
         f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
-        if f.get("kernel") == kernel and f.get("workload") == workload and f.get("source_sha256") == sha:
+        if f.get("kernel") == kernel and f.get("workload") == workload and f.get("code_sha256") == sha:
             if "steps" in f and f["steps"] != steps:
                 continue
             return int(f["traffic_bytes"])
