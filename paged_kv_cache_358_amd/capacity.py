@@ -13,7 +13,9 @@ The pages' comparison:
   throughput (ml-canon page, "where the x2-4 comes from").
 * Beam search and shared system prompts: beams and requests with a common prefix hold its
   blocks once ("Stop Wasting GPU Memory" page, "Beam Search Optimization"; ml-canon page,
-  prefix sharing).
+  prefix sharing).  Beside the blocks held, the study counts the K/V tokens one decode step
+  reads: per sequence, or with the batch cut into groups that read their shared blocks once
+  (``shared_prefixes``, as the decode kernel does).
 
 The paged side is counted by running the library's own block allocator over the lengths
 (``BlockAllocator``), so forks and copy-on-write are the real ones; the contiguous side is
@@ -28,7 +30,7 @@ import json
 
 import numpy as np
 
-from . import BlockAllocator
+from . import BlockAllocator, shared_prefixes
 
 
 def paged_footprint(lens, block_size: int = 16) -> dict:
@@ -98,6 +100,7 @@ def beam_search_footprint(width: int, prompt_len: int, steps: int, block_size: i
     beams = [next_id] * width
     live = {next_id}
     shared, unshared = [], []
+    reads, reads_grouped = [], []
     weights = 1.0 / np.arange(1, width + 1) ** skew
     weights /= weights.sum()
     for t in range(steps):
@@ -114,10 +117,18 @@ def beam_search_footprint(width: int, prompt_len: int, steps: int, block_size: i
         alloc.append_batch(children, np.ones(len(children), np.int32))
         shared.append(alloc.num_blocks - alloc.num_free())
         unshared.append(width * -(-(prompt_len + t + 1) // block_size))
+        # the decode batch with children of one parent next to each other
+        batch = [children[i] for i in np.argsort(parents, kind="stable")]
+        total, grouped = step_read_tokens(alloc, batch, block_size)
+        reads.append(total)
+        reads_grouped.append(grouped)
     return {"width": width, "prompt_len": prompt_len, "steps": steps, "skew": skew,
             "peak_blocks": int(max(shared)), "peak_blocks_without_sharing": int(max(unshared)),
             "mean_saved_frac": round(1.0 - float(np.mean(shared)) / float(np.mean(unshared)), 4),
-            "peak_saved_frac": round(1.0 - max(shared) / max(unshared), 4)}
+            "peak_saved_frac": round(1.0 - max(shared) / max(unshared), 4),
+            "mean_read_tokens": round(float(np.mean(reads)), 1),
+            "mean_read_tokens_grouped": round(float(np.mean(reads_grouped)), 1),
+            "read_saved_frac": round(1.0 - float(np.sum(reads_grouped)) / float(np.sum(reads)), 4)}
 
 
 class PrefixIndex:
@@ -142,6 +153,20 @@ class PrefixIndex:
         return self._holders[key]
 
 
+def step_read_tokens(alloc, batch, block_size: int = 16, max_members: int = 8) -> tuple[int, int]:
+    """K/V tokens one decode step over `batch` reads: every sequence its whole context, and with
+    the batch cut into groups of consecutive sequences that read their shared full blocks once
+    (at most `max_members` per group: 32 query columns over the query heads of one KV head)."""
+    lens = [alloc.seq_len(s) for s in batch]
+    width = max(1, max(-(-n // block_size) for n in lens))
+    tables, lens = alloc.build_batch(batch, width)
+    groups = shared_prefixes(np.asarray(tables, np.int32), np.asarray(lens, np.int32), max_members,
+                             block_size=block_size)
+    total = int(np.sum(lens))
+    repeated = sum((m - 1) * block_size * k for _, m, k in groups.tolist())
+    return total, total - repeated
+
+
 def shared_prompt_footprint(prompt_len: int, suffix_lens, block_size: int = 16, seed: int = 0,
                             alloc_factory=None) -> dict:
     """Requests that share one system prompt of `prompt_len` tokens, each followed by its own
@@ -157,8 +182,10 @@ def shared_prompt_footprint(prompt_len: int, suffix_lens, block_size: int = 16, 
             alloc.append(r, s)
     shared = alloc.num_blocks - alloc.num_free()
     unshared = sum(-(-(prompt_len + s) // block_size) for s in suffix_lens)
+    total, grouped = step_read_tokens(alloc, list(range(len(suffix_lens))), block_size)
     return {"requests": len(suffix_lens), "prompt_len": prompt_len, "blocks": shared,
-            "blocks_without_sharing": unshared, "saved_frac": round(1.0 - shared / unshared, 4)}
+            "blocks_without_sharing": unshared, "saved_frac": round(1.0 - shared / unshared, 4),
+            "read_tokens": total, "read_tokens_grouped": grouped, "read_saved_frac": round(1.0 - grouped / total, 4)}
 
 
 def max_batch(budget_slots: int, lens, block_size: int, reserve: int) -> dict:

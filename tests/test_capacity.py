@@ -79,6 +79,12 @@ class _ModelAllocator:
     def num_free(self):
         return self.m.num_free()
 
+    def seq_len(self, seq):
+        return self.m.seq_len(seq)
+
+    def build_batch(self, seqs, max_blocks):
+        return self.m.build_batch(seqs, max_blocks)
+
 
 def test_beam_of_width_one_shares_nothing():
     out = capacity.beam_search_footprint(1, 100, 60)
@@ -133,5 +139,54 @@ def test_study_reports_the_sharing_rows():
     beams = [r for r in rows if r["workload"] == "beam_search"]
     assert {(r["width"], r["skew"]) for r in beams} == {(4, 0.0), (4, 1.5), (8, 0.0), (8, 1.5)}
     assert all(r["mean_saved_frac"] > 0.5 for r in beams)
+    assert all(r["read_saved_frac"] > 0.5 for r in beams)
     (sp,) = [r for r in rows if r["workload"] == "shared_system_prompt"]
     assert sp["saved_frac"] > 0.8
+    assert sp["read_saved_frac"] > 0.7
+
+
+def _oracle_step_reads(alloc, batch, max_members=8, B=16):
+    """The same count through the oracle's grouping: each group's members beyond the first skip
+    its k shared blocks."""
+    from oracle.shared_prefix import shared_prefix_cover
+    width = max(1, max(-(-alloc.seq_len(b) // B) for b in batch))
+    tables, lens = alloc.build_batch(batch, width)
+    runs = shared_prefix_cover(tables, lens, B, max_members, 1)
+    total = sum(lens)
+    return total, total - sum((m - 1) * B * k for _, m, k in runs)
+
+
+@pytest.mark.parametrize("prompt,suffixes", [(2000, [0, 1, 16, 17, 500, 3, 3, 3, 9, 1000]), (64, [16, 5, 0]),
+                                             (7, [1, 9, 30])])
+def test_shared_prompt_reads_closed_form(prompt, suffixes):
+    # every request fills the prompt's floor(P/B) blocks; requests are grouped in runs of 8 in
+    # batch order, and each member beyond a run's first skips those blocks
+    B = 16
+    out = capacity.shared_prompt_footprint(prompt, suffixes)
+    total = sum(prompt + s for s in suffixes)
+    k = prompt // B
+    runs = [min(8, len(suffixes) - i) for i in range(0, len(suffixes), 8)] if k else []
+    assert out["read_tokens"] == total
+    assert out["read_tokens_grouped"] == total - sum((m - 1) * B * k for m in runs)
+
+
+def test_beam_step_reads_match_the_oracle_grouping():
+    rng = np.random.default_rng(9)
+    lib = capacity.BlockAllocator(400, 16)
+    model = _ModelAllocator(400, 16)
+    for a in (lib, model):
+        a.add(0)
+        a.append(0, 70)
+    beams, nxt = [0], 1
+    for step in range(30):
+        if step % 4 == 0 and len(beams) < 10:
+            parent = beams[int(rng.integers(len(beams)))]
+            for a in (lib, model):
+                a.fork(parent, nxt)
+            beams.insert(beams.index(parent) + 1, nxt)
+            nxt += 1
+        for a in (lib, model):
+            a.append_batch(beams, np.ones(len(beams), np.int32))
+        got = capacity.step_read_tokens(lib, beams)
+        assert got == _oracle_step_reads(model, beams)
+        assert got[1] <= got[0]
