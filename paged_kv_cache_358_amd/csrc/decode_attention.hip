@@ -238,9 +238,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
     float x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = (grp * 4 + e < nv) ? sacc[e] * a.scale_log2 : -INFINITY;
-    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float bm = rows4_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
     const float m_new = fmaxf(m, bm);
     const float alpha = (m == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
     float pr[4];
@@ -280,8 +278,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
   }
 
   // Per-wave totals: the sum over the four k-groups of this head column.
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = rows4_sum(l);
   if (grp == 0) {
     sm_m[w][col] = m;
     sm_l[w][col] = l;
@@ -793,9 +790,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = (grp * 4 + e < nv_col[t]) ? sacc[e] * a.scale_log2 : -INFINITY;
-        float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float bm = rows4_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
         const float m_new = fmaxf(m[t], bm);
         alpha[t] = (m[t] == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m[t] - m_new);
         float pr[4];
@@ -865,9 +860,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (t > 0) __syncthreads();  // the previous tile's merge has read the LDS
-      float lt = l[t];
-      lt += __shfl_xor(lt, 16);
-      lt += __shfl_xor(lt, 32);
+      const float lt = rows4_sum(l[t]);
       if (grp == 0) {
         sm_m[w][col] = m[t];
         sm_l[w][col] = lt;

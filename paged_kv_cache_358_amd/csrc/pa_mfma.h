@@ -66,6 +66,23 @@ __device__ __forceinline__ f32x4_t mfma_pv(const u32x2_t& a, const u32x2_t& b, c
   }
 }
 
+// Max and sum over the four 16-lane rows of a wavefront (lanes l, l^16, l^32, l^48: one MFMA
+// output column's four k-groups), with the gfx950 permlane swaps, which stay in the vector ALU,
+// instead of shuffles routed through LDS.  Swapping a register with itself leaves x at lane l and
+// x at lane l^16 (or l^32) in the two results, in some order; max and + do not depend on it.
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D>
 struct KVRegs {
   u32x4_t k[D / 32];  // K operand, one 16-byte chunk per QK MFMA

@@ -51,7 +51,7 @@ constexpr int kPrefillTiles = 2;                                 // 16-row MFMA 
 constexpr int kPrefillWaveRows = 16 * kPrefillTiles;             // chunk rows per wave
 constexpr int kPrefillRows = kPrefillWaves * kPrefillWaveRows;  // chunk rows per workgroup
 constexpr int kXcdCount = 8;  // accelerator complex dies of an MI355X, one L2 each
-constexpr int kPrefillRing = 2;  // K/V register sets per wave: blocks in flight + 1 (divides 64)
+constexpr int kPrefillRing = 3;  // K/V register sets per wave: block i computing, i+1 and i+2 loading
 
 template <int DT>
 __device__ __forceinline__ void prefill_store4(const PrefillArgs& a, int64_t idx, const f32x4_t& v) {
@@ -169,7 +169,17 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
   // A block whose 16 tokens all lie in the context and before the wave's first row is seen
   // whole by every row: no token needs masking (rows past the chunk are never written).
   const int p_first = n - c + r0;
-  auto compute = [&](KVRegs<D>& rg, int b, int32_t phys) {
+  // S^T tiles of a block: the matrix-core half of a block's work, issued one block ahead.
+  auto qk = [&](const KVRegs<D>& rg, f32x4_t (&s)[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) s[t] = mfma_qk<DT>(rg.k[kk], qop[t][kk], s[t]);
+    }
+  };
+  // The rest of block b's work: online softmax over its scores and O^T += V^T P^T.
+  auto finish = [&](KVRegs<D>& rg, int b, int32_t phys, const f32x4_t (&s)[NT]) {
     int nv = n - b * kBlockTokens;  // tokens of the block in the context
     nv = nv > kBlockTokens ? kBlockTokens : nv;
     if (phys < 0 || phys >= a.num_blocks) nv = 0;
@@ -177,9 +187,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
     u32x2_t p_hi[NT], p_lo[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) sacc = mfma_qk<DT>(rg.k[kk], qop[t][kk], sacc);
+      const f32x4_t sacc = s[t];
       float x[4];
       if (whole) {
 #pragma unroll
@@ -191,9 +199,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
           x[e] = (tok < nv && b * kBlockTokens + tok <= p[t]) ? sacc[e] * a.scale_log2 : -INFINITY;
         }
       }
-      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float bm = rows4_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
       const float m_new = fmaxf(m[t], bm);
       // Once the rows' running maxima settle, most blocks raise none of them: then every
       // correction factor is 1 and the rescale of the tile's O (32 accumulators a lane) is
@@ -236,8 +242,10 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
   };
 
   // A ring of NBUF register sets: blocks b+1 .. b+NBUF-1 are loading while block b computes.
-  // Block ids come 64 to a register; the lookahead reaches at most NBUF-1 < 64 blocks into
-  // the next register, which is loaded 64 blocks ahead of its first use.
+  // The scores of block b+1 are computed before block b's softmax and PV, so the matrix cores
+  // work on the next block while the vector units take this one's softmax.  Block ids come 64
+  // to a register; ids_next holds the 64 after, loaded 64 blocks ahead of its first use, and
+  // the pair advances once the blocks reach past the first register.
   int base = 0;
   int32_t ids = load_ids(0);
   int32_t ids_next = load_ids(64);
@@ -247,25 +255,32 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
   KVRegs<D> ring[NBUF];
 #pragma unroll
   for (int jj = 0; jj < NBUF - 1; ++jj) load(ring[jj], phys_at(jj), jj < nblk);
+  f32x4_t s_next[NT];
+  qk(ring[0], s_next);
   for (int b = 0; b < nblk; b += NBUF) {
-#pragma unroll
-    for (int jj = 0; jj < NBUF; ++jj) {
-      const int la = b + jj + NBUF - 1;
-      load(ring[(jj + NBUF - 1) % NBUF], phys_at(la), la < nblk);
-      if (b + jj < nblk) compute(ring[jj], b + jj, phys_at(b + jj));
-    }
-    if (((b + NBUF) & 63) == 0) {
+    if (b - base >= 64) {
       base += 64;
       ids = ids_next;
       ids_next = load_ids(base + 64);
+    }
+#pragma unroll
+    for (int jj = 0; jj < NBUF; ++jj) {
+      const int i = b + jj;
+      const int la = i + NBUF - 1;
+      load(ring[(jj + NBUF - 1) % NBUF], phys_at(la), la < nblk);
+      if (i < nblk) {
+        f32x4_t s_cur[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) s_cur[t] = s_next[t];
+        if (i + 1 < nblk) qk(ring[(jj + 1) % NBUF], s_next);
+        finish(ring[jj], i, phys_at(i), s_cur);
+      }
     }
   }
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    float lt = l[t];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = rows4_sum(l[t]);
     if (!real[t]) continue;
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const int64_t orow = (row[t] * a.hq + j) * D;
