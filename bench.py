@@ -11,7 +11,8 @@ before the timed region starts.
 Default workload: bf16 MHA decode, 64 sequences, context lengths U[128, 2048],
 32 query / 32 KV heads, head_dim 128, 16-token blocks in a shuffled pool.
 The first timed step attends over exactly those lengths; each later step one
-token more.
+token more.  --block-size 32 (64, ...) lays the same sequences out in a pool of
+larger blocks (MHA, GQA and long-context workloads).
 
 Prints one JSON line: value = algorithmic HBM bytes of the whole step / step
 time (GB/s), plus seq-tokens/s per layer, the main attention kernel's roofline
@@ -42,6 +43,8 @@ def parse():
     ap.add_argument("--chunk", type=int, default=512, help="prefill: chunk rows per sequence (at most its length)")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-context partition in tokens (0 = the workload's own)")
+    ap.add_argument("--block-size", type=int, default=16,
+                    help="decode c2/c3/c5: tokens per cache block (16; 32, 64, ... stream as 16-token tiles)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -59,6 +62,9 @@ def main():
     if args.workload == "prefill":
         run_prefill(args)
         return
+    BS = args.block_size
+    if BS != 16 and args.workload == "c4":
+        sys.exit("bench.py: the sampling workload runs on 16-token blocks only")
 
     import numpy as np
     import torch
@@ -115,6 +121,8 @@ def main():
         lens0 = None
     else:
         cfg = synth.CONFIGS[{"c2": "c2_mha_bf16", "c3": "c3_gqa_bf16", "c5": "c5_long_bf16"}[args.workload]]
+        if BS != 16:  # the same sequences in a pool of larger blocks
+            cfg = synth.scaled(cfg, name_suffix=f"_b{BS}", block_size=BS)
         part = args.partition_size or cfg.partition_size
         if W + K > cfg.pool_slack_tokens:
             sys.exit(f"{cfg.name}: warmup + steps must be <= {cfg.pool_slack_tokens}")
@@ -122,12 +130,12 @@ def main():
         lens0 = synth.context_lens(cfg)                # context at the first timed step
         plan = synth.pool_plan(cfg, lens0)
         prefill = np.maximum(lens0 - W - 1, 0)
-        max_blocks = int(synth.blocks_for(lens0.max() + K))
+        max_blocks = int(synth.blocks_for(lens0.max() + K, BS))
         layer = PagedDecodeLayer(plan.num_blocks, hkv, D, hq, tdt[dtype], S, max_blocks,
-                                 free_order=plan.free_order, partition_size=part, device=dev)
+                                 free_order=plan.free_order, partition_size=part, device=dev, block_size=BS)
         if plan.preoccupy_blocks:
             layer.alloc.add(FOREIGN)
-            layer.alloc.append(FOREIGN, plan.preoccupy_blocks * 16)
+            layer.alloc.append(FOREIGN, plan.preoccupy_blocks * BS)
         for s in range(S):
             layer.add(s)
             if prefill[s]:
@@ -140,7 +148,7 @@ def main():
         scale = cfg.softmax_scale
         kvbpt = cfg.kv_bytes_per_token()
         workload = {"workload": cfg.name, "num_seqs": S, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D,
-                    "block_size": 16, "partition_size": part, "context_lens": cfg.lens,
+                    "block_size": BS, "partition_size": part, "context_lens": cfg.lens,
                     "mean_context": float(lens0.mean()), "pool_blocks": plan.num_blocks}
     torch.cuda.synchronize()
     print(f"[bench] {workload['workload']}: workload resident on the GPU", file=sys.stderr, flush=True)
@@ -190,30 +198,30 @@ def main():
     # The events ride on the attention call's launch: start to end of the split kernel, which
     # merges split contexts itself (over groups of forked samples when they share blocks).
     main_ms = [a.elapsed_time(b) for a, b in events]
-    block_bytes = hkv * D * 16 * eb
+    block_bytes = hkv * D * BS * eb
 
     # Algorithmic bytes of one attention launch: K/V of every cached token (2 * H_kv * D * elem per
     # token), q and out, the block-table entries and context lengths read.  With shared blocks the
     # HBM-bound quantity counts each physical block once, at the most tokens any sequence uses of it.
     def attn_bytes(lens, tables=None):
         lens = np.asarray(lens, dtype=np.int64)
-        fixed = S * hq * D * eb * 2 + int(synth.blocks_for(lens).sum()) * 4 + S * 4
+        fixed = S * hq * D * eb * 2 + int(synth.blocks_for(lens, BS).sum()) * 4 + S * 4
         if tables is None:
             return int(lens.sum() * kvbpt) + fixed
         used = {}
         for s_, n in enumerate(lens.tolist()):
-            for b in range(-(-n // 16)):
+            for b in range(-(-n // BS)):
                 phys = int(tables[s_, b])
-                used[phys] = max(used.get(phys, 0), min(16, n - 16 * b))
+                used[phys] = max(used.get(phys, 0), min(BS, n - BS * b))
         return int(sum(used.values()) * kvbpt) + fixed
 
     # With groups, a group's k shared (full) blocks are one set of physical blocks and every other block
-    # is held by one sequence: each member beyond the first re-reads 16 k tokens.  The first timed step
+    # is held by one sequence: each member beyond the first re-reads B k tokens.  The first timed step
     # checks that against the count over its physical blocks.
     def group_bytes(lens, rows):
         if rows is None:
             return attn_bytes(lens)
-        dup = int(sum((m - 1) * 16 * k for _, m, k in rows.tolist()))
+        dup = int(sum((m - 1) * BS * k for _, m, k in rows.tolist()))
         return attn_bytes(lens) - dup * kvbpt
 
     logical = [attn_bytes(l) for l in step_lens]
@@ -230,7 +238,7 @@ def main():
     value = total_bytes / elapsed / 1e9
     mean_main_s = float(np.mean(main_ms)) / 1e3
     achieved = float(np.mean(attn)) / mean_main_s / 1e9
-    kernel = main_kernel_name(dtype, D, hq // hkv, S)
+    kernel = main_kernel_name(dtype, D, hq // hkv, S, BS)
 
     result = {
         "metric": METRIC,
@@ -303,9 +311,10 @@ def cache_ops_probe(layer, step_input, tables, block_bytes, reps=20, max_pairs=4
                              "frac": round(moved / t / 1e9 / PEAK_HBM_GBS, 4)}
     _, k_new, v_new = step_input
     T = k_new.shape[0]
-    if T > 0 and len(free) * 16 >= T:
-        blocks = np.asarray(free[:(T + 15) // 16], dtype=np.int64)
-        slots = torch.tensor((np.repeat(blocks, 16)[:T] * 16 + np.tile(np.arange(16), len(blocks))[:T]).astype(np.int32),
+    B = layer.block_size
+    if T > 0 and len(free) * B >= T:
+        blocks = np.asarray(free[:(T + B - 1) // B], dtype=np.int64)
+        slots = torch.tensor((np.repeat(blocks, B)[:T] * B + np.tile(np.arange(B), len(blocks))[:T]).astype(np.int32),
                              device="cuda")
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(layer.stream):
@@ -337,7 +346,7 @@ def decode_probes(layer, q, out, scale, tables, lens, part, nbytes, reps=20, flu
 
     S = len(lens)
     lens = np.asarray(lens, dtype=np.int64)
-    nb = -(-lens // 16)
+    nb = -(-lens // layer.block_size)
     num_blocks = layer.k_cache.shape[0]
     if int(nb.sum()) > num_blocks:
         return None
@@ -460,11 +469,14 @@ def run_prefill(args):
     }), flush=True)
 
 
-def main_kernel_name(dtype, head_dim, group, num_seqs):
+def main_kernel_name(dtype, head_dim, group, num_seqs, block_size=16):
     """The library's dominant kernel for this shape (its dispatch rule, restated)."""
-    if dtype == "f32" or head_dim not in (64, 128) or group > 16:
+    tiles = block_size in [16 << j for j in range(7)]
+    if dtype == "f32" or head_dim not in (64, 128) or group > 16 or not tiles:
         return "decode_generic_kernel"
-    return "decode_split_kernel" if num_seqs <= 2048 else "decode_mfma_kernel"
+    if num_seqs <= 2048:
+        return "decode_split_kernel"
+    return "decode_mfma_kernel" if block_size == 16 else "decode_generic_kernel"
 
 
 def kernel_code_hash(path):

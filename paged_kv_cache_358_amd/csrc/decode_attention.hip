@@ -71,7 +71,7 @@ struct DecodeArgs {
   int32_t group;
   int32_t head_dim;
   int32_t max_blocks;   // block-table row stride
-  int32_t ctx_limit;    // min(max_context_len, max_blocks * 16)
+  int32_t ctx_limit;    // min(max_context_len, max_blocks * block_tokens)
   int32_t part_blocks;  // blocks per partition
   int32_t block_tokens; // tokens per block (16 on the MFMA paths)
   int32_t max_parts;
@@ -88,6 +88,9 @@ struct DecodeArgs {
   const int32_t* share_groups;
   int32_t num_groups;
   int32_t slot_parts;  // partial slots per query row in the workspace (>= max_parts)
+  // split: log2 of the 16-token tiles per cache block (block_tokens = 16 << sub_log2); the split
+  // kernel then counts blocks and partitions (part_blocks) in 16-token tiles.
+  int32_t sub_log2;
 };
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s) {
@@ -392,7 +395,7 @@ __device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t tag, uint32_t
 // One partition of one (sequence, KV head) as a workgroup sees it.
 struct Item {
   int32_t s, h, p, n;  // sequence, KV head, partition, context length
-  int32_t b0, my_n;    // first block of the partition; blocks of this wave (b0 + w + 4i)
+  int32_t b0, my_n;    // first block of the partition; blocks of this wave
   int32_t np, len;     // partitions of the sequence; blocks in this partition
 };
 
@@ -403,12 +406,15 @@ struct Item {
 // loaded one partition ahead into the other of two slots (A/B), so no loaded value is copied
 // before it is used.  Per-block arithmetic is that of decode_mfma_kernel.
 // At least two waves per SIMD: the compiler keeps the kernel within 256 VGPRs.
-template <int DT, int D, int NBUF, int MODE, int WV>
+// MULTI: cache blocks of 16 << a.sub_log2 tokens (32, 64, ...), streamed as 16-token tiles:
+// tile b of a row is tile b % SB of the row's cache block b / SB (SB = 1 << sub_log2); every
+// count below (blocks, partitions, shared blocks) is then in tiles.  Without MULTI, SB = 1.
+template <int DT, int D, int NBUF, int MODE, int WV, bool MULTI>
 __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(
     DecodeArgs a) {
   constexpr int KK = D / 32;
   constexpr int NV = D / 16;
-  constexpr int kTileBytes = D * kBlockTokens * 2;
+  constexpr int kTileBytes = D * kBlockTokens * 2;  // one 16-token tile of one KV head
   constexpr int kThreads = WV * kWave;
   constexpr int NT = MODE == kGroup ? 2 : 1;  // 16-column MFMA tiles of query columns
   __shared__ __attribute__((aligned(16))) float sm_o[WV][16][D];
@@ -429,6 +435,18 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   const int S = MODE == kGroup ? a.num_groups : a.num_seqs;  // contexts: groups or sequences
   const int PB = a.part_blocks;
   const int hkv = a.hkv;
+  const int lsb = MULTI ? a.sub_log2 : 0;  // log2 of the tiles per cache block
+  const int sbm = (1 << lsb) - 1;
+  // Tile (from the partition's first) of this wave's ring position i.  Waves take blocks in
+  // turn; with several tiles per block (plain mode), a wave streams all tiles of its block on
+  // consecutive positions, so the V rows that a block's tiles split are read by one wave in
+  // quick succession.  Group mode keeps one tile per turn: a member's own tiles need not start
+  // on a block boundary of the group's tile sequence.
+  constexpr bool kBlockTurns = MULTI && MODE == kPlain;
+  auto tile_of = [&](int i) {
+    if constexpr (kBlockTurns) return ((w + WV * (i >> lsb)) << lsb) + (i & sbm);
+    else return w + WV * i;
+  };
   const int g = a.group;
   const int J = gridDim.x;          // chunks = NR rounds of R
   const int C = a.part_cost;        // fixed cost of a partition, in blocks of streaming
@@ -459,8 +477,13 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     const int mm = a.share_groups[3 * v + 1];
     return max(1, min(min(mm, a.num_seqs - first), 16 * NT / g));
   };
+  // The description counts cache blocks; the context counts tiles.
   auto group_shared = [&](int v) {
-    return max(0, min(a.share_groups[3 * v + 2], min(a.max_blocks, a.ctx_limit / kBlockTokens)));
+    if constexpr (MULTI) {
+      return max(0, min(a.share_groups[3 * v + 2], (a.ctx_limit / kBlockTokens) >> lsb)) << lsb;
+    } else {
+      return max(0, min(a.share_groups[3 * v + 2], min(a.max_blocks, a.ctx_limit / kBlockTokens)));
+    }
   };
   // Blocks of a member with n tokens beyond the k shared ones.
   auto own_blocks = [&](int n, int k) { return max(0, (n + kBlockTokens - 1) / kBlockTokens - k); };
@@ -557,7 +580,9 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     Item it;
     bool ok;
     int32_t ids;    // this wave's block ids, one per lane; lanes >= my_n are never used
-    int32_t meta;   // kGroup: per lane, (owning member + 1) << 8 | tokens of the block (owner 0 = shared)
+    // per lane: tile of its cache block << 16 (MULTI), and in kGroup
+    // (owning member + 1) << 8 | tokens of the block (owner 0 = shared)
+    int32_t meta;
     u32x4_t q[NT][KK];  // Q^T operand of each column tile
   };
   using st = uint16_t;
@@ -582,7 +607,15 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       it.np = (nb + PB - 1) / PB;
       it.len = min(PB, nb - p * PB);
       it.b0 = p * PB;
-      it.my_n = (it.len > w) ? (it.len - w + WV - 1) / WV : 0;
+      if constexpr (kBlockTurns) {
+        // Blocks of the partition (only a context's last can be partial) and this wave's share.
+        const int lenb = (it.len + sbm) >> lsb;
+        const int myb = lenb > w ? (lenb - w + WV - 1) / WV : 0;
+        it.my_n = myb << lsb;
+        if (myb > 0 && w + WV * (myb - 1) == lenb - 1) it.my_n -= (lenb << lsb) - it.len;
+      } else {
+        it.my_n = (it.len > w) ? (it.len - w + WV - 1) / WV : 0;
+      }
     }
     int64_t qrow[NT];
     if constexpr (MODE == kGroup) {
@@ -614,12 +647,13 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
         }
       }
       sl.meta = (owner << 8) | nv;
-      sl.ids = a.block_tables[static_cast<int64_t>(row) * a.max_blocks + min(max(pos, 0), a.max_blocks - 1)];
+      if constexpr (MULTI) sl.meta |= (pos & sbm) << 16;
+      sl.ids = a.block_tables[static_cast<int64_t>(row) * a.max_blocks + min(max(pos, 0) >> lsb, a.max_blocks - 1)];
     } else {
       qrow[0] = (static_cast<int64_t>(it.s) * a.hq + it.h * g + (col < g ? col : 0)) * D;
-      const int b = min(it.b0 + w + WV * lane, a.max_blocks - 1);
-      sl.meta = 0;
-      sl.ids = a.block_tables[static_cast<int64_t>(it.s) * a.max_blocks + b];
+      const int b = it.b0 + tile_of(lane);
+      sl.meta = (b & sbm) << 16;
+      sl.ids = a.block_tables[static_cast<int64_t>(it.s) * a.max_blocks + min(b >> lsb, a.max_blocks - 1)];
     }
     // Keep the id load ahead of the query loads: the lookahead waits for it while the
     // query loads may still be in flight.
@@ -648,24 +682,35 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 
   const uint8_t* kc = static_cast<const uint8_t*>(a.k);
   const uint8_t* vc = static_cast<const uint8_t*>(a.v);
-  const int64_t blk_stride = static_cast<int64_t>(hkv) * kTileBytes;
-  const int k_off = lane * 16;
-  const int v_off = col * 32 + grp * 8;
-  // phys = the block id of ring position i of a partition with my_n blocks for this wave.
-  auto load_tile = [&](KVRegs<D>& r, int32_t phys, int i, int my_n, int h) {
+  // A (cache block, KV head) holds SB tiles: K as [D/8][16 * SB][8] and V as [D][16 * SB]
+  // (one tile when SB = 1).  Tile t of it starts t * 256 bytes into each K row of 8 dims and
+  // t * 32 bytes into each V row.
+  const int head_bytes = kTileBytes << lsb;
+  const int64_t blk_stride = static_cast<int64_t>(hkv) * head_bytes;
+  const int k_off = MULTI ? ((grp << (4 + lsb)) + col) * 16 : lane * 16;  // (dims 8c.., token col), chunk c = grp
+  const int v_off = ((col * 32) << lsb) + grp * 8;    // (dim col, tokens 4 grp..) of V
+  // A V row of a block of several tiles spans them all: its cache lines are left to the default
+  // policy, so that the tiles after the first find them in L2.
+  constexpr int kLoadV = MULTI ? 0 : kLoadNT;
+  // phys = the block id of ring position i of a partition with my_n blocks for this wave; t = the
+  // tile of that block.
+  auto load_tile = [&](KVRegs<D>& r, int32_t phys, int t, int i, int my_n, int h) {
     const bool ok = i < my_n && phys >= 0 && phys < a.num_blocks;
-    const int64_t off = ok ? static_cast<int64_t>(phys) * blk_stride + static_cast<int64_t>(h) * kTileBytes : 0;
-    const int nrec = ok ? kTileBytes : 0;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kc + off), 0, nrec,
-                                                                        kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vc + off), 0, nrec,
-                                                                        kRsrcWord3);
+    const int64_t off = ok ? static_cast<int64_t>(phys) * blk_stride + static_cast<int64_t>(h) * head_bytes : 0;
+    const int tk = ok ? t * 256 : 0, tv = ok ? t * 32 : 0;
+    const int nrec = ok ? head_bytes : 0;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kc + off + tk), 0,
+                                                                        nrec - tk, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vc + off + tv), 0,
+                                                                        nrec - tv, kRsrcWord3);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      r.k[kk] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, kk * 1024, kLoadNT));
+      r.k[kk] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, (kk * 1024) << lsb, kLoadNT));
 #pragma unroll
     for (int nn = 0; nn < NV; ++nn)
-      r.v[nn] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, nn * 512, kLoadNT));
+      r.v[nn] = __builtin_bit_cast(
+          u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, (nn * 512) << lsb, kLoadV));
   };
   // Ring positions per partition: a multiple of NBUF, at least NBUF; those past my_n are empty.
   auto steps_of = [&](const Item& it) { return max(NBUF, (it.my_n + NBUF - 1) / NBUF * NBUF); };
@@ -759,7 +804,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   // Stream one partition's blocks (looking ahead into the next one).  At the end of a
   // segment, merge the four waves and write the output or the run's partial.
   auto run = [&](const Item cur, const int32_t cur_ids, const int32_t cur_meta, const u32x4_t (&qc)[NT][KK],
-                 const Item nxi, const bool nx_ok, const int32_t nx_ids) {
+                 const Item nxi, const bool nx_ok, const int32_t nx_ids, const int32_t nx_meta) {
     auto compute = [&](KVRegs<D>& r, int i) {
       const int32_t phys = __builtin_amdgcn_readlane(cur_ids, i < 63 ? i : 63);
       int nv;          // tokens of the block
@@ -767,12 +812,12 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       if constexpr (MODE == kGroup) {
         const int meta = __builtin_amdgcn_readlane(cur_meta, i < 63 ? i : 63);
         nv = meta & 0xff;
-        const int owner = meta >> 8;
+        const int owner = MULTI ? (meta >> 8) & 0xff : meta >> 8;
         if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
 #pragma unroll
         for (int t = 0; t < NT; ++t) nv_col[t] = (owner == 0 || owner - 1 == (t * 16 + col) / g) ? nv : 0;
       } else {
-        const int bl = cur.b0 + w + WV * i;
+        const int bl = cur.b0 + tile_of(i);
         nv = cur.n - bl * kBlockTokens;
         nv = nv > kBlockTokens ? kBlockTokens : nv;
         if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
@@ -832,6 +877,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
         // Ring lookahead position; past this partition's last step it is the next one's.
         int la = i + j + NBUF - 1;
         int32_t phys;
+        int tile = 0;
         int mn = cur.my_n, hh = cur.h;
         if (la >= steps) {
           // The next partition's ids were loaded after this one's first blocks.  Reading
@@ -841,12 +887,18 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
           asm volatile("" : "+v"(t));
           la -= steps;
           phys = __builtin_amdgcn_readlane(t, la < 63 ? la : 63);
+          if constexpr (MULTI) {
+            int32_t tm = nx_meta;
+            asm volatile("" : "+v"(tm));
+            tile = __builtin_amdgcn_readlane(tm, la < 63 ? la : 63) >> 16;
+          }
           mn = nx_my_n;
           hh = nxi.h;
         } else {
           phys = __builtin_amdgcn_readlane(cur_ids, la < 63 ? la : 63);
+          if constexpr (MULTI) tile = __builtin_amdgcn_readlane(cur_meta, la < 63 ? la : 63) >> 16;
         }
-        load_tile(ring[(j + NBUF - 1) % NBUF], phys, la, mn, hh);
+        load_tile(ring[(j + NBUF - 1) % NBUF], phys, tile, la, mn, hh);
         if (i + j < cur.my_n) compute(ring[j], i + j);  // positions past my_n only pad the ring
       }
     }
@@ -967,17 +1019,19 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     for (int nn = 0; nn < NV; ++nn) o[t][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   seg_p0 = A.it.p;
 #pragma unroll
-  for (int j = 0; j < NBUF - 1; ++j) load_tile(ring[j], __builtin_amdgcn_readlane(A.ids, j), j, A.it.my_n, A.it.h);
+  for (int j = 0; j < NBUF - 1; ++j)
+    load_tile(ring[j], __builtin_amdgcn_readlane(A.ids, j), MULTI ? __builtin_amdgcn_readlane(A.meta, j) >> 16 : 0, j,
+              A.it.my_n, A.it.h);
   // Weighted length of a partition: its blocks, C, and CE if it ends its context.
   auto wlen = [&](const Item& it) { return it.len + C + (it.p == it.np - 1 ? CE : 0); };
   off += wlen(A.it);
   prepare_next(A.it, off, B);
   while (true) {
-    run(A.it, A.ids, A.meta, A.q, B.it, B.ok, B.ids);
+    run(A.it, A.ids, A.meta, A.q, B.it, B.ok, B.ids, B.meta);
     if (!B.ok) break;
     off += wlen(B.it);
     prepare_next(B.it, off, A);
-    run(B.it, B.ids, B.meta, B.q, A.it, A.ok, A.ids);
+    run(B.it, B.ids, B.meta, B.q, A.it, A.ok, A.ids, A.meta);
     if (!A.ok) break;
     off += wlen(A.it);
     prepare_next(A.it, off, B);
@@ -1308,16 +1362,16 @@ int32_t device_cus(int* out) {
 }
 
 // Launch the split kernel with WV wavefronts per workgroup; sets args->run_grid / run_rounds.
-template <int DT, int D, int MODE, int WV>
+template <int DT, int D, int MODE, int WV, bool MULTI>
 int32_t launch_split_waves(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  const void* fn = reinterpret_cast<const void*>(&decode_split_kernel<DT, D, kPersistRing, MODE, WV>);
+  const void* fn = reinterpret_cast<const void*>(&decode_split_kernel<DT, D, kPersistRing, MODE, WV, MULTI>);
   int resident = 0;
   const int32_t rc = resident_workgroups(fn, WV * kWave, &resident);
   if (rc != PA_OK) return rc;
   args->run_rounds = kSplitRounds;
   args->run_grid = std::min(kSplitRounds * resident, kMaxSplitGrid / kSplitRounds * kSplitRounds);
-  hipExtLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing, MODE, WV>), dim3(static_cast<uint32_t>(args->run_grid)),
-                        dim3(WV * kWave), 0, st, start, stop, 0, *args);
+  hipExtLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing, MODE, WV, MULTI>),
+                        dim3(static_cast<uint32_t>(args->run_grid)), dim3(WV * kWave), 0, st, start, stop, 0, *args);
   return PA_OK;
 }
 
@@ -1326,34 +1380,45 @@ int32_t launch_split_waves(DecodeArgs* args, hipStream_t st, hipEvent_t start, h
 // of 8 wavefronts per CU then halves the runs, partials and merges of each context.  Measured on
 // MI355X: 4 sequences of 131072 tokens, 8 KV heads: 356 -> 339 us; with 512 to 2048 contexts the
 // 8-wavefront form was 2-21% slower.
-template <int DT, int D, int MODE>
+template <int DT, int D, int MODE, bool MULTI>
 int32_t launch_split(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   int cus = 0;
   const int32_t rc = device_cus(&cus);
   if (rc != PA_OK) return rc;
   const int64_t contexts = int64_t{MODE == kGroup ? args->num_groups : args->num_seqs} * args->hkv;
-  if (contexts < cus) return launch_split_waves<DT, D, MODE, 8>(args, st, start, stop);
-  return launch_split_waves<DT, D, MODE, 4>(args, st, start, stop);
+  if (contexts < cus) return launch_split_waves<DT, D, MODE, 8, MULTI>(args, st, start, stop);
+  return launch_split_waves<DT, D, MODE, 4, MULTI>(args, st, start, stop);
 }
 
 // One launch: over groups when the batch comes with shared prefixes, else over sequences.
-template <int DT, int D>
+template <int DT, int D, bool MULTI>
 int32_t launch_split_all(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  if (args->num_groups > 0) return launch_split<DT, D, kGroup>(args, st, start, stop);
-  return launch_split<DT, D, kPlain>(args, st, start, stop);
+  if (args->num_groups > 0) return launch_split<DT, D, kGroup, MULTI>(args, st, start, stop);
+  return launch_split<DT, D, kPlain, MULTI>(args, st, start, stop);
+}
+
+template <int DT, int D>
+int32_t launch_split_blocks(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  if (args->sub_log2 > 0) return launch_split_all<DT, D, true>(args, st, start, stop);
+  return launch_split_all<DT, D, false>(args, st, start, stop);
 }
 
 template <int DT>
 int32_t launch_decode(DecodeArgs args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   const int64_t D = args.head_dim;
-  // The MFMA kernels take 16-token blocks; other block sizes take the VALU kernel.
-  const bool fast = DT != PA_F32 && (D == 64 || D == 128) && args.group <= 16 && args.block_tokens == kBlockTokens;
+  const bool shape = DT != PA_F32 && (D == 64 || D == 128) && args.group <= 16;
+  // The MFMA kernels take 16-token blocks; the split kernel also takes blocks of 16 << j tokens
+  // (up to 1024) as 16-token tiles.  Other block sizes take the VALU kernel.
+  int lsb = 0;
+  while (lsb < 6 && (kBlockTokens << lsb) < args.block_tokens) ++lsb;
+  const bool tiles = (kBlockTokens << lsb) == args.block_tokens;
+  const bool fast = shape && args.block_tokens == kBlockTokens;
   args.part_cost = kPartCost;
   args.ctx_cost = kCtxCost;
-  // The split kernel indexes the weighted blocks of all (sequence, KV head) pairs with int32.
-  const bool split = fast && args.num_seqs <= kMaxScanSeqs &&
+  // The split kernel indexes the weighted tiles of all (sequence, KV head) pairs with int32.
+  const bool split = shape && tiles && args.num_seqs <= kMaxScanSeqs &&
                      int64_t{args.num_seqs} * args.hkv *
-                             (int64_t{args.max_blocks} + int64_t{args.part_cost} * (args.max_parts + 1) +
+                             ((int64_t{args.max_blocks} << lsb) + int64_t{args.part_cost} * (args.max_parts + 1) +
                               args.ctx_cost) <
                          0x7fffffffLL;
   args.run_grid = 0;
@@ -1365,9 +1430,11 @@ int32_t launch_decode(DecodeArgs args, hipStream_t st, hipEvent_t start, hipEven
     args.num_groups = 0;  // the other kernels take every sequence on its own
   }
   if (split) {
-    // One launch: the split kernel merges its runs in place.
-    if constexpr (DT != PA_F32) return D == 64 ? launch_split_all<DT, 64>(&args, st, start, stop)
-                                               : launch_split_all<DT, 128>(&args, st, start, stop);
+    // One launch: the split kernel merges its runs in place; it counts in 16-token tiles.
+    args.sub_log2 = lsb;
+    args.part_blocks <<= lsb;
+    if constexpr (DT != PA_F32) return D == 64 ? launch_split_blocks<DT, 64>(&args, st, start, stop)
+                                               : launch_split_blocks<DT, 128>(&args, st, start, stop);
   }
   // The per-partition kernels need the merge kernel when a context spans several partitions.
   const bool merge = args.max_parts > 1;

@@ -71,9 +71,12 @@ class _Staging:
 class PagedDecodeLayer:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, num_q_heads: int, dtype,
                  max_seqs: int, max_blocks_per_seq: int, free_order=None, partition_size: int = 512,
-                 device="cuda", stream=None, share_prefixes: bool = True, share_min_blocks: int = 4):
-        self.alloc = BlockAllocator(num_blocks, 16, free_order)
-        self.k_cache, self.v_cache = alloc_kv_cache(num_blocks, num_kv_heads, head_dim, dtype, device)
+                 device="cuda", stream=None, share_prefixes: bool = True, share_min_blocks: int = 4,
+                 block_size: int = 16):
+        self.block_size = block_size
+        self.alloc = BlockAllocator(num_blocks, block_size, free_order)
+        self.k_cache, self.v_cache = alloc_kv_cache(num_blocks, num_kv_heads, head_dim, dtype, device,
+                                                    block_size=block_size)
         self.num_q_heads = num_q_heads
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
@@ -99,7 +102,7 @@ class PagedDecodeLayer:
         probe_t = torch.empty(max_seqs, max_blocks_per_seq, dtype=torch.int32, device=device)
         ws = paged_attention_workspace_bytes(probe_q, self.k_cache, self.v_cache, probe_t,
                                              torch.empty_like(probe_q, dtype=torch.float32),
-                                             max_blocks_per_seq * 16, partition_size, shared=share_prefixes)
+                                             max_blocks_per_seq * block_size, partition_size, shared=share_prefixes)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
         # The per-step library calls go straight to the C ABI with argument blocks built here once:
         # the layer owns the caches, staging buffers and workspace, so only the step's tensors,
@@ -173,7 +176,7 @@ class PagedDecodeLayer:
         npairs = self._npairs.value
         ngroups = 0  # groups covering the batch; 0 when no two sequences share a block
         if self.share_prefixes and S >= 2 and self.share_max_members >= 2:
-            rc = lib.pa_shared_prefixes(st.c_tables, st.c_lens, S, self.max_blocks, 16, self.share_max_members,
+            rc = lib.pa_shared_prefixes(st.c_tables, st.c_lens, S, self.max_blocks, self.block_size, self.share_max_members,
                                         self.share_min_blocks, st.c_groups, self.max_seqs, ctypes.byref(self._ngroups))
             if rc != PA_OK:
                 raise PagedAttnError(rc, "pa_shared_prefixes")

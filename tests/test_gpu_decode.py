@@ -273,8 +273,9 @@ def test_start_and_stop_events_bracket_the_kernels(part):
 
 @pytest.mark.parametrize("dtype,B", [("bf16", 8), ("bf16", 32), ("f32", 32), ("f16", 64)])
 def test_other_block_sizes(dtype, B):
-    # Blocks of other than 16 tokens take the VALU kernel (and the partition merge); lengths
-    # around the block size, several blocks and several partitions.
+    # Blocks of 8 tokens, and fp32 caches, take the VALU kernel (and the partition merge); bf16/fp16
+    # blocks of 32 and 64 tokens take the split kernel as 16-token tiles.  Lengths around the block
+    # size, several blocks and several partitions.
     lens = [1, B - 1, B, B + 1, 2 * B + 3, 300, 1000]
     cfg = synth.scaled(synth.C3, lens=lens, dtype=dtype, block_size=B)
     pd = PagedDecode(cfg)
@@ -283,3 +284,35 @@ def test_other_block_sizes(dtype, B):
     assert max_err(out, pd) <= tol_for(dtype)
     out2 = pd.run(partition_size=4 * B)
     assert max_err(out2, pd) <= tol_for(dtype)
+
+
+@pytest.mark.parametrize("base,dtype,B,D", [(synth.C3, "bf16", 32, 128), (synth.C2, "bf16", 64, 128),
+                                           (synth.C3, "f16", 128, 64), (synth.C2, "f16", 32, 64)])
+def test_multi_tile_blocks(base, dtype, B, D):
+    # Blocks of 16 << j tokens go to the split kernel, which streams each as 16-token tiles:
+    # contexts ending inside a block's first tile, on a tile edge inside a block, on a block edge,
+    # and spanning several blocks and 512-token partitions.
+    lens = [1, 15, 16, 17, B - 1, B, B + 1, B + 16, 3 * B + 5, 511, 512, 513, 1500, 2047]
+    cfg = synth.scaled(base, lens=lens, dtype=dtype, block_size=B, head_dim=D)
+    pd = PagedDecode(cfg)
+    assert pd.k_cache.shape[3] == B
+    assert max_err(pd.run(), pd) <= tol_for(dtype)
+    # partitions of one block and of 1024 tokens; bf16 output
+    assert max_err(pd.run(partition_size=B), pd) <= tol_for(dtype)
+    assert max_err(pd.run(partition_size=1024), pd) <= tol_for(dtype)
+    assert max_err(pd.run(out_dtype=pd.q.dtype), pd) <= 2 * tol_for(dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_multi_tile_blocks_match_16_token_blocks(dtype):
+    # The split kernel computes the same 16-token tiles whatever the cache's block size; only the
+    # order in which a workgroup's waves sum them changes (a wave takes all tiles of its block).  The
+    # same sequences in caches of 16-, 32- and 64-token blocks agree to fp32 rounding.
+    lens = [1, 16, 33, 200, 511, 512, 513, 777, 1024, 1500, 2047, 3000]
+    outs = []
+    for B in (16, 32, 64):
+        pd = PagedDecode(synth.scaled(synth.C3, lens=lens, dtype=dtype, block_size=B))
+        outs.append(pd.run().cpu().numpy())
+    assert float(np.max(np.abs(outs[1] - outs[0]))) <= 1e-5
+    assert float(np.max(np.abs(outs[2] - outs[0]))) <= 1e-5
+    assert max_err(torch.from_numpy(outs[2]), pd) <= tol_for(dtype)

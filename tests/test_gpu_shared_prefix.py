@@ -27,16 +27,18 @@ B = 16
 
 
 class ForkedBatch:
-    def __init__(self, seed, hq, hkv, D, dtype, prompts, lone=(), partition_size=512):
+    def __init__(self, seed, hq, hkv, D, dtype, prompts, lone=(), partition_size=512, block_size=B):
         """prompts: list of (prefix_len, [tokens appended by each sample]).  lone: context lengths of
         unforked sequences placed after each prompt's samples in turn."""
         rng = np.random.default_rng(seed)
         self.hq, self.hkv, self.D, self.dtype, self.part = hq, hkv, D, dtype, partition_size
-        need = sum(-(-L // B) + len(sm) * (-(-max(sm) // B) + 1) for L, sm in prompts) + sum(-(-n // B) for n in lone)
+        self.bs = bs = block_size
+        need = sum(-(-L // bs) + len(sm) * (-(-max(sm) // bs) + 1) for L, sm in prompts) + \
+            sum(-(-n // bs) for n in lone)
         nblocks = need + 8
-        self.alloc = pa.BlockAllocator(nblocks, B, rng.permutation(nblocks).astype(np.int32))
+        self.alloc = pa.BlockAllocator(nblocks, bs, rng.permutation(nblocks).astype(np.int32))
         tdt = TORCH_DTYPE[dtype]
-        self.k_cache, self.v_cache = pa.alloc_kv_cache(nblocks, hkv, D, tdt, "cuda")
+        self.k_cache, self.v_cache = pa.alloc_kv_cache(nblocks, hkv, D, tdt, "cuda", block_size=bs)
         self.k_cache.fill_(float("nan"))
         self.v_cache.fill_(float("nan"))
 
@@ -79,7 +81,7 @@ class ForkedBatch:
                 sid += 1
         S = len(self.order)
         self.lens_np = np.array([self.truth[s][0].shape[0] for s in self.order], np.int32)
-        self.max_blocks = int(max(1, -(-self.lens_np.max() // B)))
+        self.max_blocks = int(max(1, -(-self.lens_np.max() // bs)))
         tables, lens = self.alloc.build_batch(self.order, self.max_blocks)
         assert np.array_equal(lens, self.lens_np)
         self.tables_np = tables.copy()
@@ -91,7 +93,7 @@ class ForkedBatch:
 
     def groups(self, max_members=None, min_blocks=1):
         mm = 32 // (self.hq // self.hkv) if max_members is None else max_members
-        return pa.shared_prefixes(self.tables_np, self.lens_np, mm, min_blocks)
+        return pa.shared_prefixes(self.tables_np, self.lens_np, mm, min_blocks, block_size=self.bs)
 
     def run(self, shared=None, out_dtype=torch.float32):
         out = torch.empty(self.q.shape, dtype=out_dtype, device="cuda")
@@ -215,3 +217,15 @@ def test_groups_of_one_and_an_empty_context():
                                    synth.decode_f64(v, "bf16"), fb.scale)
         errs.append(float(np.max(np.abs(o[i] - ref))))
     assert max(errs) <= 5e-3
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_blocks_of_several_tiles(bs):
+    # Blocks of 32 or 64 tokens: the groups count whole blocks, the kernel streams 16-token tiles of
+    # them (a shared block is several shared tiles; a member's own blocks start on a block edge).
+    prompts = [(700, [0, 1, 31, 32, 33, 100, 500, 9]), (96, [1, 64, 2])]
+    fb = ForkedBatch(8, 32, 8, 128, "bf16", prompts, lone=[65, 0], block_size=bs)
+    assert fb.k_cache.shape[3] == bs
+    gr, _ = check(fb)
+    assert gr.tolist() == [[0, 8, 700 // bs], [8, 1, 0], [9, 3, 96 // bs], [12, 1, 0]]
+    check(fb, max_members=3)
