@@ -395,7 +395,7 @@ __device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t tag, uint32_t
 // One partition of one (sequence, KV head) as a workgroup sees it.
 struct Item {
   int32_t s, h, p, n;  // sequence, KV head, partition, context length
-  int32_t b0, my_n;    // first block of the partition; blocks of this wave
+  int32_t b0, my_n;    // first block (tile) of the partition; ring positions of this wave
   int32_t np, len;     // partitions of the sequence; blocks in this partition
 };
 
@@ -437,14 +437,18 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   const int hkv = a.hkv;
   const int lsb = MULTI ? a.sub_log2 : 0;  // log2 of the tiles per cache block
   const int sbm = (1 << lsb) - 1;
-  // Tile (from the partition's first) of this wave's ring position i.  Waves take blocks in
-  // turn; with several tiles per block (plain mode), a wave streams all tiles of its block on
-  // consecutive positions, so the V rows that a block's tiles split are read by one wave in
-  // quick succession.  Group mode keeps one tile per turn: a member's own tiles need not start
-  // on a block boundary of the group's tile sequence.
-  constexpr bool kBlockTurns = MULTI && MODE == kPlain;
-  auto tile_of = [&](int i) {
-    if constexpr (kBlockTurns) return ((w + WV * (i >> lsb)) << lsb) + (i & sbm);
+  // PAIR (plain mode on blocks of 32 or more tokens): a ring position holds 32 tokens, two
+  // tiles, so that every V load covers whole rows of 32 tokens and the PV product runs on
+  // 16x16x32 MFMAs; waves take blocks in turn and a wave streams all pairs of its block on
+  // consecutive positions.  Group mode keeps one tile per position and per turn: a member's own
+  // tiles need not start on a block boundary of the group's tile sequence.
+  constexpr bool PAIR = MULTI && MODE == kPlain;
+  constexpr int kUnitTokens = PAIR ? 2 * kBlockTokens : kBlockTokens;  // tokens per ring position
+  const int lu = PAIR ? lsb - 1 : lsb;  // log2 of the ring units per cache block
+  const int um = (1 << lu) - 1;
+  // Unit (from the partition's first) of this wave's ring position i.
+  auto unit_of = [&](int i) {
+    if constexpr (PAIR) return ((w + WV * (i >> lu)) << lu) + (i & um);
     else return w + WV * i;
   };
   const int g = a.group;
@@ -607,12 +611,14 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       it.np = (nb + PB - 1) / PB;
       it.len = min(PB, nb - p * PB);
       it.b0 = p * PB;
-      if constexpr (kBlockTurns) {
-        // Blocks of the partition (only a context's last can be partial) and this wave's share.
-        const int lenb = (it.len + sbm) >> lsb;
+      if constexpr (PAIR) {
+        // Pairs and blocks of the partition (only a context's last can be partial) and this
+        // wave's share of the pairs.
+        const int lenu = (it.len + 1) >> 1;
+        const int lenb = (lenu + um) >> lu;
         const int myb = lenb > w ? (lenb - w + WV - 1) / WV : 0;
-        it.my_n = myb << lsb;
-        if (myb > 0 && w + WV * (myb - 1) == lenb - 1) it.my_n -= (lenb << lsb) - it.len;
+        it.my_n = myb << lu;
+        if (myb > 0 && w + WV * (myb - 1) == lenb - 1) it.my_n -= (lenb << lu) - lenu;
       } else {
         it.my_n = (it.len > w) ? (it.len - w + WV - 1) / WV : 0;
       }
@@ -651,9 +657,9 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       sl.ids = a.block_tables[static_cast<int64_t>(row) * a.max_blocks + min(max(pos, 0) >> lsb, a.max_blocks - 1)];
     } else {
       qrow[0] = (static_cast<int64_t>(it.s) * a.hq + it.h * g + (col < g ? col : 0)) * D;
-      const int b = it.b0 + tile_of(lane);
-      sl.meta = (b & sbm) << 16;
-      sl.ids = a.block_tables[static_cast<int64_t>(it.s) * a.max_blocks + min(b >> lsb, a.max_blocks - 1)];
+      const int u = (PAIR ? it.b0 >> 1 : it.b0) + unit_of(lane);  // partitions start on a block
+      sl.meta = (u & um) << 16;
+      sl.ids = a.block_tables[static_cast<int64_t>(it.s) * a.max_blocks + min(u >> lu, a.max_blocks - 1)];
     }
     // Keep the id load ahead of the query loads: the lookahead waits for it while the
     // query loads may still be in flight.
@@ -682,40 +688,62 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 
   const uint8_t* kc = static_cast<const uint8_t*>(a.k);
   const uint8_t* vc = static_cast<const uint8_t*>(a.v);
-  // A (cache block, KV head) holds SB tiles: K as [D/8][16 * SB][8] and V as [D][16 * SB]
-  // (one tile when SB = 1).  Tile t of it starts t * 256 bytes into each K row of 8 dims and
-  // t * 32 bytes into each V row.
+  // A (cache block, KV head) holds 16 * SB tokens: K as [D/8][16 * SB][8] and V as [D][16 * SB]
+  // (SB = 1 without MULTI).  Ring unit t of it (kUnitTokens tokens) starts t * 16 * kUnitTokens
+  // bytes into each K row of 8 dims and t * 2 * kUnitTokens bytes into each V row.
   const int head_bytes = kTileBytes << lsb;
   const int64_t blk_stride = static_cast<int64_t>(hkv) * head_bytes;
-  const int k_off = MULTI ? ((grp << (4 + lsb)) + col) * 16 : lane * 16;  // (dims 8c.., token col), chunk c = grp
-  const int v_off = ((col * 32) << lsb) + grp * 8;    // (dim col, tokens 4 grp..) of V
-  // A V row of a block of several tiles spans them all: its cache lines are left to the default
-  // policy, so that the tiles after the first find them in L2.
+  // Per-lane byte offsets: K chunk c = grp of the lane's token (K half h in PAIR), and V dim col
+  // at the lane's first token.
+  int k_off[PAIR ? 2 : 1];
+  if constexpr (PAIR) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) k_off[h] = ((grp << (4 + lsb)) + 8 * (col >> 2) + 4 * h + (col & 3)) * 16;
+  } else {
+    k_off[0] = MULTI ? ((grp << (4 + lsb)) + col) * 16 : lane * 16;
+  }
+  const int v_off = ((col * 32) << lsb) + grp * (PAIR ? 16 : 8);
+  // A V row of a block of several units spans them all: its cache lines are left to the default
+  // policy, so that the units after the first find them in L2.
   constexpr int kLoadV = MULTI ? 0 : kLoadNT;
-  // phys = the block id of ring position i of a partition with my_n blocks for this wave; t = the
-  // tile of that block.
-  auto load_tile = [&](KVRegs<D>& r, int32_t phys, int t, int i, int my_n, int h) {
+  using Regs = std::conditional_t<PAIR, KVPairRegs<D>, KVRegs<D>>;
+  // phys = the block id of ring position i of a partition with my_n positions for this wave;
+  // t = the unit of that block.
+  auto load_tile = [&](Regs& r, int32_t phys, int t, int i, int my_n, int h) {
     const bool ok = i < my_n && phys >= 0 && phys < a.num_blocks;
     const int64_t off = ok ? static_cast<int64_t>(phys) * blk_stride + static_cast<int64_t>(h) * head_bytes : 0;
-    const int tk = ok ? t * 256 : 0, tv = ok ? t * 32 : 0;
+    const int tk = ok ? t * 16 * kUnitTokens : 0, tv = ok ? t * 2 * kUnitTokens : 0;
     const int nrec = ok ? head_bytes : 0;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kc + off + tk), 0,
                                                                         nrec - tk, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vc + off + tv), 0,
                                                                         nrec - tv, kRsrcWord3);
+    if constexpr (PAIR) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      r.k[kk] = __builtin_bit_cast(
-          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, (kk * 1024) << lsb, kLoadNT));
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int nn = 0; nn < NV; ++nn)
-      r.v[nn] = __builtin_bit_cast(
-          u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, (nn * 512) << lsb, kLoadV));
+        for (int kk = 0; kk < KK; ++kk)
+          r.k[hh][kk] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off[hh], (kk * 1024) << lsb, kLoadNT));
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn)
+        r.v[nn] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off, (nn * 512) << lsb, kLoadV));
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        r.k[kk] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off[0], (kk * 1024) << lsb, kLoadNT));
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn)
+        r.v[nn] = __builtin_bit_cast(
+            u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, (nn * 512) << lsb, kLoadV));
+    }
   };
   // Ring positions per partition: a multiple of NBUF, at least NBUF; those past my_n are empty.
   auto steps_of = [&](const Item& it) { return max(NBUF, (it.my_n + NBUF - 1) / NBUF * NBUF); };
 
-  KVRegs<D> ring[NBUF];
+  Regs ring[NBUF];
   f32x4_t o[NT][NV];
   float m[NT], l[NT];
 #pragma unroll
@@ -805,7 +833,56 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   // segment, merge the four waves and write the output or the run's partial.
   auto run = [&](const Item cur, const int32_t cur_ids, const int32_t cur_meta, const u32x4_t (&qc)[NT][KK],
                  const Item nxi, const bool nx_ok, const int32_t nx_ids, const int32_t nx_meta) {
-    auto compute = [&](KVRegs<D>& r, int i) {
+    // PAIR: one 32-token unit.  Scores of the two K halves, one softmax update over the 32
+    // tokens, and O^T += V^T P^T as 16x16x32 MFMAs (lane group j holds tokens 8 j .. 8 j + 7 of
+    // both V and P).
+    auto compute_pair = [&](KVPairRegs<D>& r, int i) {
+      const int32_t phys = __builtin_amdgcn_readlane(cur_ids, i < 63 ? i : 63);
+      int nv = cur.n - ((cur.b0 >> 1) + unit_of(i)) * kUnitTokens;  // tokens of the unit
+      nv = nv > kUnitTokens ? kUnitTokens : nv;
+      if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
+      f32x4_t sacc[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        sacc[hh] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) sacc[hh] = mfma_qk<DT>(r.k[hh][kk], qc[0][kk], sacc[hh]);
+      }
+      float x[8];  // token 8 grp + j of the unit: half j / 4, row 4 grp + j % 4
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = (grp * 8 + j < nv) ? sacc[j >> 2][j & 3] * a.scale_log2 : -INFINITY;
+      const float bm = rows4_max(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
+      const float m_new = fmaxf(m[0], bm);
+      const float alpha = (m[0] == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m[0] - m_new);
+      float pr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pr[j] = (x[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[j] - m_new);
+      l[0] = l[0] * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+      m[0] = m_new;
+      u32x2_t h0, l0, h1, l1;
+      PSplit<DT>::split(pr, h0, l0);
+      PSplit<DT>::split(pr + 4, h1, l1);
+      const u32x4_t p_hi = {h0[0], h0[1], h1[0], h1[1]}, p_lo = {l0[0], l0[1], l1[0], l1[1]};
+      if (nv < kUnitTokens) {  // tokens past the context: selected out of V in place
+        uint32_t keep[4];
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          const int t0 = grp * 8 + 2 * wd;
+          keep[wd] = (t0 < nv ? 0x0000ffffu : 0u) | (t0 + 1 < nv ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int nn = 0; nn < NV; ++nn)
+          r.v[nn] = u32x4_t{r.v[nn][0] & keep[0], r.v[nn][1] & keep[1], r.v[nn][2] & keep[2], r.v[nn][3] & keep[3]};
+      }
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) {
+        o[0][nn] *= alpha;
+        o[0][nn] = mfma_qk<DT>(r.v[nn], p_hi, o[0][nn]);
+        o[0][nn] = mfma_qk<DT>(r.v[nn], p_lo, o[0][nn]);
+      }
+    };
+    auto compute_tile = [&](KVRegs<D>& r, int i) {
       const int32_t phys = __builtin_amdgcn_readlane(cur_ids, i < 63 ? i : 63);
       int nv;          // tokens of the block
       int nv_col[NT];  // tokens of the block this lane's query column sees, per column tile
@@ -817,7 +894,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
         for (int t = 0; t < NT; ++t) nv_col[t] = (owner == 0 || owner - 1 == (t * 16 + col) / g) ? nv : 0;
       } else {
-        const int bl = cur.b0 + tile_of(i);
+        const int bl = cur.b0 + unit_of(i);
         nv = cur.n - bl * kBlockTokens;
         nv = nv > kBlockTokens ? kBlockTokens : nv;
         if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
@@ -867,6 +944,10 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2)))
           o[t][nn] = mfma_pv<DT>(r.v[nn], p_lo[t], o[t][nn]);
         }
       }
+    };
+    auto compute = [&](Regs& r, int i) {
+      if constexpr (PAIR) compute_pair(r, i);
+      else compute_tile(r, i);
     };
 
     const int steps = steps_of(cur);
