@@ -12,7 +12,8 @@ Default workload: bf16 MHA decode, 64 sequences, context lengths U[128, 2048],
 32 query / 32 KV heads, head_dim 128, 16-token blocks in a shuffled pool.
 The first timed step attends over exactly those lengths; each later step one
 token more.  --block-size 32 (64, ...) lays the same sequences out in a pool of
-larger blocks (MHA, GQA and long-context workloads).
+larger blocks, --head-dim 256 (or 64) gives them another head size (MHA, GQA and
+long-context workloads).
 
 Prints one JSON line: value = algorithmic HBM bytes of the whole step / step
 time (GB/s), plus seq-tokens/s per layer, the main attention kernel's roofline
@@ -45,6 +46,8 @@ def parse():
                     help="split-context partition in tokens (0 = the workload's own)")
     ap.add_argument("--block-size", type=int, default=16,
                     help="decode c2/c3/c5: tokens per cache block (16; 32, 64, ... stream as 16-token tiles)")
+    ap.add_argument("--head-dim", type=int, default=0,
+                    help="decode c2/c3/c5: head_dim other than the workload's 128 (64 or 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -63,8 +66,8 @@ def main():
         run_prefill(args)
         return
     BS = args.block_size
-    if BS != 16 and args.workload == "c4":
-        sys.exit("bench.py: the sampling workload runs on 16-token blocks only")
+    if (BS != 16 or args.head_dim) and args.workload == "c4":
+        sys.exit("bench.py: the sampling workload runs on 16-token blocks and head_dim 128 only")
 
     import numpy as np
     import torch
@@ -121,8 +124,9 @@ def main():
         lens0 = None
     else:
         cfg = synth.CONFIGS[{"c2": "c2_mha_bf16", "c3": "c3_gqa_bf16", "c5": "c5_long_bf16"}[args.workload]]
-        if BS != 16:  # the same sequences in a pool of larger blocks
-            cfg = synth.scaled(cfg, name_suffix=f"_b{BS}", block_size=BS)
+        suffix = (f"_d{args.head_dim}" if args.head_dim else "") + (f"_b{BS}" if BS != 16 else "")
+        if suffix:  # the same context lengths with another head size, or in a pool of larger blocks
+            cfg = synth.scaled(cfg, name_suffix=suffix, block_size=BS, head_dim=args.head_dim or cfg.head_dim)
         part = args.partition_size or cfg.partition_size
         if W + K > cfg.pool_slack_tokens:
             sys.exit(f"{cfg.name}: warmup + steps must be <= {cfg.pool_slack_tokens}")
@@ -472,7 +476,11 @@ def run_prefill(args):
 def main_kernel_name(dtype, head_dim, group, num_seqs, block_size=16):
     """The library's dominant kernel for this shape (its dispatch rule, restated)."""
     tiles = block_size in [16 << j for j in range(7)]
-    if dtype == "f32" or head_dim not in (64, 128) or group > 16 or not tiles:
+    if dtype == "f32" or group > 16:
+        return "decode_generic_kernel"
+    if head_dim == 256:
+        return "decode_split_kernel" if block_size == 16 and num_seqs <= 2048 else "decode_generic_kernel"
+    if head_dim not in (64, 128) or not tiles:
         return "decode_generic_kernel"
     if num_seqs <= 2048:
         return "decode_split_kernel"

@@ -405,12 +405,14 @@ struct Item {
 // loading while the current one finishes.  The next partition's block ids and query are
 // loaded one partition ahead into the other of two slots (A/B), so no loaded value is copied
 // before it is used.  Per-block arithmetic is that of decode_mfma_kernel.
-// At least two waves per SIMD: the compiler keeps the kernel within 256 VGPRs.
+// At least two waves per SIMD for head_dim 64 and 128: the compiler keeps the kernel within 256
+// VGPRs.  Head_dim 256 (plain mode, 4 wavefronts, 16-token blocks) runs one wave per SIMD with the
+// accumulators partly in AGPRs: twice the bytes per ring slot keep as many bytes in flight per CU.
 // MULTI: cache blocks of 16 << a.sub_log2 tokens (32, 64, ...), streamed as 16-token tiles:
 // tile b of a row is tile b % SB of the row's cache block b / SB (SB = 1 << sub_log2); every
 // count below (blocks, partitions, shared blocks) is then in tiles.  Without MULTI, SB = 1.
 template <int DT, int D, int NBUF, int MODE, int WV, bool MULTI>
-__global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(
+__global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2))) void decode_split_kernel(
     DecodeArgs a) {
   constexpr int KK = D / 32;
   constexpr int NV = D / 16;
@@ -1480,8 +1482,13 @@ int32_t launch_split_all(DecodeArgs* args, hipStream_t st, hipEvent_t start, hip
 
 template <int DT, int D>
 int32_t launch_split_blocks(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  if (args->sub_log2 > 0) return launch_split_all<DT, D, true>(args, st, start, stop);
-  return launch_split_all<DT, D, false>(args, st, start, stop);
+  if constexpr (D == 256) {
+    // Plain mode on 16-token blocks only: the other forms would spill.
+    return launch_split_waves<DT, 256, kPlain, 4, false>(args, st, start, stop);
+  } else {
+    if (args->sub_log2 > 0) return launch_split_all<DT, D, true>(args, st, start, stop);
+    return launch_split_all<DT, D, false>(args, st, start, stop);
+  }
 }
 
 template <int DT>
@@ -1489,22 +1496,24 @@ int32_t launch_decode(DecodeArgs args, hipStream_t st, hipEvent_t start, hipEven
   const int64_t D = args.head_dim;
   const bool shape = DT != PA_F32 && (D == 64 || D == 128) && args.group <= 16;
   // The MFMA kernels take 16-token blocks; the split kernel also takes blocks of 16 << j tokens
-  // (up to 1024) as 16-token tiles.  Other block sizes take the VALU kernel.
+  // (up to 1024) as 16-token tiles, and head_dim 256 on 16-token blocks.  Other shapes take the
+  // VALU kernel.
   int lsb = 0;
   while (lsb < 6 && (kBlockTokens << lsb) < args.block_tokens) ++lsb;
   const bool tiles = (kBlockTokens << lsb) == args.block_tokens;
   const bool fast = shape && args.block_tokens == kBlockTokens;
+  const bool wide = DT != PA_F32 && D == 256 && args.group <= 16 && args.block_tokens == kBlockTokens;
   args.part_cost = kPartCost;
   args.ctx_cost = kCtxCost;
   // The split kernel indexes the weighted tiles of all (sequence, KV head) pairs with int32.
-  const bool split = shape && tiles && args.num_seqs <= kMaxScanSeqs &&
+  const bool split = ((shape && tiles) || wide) && args.num_seqs <= kMaxScanSeqs &&
                      int64_t{args.num_seqs} * args.hkv *
                              ((int64_t{args.max_blocks} << lsb) + int64_t{args.part_cost} * (args.max_parts + 1) +
                               args.ctx_cost) <
                          0x7fffffffLL;
   args.run_grid = 0;
   args.run_rounds = 0;
-  if (split && args.num_groups > 0) {
+  if (split && args.num_groups > 0 && !wide) {
     // Group contexts span several members' blocks: their partitions index the larger slot range.
     args.max_parts = args.slot_parts;
   } else {
@@ -1514,8 +1523,11 @@ int32_t launch_decode(DecodeArgs args, hipStream_t st, hipEvent_t start, hipEven
     // One launch: the split kernel merges its runs in place; it counts in 16-token tiles.
     args.sub_log2 = lsb;
     args.part_blocks <<= lsb;
-    if constexpr (DT != PA_F32) return D == 64 ? launch_split_blocks<DT, 64>(&args, st, start, stop)
-                                               : launch_split_blocks<DT, 128>(&args, st, start, stop);
+    if constexpr (DT != PA_F32) {
+      if (D == 64) return launch_split_blocks<DT, 64>(&args, st, start, stop);
+      if (D == 256) return launch_split_blocks<DT, 256>(&args, st, start, stop);
+      return launch_split_blocks<DT, 128>(&args, st, start, stop);
+    }
   }
   // The per-partition kernels need the merge kernel when a context spans several partitions.
   const bool merge = args.max_parts > 1;

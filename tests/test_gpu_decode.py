@@ -75,9 +75,11 @@ def test_head_dim_64_and_group_4():
 
 
 def test_generic_path_shapes():
-    # group 32 (> 16 query heads per KV head) and head_dim 256 take the VALU kernel
+    # group 32 (> 16 query heads per KV head), fp32 head_dim 256 and head_dim 256 on 32-token blocks
+    # take the VALU kernel
     for cfg in (synth.DecodeConfig("g32", 32, 3, 32, 1, 128, "bf16", "fixed", (5, 600, 1100)),
-                synth.DecodeConfig("d256", 33, 3, 4, 2, 256, "bf16", "fixed", (7, 530, 40)),
+                synth.DecodeConfig("d256_f32", 33, 3, 4, 2, 256, "f32", "fixed", (7, 530, 40)),
+                synth.DecodeConfig("d256_b32", 33, 3, 4, 2, 256, "bf16", "fixed", (7, 530, 40), block_size=32),
                 synth.DecodeConfig("f32_gqa", 34, 3, 8, 2, 64, "f32", "fixed", (3, 1030, 48))):
         pd = PagedDecode(cfg)
         out = pd.run()
@@ -316,3 +318,24 @@ def test_multi_tile_blocks_match_16_token_blocks(dtype):
     assert float(np.max(np.abs(outs[1] - outs[0]))) <= 1e-5
     assert float(np.max(np.abs(outs[2] - outs[0]))) <= 1e-5
     assert max_err(torch.from_numpy(outs[2]), pd) <= tol_for(dtype)
+
+
+@pytest.mark.parametrize("dtype,hq,hkv", [("bf16", 16, 4), ("f16", 8, 8), ("bf16", 32, 2)])
+def test_head_dim_256_split_kernel(dtype, hq, hkv):
+    # head_dim 256 on 16-token blocks: the split kernel's plain mode, one wave per SIMD.  Lengths
+    # around block and partition edges, several partitions; partitions of one block and of 1024
+    # tokens; a shared-prefix description is accepted and the batch taken sequence by sequence.
+    import paged_kv_cache_358_amd as pa
+    lens = [1, 15, 16, 17, 300, 511, 512, 513, 1600, 2500]
+    cfg = synth.DecodeConfig("d256_split", 35, len(lens), hq, hkv, 256, dtype, "fixed", tuple(lens))
+    pd = PagedDecode(cfg)
+    out = pd.run()
+    assert max_err(out, pd) <= tol_for(dtype)
+    for part in (16, 1024):
+        assert max_err(pd.run(partition_size=part), pd) <= tol_for(dtype)
+    sh = torch.tensor([[0, 2, 0], [2, len(lens) - 2, 0]], dtype=torch.int32, device="cuda")
+    o2 = torch.empty_like(out)
+    pa.paged_attention_decode(pd.q, pd.k_cache, pd.v_cache, pd.block_tables, pd.context_lens,
+                              cfg.softmax_scale, o2, max_context_len=pd.max_context_len, shared=sh)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, out)
