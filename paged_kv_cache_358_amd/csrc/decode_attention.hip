@@ -3,13 +3,13 @@
 // What is computed: per sequence, query head and its KV head, softmax attention of
 // the one decode query over the sequence's cached tokens.  Paging does not change
 // this math (zhichai.net page, Key points, "Engineering insight"); the kernel only
-// follows each sequence's block table to find the scattered 16-token blocks
-// (zhichai.net page, "Why it matters"; "Stop Wasting GPU Memory" page, Technical
+// follows each sequence's block table to find the scattered blocks, 16 tokens each by
+// default (zhichai.net page, "Why it matters"; "Stop Wasting GPU Memory" page, Technical
 // Details, "Core Architecture").  Softmax is taken online, block by block, as in the
 // FlashAttention kernels the ml-canon page's "Connections" section says vLLM uses.
 //
 // Work decomposition.  A context is split into partitions of P tokens; a workgroup's
-// waves take a partition's blocks round-robin.  Each wave keeps a running max, sum and
+// waves take a partition's blocks in turn.  Each wave keeps a running max, sum and
 // unnormalised output per query head; the waves merge through LDS.  The main (split)
 // kernel runs one workgroup per resident slot over a balanced run of partitions and
 // merges contexts that span several runs in the same launch (the last run to finish
@@ -18,20 +18,20 @@
 // second kernel merges them.
 //
 // bf16/fp16 fast path (MFMA).  All g = H_q / H_kv query heads of a KV head share
-// each K/V block, so a block is one dense contraction, done on the matrix cores with
-// v_mfma_f32_16x16x32_{bf16,f16}:
-//   S^T[16 tokens x 16 heads] = K_blk[16 x D] . Q^T[D x 16]     (D/32 MFMAs)
-//   O^T[D x 16 heads]        += V_blk^T[D x 16] . P^T[16 x 16]  (D/16 MFMAs)
+// each K/V block, so a 16-token tile is one dense contraction on the matrix cores:
+//   S^T[16 tokens x 16 heads] = K[16 x D] . Q^T[D x 16]     (D/32 v_mfma_f32_16x16x32)
+//   O^T[D x 16 heads]        += V^T[D x 16] . P^T[16 x 16]  (D/16 v_mfma_f32_16x16x16, twice)
 // Query heads beyond g are zero columns.  The lane that holds S for (head, 4 tokens)
 // after the first product is exactly the lane that must supply P for them in the
 // second, so scores never leave registers.  P is split as P_hi + P_lo, both in the
-// input's 16-bit type, and the 32-wide contraction slot of the second MFMA carries
-// (token, hi) and (token, lo) pairs against a duplicated V, so the probabilities enter
-// with ~16 significant bits instead of 8 while V and the accumulation stay exact fp32.
+// input's 16-bit type, and each half goes through its own PV MFMA, so the probabilities
+// enter with ~16 significant bits instead of 8 while V and the accumulation stay exact
+// fp32.  Blocks of 32 or more tokens (plain mode) take 32 tokens per step with
+// 16x16x32 PV MFMAs.
 // The cache layout makes every load a contiguous run per instruction: K is stored in
-// 16-byte chunks [D/8][16 tokens][8], so the 64 lanes of one MFMA operand load read
-// 1 KiB contiguously; V is stored transposed [D][16 tokens], so a PV operand load reads
-// 512 contiguous bytes (16 dims x 16 tokens).
+// 16-byte chunks [D/8][B tokens][8], so the 64 lanes of one QK operand load read 16
+// tokens of 4 chunks; V is stored transposed [D][B tokens], so a PV operand load reads
+// 16 dims x 16 tokens.
 //
 // fp32 (and any shape outside the fast path): a plain VALU kernel, one wavefront per
 // (partition, query head, sequence).
