@@ -397,6 +397,7 @@ struct Item {
   int32_t s, h, p, n;  // sequence, KV head, partition, context length
   int32_t b0, my_n;    // first block (tile) of the partition; ring positions of this wave
   int32_t np, len;     // partitions of the sequence; blocks in this partition
+  int32_t nt;          // column tiles holding query heads (group mode: members * g / 16, rounded up)
 };
 
 // Split form of the MFMA kernel: one workgroup per chunk of the schedule above walks its run
@@ -602,7 +603,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
   // go to valid addresses, row 0).
   auto fill = [&](Slot& sl, bool ok, int s, int h, int p) {
     Item& it = sl.it;
-    it = Item{0, 0, 0, 0, 0, 0, 1, 0};
+    it = Item{0, 0, 0, 0, 0, 0, 1, 0, 1};
     sl.ok = ok;
     if (ok) {
       const int nb = __builtin_amdgcn_readfirstlane(nb_s[s]);
@@ -632,6 +633,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       const int first = __builtin_amdgcn_readfirstlane(group_first(it.s));
       const int mm = __builtin_amdgcn_readfirstlane(group_members(it.s, first));
       const int k = __builtin_amdgcn_readfirstlane(group_shared(it.s));
+      it.nt = (mm * g + 15) / 16;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int c = t * 16 + col < mm * g ? t * 16 + col : 0;
@@ -888,6 +890,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       const int32_t phys = __builtin_amdgcn_readlane(cur_ids, i < 63 ? i : 63);
       int nv;          // tokens of the block
       int nv_col[NT];  // tokens of the block this lane's query column sees, per column tile
+      int t_lo = 0, t_hi = NT - 1;  // column tiles to compute (wave-uniform)
       if constexpr (MODE == kGroup) {
         const int meta = __builtin_amdgcn_readlane(cur_meta, i < 63 ? i : 63);
         nv = meta & 0xff;
@@ -895,6 +898,10 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
         if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
 #pragma unroll
         for (int t = 0; t < NT; ++t) nv_col[t] = (owner == 0 || owner - 1 == (t * 16 + col) / g) ? nv : 0;
+        // Column tiles with no column that sees the block (a member's own block is seen by its g
+        // columns only; tiles past the group's columns hold none) would add exact zeros: skipped.
+        t_lo = owner == 0 ? 0 : ((owner - 1) * g) / 16;
+        t_hi = owner == 0 ? cur.nt - 1 : ((owner - 1) * g + g - 1) / 16;
       } else {
         const int bl = cur.b0 + unit_of(i);
         nv = cur.n - bl * kBlockTokens;
@@ -907,6 +914,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       u32x2_t p_hi[NT], p_lo[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
+        if (NT > 1 && (t < t_lo || t > t_hi)) continue;
         f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) sacc = mfma_qk<DT>(r.k[kk], qc[t][kk], sacc);
@@ -941,6 +949,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       for (int nn = 0; nn < NV; ++nn) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
+          if (NT > 1 && (t < t_lo || t > t_hi)) continue;
           o[t][nn] *= alpha[t];
           o[t][nn] = mfma_pv<DT>(r.v[nn], p_hi[t], o[t][nn]);
           o[t][nn] = mfma_pv<DT>(r.v[nn], p_lo[t], o[t][nn]);
