@@ -31,7 +31,7 @@ def run_sampling(cfg: synth.SamplingConfig, check_steps, check_seqs, share_prefi
     order = cfg.free_order()
     layer = PagedDecodeLayer(cfg.pool_blocks(), cfg.num_kv_heads, cfg.head_dim, cfg.num_q_heads, torch.bfloat16,
                              max_seqs=cfg.num_seqs, max_blocks_per_seq=max_blocks, free_order=order,
-                             partition_size=cfg.partition_size, share_prefixes=share_prefixes)
+                             partition_size=cfg.partition_size, share_prefixes=share_prefixes, block_size=B)
     layer.k_cache.fill_(float("nan"))
     layer.v_cache.fill_(float("nan"))
     model = BlockAllocatorModel(cfg.pool_blocks(), B, order.tolist())
@@ -96,6 +96,13 @@ def run_sampling(cfg: synth.SamplingConfig, check_steps, check_seqs, share_prefi
 def test_cow_sampling_small_all_sequences(share_prefixes):
     cfg = dataclasses.replace(synth.C4, num_prompts=3, steps=24, slack_blocks=16)
     run_sampling(cfg, {1, 2, 17, 24}, list(range(cfg.num_seqs)), share_prefixes)
+
+
+def test_cow_sampling_32_token_blocks():
+    # the same flow on 32-token blocks: the 1000-token prompt leaves an 8-token partial block that
+    # every sample but the last copies at the first step; groups count 32-token blocks
+    cfg = dataclasses.replace(synth.C4, num_prompts=3, steps=40, slack_blocks=16, block_size=32)
+    run_sampling(cfg, {1, 2, 24, 25, 40}, list(range(cfg.num_seqs)))
 
 
 def test_cow_sampling_full_sampled():
