@@ -441,8 +441,8 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
   const int lsb = MULTI ? a.sub_log2 : 0;  // log2 of the tiles per cache block
   const int sbm = (1 << lsb) - 1;
   // PAIR (plain mode on blocks of 32 or more tokens): a ring position holds 32 tokens, two
-  // tiles, so that every V load covers whole rows of 32 tokens and the PV product runs on
-  // 16x16x32 MFMAs; waves take blocks in turn and a wave streams all pairs of its block on
+  // tiles, so that every V load covers 32 consecutive tokens of each V row (the whole row of a
+  // 32-token block) and the PV product runs on 16x16x32 MFMAs; waves take blocks in turn and a wave streams all pairs of its block on
   // consecutive positions.  Group mode keeps one tile per position and per turn: a member's own
   // tiles need not start on a block boundary of the group's tile sequence.
   constexpr bool PAIR = MULTI && MODE == kPlain;
