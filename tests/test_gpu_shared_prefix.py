@@ -229,3 +229,14 @@ def test_blocks_of_several_tiles(bs):
     gr, _ = check(fb)
     assert gr.tolist() == [[0, 8, 700 // bs], [8, 1, 0], [9, 3, 96 // bs], [12, 1, 0]]
     check(fb, max_members=3)
+
+
+@pytest.mark.parametrize("hq,hkv", [(24, 8), (12, 2)])
+def test_member_heads_straddling_column_tiles(hq, hkv):
+    # g = 3 (ten members, 30 columns) and g = 6 (five members): a member's query heads can sit in
+    # both 16-column tiles, so its own blocks are computed on both
+    prompts = [(400, [3, 0, 50, 17, 200, 1, 16, 90, 5, 33]), (150, [2, 40])]
+    fb = ForkedBatch(9, hq, hkv, 128, "bf16", prompts, lone=[77])
+    gr, _ = check(fb)
+    g = hq // hkv
+    assert gr[0].tolist() == [0, min(10, 32 // g), 400 // B]
