@@ -134,13 +134,27 @@ const char* pa_last_error(void);
 
 /* ----------------------------------------------------------------------- decode attention */
 
-/* Device workspace bytes paged_attention_decode needs for these parameters: when more than one partition
- * can occur, P = num_seqs * H_q * n fp32 partial rows of head_dim + 2 values (P * (head_dim + 2) * 4 bytes),
- * then num_seqs * H_kv uint64 arrival counters; else 0.  n = ceil(max_context_len / partition_size), or with
- * p->shared set the partitions of a group of min(32 / (H_q / H_kv), num_seqs) members of ceil(max_context_len
- * / 16) blocks each.  Returns 0 for invalid parameters (the decode call then reports the error).  The contents need no initialisation (the counters carry a per-call tag)
- * and are scratch between calls; two calls in flight at once must not share a workspace. */
+/* Device workspace bytes paged_attention_decode needs for these parameters (0 when no context can span more
+ * than one partition).  The call takes one of three kernels (paged_attention_decode_kernel names it):
+ *   decode_split_kernel (bf16/fp16; head_dim 64 or 128 on blocks of 16 << j tokens, or 256 on 16-token blocks;
+ *     H_q / H_kv <= 16; num_seqs <= 2048): at most 1024 workgroups ("runs") each write at most two partials,
+ *     so the workspace is 1024 * 2 * C fp32 rows of head_dim + 2 values (C = H_q / H_kv query columns, or 32
+ *     when p->shared is set), then num_seqs * H_kv uint64 arrival counters.  Its size does not grow with the
+ *     batch's context lengths.
+ *   decode_mfma_kernel / decode_generic_kernel (other shapes, larger batches): P = num_seqs * H_q * n fp32
+ *     partial rows of head_dim + 2 values, n = ceil(min(max_context_len, max_blocks_per_seq * block_size) /
+ *     partition_size).
+ * Returns 0 for invalid parameters (the decode call then reports the error).  The contents need no
+ * initialisation (the counters carry a per-call tag) and are scratch between calls; two calls in flight at
+ * once must not share a workspace. */
 size_t paged_attention_workspace_bytes(const pa_decode_params* p);
+
+/* Name of the kernel that streams the K/V blocks of a paged_attention_decode call with these parameters:
+ * "decode_split_kernel", "decode_mfma_kernel" or "decode_generic_kernel" (the last two are followed by
+ * reduce_partitions_kernel when a context spans several partitions).  The decode call chooses its kernel
+ * with the same host rule.  "" for invalid parameters or num_seqs = 0 (nothing is launched).  A static
+ * string; no device is touched. */
+const char* paged_attention_decode_kernel(const pa_decode_params* p);
 
 /*
  * Single-query decode attention over a paged KV cache.
@@ -178,6 +192,9 @@ int32_t paged_attention_decode(const void* q, const void* k_cache, const void* v
  *   k_new, v_new   device [num_tokens][num_kv_heads][head_dim], cache dtype
  *   slot_mapping   device int32 [num_tokens]
  * Two tokens naming the same slot race (which one lands is undefined); the allocator never produces that.
+ * With the environment variable PA_DEBUG_CHECKS set (and not "0") the call first copies slot_mapping back
+ * to the host, synchronously, and returns PA_ERR_INVALID_ARG without launching if two in-range slots are
+ * equal.
  */
 int32_t kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping, int32_t num_tokens,
                   void* k_cache, void* v_cache, const pa_cache_desc* cache, void* stream);
@@ -186,7 +203,10 @@ int32_t kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapp
  * block_copy: for each pair i in [0, num_pairs), copy physical block pairs[2i] (source) onto block
  * pairs[2i + 1] (destination): every slot, every KV head, K and V.  Pairs with an index outside
  * [0, num_blocks) are skipped.  Destinations must be distinct and must not be a source of the same call
- * (the allocator's copy-on-write pairs satisfy both); otherwise the result is undefined.
+ * (the allocator's copy-on-write pairs satisfy both); otherwise the result is undefined.  With the
+ * environment variable PA_DEBUG_CHECKS set (and not "0") the call first copies pairs back to the host,
+ * synchronously, and returns PA_ERR_INVALID_ARG without launching if an in-range pair has src == dst, two
+ * share a destination, or a destination is also a source.
  *   pairs   device int32 [num_pairs][2]
  */
 int32_t block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,

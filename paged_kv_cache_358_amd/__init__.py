@@ -17,7 +17,8 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libpagedattn.so")
+# PAGEDATTN_LIB names another build of the same library (the host-sanitizer build of the tests).
+LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(_PKG, "libpagedattn.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_OUT_OF_BLOCKS, PA_ERR_HIP, PA_ERR_WORKSPACE = range(6)
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
@@ -57,6 +58,7 @@ SIGNATURES = {
     "pa_version": (_i32, []),
     "pa_last_error": (ctypes.c_char_p, []),
     "paged_attention_workspace_bytes": (_sz, [ctypes.POINTER(DecodeParams)]),
+    "paged_attention_decode_kernel": (ctypes.c_char_p, [ctypes.POINTER(DecodeParams)]),
     "paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, ctypes.POINTER(DecodeParams)]),
     "kv_append": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc), _vp]),
     "block_copy": (_i32, [_vp, _vp, _vp, _i32, ctypes.POINTER(CacheDesc), _vp]),
@@ -207,6 +209,15 @@ def paged_attention_workspace_bytes(q, k_cache, v_cache, block_tables, out, max_
     return int(lib.paged_attention_workspace_bytes(ctypes.byref(p)))
 
 
+def paged_attention_decode_kernel(q, k_cache, v_cache, block_tables, out, max_context_len: int,
+                                  partition_size: int = 0) -> str:
+    """Name of the kernel that streams K/V for a decode call with these arguments, as the library
+    chooses it ("" when nothing would be launched).  Shared-prefix groups change the kernel's mode,
+    not the kernel."""
+    p = decode_params(q, k_cache, v_cache, block_tables, out, max_context_len, partition_size)
+    return lib.paged_attention_decode_kernel(ctypes.byref(p)).decode()
+
+
 def shared_prefixes(tables, lens, max_members: int, min_blocks: int = 1, block_size: int = BLOCK_SIZE,
                     groups_out=None):
     """The batch (host block tables int32 [S, max_blocks], lengths int32 [S]) cut into groups of
@@ -243,13 +254,22 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     group's shared leading blocks are read once for all its members.
     """
     torch = _torch()
+    # Shapes first: the kernels read context_lens[s] and table row s (row stride block_tables.shape[1]) for
+    # every s < S, so undersized metadata would send them outside its allocation.
+    if q.dim() != 3:
+        raise ValueError("q must be [S, H_q, D]")
+    S = q.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or block_tables.shape[1] < 1:
+        raise ValueError(f"block_tables must be [S={S}, max_blocks >= 1], got {tuple(block_tables.shape)}")
+    if context_lens.dim() != 1 or context_lens.numel() != S:
+        raise ValueError(f"context_lens must be [S={S}], got {tuple(context_lens.shape)}")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
     _require_device(q, k_cache, v_cache, block_tables, context_lens, out)
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise ValueError("block_tables and context_lens must be int32")
     if q.dtype != k_cache.dtype:
         raise ValueError("q must have the cache dtype")
-    if tuple(out.shape) != tuple(q.shape):
-        raise ValueError("out must have q's shape")
     sh = None
     if shared is not None:
         _require_device(shared)
@@ -464,7 +484,7 @@ class BlockAllocator:
         return tables_out[:n, :max_blocks], lens_out[:n]
 
 
-__all__ = ["paged_attention_decode", "paged_attention_workspace_bytes", "shared_prefixes", "SharedPrefix", "paged_attention_prefill", "kv_append", "block_copy", "stage_copy",
+__all__ = ["paged_attention_decode", "paged_attention_workspace_bytes", "paged_attention_decode_kernel", "shared_prefixes", "SharedPrefix", "paged_attention_prefill", "kv_append", "block_copy", "stage_copy",
            "stage_append",
            "BlockAllocator",
            "alloc_kv_cache", "cache_shapes", "cache_desc", "PagedAttnError", "lib", "LIB_PATH", "SIGNATURES",

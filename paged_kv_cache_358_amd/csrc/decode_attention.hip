@@ -62,8 +62,8 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;
-  float* part_o;   // [S][H_q][max_parts][D], normalised partition outputs
-  float* part_ml;  // [S][H_q][max_parts][2], (max in log2 units, sum)
+  float* part_o;   // normalised partial outputs: [S][H_q][max_parts][D] (per-partition kernels) or per run (split)
+  float* part_ml;  // (max in log2 units, sum) of each partial: [S][H_q][max_parts][2] or per run (split)
   float scale_log2;
   int32_t num_seqs;
   int32_t hq;
@@ -87,7 +87,10 @@ struct DecodeArgs {
   // sequence, members, prefix blocks; the groups cover the batch in order.
   const int32_t* share_groups;
   int32_t num_groups;
-  int32_t slot_parts;  // partial slots per query row in the workspace (>= max_parts)
+  // split: query columns per partial slot.  The split kernel's partials are indexed by run: run k writes
+  // at most two, [k][slot][column][D] (and [k][slot][column][2]), slot 0 for the run's last segment and
+  // slot 1 for its first segment when another context follows it in the run.
+  int32_t part_cols;
   // split: log2 of the 16-token tiles per cache block (block_tokens = 16 << sub_log2); the split
   // kernel then counts blocks and partitions (part_blocks) in 16-token tiles.
   int32_t sub_log2;
@@ -328,7 +331,8 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
 constexpr int kMaxScanSeqs = 2048;  // sequences the split kernel's in-LDS index covers
 constexpr int kPersistRing = 2;     // ring depth of the split kernel
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X, each with its own L2
-constexpr int kMaxSplitGrid = 4095;  // chunks (workgroups) of the split kernel, at most
+constexpr int kMaxRuns = 1024;      // chunks (workgroups, runs) of the split kernel, at most
+constexpr int kMaxCols = 32;        // query columns of a context in the split kernel (two 16-column tiles)
 
 // Modes of the split kernel.  kPlain: one context per sequence.  kGroup: one context per group of
 // consecutive sequences whose block tables share their first k blocks (forked samples or beams of
@@ -373,16 +377,15 @@ __device__ __forceinline__ int64_t chunk_owner(int64_t off, int64_t W, int R, in
 // that last wrote it, the low 32 the partitions whose runs have published their partials.
 // The workspace is never cleared: a counter still holding another launch's tag counts as 0.
 // Returns the partitions published before this call's `add`.
-// Common case, one fetch-add: the counter already carries this launch's tag.  An add that
-// landed on a stale counter is redone: the first such run swaps in (tag, add), every later
-// one adds again.  Exactly one swap succeeds (the tag never changes back within a launch), so
-// the count of the launch is exact.  Runs of one context arrive together at the end of the
-// kernel; a swap loop there would retry once per competitor, a fetch-add never retries.
+// A run first reads the counter.  If it carries another launch's tag (or garbage), the run
+// swaps in (tag, add); exactly one swap per launch succeeds, since the tag never changes back
+// within a launch, and a run whose swap fails has re-read the counter and finds the tag there.
+// Only then does a run fetch-add, so every add lands on a counter with this launch's tag and a
+// count of at most the context's partitions: no add can carry out of the low word into the tag
+// (an add on a stale counter whose low word is near 2^32 could forge this launch's tag).
 __device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t tag, uint32_t add) {
   const uint64_t mine = static_cast<uint64_t>(tag) << 32;
-  uint64_t old = __hip_atomic_fetch_add(ctr, static_cast<uint64_t>(add), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if ((old >> 32) == tag) return static_cast<uint32_t>(old);
-  old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   while ((old >> 32) != tag) {
     if (__hip_atomic_compare_exchange_strong(ctr, &old, mine | add, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT))
@@ -428,7 +431,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
   __shared__ int32_t ctx_s[kMaxScanSeqs];       // clamped context length of sequence s (both modes)
   __shared__ int32_t scan[WV];  // per-wave totals of the prologue's scan
   __shared__ int32_t merge_flag[2];  // thread 0's arrivals completed these contexts
-  static_assert(WV * 16 * D > kMaxSplitGrid, "run starts of one context fit in sm_o");
+  static_assert(WV * 16 * D > kMaxRuns, "run starts of one context fit in sm_o");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -782,6 +785,10 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
     const int64_t k0 = chunk_owner(A, W, R, NR);
     const int64_t k1 = chunk_owner(A + static_cast<int64_t>(np - 1) * PW, W, R, NR);
     const int nr = static_cast<int>(k1 - k0 + 1);
+    // Runs k0 .. k1 - 1 end inside this context: it is their last segment (slot 0).  Run k1 starts inside it
+    // and holds it as its first segment, in slot 1 when the next context's first partition (at weighted offset
+    // A + wnb_of(nb)) also starts in run k1, else in slot 0.
+    const int last_slot = A + wnb_of(nb) < chunk_lo(k1 + 1, W, R, NR) ? 1 : 0;
     for (int i = tid; i <= nr; i += kThreads)
       run_p0[i] = i == 0 ? 0 : i == nr ? np : static_cast<int>((chunk_lo(k0 + i, W, R, NR) - A + PW - 1) / PW);
     __syncthreads();
@@ -805,7 +812,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
           pl[j] = 0.f;
           po[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           if (ok) {
-            const int64_t prow = row * a.max_parts + p0;
+            const int64_t prow = ((k0 + r) * 2 + (r == nr - 1 ? last_slot : 0)) * a.part_cols + cc;
             pm[j] = __hip_atomic_load(a.part_ml + prow * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             pl[j] = __hip_atomic_load(a.part_ml + prow * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
@@ -1042,7 +1049,9 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
           if (final) {
             store_out4<DT>(a, row * D + d0, res);
           } else {
-            const int64_t prow = row * a.max_parts + seg_p0;
+            // This run's partial of the context: slot 0 if the segment is the run's last, else (the run's
+            // first segment, another context following it) slot 1.
+            const int64_t prow = (static_cast<int64_t>(k) * 2 + (nx_ok ? 1 : 0)) * a.part_cols + t * 16 + cc;
             // Device-scope stores: the run that merges this context may sit on another XCD.
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -1329,13 +1338,32 @@ using namespace pa;
 
 namespace {
 
+// Balance weights beyond the blocks, in blocks of streaming time: per partition its query and
+// table loads and the ring's minimum depth; per context the merge through LDS and the output
+// stores at its end.  Without them, a workgroup whose chunk holds many short contexts
+// finishes last by tens of microseconds.
+constexpr int kPartCost = 5;
+constexpr int kCtxCost = 5;
+
+// Which kernel serves a call.  kSplit: decode_split_kernel (bf16/fp16, head_dim 64/128 on blocks of
+// 16 << j tokens or head_dim 256 on 16-token blocks, at most 16 query heads per KV head, at most
+// kMaxScanSeqs sequences); it merges split contexts itself.  kMfma: decode_mfma_kernel, one workgroup per
+// (partition, KV head, sequence), for larger batches on 16-token blocks.  kGeneric: decode_generic_kernel
+// (VALU) for every other shape.  The last two write per-partition partials that
+// reduce_partitions_kernel merges.
+enum Route : int32_t { kRouteSplit = 0, kRouteMfma = 1, kRouteGeneric = 2 };
+
 struct Plan {
   int32_t part_tokens;
   int32_t part_blocks;
   int32_t ctx_limit;
-  int32_t max_parts;   // partitions of the longest context
-  int32_t slot_parts;  // partial slots per query row: max_parts, or a whole group's partitions with sharing
-  size_t counter_offset;  // byte offset of the arrival counters in the workspace
+  int32_t max_parts;      // partitions of the longest context
+  Route route;
+  int32_t sub_log2;       // kSplit: log2 of the 16-token tiles per cache block
+  bool group;             // kSplit: over groups of sequences sharing leading blocks
+  int32_t part_cols;      // kSplit: query columns per partial slot
+  size_t ml_offset;       // floats from the workspace start to the (max, sum) pairs
+  size_t counter_offset;  // bytes from the workspace start to the arrival counters
   size_t workspace;
 };
 
@@ -1362,24 +1390,54 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
   out->part_blocks = pt / B;
   out->ctx_limit = limit;
   out->max_parts = parts;
-  out->slot_parts = parts;
+  // A group's context holds at most 32 / g members' blocks (each at most ceil(limit / B)).
+  int64_t gparts = parts;
   if (p->shared) {
     const pa_shared_prefix& sh = *p->shared;
     if (sh.num_groups < 0 || sh.num_groups > p->num_seqs) return PA_ERR_INVALID_ARG;
     if (sh.num_groups > 0 && !sh.groups) return PA_ERR_INVALID_ARG;
-    // A group's context holds at most 32 / g members' blocks (each at most ceil(limit / B)).
-    const int64_t members = std::max(1, std::min(32 / (p->num_q_heads / c.num_kv_heads), std::max(1, p->num_seqs)));
+    const int64_t members = std::max(1, std::min(kMaxCols / (p->num_q_heads / c.num_kv_heads), std::max(1, p->num_seqs)));
     const int64_t gblocks = members * ((int64_t{limit} + B - 1) / B);
-    const int64_t gparts = std::max<int64_t>(1, (gblocks + out->part_blocks - 1) / out->part_blocks);
+    gparts = std::max<int64_t>(1, (gblocks + out->part_blocks - 1) / out->part_blocks);
     if (gparts > 8192) return PA_ERR_UNSUPPORTED;
-    out->slot_parts = std::max(parts, static_cast<int32_t>(gparts));
   }
-  // Partials [S][H_q][slot_parts][D] and [S][H_q][slot_parts][2] (fp32),
-  const size_t rows = static_cast<size_t>(p->num_seqs) * p->num_q_heads * out->slot_parts;
-  // then the per (sequence, KV head) arrival counters [S * H_kv] (uint64; the partials end 8-byte aligned)
-  out->counter_offset = rows * (static_cast<size_t>(c.head_dim) + 2) * sizeof(float);
-  out->workspace =
-      out->slot_parts > 1 ? out->counter_offset + static_cast<size_t>(p->num_seqs) * c.num_kv_heads * 8 : 0;
+
+  // The route.
+  const int32_t D = c.head_dim, g = p->num_q_heads / c.num_kv_heads;
+  int32_t lsb = 0;
+  while (lsb < 6 && (kBlockTokens << lsb) < B) ++lsb;
+  const bool tiles = (kBlockTokens << lsb) == B;
+  const bool half = c.dtype != PA_F32 && g <= 16;
+  const bool shape = half && (D == 64 || D == 128);
+  const bool wide = half && D == 256 && B == kBlockTokens;
+  // The split kernel indexes the weighted tiles of all (sequence, KV head) pairs with int32.
+  const bool split = ((shape && tiles) || wide) && p->num_seqs <= kMaxScanSeqs &&
+                     int64_t{p->num_seqs} * c.num_kv_heads *
+                             ((int64_t{p->max_blocks_per_seq} << lsb) + int64_t{kPartCost} * (parts + 1) + kCtxCost) <
+                         0x7fffffffLL;
+  out->route = split ? kRouteSplit : (shape && B == kBlockTokens) ? kRouteMfma : kRouteGeneric;
+  out->sub_log2 = split ? lsb : 0;
+  // Head_dim 256 runs sequence by sequence (its grouped form would spill).
+  out->group = split && !wide && p->shared && p->shared->num_groups > 0;
+
+  if (split) {
+    // Partials per run (see DecodeArgs::part_cols); a context of one partition never spans runs.  A
+    // description of shared prefixes sizes for whole groups' columns, with or without groups.
+    out->part_cols = (p->shared && !wide) ? kMaxCols : g;
+    const bool partials = (p->shared && !wide) ? gparts > 1 : parts > 1;
+    const size_t slots = size_t{kMaxRuns} * 2 * out->part_cols;
+    out->ml_offset = slots * D;
+    out->counter_offset = slots * (size_t{static_cast<uint32_t>(D)} + 2) * sizeof(float);
+    out->workspace =
+        partials ? out->counter_offset + static_cast<size_t>(p->num_seqs) * c.num_kv_heads * sizeof(uint64_t) : 0;
+  } else {
+    // Partials [S][H_q][max_parts][D] and [S][H_q][max_parts][2] (fp32).
+    out->part_cols = 0;
+    const size_t rows = static_cast<size_t>(p->num_seqs) * p->num_q_heads * parts;
+    out->ml_offset = rows * D;
+    out->counter_offset = rows * (size_t{static_cast<uint32_t>(D)} + 2) * sizeof(float);
+    out->workspace = parts > 1 ? out->counter_offset : 0;
+  }
   return PA_OK;
 }
 
@@ -1427,13 +1485,6 @@ int32_t resident_workgroups(const void* kernel, int threads, int* out) {
 // out the finish times but add partials and workgroup start-up costs that outweigh that.
 constexpr int kSplitRounds = 1;
 
-// Balance weights beyond the blocks, in blocks of streaming time: per partition its query and
-// table loads and the ring's minimum depth; per context the merge through LDS and the output
-// stores at its end.  Without them, a workgroup whose chunk holds many short contexts
-// finishes last by tens of microseconds.
-constexpr int kPartCost = 5;
-constexpr int kCtxCost = 5;
-
 // Compute units of the current device, looked up once per device.
 int32_t device_cus(int* out) {
   static std::mutex mu;
@@ -1461,7 +1512,7 @@ int32_t launch_split_waves(DecodeArgs* args, hipStream_t st, hipEvent_t start, h
   const int32_t rc = resident_workgroups(fn, WV * kWave, &resident);
   if (rc != PA_OK) return rc;
   args->run_rounds = kSplitRounds;
-  args->run_grid = std::min(kSplitRounds * resident, kMaxSplitGrid / kSplitRounds * kSplitRounds);
+  args->run_grid = std::min(kSplitRounds * resident, kMaxRuns / kSplitRounds * kSplitRounds);
   hipExtLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing, MODE, WV, MULTI>),
                         dim3(static_cast<uint32_t>(args->run_grid)), dim3(WV * kWave), 0, st, start, stop, 0, *args);
   return PA_OK;
@@ -1501,47 +1552,28 @@ int32_t launch_split_blocks(DecodeArgs* args, hipStream_t st, hipEvent_t start, 
 }
 
 template <int DT>
-int32_t launch_decode(DecodeArgs args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+int32_t launch_decode(DecodeArgs args, const Plan& plan, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   const int64_t D = args.head_dim;
-  const bool shape = DT != PA_F32 && (D == 64 || D == 128) && args.group <= 16;
-  // The MFMA kernels take 16-token blocks; the split kernel also takes blocks of 16 << j tokens
-  // (up to 1024) as 16-token tiles, and head_dim 256 on 16-token blocks.  Other shapes take the
-  // VALU kernel.
-  int lsb = 0;
-  while (lsb < 6 && (kBlockTokens << lsb) < args.block_tokens) ++lsb;
-  const bool tiles = (kBlockTokens << lsb) == args.block_tokens;
-  const bool fast = shape && args.block_tokens == kBlockTokens;
-  const bool wide = DT != PA_F32 && D == 256 && args.group <= 16 && args.block_tokens == kBlockTokens;
   args.part_cost = kPartCost;
   args.ctx_cost = kCtxCost;
-  // The split kernel indexes the weighted tiles of all (sequence, KV head) pairs with int32.
-  const bool split = ((shape && tiles) || wide) && args.num_seqs <= kMaxScanSeqs &&
-                     int64_t{args.num_seqs} * args.hkv *
-                             ((int64_t{args.max_blocks} << lsb) + int64_t{args.part_cost} * (args.max_parts + 1) +
-                              args.ctx_cost) <
-                         0x7fffffffLL;
   args.run_grid = 0;
   args.run_rounds = 0;
-  if (split && args.num_groups > 0 && !wide) {
-    // Group contexts span several members' blocks: their partitions index the larger slot range.
-    args.max_parts = args.slot_parts;
-  } else {
-    args.num_groups = 0;  // the other kernels take every sequence on its own
-  }
-  if (split) {
+  if (!plan.group) args.num_groups = 0;  // every sequence on its own
+  if (plan.route == kRouteSplit) {
     // One launch: the split kernel merges its runs in place; it counts in 16-token tiles.
-    args.sub_log2 = lsb;
-    args.part_blocks <<= lsb;
+    args.sub_log2 = plan.sub_log2;
+    args.part_blocks <<= plan.sub_log2;
     if constexpr (DT != PA_F32) {
       if (D == 64) return launch_split_blocks<DT, 64>(&args, st, start, stop);
       if (D == 256) return launch_split_blocks<DT, 256>(&args, st, start, stop);
       return launch_split_blocks<DT, 128>(&args, st, start, stop);
     }
+    return PA_ERR_UNSUPPORTED;
   }
   // The per-partition kernels need the merge kernel when a context spans several partitions.
   const bool merge = args.max_parts > 1;
   hipEvent_t main_stop = merge ? nullptr : stop;
-  if (fast) {
+  if (plan.route == kRouteMfma) {
     const int64_t nwg = int64_t{args.max_parts} * args.hkv * args.num_seqs;
     if (nwg > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
     if constexpr (DT != PA_F32) {
@@ -1567,6 +1599,16 @@ int32_t launch_decode(DecodeArgs args, hipStream_t st, hipEvent_t start, hipEven
 extern "C" size_t paged_attention_workspace_bytes(const pa_decode_params* p) {
   Plan plan;
   return make_plan(p, &plan) == PA_OK ? plan.workspace : 0;
+}
+
+extern "C" const char* paged_attention_decode_kernel(const pa_decode_params* p) {
+  Plan plan;
+  if (make_plan(p, &plan) != PA_OK || p->num_seqs == 0) return "";
+  switch (plan.route) {
+    case kRouteSplit: return "decode_split_kernel";
+    case kRouteMfma: return "decode_mfma_kernel";
+    default: return "decode_generic_kernel";
+  }
 }
 
 extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -1596,10 +1638,8 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = out;
-  a.part_o = static_cast<float*>(p->workspace);
-  a.part_ml = a.part_o ? a.part_o + static_cast<size_t>(p->num_seqs) * p->num_q_heads * plan.slot_parts *
-                                        p->cache.head_dim
-                       : nullptr;
+  a.part_o = plan.workspace > 0 ? static_cast<float*>(p->workspace) : nullptr;
+  a.part_ml = a.part_o ? a.part_o + plan.ml_offset : nullptr;
   a.scale_log2 = scale * kLog2e;
   a.num_seqs = p->num_seqs;
   a.hq = p->num_q_heads;
@@ -1611,13 +1651,13 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   a.part_blocks = plan.part_blocks;
   a.block_tokens = p->cache.block_size;
   a.max_parts = plan.max_parts;
-  a.slot_parts = plan.slot_parts;
+  a.part_cols = plan.part_cols;
   a.out_f32 = p->out_dtype == PA_F32 ? 1 : 0;
   a.num_blocks = p->cache.num_blocks;
-  a.run_done = plan.slot_parts > 1
+  a.run_done = (plan.route == kRouteSplit && plan.workspace > 0)
                    ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(p->workspace) + plan.counter_offset)
                    : nullptr;
-  if (p->shared && p->shared->num_groups > 0) {
+  if (plan.group) {
     a.share_groups = p->shared->groups;
     a.num_groups = p->shared->num_groups;
   }
@@ -1633,9 +1673,9 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   int32_t rc;
   hipEvent_t start = static_cast<hipEvent_t>(p->start_event), stop = static_cast<hipEvent_t>(p->stop_event);
   switch (p->cache.dtype) {
-    case PA_F32: rc = launch_decode<PA_F32>(a, stream, start, stop); break;
-    case PA_BF16: rc = launch_decode<PA_BF16>(a, stream, start, stop); break;
-    default: rc = launch_decode<PA_F16>(a, stream, start, stop); break;
+    case PA_F32: rc = launch_decode<PA_F32>(a, plan, stream, start, stop); break;
+    case PA_BF16: rc = launch_decode<PA_BF16>(a, plan, stream, start, stop); break;
+    default: rc = launch_decode<PA_F16>(a, plan, stream, start, stop); break;
   }
   if (rc != PA_OK) return rc;
   return PA_HIP_STATUS("paged_attention_decode", hipGetLastError());

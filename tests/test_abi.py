@@ -47,24 +47,86 @@ def _params(**kw):
     return p
 
 
+def _split_ws(cols, d, contexts):
+    # decode_split_kernel: at most 1024 runs, each with two partial slots of `cols` query columns
+    # (output row + max + sum), then one uint64 arrival counter per (sequence, KV head)
+    return 1024 * 2 * cols * (d + 2) * 4 + contexts * 8
+
+
+def _part_ws(S, hq, parts, d):
+    # per-partition kernels: a partial (output row + max + sum) per (sequence, query head, partition)
+    return S * hq * parts * (d + 2) * 4
+
+
 def test_workspace_bytes():
     ws = pa.lib.paged_attention_workspace_bytes
     assert ws(ctypes.byref(_params())) == 0                      # one partition: no workspace
+    # long context on the split kernel: 8 query columns per KV head; the size does not grow with the context
     p = _params(S=4, hq=64, hkv=8, d=128, maxb=8192, maxctx=131072, dtype=pa.PA_BF16, out=pa.PA_F32)
-    # partials (output row + max + sum per query head and partition), then S * H_kv uint64
-    # arrival counters
-    def expect(S, hq, hkv, parts, d):
-        return S * hq * parts * (d + 2) * 4 + S * hkv * 8
-    assert ws(ctypes.byref(p)) == expect(4, 64, 8, 256, 128)
+    assert ws(ctypes.byref(p)) == _split_ws(8, 128, 4 * 8)
+    p = _params(S=4, hq=64, hkv=8, d=128, maxb=1024, maxctx=16384, dtype=pa.PA_BF16, out=pa.PA_F32)
+    assert ws(ctypes.byref(p)) == _split_ws(8, 128, 4 * 8)
+    # fp32 takes the per-partition VALU kernel
     p = _params(maxb=100, maxctx=1000, part=256)
-    assert ws(ctypes.byref(p)) == expect(4, 4, 4, 4, 64)
+    assert ws(ctypes.byref(p)) == _part_ws(4, 4, 4, 64)
     # 32-token blocks: the table covers 100 * 32 tokens; default partitions of 512 tokens
     p = _params(maxb=100, maxctx=5000, bs=32)
-    assert ws(ctypes.byref(p)) == expect(4, 4, 4, 7, 64)          # min(5000, 3200) / 512 -> 7
+    assert ws(ctypes.byref(p)) == _part_ws(4, 4, 7, 64)          # min(5000, 3200) / 512 -> 7
     # 48-token blocks: the default partition rounds 512 down to 480
     p = _params(maxb=100, maxctx=1000, bs=48)
-    assert ws(ctypes.byref(p)) == expect(4, 4, 4, 3, 64)
+    assert ws(ctypes.byref(p)) == _part_ws(4, 4, 3, 64)
+    # more than 2048 sequences: the per-partition MFMA kernel
+    p = _params(S=3000, hq=8, hkv=2, d=128, maxb=64, maxctx=1024, dtype=pa.PA_BF16)
+    assert ws(ctypes.byref(p)) == _part_ws(3000, 8, 2, 128)
     assert ws(None) == 0
+
+
+@pytest.mark.parametrize("dtype,d,g,S,bs,kernel", [
+    (pa.PA_BF16, 128, 1, 64, 16, "decode_split_kernel"),
+    (pa.PA_F16, 64, 16, 2048, 16, "decode_split_kernel"),
+    (pa.PA_BF16, 128, 4, 2049, 16, "decode_mfma_kernel"),
+    (pa.PA_BF16, 128, 4, 64, 32, "decode_split_kernel"),
+    (pa.PA_BF16, 64, 8, 64, 1024, "decode_split_kernel"),
+    (pa.PA_BF16, 128, 4, 4096, 32, "decode_generic_kernel"),
+    (pa.PA_BF16, 128, 4, 64, 48, "decode_generic_kernel"),
+    (pa.PA_BF16, 128, 4, 64, 8, "decode_generic_kernel"),
+    (pa.PA_BF16, 256, 4, 64, 16, "decode_split_kernel"),
+    (pa.PA_BF16, 256, 4, 64, 32, "decode_generic_kernel"),
+    (pa.PA_BF16, 256, 4, 4096, 16, "decode_generic_kernel"),
+    (pa.PA_BF16, 128, 32, 64, 16, "decode_generic_kernel"),
+    (pa.PA_BF16, 96, 4, 64, 16, "decode_generic_kernel"),
+    (pa.PA_F32, 128, 1, 64, 16, "decode_generic_kernel"),
+])
+def test_decode_kernel_query(dtype, d, g, S, bs, kernel):
+    # The library names the kernel its own dispatch picks (no device needed).
+    p = _params(S=S, hq=4 * g, hkv=4, d=d, bs=bs, maxb=64, maxctx=64 * bs, dtype=dtype)
+    assert pa.lib.paged_attention_decode_kernel(ctypes.byref(p)) == kernel.encode()
+    assert pa.lib.paged_attention_decode_kernel(ctypes.byref(_params(S=0))) == b""
+    assert pa.lib.paged_attention_decode_kernel(ctypes.byref(_params(hq=6))) == b""
+    assert pa.lib.paged_attention_decode_kernel(None) == b""
+
+
+def test_decode_binding_checks_metadata_shapes():
+    # The kernels read context_lens[s] and table row s for every s < S: undersized metadata is rejected
+    # before anything touches a device (these tensors are on the host; the shape check comes first).
+    import torch
+    q = torch.zeros(4, 8, 64, dtype=torch.bfloat16)
+    out = torch.zeros(4, 8, 64)
+    kc = torch.zeros(8, 2, 8, 16, 8, dtype=torch.bfloat16)
+    vc = torch.zeros(8, 2, 64, 16, dtype=torch.bfloat16)
+    lens = torch.ones(4, dtype=torch.int32)
+    tables = torch.zeros(4, 2, dtype=torch.int32)
+    for bt, cl, msg in ((torch.zeros(3, 2, dtype=torch.int32), lens, "block_tables"),
+                        (torch.zeros(8, dtype=torch.int32), lens, "block_tables"),
+                        (torch.zeros(4, 0, dtype=torch.int32), lens, "block_tables"),
+                        (tables, torch.ones(3, dtype=torch.int32), "context_lens"),
+                        (tables, torch.ones(4, 1, dtype=torch.int32), "context_lens")):
+        with pytest.raises(ValueError, match=msg):
+            pa.paged_attention_decode(q, kc, vc, bt, cl, 0.125, out, max_context_len=16)
+    with pytest.raises(ValueError, match="q must be"):
+        pa.paged_attention_decode(q[0], kc, vc, tables, lens, 0.125, out, max_context_len=16)
+    with pytest.raises(ValueError, match="on the GPU"):       # well-shaped host tensors: the device check
+        pa.paged_attention_decode(q, kc, vc, tables, lens, 0.125, out, max_context_len=16)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -126,21 +188,22 @@ def test_workspace_bytes_with_shared_prefixes():
     ws = pa.lib.paged_attention_workspace_bytes
     sh = pa.SharedPrefix(None, 0)
 
-    def expect(S, hq, hkv, parts, d):
-        return S * hq * parts * (d + 2) * 4 + S * hkv * 8
+    def shared(**kw):
+        p = _params(dtype=pa.PA_BF16, **kw)
+        p.shared = ctypes.pointer(sh)
+        return p
 
     # a group holds min(32 / g, S) members' blocks: 8 members (g = 4) of 4 blocks = 1 partition of 512
-    p = _params(S=8, hq=8, hkv=2, d=64)
-    p.shared = ctypes.pointer(sh)
-    assert ws(ctypes.byref(p)) == 0
-    # 8 members of 32 blocks = 8 partitions of 512 tokens
-    p = _params(S=8, hq=8, hkv=2, d=64, maxb=32, maxctx=512)
-    p.shared = ctypes.pointer(sh)
-    assert ws(ctypes.byref(p)) == expect(8, 8, 2, 8, 64)
-    # MHA: at most the batch's 3 sequences per group, 63 blocks each -> ceil(189 / 16) partitions of 256
-    p = _params(S=3, hq=4, hkv=4, d=64, maxb=100, maxctx=1000, part=256)
-    p.shared = ctypes.pointer(sh)
-    assert ws(ctypes.byref(p)) == expect(3, 4, 4, 12, 64)
+    assert ws(ctypes.byref(shared(S=8, hq=8, hkv=2, d=64))) == 0
+    # 8 members of 32 blocks = 8 partitions of 512 tokens: partial slots of 32 query columns per run
+    assert ws(ctypes.byref(shared(S=8, hq=8, hkv=2, d=64, maxb=32, maxctx=512))) == _split_ws(32, 64, 8 * 2)
+    # the same without sharing: one partition per sequence, no workspace
+    assert ws(ctypes.byref(_params(S=8, hq=8, hkv=2, d=64, maxb=32, maxctx=512, dtype=pa.PA_BF16))) == 0
+    # MHA: at most the batch's 3 sequences per group, 63 blocks each -> 12 partitions of 256
+    assert ws(ctypes.byref(shared(S=3, hq=4, hkv=4, d=64, maxb=100, maxctx=1000, part=256))) == \
+        _split_ws(32, 64, 3 * 4)
+    # head_dim 256 runs sequence by sequence: its partials have g columns
+    assert ws(ctypes.byref(shared(S=3, hq=8, hkv=2, d=256, maxb=100, maxctx=1000))) == _split_ws(4, 256, 3 * 2)
     # more groups than sequences, a negative count, or groups without an array: rejected
     for bad in (pa.SharedPrefix(None, 5), pa.SharedPrefix(None, -1), pa.SharedPrefix(None, 1)):
         p = _params(S=4)
