@@ -1,29 +1,34 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the paged KV cache on one MI355X.
 
-A step is one decode step of one attention layer over a batch of sequences:
-the C++ allocator appends one token per sequence (copy-on-write where blocks are
+A step is one decode step of one attention layer over a batch of sequences: the
+C++ allocator appends one token per sequence (copy-on-write where blocks are
 shared), the step's slot mapping / block tables go to the device, then
-block_copy -> kv_append -> paged_attention_decode (+ partition merge) run on one
-stream.  Inputs (cache contents, per-step q and new K/V) are resident in HBM
-before the timed region starts.
+block_copy -> kv_append -> paged_attention_decode run on one stream.  Inputs
+(cache contents, per-step q and new K/V) are resident in HBM before the timed
+region starts.
 
-Default workload: bf16 MHA decode, 64 sequences, context lengths U[128, 2048],
-32 query / 32 KV heads, head_dim 128, 16-token blocks in a shuffled pool.
-The first timed step attends over exactly those lengths; each later step one
-token more.  --block-size 32 (64, ...) lays the same sequences out in a pool of
-larger blocks, --head-dim 256 (or 64) gives them another head size (MHA, GQA and
-long-context workloads).
+By default every workload runs in turn, each with --warmup untimed and --steps
+timed steps, and one JSON line reports them all:
+  c1  tiny fp32 MHA decode, contexts {1, 15, 16, 33}, 4 heads, head_dim 64 (launch-bound: microseconds)
+  c2  bf16 MHA decode, 64 sequences, contexts U[128, 2048], 32/32 heads, head_dim 128
+  c3  bf16 GQA decode, 256 sequences, log-normal contexts (median 1024, clipped to [16, 8192]),
+      64/8 heads, 30% of the pool held by another sequence
+  c4  parallel sampling: 64 prompts x 8 samples on a shared 1000-token prefix, 32/8 heads,
+      copy-on-write at the first appended token (bytes counted once per physical block)
+  c5  long context: 4 sequences of 131072 tokens, 64/8 heads, 512-token partitions
+The headline (top-level value, config, roofline, cpu_baseline) is c5, the
+largest single-GPU workload; the others sit under "configs".  --workload picks
+one of them alone (or "prefill": chunked prefill attention on c2's sequences).
 
-Prints one JSON line: value = algorithmic HBM bytes of the whole step / step
-time (GB/s), plus seq-tokens/s per layer, the main attention kernel's roofline
-(bytes / its HIP-event-timed duration against 8 TB/s) and the fp64 oracle timed
-on the host as a CPU baseline.
+value = algorithmic HBM bytes of the whole step / step time (GB/s).  roofline =
+the main attention kernel's algorithmic bytes / its HIP-event-timed duration
+against 8 TB/s.  cpu_baseline = the fp64 oracle on a bounded sample of the same
+workload, on the host's cores.
 """
 import argparse
 import gc
 import json
-import math
 import os
 import sys
 import time
@@ -32,27 +37,42 @@ METRIC = "decode attention achieved HBM GB/s (% of peak) + seq-tokens/sec per la
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 FOREIGN = -1
+WORKLOADS = {"c1": "c1_tiny_f32", "c2": "c2_mha_bf16", "c3": "c3_gqa_bf16", "c4": "c4_cow_sampling_bf16",
+             "c5": "c5_long_bf16"}
+HEADLINE = "c5"
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=55)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5", "prefill"],
-                    help="decode workloads c2..c5; 'prefill' times chunked prefill attention on c2's sequences")
+    ap.add_argument("--workload", default="all", choices=["all", "c1", "c2", "c3", "c4", "c5", "prefill"],
+                    help="all decode workloads (default), one of them, or chunked prefill on c2's sequences")
+    ap.add_argument("--dtype", default="", choices=["", "bf16", "f16"],
+                    help="16-bit type of the c2/c3/c4/c5 caches (default: the workload's bf16)")
     ap.add_argument("--chunk", type=int, default=512, help="prefill: chunk rows per sequence (at most its length)")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-context partition in tokens (0 = the workload's own)")
     ap.add_argument("--block-size", type=int, default=16,
-                    help="decode c2/c3/c5: tokens per cache block (16; 32, 64, ... stream as 16-token tiles)")
+                    help="decode c2/c3/c5: tokens per cache block (16; 8, 32, 64, ...)")
     ap.add_argument("--head-dim", type=int, default=0,
                     help="decode c2/c3/c5: head_dim other than the workload's 128 (64 or 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget for the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time budget of the headline CPU baseline (the other workloads get a third)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size before the steps (counter calibration)")
     return ap.parse_args()
+
+
+def host_threads():
+    """Host cores this process may use: its CPU affinity, capped by OMP_NUM_THREADS when set."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
 
 
 def main():
@@ -65,27 +85,20 @@ def main():
     if args.workload == "prefill":
         run_prefill(args)
         return
-    BS = args.block_size
-    if (BS != 16 or args.head_dim) and args.workload == "c4":
-        sys.exit("bench.py: the sampling workload runs on 16-token blocks and head_dim 128 only")
+    names = list(WORKLOADS) if args.workload == "all" else [args.workload]
+    if (args.block_size != 16 or args.head_dim) and "c4" in names:
+        if args.workload == "c4":
+            sys.exit("bench.py: the sampling workload runs on 16-token blocks and head_dim 128 only")
+        names.remove("c4")
+    if args.dtype and "c1" in names and args.workload == "all":
+        names.remove("c1")  # the tiny workload is fp32 by definition
 
-    import numpy as np
     import torch
-
-    import synth
-    from paged_kv_cache_358_amd.engine import PagedDecodeLayer
+    from concurrent.futures import ThreadPoolExecutor
 
     torch.cuda.init()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    W, K = args.warmup, args.steps
-    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
-
-    def up(a, dtype):
-        a = np.ascontiguousarray(a)
-        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" else torch.from_numpy(a)
-        return t.to(dev)
-
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -94,9 +107,72 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ------------------------------------------------------------------ workload
-    if args.workload == "c4":
+    blocks = {}
+    with ThreadPoolExecutor(max_workers=host_threads()) as pool:
+        for w in names:
+            blocks[w] = run_decode(args, w, dev, pool)
+            gc.collect()
+            torch.cuda.empty_cache()
+    head_key = HEADLINE if HEADLINE in blocks else names[0]
+    head = blocks[head_key]
+    result = {k: head[k] for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                                   "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config")}
+    for k, v in head.items():
+        if k not in result and k not in ("cpu_oracle", "metric"):
+            result[k] = v
+    if not args.no_cpu_baseline and "cpu_oracle" in head:
+        result["cpu_baseline"] = head["cpu_oracle"]
+    if len(blocks) > 1:
+        result["configs"] = {blocks[w]["config"]["workload"]: config_summary(blocks[w]) for w in names}
+    print(json.dumps(result), flush=True)
+
+
+def config_summary(b):
+    """The per-workload record inside the headline line."""
+    keys = ("ms_per_step", "value", "unit", "pct_of_peak_hbm", "seq_tokens_per_s_per_layer",
+            "context_tokens_per_s_per_layer", "dtype", "steps", "warmup", "kernel", "kernel_us", "roofline",
+            "copy_on_write_blocks", "shared_prefix_groups", "logical_attention_bytes_per_launch",
+            "effective_logical_gbs", "cache_ops", "decode_probes", "cpu_oracle", "cpu_oracle_1_thread", "note")
+    out = {"config": b["config"]}
+    out.update({k: b[k] for k in keys if k in b})
+    return out
+
+
+# ---------------------------------------------------------------------------------------- workloads
+def _up(a, dtype, dev):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" else torch.from_numpy(a)
+    return t.to(dev)
+
+
+def _draw_heads(pool, fn, heads):
+    """K and V [n, H_kv, D] of one sequence, its KV heads drawn in parallel (each head has its own seed
+    stream, so the values do not depend on the split)."""
+    import numpy as np
+    parts = list(pool.map(lambda h: fn([h]), heads))
+    return (np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1))
+
+
+def run_decode(args, w, dev, pool):
+    import numpy as np
+    import torch
+
+    import synth
+    import paged_kv_cache_358_amd as pa
+    from paged_kv_cache_358_amd.engine import PagedDecodeLayer
+
+    W, K = args.warmup, args.steps
+    BS = args.block_size if w != "c4" else 16
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+    t_setup = time.perf_counter()
+
+    if w == "c4":
         cfg = synth.C4
+        if args.dtype:
+            import dataclasses
+            cfg = dataclasses.replace(cfg, dtype=args.dtype, name=cfg.name.replace("bf16", args.dtype))
         part = args.partition_size or cfg.partition_size
         if W + K > cfg.steps:
             sys.exit(f"c4 runs at most {cfg.steps} decode steps")
@@ -104,35 +180,49 @@ def main():
         max_blocks = -(-(cfg.prefix_len + cfg.steps) // 16)
         layer = PagedDecodeLayer(cfg.pool_blocks(), hkv, D, hq, tdt[dtype], S, max_blocks,
                                  free_order=cfg.free_order(), partition_size=part, device=dev)
+        heads = list(range(hkv))
         for i in range(cfg.num_prompts):
             root = i * cfg.samples
-            k, v = cfg.prefix_kv(i)
+            k, v = _draw_heads(pool, lambda hs: cfg.prefix_kv(i, hs), heads)
             layer.add(root)
-            layer.prefill(root, up(k, dtype), up(v, dtype))
+            layer.prefill(root, _up(k, dtype, dev), _up(v, dtype, dev))
             for c in range(1, cfg.samples):
                 layer.fork(root, root + c)
-        step_inputs = []
-        for st in range(1, W + K + 1):
-            kn, vn = cfg.step_kv(st)
-            step_inputs.append((up(cfg.step_q(st), dtype), up(kn, dtype), up(vn, dtype)))
+        steps = list(range(1, W + K + 1))
+        drawn = list(pool.map(lambda st: (cfg.step_q(st), *cfg.step_kv(st)), steps))
+        step_inputs = [tuple(_up(x, dtype, dev) for x in d) for d in drawn]
         scale = cfg.softmax_scale
         kvbpt = cfg.kv_bytes_per_token()
         workload = {"workload": cfg.name, "prompts": cfg.num_prompts, "samples": cfg.samples,
                     "prefix_len": cfg.prefix_len, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D,
-                    "block_size": 16, "partition_size": part,
-                    "timed_steps": f"{W + 1}..{W + K}"}
+                    "block_size": 16, "partition_size": part, "timed_steps": f"{W + 1}..{W + K}"}
         lens0 = None
     else:
-        cfg = synth.CONFIGS[{"c2": "c2_mha_bf16", "c3": "c3_gqa_bf16", "c5": "c5_long_bf16"}[args.workload]]
-        suffix = (f"_d{args.head_dim}" if args.head_dim else "") + (f"_b{BS}" if BS != 16 else "")
-        if suffix:  # the same context lengths with another head size, or in a pool of larger blocks
-            cfg = synth.scaled(cfg, name_suffix=suffix, block_size=BS, head_dim=args.head_dim or cfg.head_dim)
+        cfg = synth.CONFIGS[WORKLOADS[w]]
+        kw = {}
+        suffix = ""
+        if args.head_dim and w != "c1":
+            kw["head_dim"] = args.head_dim
+            suffix += f"_d{args.head_dim}"
+        if BS != 16 and w != "c1":
+            kw["block_size"] = BS
+            suffix += f"_b{BS}"
+        if args.dtype and w != "c1" and args.dtype != cfg.dtype:
+            kw["dtype"] = args.dtype
+        if kw:  # the same context lengths with another head size, block size or 16-bit type
+            import dataclasses
+            name = cfg.name + suffix
+            if "dtype" in kw:
+                name = name.replace("_" + cfg.dtype, "_" + args.dtype)
+            cfg = dataclasses.replace(cfg, name=name, **kw)
+        BS = cfg.block_size
         part = args.partition_size or cfg.partition_size
-        if W + K > cfg.pool_slack_tokens:
-            sys.exit(f"{cfg.name}: warmup + steps must be <= {cfg.pool_slack_tokens}")
         S, hq, hkv, D, dtype = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.dtype
         lens0 = synth.context_lens(cfg)                # context at the first timed step
         plan = synth.pool_plan(cfg, lens0)
+        need = int(synth.blocks_for(lens0 + K, BS).sum()) + plan.preoccupy_blocks
+        if need > plan.num_blocks:
+            sys.exit(f"{cfg.name}: {K} steps need {need} blocks, the pool holds {plan.num_blocks}")
         prefill = np.maximum(lens0 - W - 1, 0)
         max_blocks = int(synth.blocks_for(lens0.max() + K, BS))
         layer = PagedDecodeLayer(plan.num_blocks, hkv, D, hq, tdt[dtype], S, max_blocks,
@@ -140,25 +230,31 @@ def main():
         if plan.preoccupy_blocks:
             layer.alloc.add(FOREIGN)
             layer.alloc.append(FOREIGN, plan.preoccupy_blocks * BS)
+        heads = list(range(hkv))
         for s in range(S):
             layer.add(s)
             if prefill[s]:
-                k, v = synth.seq_kv(cfg, s, int(prefill[s]))
-                layer.prefill(s, up(k, dtype), up(v, dtype))
-        step_inputs = []
-        for st in range(W + K):
-            kn, vn = synth.new_tokens_kv(cfg.cfg_id, 1000 + st, S, hkv, D, dtype)
-            step_inputs.append((up(synth.queries(cfg, step=1000 + st), dtype), up(kn, dtype), up(vn, dtype)))
+                k, v = _draw_heads(pool, lambda hs: synth.seq_kv(cfg, s, int(prefill[s]), hs), heads)
+                layer.prefill(s, _up(k, dtype, dev), _up(v, dtype, dev))
+        drawn = list(pool.map(lambda st: (synth.queries(cfg, step=1000 + st),
+                                          *synth.new_tokens_kv(cfg.cfg_id, 1000 + st, S, hkv, D, dtype)),
+                              range(W + K)))
+        step_inputs = [tuple(_up(x, dtype, dev) for x in d) for d in drawn]
         scale = cfg.softmax_scale
         kvbpt = cfg.kv_bytes_per_token()
         workload = {"workload": cfg.name, "num_seqs": S, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D,
                     "block_size": BS, "partition_size": part, "context_lens": cfg.lens,
                     "mean_context": float(lens0.mean()), "pool_blocks": plan.num_blocks}
+    del drawn
     torch.cuda.synchronize()
-    print(f"[bench] {workload['workload']}: workload resident on the GPU", file=sys.stderr, flush=True)
+    print(f"[bench] {workload['workload']}: workload resident on the GPU "
+          f"({time.perf_counter() - t_setup:.1f} s)", file=sys.stderr, flush=True)
     seqs = np.arange(S, dtype=np.int64)
     eb = synth.ELEM_BYTES[dtype]
     out = torch.empty(S, hq, D, dtype=tdt[dtype], device=dev)
+    kernel = pa.paged_attention_decode_kernel(step_inputs[0][0], layer.k_cache, layer.v_cache,
+                                              torch.empty(S, max_blocks, dtype=torch.int32, device=dev), out,
+                                              max_blocks * BS, part)
 
     for i in range(W):
         q, kn, vn = step_inputs[i]
@@ -178,12 +274,12 @@ def main():
     # milliseconds; collect now and keep everything allocated so far out of later passes.
     gc.collect()
     gc.freeze()
-    shared = args.workload == "c4"  # forked samples share blocks: count each physical block once
+    shared = w == "c4"  # forked samples share blocks: count each physical block once
     step_lens, step_pairs = [], []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     step_groups, step_group_rows = [], []
     first_tables = None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for i in range(K):
         q, kn, vn = step_inputs[W + i]
         step_pairs.append(layer.decode_step(seqs, q, kn, vn, out, scale, timing=events[i]))
@@ -195,9 +291,10 @@ def main():
     t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.unfreeze()
     elapsed = t1 - t0
-    print(f"[bench] {K} timed steps: {elapsed / K * 1e3:.3f} ms/step (host enqueue done after "
-          f"{(t_enq - t0) / K * 1e3:.3f} ms/step)", file=sys.stderr, flush=True)
+    print(f"[bench] {workload['workload']}: {K} timed steps, {elapsed / K * 1e3:.3f} ms/step (host enqueue done "
+          f"after {(t_enq - t0) / K * 1e3:.3f} ms/step)", file=sys.stderr, flush=True)
 
     # The events ride on the attention call's launch: start to end of the split kernel, which
     # merges split contexts itself (over groups of forked samples when they share blocks).
@@ -242,9 +339,8 @@ def main():
     value = total_bytes / elapsed / 1e9
     mean_main_s = float(np.mean(main_ms)) / 1e3
     achieved = float(np.mean(attn)) / mean_main_s / 1e9
-    kernel = main_kernel_name(dtype, D, hq // hkv, S, BS)
 
-    result = {
+    block = {
         "metric": METRIC,
         "value": round(value, 1),
         "unit": "GB/s",
@@ -261,6 +357,8 @@ def main():
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
         "seq_tokens_per_s_per_layer": round(S / (elapsed / K), 1),
         "context_tokens_per_s_per_layer": round(float(np.mean([np.sum(l) for l in step_lens])) / (elapsed / K), 1),
+        "kernel": kernel,
+        "kernel_us": round(mean_main_s * 1e6, 2),
         "attention_ms": {"main_kernel": round(float(np.mean(main_ms)), 4)},
         "shared_prefix_groups": int(max(step_groups)),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -269,19 +367,28 @@ def main():
                      "kernel": kernel, "bytes_per_launch": int(np.mean(attn))},
         "copy_on_write_blocks": int(sum(step_pairs)),
     }
+    if w == "c1":
+        block["note"] = ("launch-bound: the step moves about 0.15 MB, 20 ns at peak; its figures are "
+                         "microseconds, not a fraction of the HBM roofline")
     if shared:
-        result["logical_attention_bytes_per_launch"] = int(np.mean(logical))
-        result["effective_logical_gbs"] = round(float(np.mean(logical)) / mean_main_s / 1e9, 1)
+        block["logical_attention_bytes_per_launch"] = int(np.mean(logical))
+        block["effective_logical_gbs"] = round(float(np.mean(logical)) / mean_main_s / 1e9, 1)
 
     last_tables = layer.last_tables.copy()
-    result["cache_ops"] = cache_ops_probe(layer, step_inputs[-1], last_tables, block_bytes)
-    if not shared:
-        result["decode_probes"] = decode_probes(layer, step_inputs[-1][0], out, scale, last_tables,
-                                                step_lens[-1], part, attn[-1])
+    block["cache_ops"] = cache_ops_probe(layer, step_inputs[-1], last_tables, block_bytes)
+    if not shared and w != "c1":
+        block["decode_probes"] = decode_probes(layer, step_inputs[-1][0], out, scale, last_tables,
+                                               step_lens[-1], part, attn[-1])
+    del layer, step_inputs, out
+    gc.collect()
+    torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args, cfg, lens0, kvbpt)
-    print(json.dumps(result), flush=True)
+        budget = args.cpu_seconds if w == HEADLINE else args.cpu_seconds / 3
+        block["cpu_oracle"] = cpu_oracle(cfg, lens0, kvbpt, budget, host_threads(), pool)
+        if w == "c2":
+            block["cpu_oracle_1_thread"] = cpu_oracle(cfg, lens0, kvbpt, args.cpu_seconds / 3, 1, pool)
+    return block
 
 
 def cache_ops_probe(layer, step_input, tables, block_bytes, reps=20, max_pairs=448):
@@ -473,20 +580,6 @@ def run_prefill(args):
     }), flush=True)
 
 
-def main_kernel_name(dtype, head_dim, group, num_seqs, block_size=16):
-    """The library's dominant kernel for this shape (its dispatch rule, restated)."""
-    tiles = block_size in [16 << j for j in range(7)]
-    if dtype == "f32" or group > 16:
-        return "decode_generic_kernel"
-    if head_dim == 256:
-        return "decode_split_kernel" if block_size == 16 and num_seqs <= 2048 else "decode_generic_kernel"
-    if head_dim not in (64, 128) or not tiles:
-        return "decode_generic_kernel"
-    if num_seqs <= 2048:
-        return "decode_split_kernel"
-    return "decode_mfma_kernel" if block_size == 16 else "decode_generic_kernel"
-
-
 def kernel_code_hash(path):
     """sha256[:16] of a source file's code: comments and blank lines removed, so that edits to
     comments alone leave measurements taken on the file valid."""
@@ -516,55 +609,67 @@ def measured_traffic(kernel, workload, steps=None):
     return None
 
 
-def cpu_baseline(args, cfg, lens0, kvbpt):
-    """The fp64 oracle on a bounded sample of the same workload, one host thread."""
+def cpu_oracle(cfg, lens0, kvbpt, budget_s, threads, pool):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload with `threads` BLAS
+    threads.  Sequences are drawn one at a time in a seeded order (each drawn once, its inputs decoded
+    to float64 beforehand, outside the timing) and the oracle is run on each for its share of the
+    budget.  A long-context sequence is sampled by two of its KV heads (and their query heads) and
+    scaled to the whole sequence.  Reports the oracle's K/V GB/s and sequences per second (one decode
+    step of one layer)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import synth
     from oracle.attention import decode_attention_seq
 
+    hkv = cfg.num_kv_heads
     if lens0 is None:  # parallel sampling: every sample at its final context, prefix + appended tokens
         n_ctx = cfg.prefix_len + cfg.steps
-        steps = [cfg.step_kv(t) for t in range(1, cfg.steps + 1)]
+        step_kv = list(pool.map(cfg.step_kv, range(1, cfg.steps + 1)))
 
-        def draw(s):
-            pk, pv = cfg.prefix_kv(s // cfg.samples)
-            return (np.concatenate([pk, np.stack([k[s] for k, _ in steps])]),
-                    np.concatenate([pv, np.stack([v[s] for _, v in steps])]))
+        def draw(s, heads):
+            pk, pv = cfg.prefix_kv(s // cfg.samples, heads)
+            return (np.concatenate([pk, np.stack([k[s][heads] for k, _ in step_kv])]),
+                    np.concatenate([pv, np.stack([v[s][heads] for _, v in step_kv])]))
         lens = [n_ctx] * cfg.num_seqs
+        q = cfg.step_q(cfg.steps)
     else:
-        draw = lambda s: synth.seq_kv(cfg, s, int(lens0[s]))
+        def draw(s, heads):
+            return _draw_heads(pool, lambda hs: synth.seq_kv(cfg, s, int(lens0[s]), hs), heads)
         lens = lens0.tolist()
-    q = synth.queries(cfg) if lens0 is not None else cfg.step_q(cfg.steps)
-    order = np.random.default_rng(0).permutation(len(lens))
-    # One pass over the sequences; each is drawn once and the oracle is re-run on it until its
-    # share of the time budget is used (at least once), so memory stays one sequence deep.
-    share = args.cpu_seconds / len(order)
-    spent, done, ctx_tokens = 0.0, 0, 0
-    with threadpool_limits(limits=1):
+        q = synth.queries(cfg)
+    long_ctx = max(lens) > 65536
+    # at most 8 sequences (2 of a long-context workload), in a seeded order
+    order = np.random.default_rng(0).permutation(len(lens))[:2 if long_ctx else 8]
+    heads = list(range(2)) if long_ctx else list(range(hkv))   # KV heads drawn per sequence
+    g = cfg.num_q_heads // hkv
+    per = budget_s / len(order)
+    spent, done, ctx_tokens = 0.0, 0.0, 0
+    t_all = time.perf_counter()
+    with threadpool_limits(limits=threads):
         for i, s in enumerate(order):
-            k, v = draw(int(s))
+            k, v = draw(int(s), heads)
             k64, v64 = synth.decode_f64(k, cfg.dtype), synth.decode_f64(v, cfg.dtype)
-            q64 = synth.decode_f64(q[s], cfg.dtype)
+            q64 = synth.decode_f64(q[s], cfg.dtype)[heads[0] * g:(heads[-1] + 1) * g]
             mine = 0.0
-            while mine < share or mine == 0.0:
+            while mine < per or mine == 0.0:
                 t = time.perf_counter()
                 decode_attention_seq(q64, k64, v64, cfg.softmax_scale)
                 mine += time.perf_counter() - t
-                done += 1
-                ctx_tokens += int(lens[s])
+                done += len(heads) / hkv
+                ctx_tokens += int(lens[s]) * len(heads) / hkv
             spent += mine
-            if i % 16 == 15 or i == len(order) - 1:
-                print(f"[bench] cpu baseline: {i + 1}/{len(order)} sequences, {spent:.1f} s", file=sys.stderr,
-                      flush=True)
+            if spent >= budget_s or time.perf_counter() - t_all > 3 * budget_s + 30:
+                break
     gbs = ctx_tokens * kvbpt / spent / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seq_tokens_per_s_per_layer": round(done / spent, 2),
-            "sample": f"fp64 oracle, {done} sequence evaluations over all {len(lens)} sequences of the "
-                      f"workload (each drawn once and evaluated until it had {share:.2f} s; all "
-                      f"{cfg.num_q_heads} query heads; {ctx_tokens} context tokens in total), {spent:.1f} s "
-                      f"on 1 host thread; inputs decoded to float64 beforehand"}
+    what = (f"{len(heads)} of {hkv} KV heads ({len(heads) * g} query heads) of {i + 1} sequence(s) of "
+            f"{max(lens)} tokens, scaled to whole sequences" if long_ctx else
+            f"{i + 1} of {len(lens)} sequences (seeded choice), all {cfg.num_q_heads} query heads")
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seq_tokens_per_s_per_layer": round(done / spent, 3),
+            "sample": f"fp64 oracle on {what}: {done:.2f} sequence evaluations, {ctx_tokens:.0f} context "
+                      f"tokens in {spent:.1f} s with {threads} BLAS thread(s); inputs drawn and decoded to "
+                      f"float64 outside the timing"}
 
 
 if __name__ == "__main__":

@@ -1,9 +1,7 @@
 """Host-side rules of bench.py, on the CPU.
 
-* main_kernel_name restates the library's decode dispatch (the kernel whose launches the
-  roofline times): the split kernel for bf16/fp16 with head_dim 64/128 on blocks of 16 << j
-  tokens and head_dim 256 on 16-token blocks (at most 2048 sequences), the per-partition MFMA
-  kernel beyond 2048 sequences on 16-token blocks, the VALU kernel for everything else.
+* the kernel the roofline times is named by the library itself (paged_attention_decode_kernel,
+  tested in test_abi.py), not restated here.
 * kernel_code_hash ignores comments and blank lines, and nothing else.
 * bench.py measures one GPU: asking for more exits with status 2 before touching a device.
 """
@@ -16,26 +14,6 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
-
-
-@pytest.mark.parametrize("args,kernel", [
-    (("bf16", 128, 1, 64, 16), "decode_split_kernel"),
-    (("f16", 64, 16, 2048, 16), "decode_split_kernel"),
-    (("bf16", 128, 4, 2049, 16), "decode_mfma_kernel"),
-    (("bf16", 128, 4, 64, 32), "decode_split_kernel"),
-    (("bf16", 64, 8, 64, 1024), "decode_split_kernel"),
-    (("bf16", 128, 4, 4096, 32), "decode_generic_kernel"),
-    (("bf16", 128, 4, 64, 48), "decode_generic_kernel"),
-    (("bf16", 128, 4, 64, 8), "decode_generic_kernel"),
-    (("bf16", 256, 4, 64, 16), "decode_split_kernel"),
-    (("bf16", 256, 4, 64, 32), "decode_generic_kernel"),
-    (("bf16", 256, 4, 4096, 16), "decode_generic_kernel"),
-    (("bf16", 128, 32, 64, 16), "decode_generic_kernel"),
-    (("bf16", 96, 4, 64, 16), "decode_generic_kernel"),
-    (("f32", 128, 1, 64, 16), "decode_generic_kernel"),
-])
-def test_main_kernel_name(args, kernel):
-    assert bench.main_kernel_name(*args) == kernel
 
 
 def test_kernel_code_hash_ignores_comments_only(tmp_path):
