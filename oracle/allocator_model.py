@@ -12,7 +12,7 @@ Policy, in the order the pages describe it:
 * Appending.  A token is written into the current last block; a new physical
   block is taken from the free pool only when the last one is full, so waste is
   confined to the unfilled slots of the last block (same page, "Single Sequence
-  Generation"; the sketch's "need a new block?" test, read with len = tokens
+  Generation"; the sketch's test for whether the table needs one more block, read with len = tokens
   before this append, so a block is taken exactly when len % B == 0).  The
   token's slot is  table[-1] * B + len % B  (the sketch writes into the last
   block without naming the offset; len % B is the offset its test implies), and
