@@ -1,10 +1,13 @@
 """Build libpagedattn.so (HIP kernels for gfx950 + host allocator) in-tree.
 
-    python paged_kv_cache_358_amd/build.py
+    python paged_kv_cache_358_amd/build.py [--sanitize]
 
 compiles every source under ``csrc/`` with hipcc (HIP files) or g++ (host C++),
 objects under ``_build/`` at the repository root, and links
-``paged_kv_cache_358_amd/libpagedattn.so``.  Always recompiles.
+``paged_kv_cache_358_amd/libpagedattn.so``.  Always recompiles.  ``--sanitize``
+builds ``_build/asan/libpagedattn_asan.so`` instead: the host C++ code with
+AddressSanitizer and UndefinedBehaviorSanitizer (the tests load it through
+``PAGEDATTN_LIB``).
 """
 from __future__ import annotations
 
@@ -71,5 +74,61 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+# Host sanitizers for the C++ allocator and the C ABI's host code: AddressSanitizer and
+# UndefinedBehaviorSanitizer, with g++ and its runtimes.  The HIP objects are the regular ones (no
+# device code is built with a sanitizer); the library is linked by g++ against the HIP runtime.
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+SAN_LIB_PATH = os.path.join(BUILD, "asan", "libpagedattn_asan.so")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Build ``_build/asan/libpagedattn_asan.so``: the host C++ sources with ASan + UBSan, linked with
+    the HIP objects of the regular build (compiled first if missing).  Load it with the sanitizer
+    runtimes preloaded (``sanitizer_env``)."""
+    hipcc = _hipcc()
+    san_dir = os.path.dirname(SAN_LIB_PATH)
+    os.makedirs(san_dir, exist_ok=True)
+    jobs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        if not os.path.exists(obj) or os.path.getmtime(obj) < os.path.getmtime(os.path.join(CSRC, src)):
+            jobs.append((obj, [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+    for src in CXX_SOURCES:
+        obj = os.path.join(san_dir, src + ".o")
+        jobs.append((obj, ["g++", *CXX_FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        outs = list(ex.map(lambda j: _run(j[1]), jobs))
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+    objs = [os.path.join(BUILD, src + ".o") for src in HIP_SOURCES] + \
+           [os.path.join(san_dir, src + ".o") for src in CXX_SOURCES]
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc)))
+    tmp = SAN_LIB_PATH + ".tmp"
+    _run(["g++", "-shared", *SAN_FLAGS, "-o", tmp, *objs, "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+          f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"])
+    os.replace(tmp, SAN_LIB_PATH)
+    return SAN_LIB_PATH
+
+
+def sanitizer_env(env=None) -> dict:
+    """Environment that loads the sanitized library in a fresh Python: the g++ ASan / UBSan runtimes
+    preloaded (the interpreter itself is not instrumented), leak reports off (the interpreter keeps
+    allocations alive at exit), any error fatal."""
+    def runtime(name):
+        return subprocess.run(["g++", f"-print-file-name={name}"], stdout=subprocess.PIPE, text=True,
+                              check=True).stdout.strip()
+    env = dict(os.environ if env is None else env)
+    env["LD_PRELOAD"] = " ".join([runtime("libasan.so"), runtime("libubsan.so")])
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=0:halt_on_error=1:verify_asan_link_order=0"
+    env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1"
+    env["PAGEDATTN_LIB"] = SAN_LIB_PATH
+    return env
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

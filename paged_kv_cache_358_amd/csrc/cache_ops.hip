@@ -8,6 +8,11 @@
 // duplicated (same page, "Copy-on-Write for Parallel Sampling").
 //
 // Both are pure byte movement: bit-exact, no arithmetic on the values.
+#include <cstdlib>
+#include <cstring>
+#include <unordered_set>
+#include <vector>
+
 #include "pa_device.h"
 #include "pa_status.h"
 
@@ -133,6 +138,45 @@ static const void* device_view(const void* p, bool host_only) {
   return (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) ? p : nullptr;
 }
 
+// Debug checks (environment PA_DEBUG_CHECKS set and not "0"): the call reads its device index
+// arrays back to the host (a synchronous copy) and rejects what the kernels leave undefined, before
+// launching anything.
+static bool debug_checks() {
+  const char* e = std::getenv("PA_DEBUG_CHECKS");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
+static int32_t read_back(std::vector<int32_t>* out, const int32_t* dev, size_t n, void* stream, const char* what) {
+  out->resize(n);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipMemcpy(out->data(), dev, n * sizeof(int32_t), hipMemcpyDefault);
+  return PA_HIP_STATUS(what, e);
+}
+
+// Copy pairs whose blocks are in range must have src != dst, distinct destinations, and no destination
+// that is also a source of the same call (the copies run in parallel).
+static bool pairs_ok(const std::vector<int32_t>& v, int64_t num_blocks) {
+  std::unordered_set<int32_t> srcs, dsts;
+  const size_t n = v.size() / 2;
+  for (size_t i = 0; i < n; ++i) {
+    const int32_t s = v[2 * i], d = v[2 * i + 1];
+    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) continue;  // skipped by the kernel
+    if (s == d || !dsts.insert(d).second) return false;
+    srcs.insert(s);
+  }
+  for (int32_t d : dsts)
+    if (srcs.count(d)) return false;
+  return true;
+}
+
+// Slots in range must be distinct (two tokens written to one slot race).
+static bool slots_ok(const std::vector<int32_t>& v, int64_t num_slots) {
+  std::unordered_set<int32_t> seen;
+  for (int32_t s : v)
+    if (s >= 0 && s < num_slots && !seen.insert(s).second) return false;
+  return true;
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -149,6 +193,12 @@ extern "C" int32_t kv_append(const void* k_new, const void* v_new, const int32_t
   const dim3 grid(static_cast<uint32_t>((total + 255) / 256));
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind
+  if (debug_checks()) {
+    std::vector<int32_t> v;
+    const int32_t rc = read_back(&v, slot_mapping, static_cast<size_t>(num_tokens), stream, "kv_append: debug check");
+    if (rc != PA_OK) return rc;
+    if (!slots_ok(v, num_slots)) return PA_ERR_INVALID_ARG;
+  }
   if (eb == 4) {
     hipLaunchKernelGGL(kv_append_kernel<4>, grid, dim3(256), 0, s, static_cast<const uint8_t*>(k_new),
                        static_cast<const uint8_t*>(v_new), slot_mapping, total, static_cast<uint8_t*>(k_cache),
@@ -175,6 +225,12 @@ extern "C" int32_t block_copy(void* k_cache, void* v_cache, const int32_t* pairs
   const int64_t nwg = chunks * num_pairs;
   if (nwg > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
   (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind
+  if (debug_checks()) {
+    std::vector<int32_t> v;
+    const int32_t rc = read_back(&v, pairs, 2 * static_cast<size_t>(num_pairs), stream, "block_copy: debug check");
+    if (rc != PA_OK) return rc;
+    if (!pairs_ok(v, cache->num_blocks)) return PA_ERR_INVALID_ARG;
+  }
   hipLaunchKernelGGL(block_copy_kernel, dim3(static_cast<uint32_t>(nwg), 2), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
                      pairs, cache->num_blocks, block_bytes, chunks);

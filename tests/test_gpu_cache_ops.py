@@ -155,3 +155,38 @@ def test_stage_append_either_part_empty_and_bad_slots():
                                 ctypes.c_void_p(pageable.data_ptr()), 1, ctypes.c_void_p(k_cache.data_ptr()),
                                 ctypes.c_void_p(v_cache.data_ptr()), ctypes.byref(c), None)
     assert rc == pa.PA_ERR_INVALID_ARG
+
+
+def test_debug_checks_reject_undefined_copies_and_appends(monkeypatch):
+    # With PA_DEBUG_CHECKS set, block_copy and kv_append read their index arrays back and refuse what
+    # the kernels leave undefined, launching nothing; valid calls still copy byte for byte.
+    k_cache, v_cache, kh, vh = random_cache(16, 2, 64, "bf16", 7)
+    before_k, before_v = raw_view(k_cache), raw_view(v_cache)
+
+    def pairs(rows):
+        return torch.tensor(rows, dtype=torch.int32, device="cuda")
+
+    bad_pairs = ([[3, 3]],                    # source is the destination
+                 [[1, 5], [2, 5]],            # two copies onto one block
+                 [[1, 5], [5, 6]])            # a destination that another pair reads
+    for rows in bad_pairs:                    # without the checks these are the caller's problem
+        monkeypatch.setenv("PA_DEBUG_CHECKS", "1")
+        with pytest.raises(pa.PagedAttnError) as e:
+            pa.block_copy(k_cache, v_cache, pairs(rows))
+        assert e.value.status == pa.PA_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert np.array_equal(raw_view(k_cache), before_k) and np.array_equal(raw_view(v_cache), before_v)
+    # out-of-range pairs are skipped, not errors; a valid call copies
+    pa.block_copy(k_cache, v_cache, pairs([[1, 5], [2, 6], [99, 3], [-1, 4]]))
+    torch.cuda.synchronize()
+    ek, ev = pl.apply_block_copy(storage_raw(kh, "bf16"), storage_raw(vh, "bf16"), [(1, 5), (2, 6)], 2, 64, 16)
+    assert np.array_equal(raw_view(k_cache), ek) and np.array_equal(raw_view(v_cache), ev)
+
+    new = to_torch(synth.encode(np.ones((3, 2, 64), np.float32), "bf16"), "bf16")
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.kv_append(new, new, torch.tensor([17, 40, 17], dtype=torch.int32, device="cuda"), k_cache, v_cache)
+    assert e.value.status == pa.PA_ERR_INVALID_ARG
+    pa.kv_append(new, new, torch.tensor([17, -1, -1], dtype=torch.int32, device="cuda"), k_cache, v_cache)  # -1: skipped
+    monkeypatch.setenv("PA_DEBUG_CHECKS", "0")
+    pa.block_copy(k_cache, v_cache, pairs([[7, 8]]))                    # checks off: plain launch
+    torch.cuda.synchronize()
