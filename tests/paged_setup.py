@@ -5,6 +5,9 @@ the oracle side sees only the contiguous per-sequence truth from ``synth``.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -14,6 +17,26 @@ from oracle.attention import decode_attention_seq
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 FOREIGN = -1  # id of the sequence that pre-occupies part of the pool
+FRAC_BITS = {"bf16": 7, "f16": 10}
+_POOL = None
+
+
+def pool() -> ThreadPoolExecutor:
+    """Host threads for drawing inputs and running the oracle (numpy releases the GIL in both)."""
+    global _POOL
+    if _POOL is None:
+        _POOL = ThreadPoolExecutor(max_workers=max(1, min(16, len(os.sched_getaffinity(0)))))
+    return _POOL
+
+
+def draw_seq(cfg, s: int, n: int, kv_heads=None):
+    """synth.seq_kv with long sequences drawn one KV head per thread (each head has its own seed
+    stream, so the values are the same)."""
+    heads = list(range(cfg.num_kv_heads) if kv_heads is None else kv_heads)
+    if n * len(heads) < (1 << 16) or len(heads) == 1:
+        return synth.seq_kv(cfg, s, n, heads)
+    parts = list(pool().map(lambda h: synth.seq_kv(cfg, s, n, [h]), heads))
+    return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1)
 
 
 def to_torch(arr: np.ndarray, dtype: str, device="cuda"):
@@ -70,7 +93,7 @@ class PagedDecode:
             assert len(pairs) == 0
             if n == 0:
                 continue
-            k, v = synth.seq_kv(cfg, s, n)
+            k, v = draw_seq(cfg, s, n)
             if keep_truth:
                 self.truth[s] = (k, v)
             pa.kv_append(to_torch(k, cfg.dtype, device), to_torch(v, cfg.dtype, device),
@@ -107,6 +130,29 @@ class PagedDecode:
         return decode_attention_seq(q64, synth.decode_f64(k, cfg.dtype), synth.decode_f64(v, cfg.dtype),
                                     cfg.softmax_scale, heads)
 
+    def oracle_rows(self, s: int, heads) -> np.ndarray:
+        """Oracle for the query heads ``heads`` of sequence s, one KV head at a time (its truth drawn
+        alone), the KV heads in parallel: memory stays one KV head deep per thread."""
+        cfg = self.cfg
+        n = int(self.lens[s])
+        g = cfg.group
+        heads = list(heads)
+        q64 = synth.decode_f64(self.q_np[s], cfg.dtype)
+
+        def one(h):
+            k, v = synth.seq_kv(cfg, s, n, kv_heads=[h])
+            mine = [j for j in heads if j // g == h]
+            rows = decode_attention_seq(q64[h * g:(h + 1) * g], synth.decode_f64(k, cfg.dtype),
+                                        synth.decode_f64(v, cfg.dtype), cfg.softmax_scale,
+                                        [j - h * g for j in mine])
+            return mine, rows
+
+        out = np.empty((len(heads), cfg.head_dim))
+        for mine, rows in pool().map(one, sorted({j // g for j in heads})):
+            for j, r in zip(mine, rows):
+                out[heads.index(j)] = r
+        return out
+
     def oracle_sampled(self, s: int, heads) -> np.ndarray:
         """Oracle for a few query heads, drawing only their KV heads' truth."""
         cfg = self.cfg
@@ -126,3 +172,23 @@ class PagedDecode:
 
 def tol_for(dtype: str) -> float:
     return 1e-5 if dtype == "f32" else 5e-3
+
+
+def half_ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Half the spacing of the 16-bit type's values at |x| (for fp16 at least half its subnormal
+    spacing, 2^-25)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 1e-30)))
+    h = np.exp2(e - FRAC_BITS[dtype] - 1)
+    return np.maximum(h, 2.0 ** -25) if dtype == "f16" else h
+
+
+def check_16bit_output(o16: np.ndarray, o32: np.ndarray, dtype: str):
+    """A 16-bit output is the kernel's fp32 result rounded once: within half an ulp of it."""
+    bad = np.abs(o16 - o32) > half_ulp(o32, dtype)
+    assert not bad.any(), (int(bad.sum()), float(np.max(np.abs(o16 - o32))))
+
+
+def bound_16bit(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """The bound of a 16-bit output against the fp64 oracle: 5e-3 plus half an ulp of the type at the
+    oracle's value (the rounding of the final store)."""
+    return 5e-3 + half_ulp(ref, dtype)
