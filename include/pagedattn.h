@@ -183,6 +183,25 @@ int32_t paged_attention_decode(const void* q, const void* k_cache, const void* v
                                const int32_t* block_tables, const int32_t* context_lens, float scale,
                                void* out, const pa_decode_params* p);
 
+/*
+ * paged_attention_decode_noalloc: paged_attention_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments
+ * and results; p->workspace and p->workspace_bytes are ignored.  The partials and arrival counters live in
+ * a scratch array of paged_attention_noalloc_scratch_bytes() (64 MiB) that the library keeps on each GPU
+ * it runs on until the process ends.  Nothing is allocated per call (no hipMalloc, hipFree or allocating
+ * library routine).  The scratch needs no clearing (the counters carry a per-call tag) and holds the last
+ * call's contents.  Returns PA_ERR_WORKSPACE, launching nothing, when paged_attention_workspace_bytes(p)
+ * exceeds the scratch (large batches on the per-partition kernels); every decode_split_kernel call fits.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time on one GPU (on different
+ * streams, or from different threads) race and give undefined results.
+ */
+int32_t paged_attention_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                       void* out, const pa_decode_params* p);
+
+/* Bytes of the per-GPU scratch array of paged_attention_decode_noalloc. */
+size_t paged_attention_noalloc_scratch_bytes(void);
+
 /* ----------------------------------------------------------------------- cache writes */
 
 /*

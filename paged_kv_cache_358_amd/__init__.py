@@ -60,6 +60,8 @@ SIGNATURES = {
     "paged_attention_workspace_bytes": (_sz, [ctypes.POINTER(DecodeParams)]),
     "paged_attention_decode_kernel": (ctypes.c_char_p, [ctypes.POINTER(DecodeParams)]),
     "paged_attention_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, ctypes.POINTER(DecodeParams)]),
+    "paged_attention_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, ctypes.POINTER(DecodeParams)]),
+    "paged_attention_noalloc_scratch_bytes": (_sz, []),
     "kv_append": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc), _vp]),
     "block_copy": (_i32, [_vp, _vp, _vp, _i32, ctypes.POINTER(CacheDesc), _vp]),
     "pa_stage_copy": (_i32, [_vp, _vp, _sz, _vp]),
@@ -288,6 +290,40 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     return out
 
 
+def paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
+                                   max_context_len: int, partition_size: int = 0, stream=None, start_event=None,
+                                   stop_event=None, shared=None):
+    """paged_attention_decode without a workspace: the library's per-GPU scratch array holds the partials
+    (nothing is allocated; calls that overlap on one GPU race).  Same arguments otherwise."""
+    torch = _torch()
+    if q.dim() != 3:
+        raise ValueError("q must be [S, H_q, D]")
+    S = q.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or block_tables.shape[1] < 1:
+        raise ValueError(f"block_tables must be [S={S}, max_blocks >= 1], got {tuple(block_tables.shape)}")
+    if context_lens.dim() != 1 or context_lens.numel() != S:
+        raise ValueError(f"context_lens must be [S={S}], got {tuple(context_lens.shape)}")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    _require_device(q, k_cache, v_cache, block_tables, context_lens, out)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if q.dtype != k_cache.dtype:
+        raise ValueError("q must have the cache dtype")
+    sh = None
+    if shared is not None:
+        _require_device(shared)
+        if shared.dtype != torch.int32 or (shared.numel() and (shared.dim() != 2 or shared.shape[1] != 3)):
+            raise ValueError("shared must be int32 [G, 3]")
+        sh = SharedPrefix(_ptr(shared).value, shared.shape[0] if shared.numel() else 0)
+    p = decode_params(q, k_cache, v_cache, block_tables, out, max_context_len, partition_size, None, stream,
+                      start_event, stop_event, sh)
+    _check(lib.paged_attention_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                              _ptr(context_lens), float(scale), _ptr(out), ctypes.byref(p)),
+           "paged_attention_decode_noalloc")
+    return out
+
+
 def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float, out, *,
                             max_query_len: int, stream=None, start_event=None, stop_event=None):
     """out[row, j] = causal attention of chunk row `row` over its sequence's cached tokens.
@@ -484,7 +520,7 @@ class BlockAllocator:
         return tables_out[:n, :max_blocks], lens_out[:n]
 
 
-__all__ = ["paged_attention_decode", "paged_attention_workspace_bytes", "paged_attention_decode_kernel", "shared_prefixes", "SharedPrefix", "paged_attention_prefill", "kv_append", "block_copy", "stage_copy",
+__all__ = ["paged_attention_decode", "paged_attention_decode_noalloc", "paged_attention_workspace_bytes", "paged_attention_decode_kernel", "shared_prefixes", "SharedPrefix", "paged_attention_prefill", "kv_append", "block_copy", "stage_copy",
            "stage_append",
            "BlockAllocator",
            "alloc_kv_cache", "cache_shapes", "cache_desc", "PagedAttnError", "lib", "LIB_PATH", "SIGNATURES",

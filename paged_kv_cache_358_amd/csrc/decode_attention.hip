@@ -1596,6 +1596,42 @@ int32_t launch_decode(DecodeArgs args, const Plan& plan, hipStream_t st, hipEven
 
 }  // namespace
 
+// ------------------------------------------------------------------ the entry point that allocates nothing
+
+// Scratch of paged_attention_decode_noalloc: a file-scope device array, one copy per GPU for the life of
+// the process.  Host code never passes `scratch` itself to a kernel (its host-side name is a stand-in, not
+// a device address): each device's address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+int32_t scratch_address(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;  // device -> address of its copy of scratch
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return PA_HIP_STATUS("paged_attention_decode_noalloc: hipGetDevice", e);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return PA_HIP_STATUS("paged_attention_decode_noalloc: scratch address", e);
+    it = addr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" size_t paged_attention_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" int32_t paged_attention_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                                  const int32_t* block_tables, const int32_t* context_lens,
+                                                  float scale, void* out, const pa_decode_params* p);
+
 extern "C" size_t paged_attention_workspace_bytes(const pa_decode_params* p) {
   Plan plan;
   return make_plan(p, &plan) == PA_OK ? plan.workspace : 0;
@@ -1679,4 +1715,22 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   }
   if (rc != PA_OK) return rc;
   return PA_HIP_STATUS("paged_attention_decode", hipGetLastError());
+}
+
+extern "C" int32_t paged_attention_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                                  const int32_t* block_tables, const int32_t* context_lens,
+                                                  float scale, void* out, const pa_decode_params* p) {
+  Plan plan;
+  const int32_t st = make_plan(p, &plan);
+  if (st != PA_OK) return st;
+  if (plan.workspace > kScratchBytes) return PA_ERR_WORKSPACE;
+  pa_decode_params local = *p;
+  local.workspace = nullptr;
+  local.workspace_bytes = 0;
+  if (plan.workspace > 0 && p->num_seqs > 0) {
+    const int32_t rc = scratch_address(&local.workspace);
+    if (rc != PA_OK) return rc;
+    local.workspace_bytes = kScratchBytes;
+  }
+  return paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, &local);
 }
