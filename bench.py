@@ -338,7 +338,8 @@ def run_decode(args, w, dev, pool):
     total_bytes = sum(attn) + K * append_b + sum(copy_b)
     value = total_bytes / elapsed / 1e9
     mean_main_s = float(np.mean(main_ms)) / 1e3
-    achieved = float(np.mean(attn)) / mean_main_s / 1e9
+    launch_bytes = float(np.mean(attn))
+    achieved = launch_bytes / mean_main_s / 1e9
 
     block = {
         "metric": METRIC,
@@ -364,7 +365,7 @@ def run_decode(args, w, dev, pool):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(kernel, workload["workload"], workload.get("timed_steps")),
-                     "kernel": kernel, "bytes_per_launch": int(np.mean(attn))},
+                     "kernel": kernel, "bytes_per_launch": int(launch_bytes)},
         "copy_on_write_blocks": int(sum(step_pairs)),
     }
     if w == "c1":

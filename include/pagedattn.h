@@ -88,7 +88,7 @@ typedef struct pa_cache_desc {
  * Each shared block is read once for all members; every output is the same softmax attention as
  * without the description, within rounding.  pa_shared_prefixes builds the groups from host copies of
  * the tables and lengths.
- *   groups   device int32 [num_groups][3]: first sequence, members, prefix_blocks
+ *   groups   int32 [num_groups][3] (device or pinned host memory): first sequence, members, prefix_blocks
  * members * (H_q / H_kv) must not exceed 32 (the query columns of two matrix-core tiles).  A description
  * that does not match the tables gives undefined results (never out-of-bounds accesses).  Used by the
  * bf16/fp16, head_dim 64/128, up-to-2048-sequence path; the other paths ignore it.
@@ -169,9 +169,10 @@ const char* paged_attention_decode_kernel(const pa_decode_params* p);
  *
  *   q             device [num_seqs][H_q][head_dim], cache dtype
  *   k_cache/v_cache  device, layout above
- *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries past ceil(n / B) are never read
- *   context_lens  device int32 [num_seqs]; values are clamped to [0, min(max_context_len,
- *                 max_blocks_per_seq * B)]
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq], device memory or pinned host memory (see
+ *                 pa_device_address); entries past ceil(n / B) are never read
+ *   context_lens  int32 [num_seqs], device or pinned host memory; values are clamped to [0,
+ *                 min(max_context_len, max_blocks_per_seq * B)]
  *   scale         softmax scale (usually 1/sqrt(head_dim)), taken as float32
  *   out           device [num_seqs][H_q][head_dim], out_dtype
  * Table entries outside [0, num_blocks) are a caller error: the kernel never dereferences them and treats
@@ -209,7 +210,7 @@ size_t paged_attention_noalloc_scratch_bytes(void);
  * k_new[i, :, :] and v_new[i, :, :] into that slot (block slot / B, offset slot % B) of k_cache / v_cache;
  * other slots (-1 = padding) are skipped.
  *   k_new, v_new   device [num_tokens][num_kv_heads][head_dim], cache dtype
- *   slot_mapping   device int32 [num_tokens]
+ *   slot_mapping   int32 [num_tokens], device or pinned host memory
  * Two tokens naming the same slot race (which one lands is undefined); the allocator never produces that.
  * With the environment variable PA_DEBUG_CHECKS set (and not "0") the call first copies slot_mapping back
  * to the host, synchronously, and returns PA_ERR_INVALID_ARG without launching if two in-range slots are
@@ -226,7 +227,7 @@ int32_t kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapp
  * environment variable PA_DEBUG_CHECKS set (and not "0") the call first copies pairs back to the host,
  * synchronously, and returns PA_ERR_INVALID_ARG without launching if an in-range pair has src == dst, two
  * share a destination, or a destination is also a source.
- *   pairs   device int32 [num_pairs][2]
+ *   pairs   int32 [num_pairs][2], device or pinned host memory
  */
 int32_t block_copy(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                    const pa_cache_desc* cache, void* stream);
@@ -265,6 +266,15 @@ typedef struct pa_prefill_params {
 int32_t paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                 const int32_t* context_lens, const int32_t* query_start, float scale, void* out,
                                 const pa_prefill_params* p);
+
+/*
+ * pa_device_address: the address a kernel uses for p, which is device memory (returned as is) or pinned host
+ * memory (hipHostMalloc, torch pin_memory: the device-side address of the same bytes, read over the bus).
+ * The index arrays of the GPU entry points (block tables, context lengths, shared-prefix groups, slot
+ * mappings, copy pairs) may live in pinned host memory given by such an address; K/V, q, out and the
+ * workspace must be device memory.  PA_ERR_INVALID_ARG for NULL or memory HIP does not know.
+ */
+int32_t pa_device_address(const void* p, const void** out);
 
 /*
  * pa_stage_copy: copy `bytes` (a multiple of 4) from src to dst with one kernel on `stream`.  It moves

@@ -65,6 +65,7 @@ SIGNATURES = {
     "kv_append": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc), _vp]),
     "block_copy": (_i32, [_vp, _vp, _vp, _i32, ctypes.POINTER(CacheDesc), _vp]),
     "pa_stage_copy": (_i32, [_vp, _vp, _sz, _vp]),
+    "pa_device_address": (_i32, [_vp, ctypes.POINTER(_vp)]),
     "paged_attention_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                        ctypes.POINTER(PrefillParams)]),
     "pa_stage_append": (_i32, [_vp, _vp, _sz, _vp, _vp, _vp, _i32, _vp, _vp, ctypes.POINTER(CacheDesc), _vp]),
@@ -180,6 +181,20 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _require_index(*ts):
+    """Index arrays (tables, lengths, groups, slots, pairs) may be device tensors or pinned host tensors."""
+    for t in ts:
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError("index arrays must be on the GPU or in pinned host memory")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _iptr(t):
+    """Kernel address of an index array (device tensor, or pinned host tensor read over the bus)."""
+    return ctypes.c_void_p(device_address(t)) if t is not None else ctypes.c_void_p(0)
+
+
 def _require_device(*ts):
     for t in ts:
         if not t.is_cuda:
@@ -189,6 +204,17 @@ def _require_device(*ts):
 
 
 # ----------------------------------------------------------------------------- kernels
+def device_address(t) -> int:
+    """The address a kernel uses for a device tensor or a pinned host tensor (read over the bus)."""
+    if t.is_cuda:
+        return t.data_ptr()
+    if not t.is_pinned():
+        raise ValueError("host memory must be pinned for the device to read it")
+    out = _vp()
+    _check(lib.pa_device_address(_ptr(t), ctypes.byref(out)), "pa_device_address")
+    return out.value
+
+
 def decode_params(q, k_cache, v_cache, block_tables, out, max_context_len: int, partition_size: int = 0,
                   workspace=None, stream=None, start_event=None, stop_event=None, shared=None) -> DecodeParams:
     """``shared`` is a SharedPrefix (kept alive by the caller for the call) or None."""
@@ -267,17 +293,18 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         raise ValueError(f"context_lens must be [S={S}], got {tuple(context_lens.shape)}")
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
-    _require_device(q, k_cache, v_cache, block_tables, context_lens, out)
+    _require_device(q, k_cache, v_cache, out)
+    _require_index(block_tables, context_lens)
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise ValueError("block_tables and context_lens must be int32")
     if q.dtype != k_cache.dtype:
         raise ValueError("q must have the cache dtype")
     sh = None
     if shared is not None:
-        _require_device(shared)
+        _require_index(shared)
         if shared.dtype != torch.int32 or (shared.numel() and (shared.dim() != 2 or shared.shape[1] != 3)):
             raise ValueError("shared must be int32 [G, 3]")
-        sh = SharedPrefix(_ptr(shared).value, shared.shape[0] if shared.numel() else 0)
+        sh = SharedPrefix(_iptr(shared).value, shared.shape[0] if shared.numel() else 0)
     if workspace is None:
         need = paged_attention_workspace_bytes(q, k_cache, v_cache, block_tables, out, max_context_len,
                                                partition_size, shared=sh is not None)
@@ -285,8 +312,9 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     p = decode_params(q, k_cache, v_cache, block_tables, out, max_context_len, partition_size, workspace, stream,
                       start_event, stop_event, sh)
-    _check(lib.paged_attention_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
-                                      float(scale), _ptr(out), ctypes.byref(p)), "paged_attention_decode")
+    _check(lib.paged_attention_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _iptr(block_tables),
+                                      _iptr(context_lens), float(scale), _ptr(out), ctypes.byref(p)),
+           "paged_attention_decode")
     return out
 
 
@@ -305,21 +333,22 @@ def paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, context_le
         raise ValueError(f"context_lens must be [S={S}], got {tuple(context_lens.shape)}")
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
-    _require_device(q, k_cache, v_cache, block_tables, context_lens, out)
+    _require_device(q, k_cache, v_cache, out)
+    _require_index(block_tables, context_lens)
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise ValueError("block_tables and context_lens must be int32")
     if q.dtype != k_cache.dtype:
         raise ValueError("q must have the cache dtype")
     sh = None
     if shared is not None:
-        _require_device(shared)
+        _require_index(shared)
         if shared.dtype != torch.int32 or (shared.numel() and (shared.dim() != 2 or shared.shape[1] != 3)):
             raise ValueError("shared must be int32 [G, 3]")
-        sh = SharedPrefix(_ptr(shared).value, shared.shape[0] if shared.numel() else 0)
+        sh = SharedPrefix(_iptr(shared).value, shared.shape[0] if shared.numel() else 0)
     p = decode_params(q, k_cache, v_cache, block_tables, out, max_context_len, partition_size, None, stream,
                       start_event, stop_event, sh)
-    _check(lib.paged_attention_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                              _ptr(context_lens), float(scale), _ptr(out), ctypes.byref(p)),
+    _check(lib.paged_attention_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _iptr(block_tables),
+                                              _iptr(context_lens), float(scale), _ptr(out), ctypes.byref(p)),
            "paged_attention_decode_noalloc")
     return out
 
@@ -357,9 +386,11 @@ def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, que
 
 
 def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, *, stream=None):
-    """Write k_new/v_new [T, H_kv, D] into the cache slots slot_mapping[T] (int32, -1 = skip)."""
+    """Write k_new/v_new [T, H_kv, D] into the cache slots slot_mapping[T] (int32, -1 = skip; a device
+    tensor or a pinned host tensor)."""
     torch = _torch()
-    _require_device(k_new, v_new, slot_mapping, k_cache, v_cache)
+    _require_device(k_new, v_new, k_cache, v_cache)
+    _require_index(slot_mapping)
     if slot_mapping.dtype != torch.int32:
         raise ValueError("slot_mapping must be int32")
     c = cache_desc(k_cache, v_cache)
@@ -368,19 +399,21 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, *, stream=None):
         raise ValueError("k_new / v_new must be [T, H_kv, D]")
     if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
         raise ValueError("k_new / v_new must have the cache dtype")
-    _check(lib.kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache),
+    _check(lib.kv_append(_ptr(k_new), _ptr(v_new), _iptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache),
                          ctypes.byref(c), _stream_ptr(stream)), "kv_append")
 
 
 def block_copy(k_cache, v_cache, pairs, *, stream=None):
-    """Copy whole blocks pairs[i, 0] -> pairs[i, 1] (int32 [n, 2]), K and V."""
+    """Copy whole blocks pairs[i, 0] -> pairs[i, 1] (int32 [n, 2], a device tensor or a pinned host
+    tensor), K and V."""
     torch = _torch()
-    _require_device(k_cache, v_cache, pairs)
+    _require_device(k_cache, v_cache)
+    _require_index(pairs)
     if pairs.dtype != torch.int32 or (pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2)):
         raise ValueError("pairs must be int32 [n, 2]")
     c = cache_desc(k_cache, v_cache)
     n = pairs.shape[0] if pairs.numel() else 0
-    _check(lib.block_copy(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), n, ctypes.byref(c), _stream_ptr(stream)),
+    _check(lib.block_copy(_ptr(k_cache), _ptr(v_cache), _iptr(pairs), n, ctypes.byref(c), _stream_ptr(stream)),
            "block_copy")
 
 
@@ -520,7 +553,7 @@ class BlockAllocator:
         return tables_out[:n, :max_blocks], lens_out[:n]
 
 
-__all__ = ["paged_attention_decode", "paged_attention_decode_noalloc", "paged_attention_workspace_bytes", "paged_attention_decode_kernel", "shared_prefixes", "SharedPrefix", "paged_attention_prefill", "kv_append", "block_copy", "stage_copy",
+__all__ = ["paged_attention_decode", "device_address", "paged_attention_decode_noalloc", "paged_attention_workspace_bytes", "paged_attention_decode_kernel", "shared_prefixes", "SharedPrefix", "paged_attention_prefill", "kv_append", "block_copy", "stage_copy",
            "stage_append",
            "BlockAllocator",
            "alloc_kv_cache", "cache_shapes", "cache_desc", "PagedAttnError", "lib", "LIB_PATH", "SIGNATURES",

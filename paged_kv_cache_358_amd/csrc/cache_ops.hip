@@ -237,6 +237,14 @@ extern "C" int32_t block_copy(void* k_cache, void* v_cache, const int32_t* pairs
   return PA_HIP_STATUS("block_copy", hipGetLastError());
 }
 
+extern "C" int32_t pa_device_address(const void* p, const void** out) {
+  if (!p || !out) return PA_ERR_INVALID_ARG;
+  const void* d = device_view(p, false);
+  if (!d) return PA_ERR_INVALID_ARG;
+  *out = d;
+  return PA_OK;
+}
+
 extern "C" int32_t pa_stage_copy(void* dst, const void* src, size_t bytes, void* stream) {
   if (bytes == 0) return PA_OK;
   if (!dst || !src || bytes % 4 != 0) return PA_ERR_INVALID_ARG;

@@ -190,3 +190,19 @@ def test_debug_checks_reject_undefined_copies_and_appends(monkeypatch):
     monkeypatch.setenv("PA_DEBUG_CHECKS", "0")
     pa.block_copy(k_cache, v_cache, pairs([[7, 8]]))                    # checks off: plain launch
     torch.cuda.synchronize()
+
+
+def test_index_arrays_in_pinned_host_memory():
+    # kv_append's slots and block_copy's pairs read from pinned host memory: the same bytes as from the device.
+    k1, v1, kh, vh = random_cache(24, 4, 64, "bf16", 9)
+    k2, v2 = k1.clone(), v1.clone()
+    rng = np.random.default_rng(10)
+    slots = torch.from_numpy(rng.choice(24 * 16, size=50, replace=False).astype(np.int32))
+    new = to_torch(synth.encode(rng.standard_normal((50, 4, 64), dtype=np.float32), "bf16"), "bf16")
+    pairs = torch.tensor([[1, 20], [2, 21], [3, 22]], dtype=torch.int32)
+    pa.kv_append(new, new, slots.cuda(), k1, v1)
+    pa.block_copy(k1, v1, pairs.cuda())
+    pa.kv_append(new, new, slots.pin_memory(), k2, v2)
+    pa.block_copy(k2, v2, pairs.pin_memory())
+    torch.cuda.synchronize()
+    assert np.array_equal(raw_view(k1), raw_view(k2)) and np.array_equal(raw_view(v1), raw_view(v2))
