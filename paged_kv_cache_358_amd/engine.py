@@ -1,16 +1,17 @@
-"""One decode layer driven end to end: allocator step -> copies -> append -> attention.
+"""One decode layer driven end to end: allocator step -> copies -> appends -> attention.
 
 Host orchestration only; all device work is the library's kernels.  Per decode
 step the C++ allocator appends one token to each sequence (opening blocks as
 they fill, copy-on-write for shared partial blocks: "Stop Wasting GPU Memory"
 page, Technical Details, "Single Sequence Generation" and "Copy-on-Write for
-Parallel Sampling") and writes its slot mapping, copy pairs and block tables into
-pinned host memory, which the kernels read over the bus (no copy to the device:
-the decode kernel ran as fast on pinned tables as on device ones).  On the
-compute stream ``block_copy`` runs when the step has copy-on-write pairs, then
-``kv_append`` and ``paged_attention_decode``.  Nothing in a step waits for the
-device, except when a pinned staging buffer is about to be reused while the
-kernels of an earlier step may still read it.
+Parallel Sampling"), its slot mapping, copy pairs and block tables are staged in
+pinned host memory and copied to the device on the compute stream, then
+``block_copy`` -> ``kv_append`` -> ``paged_attention_decode`` run on that stream
+in that order.  (The kernels could read the pinned buffer in place, but the
+attention kernel then fetches its lengths and tables over the bus: measured on
+MI355X the step time was the same and the attention kernel 1-3% slower, so the
+metadata is copied, in the same launch as the append.)  Nothing in a step waits for the device, except when a pinned
+staging buffer is about to be reused while its previous copy is still pending.
 
 Forked sequences keep the blocks they inherited until they write into one, so
 consecutive samples or beams of one prompt share their leading blocks; each step
@@ -25,17 +26,16 @@ import numpy as np
 import torch
 
 from . import (PA_OK, BlockAllocator, DecodeParams, PagedAttnError, SharedPrefix, _P32, _P64, alloc_kv_cache,
-               block_copy, cache_desc, device_address, kv_append, lib, paged_attention_workspace_bytes,
-               torch_dtype_code)
+               block_copy, cache_desc, kv_append, lib, paged_attention_workspace_bytes, stage_copy, torch_dtype_code)
 
 
 class _Staging:
-    """One pinned host buffer holding a step's metadata, int32: context lengths [max_seqs] |
-    slots [max_tokens] | copy pairs [max_seqs, 2] | groups of sequences sharing leading blocks
-    [max_seqs, 3] | block tables [max_seqs, max_blocks].  The kernels read it in place, through
-    its device-side address."""
+    """One pinned host buffer and one device buffer holding a step's metadata, int32:
+    context lengths [max_seqs] | slots [max_tokens] | copy pairs [max_seqs, 2] | groups of
+    sequences sharing leading blocks [max_seqs, 3] | block tables [max_seqs, max_blocks].
+    A step moves the used prefix in one host->device copy."""
 
-    def __init__(self, max_seqs: int, max_blocks: int, max_tokens: int):
+    def __init__(self, max_seqs: int, max_blocks: int, max_tokens: int, device):
         self.o_lens = 0
         self.o_slots = max_seqs
         self.o_pairs = self.o_slots + max_tokens
@@ -44,13 +44,15 @@ class _Staging:
         total = (self.o_tables + max_seqs * max_blocks + 3) // 4 * 4
         self.max_blocks = max_blocks
         self.host = torch.empty(total, dtype=torch.int32, pin_memory=True)
-        self.addr = device_address(self.host)  # where the kernels read it
+        self.dev = torch.empty(total, dtype=torch.int32, device=device)
         h = self.host.numpy()
         self.h_lens = h[self.o_lens:self.o_slots]
         self.h_slots = h[self.o_slots:self.o_pairs]
         self.h_pairs = h[self.o_pairs:self.o_groups].reshape(max_seqs, 2)
         self.h_groups = h[self.o_groups:self.o_tables].reshape(max_seqs, 3)
         self.h_tables = h[self.o_tables:].reshape(max_seqs, max_blocks)
+        self.host_ptr = self.host.data_ptr()
+        self.dev_ptr = self.dev.data_ptr()
         # ctypes views of the host regions for the allocator calls
         self.c_slots = self.h_slots.ctypes.data_as(_P32)
         self.c_pairs = self.h_pairs.ctypes.data_as(_P32)
@@ -60,6 +62,12 @@ class _Staging:
         self.done = None  # event that ends the step that last read this buffer
         self.own_done = torch.cuda.Event()
         self.own_done.record()  # create it now: kernel launches can only mark existing events
+
+    def d_slots(self, n):
+        return self.dev[self.o_slots:self.o_slots + n]
+
+    def d_pairs(self, n):
+        return self.dev[self.o_pairs:self.o_pairs + 2 * n].view(n, 2)
 
 
 
@@ -87,7 +95,7 @@ class PagedDecodeLayer:
         self.stream = torch.cuda.current_stream() if stream is None else stream
         # Three staging buffers: the host fills one while the stream may still read the two
         # before it, so host work on a step overlaps the GPU's previous steps.
-        self._stage = [_Staging(max_seqs, max_blocks_per_seq, max_seqs) for _ in range(3)]
+        self._stage = [_Staging(max_seqs, max_blocks_per_seq, max_seqs, device) for _ in range(3)]
         self._turn = 0
         self._ones = np.ones(max_seqs, np.int32)
         self._c_ones = self._ones.ctypes.data_as(_P32)
@@ -151,7 +159,7 @@ class PagedDecodeLayer:
         st = self._stage[self._turn]
         self._turn = (self._turn + 1) % len(self._stage)
         if st.done is not None:
-            st.done.synchronize()  # the kernels that read this pinned buffer two steps ago have finished
+            st.done.synchronize()  # previous copies out of this pinned buffer have finished
         if S > self.max_seqs:
             raise ValueError("decode_step: more sequences than the layer was sized for")
         ids = np.ascontiguousarray(seqs, dtype=np.int64)  # no copy for a contiguous int64 array
@@ -176,18 +184,20 @@ class PagedDecodeLayer:
             if rc != PA_OK:
                 raise PagedAttnError(rc, "pa_shared_prefixes")
             ngroups = self._ngroups.value if self._ngroups.value < S else 0
-        base = st.addr  # the kernels read the staging buffer in place
+        used = st.o_tables + S * self.max_blocks  # lengths, slots, pairs, sharing and the first S table rows
         if npairs:
             # copy-on-write blocks are copied before the append writes into them
-            rc = lib.block_copy(self._k_ptr, self._v_ptr, base + 4 * st.o_pairs, npairs, ctypes.byref(self._cdesc),
-                                self._stream_ptr)
+            stage_copy(st.dev, st.host, used * 4, stream=self.stream)
+            block_copy(self.k_cache, self.v_cache, st.d_pairs(npairs), stream=self.stream)
+            kv_append(k_new, v_new, st.d_slots(S), self.k_cache, self.v_cache, stream=self.stream)
+        else:
+            # one launch: the metadata copy, and the append reading its slots from the staging buffer
+            rc = lib.pa_stage_append(st.dev_ptr, st.host_ptr, used * 4, k_new.data_ptr(), v_new.data_ptr(),
+                                     st.host_ptr + 4 * st.o_slots, S, self._k_ptr, self._v_ptr,
+                                     ctypes.byref(self._cdesc), self._stream_ptr)
             if rc != PA_OK:
-                raise PagedAttnError(rc, "block_copy")
-        rc = lib.kv_append(k_new.data_ptr(), v_new.data_ptr(), base + 4 * st.o_slots, S, self._k_ptr, self._v_ptr,
-                           ctypes.byref(self._cdesc), self._stream_ptr)
-        if rc != PA_OK:
-            raise PagedAttnError(rc, "kv_append")
-        # the kernels of this step are done with the buffer when the attention call is
+                raise PagedAttnError(rc, "pa_stage_append")
+        # the staging copies (earlier in the stream) are done when the attention kernels are
         st.done = st.own_done if timing is None else timing[1]
         p = self._params
         p.num_seqs = S
@@ -196,13 +206,13 @@ class PagedDecodeLayer:
         p.start_event = None if timing is None else timing[0].cuda_event
         p.stop_event = st.done.cuda_event
         if ngroups:
-            self._shared.groups = base + 4 * st.o_groups
+            self._shared.groups = st.dev_ptr + 4 * st.o_groups
             self._shared.num_groups = ngroups
             p.shared = ctypes.pointer(self._shared)
         else:
             p.shared = None
-        rc = lib.paged_attention_decode(q.data_ptr(), self._k_ptr, self._v_ptr, base + 4 * st.o_tables,
-                                        base + 4 * st.o_lens, float(scale), out.data_ptr(), ctypes.byref(p))
+        rc = lib.paged_attention_decode(q.data_ptr(), self._k_ptr, self._v_ptr, st.dev_ptr + 4 * st.o_tables,
+                                        st.dev_ptr + 4 * st.o_lens, float(scale), out.data_ptr(), ctypes.byref(p))
         if rc != PA_OK:
             raise PagedAttnError(rc, "paged_attention_decode")
         self.last_groups = ngroups
