@@ -82,9 +82,6 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "the paged decode path has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
-    if args.workload == "prefill":
-        run_prefill(args)
-        return
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]
     if (args.block_size != 16 or args.head_dim) and "c4" in names:
         if args.workload == "c4":
@@ -106,6 +103,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload == "prefill":
+        run_prefill(args)
+        return
 
     blocks = {}
     with ThreadPoolExecutor(max_workers=host_threads()) as pool:
@@ -576,7 +576,7 @@ def run_prefill(args):
         "kernel_ms": round(kern_s * 1e3, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_mfma_kernel", "flops_per_launch": flops},
+                     "kernel": "prefill_tiled_kernel", "flops_per_launch": flops},
         "kv_bytes_per_launch": kv_bytes, "kv_gbs_if_read_once": round(kv_bytes / kern_s / 1e9, 1),
     }), flush=True)
 

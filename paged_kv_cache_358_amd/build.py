@@ -34,6 +34,11 @@ HIPCC_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", 
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-I", INCLUDE, "-I", CSRC]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE]
+# Per-file additions.  The prefill kernel's softmax takes maxima of raw MFMA scores; with NaNs honoured
+# every fmax first canonicalises its operands (one extra VALU op per score).  No NaN reaches those
+# maxima: scores of tokens a row must not see are replaced by -inf with a select, and V slots past
+# the context are cleared with integer masks, before any floating-point use.
+HIP_FILE_FLAGS = {"prefill_attention.hip": ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:
@@ -58,7 +63,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        jobs.append((obj, [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+        jobs.append((obj, [hipcc, *HIPCC_FLAGS, *HIP_FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]))
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         jobs.append((obj, ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
@@ -92,7 +97,7 @@ def build_sanitized(verbose: bool = False) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         if not os.path.exists(obj) or os.path.getmtime(obj) < os.path.getmtime(os.path.join(CSRC, src)):
-            jobs.append((obj, [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+            jobs.append((obj, [hipcc, *HIPCC_FLAGS, *HIP_FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]))
     for src in CXX_SOURCES:
         obj = os.path.join(san_dir, src + ".o")
         jobs.append((obj, ["g++", *CXX_FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))

@@ -7,15 +7,14 @@
 // page, Key points), gathered through the block table.  Chunk row i of a sequence with n
 // cached tokens, c of them in the chunk, is position p = n - c + i and sees tokens 0..p.
 //
-// One workgroup per (128-row tile of a chunk, query head, sequence), the tiles of one
-// (sequence, query head) placed on one XCD so they share its L2; each wave owns 32 chunk
-// rows, the columns of two 16-column MFMA tiles that share every K/V block's registers, and
-// streams the K/V blocks its last row can see through a ring of register sets (the next
-// blocks load while one computes).  The four
-// waves of a workgroup read the same blocks, so the caches serve the repeats.  Per block:
-// S^T = K Q^T with v_mfma_f32_16x16x32, an online softmax per column (query row) with the
-// causal bound applied per (token, column), and O^T += V^T (P_hi + P_lo) with two
-// v_mfma_f32_16x16x16 as in the decode kernels.  Each wave writes its own rows.
+// One workgroup of four waves per (128-row tile of a chunk, query head, sequence), the tiles of
+// one (sequence, query head) placed on one XCD so that they share its L2.  Each wave owns 32 chunk
+// rows, two 16-column MFMA tiles.  The K/V blocks the tile's last row can see are streamed in
+// stages of four 16-token blocks: each wave loads one block of the next stage into registers and
+// writes it to LDS while the current stage computes, one barrier per stage.  Per stage and row
+// tile: S^T = K Q^T with v_mfma_f32_16x16x32 (K read from LDS), one online-softmax update over the
+// stage's 64 tokens with the causal bound applied only on the stages that need it, and
+// O^T += V^T (P_hi + P_lo) with v_mfma_f32_16x16x32 over block pairs.  Each wave writes its own rows.
 #include <hip/hip_ext.h>
 
 #include <cmath>
@@ -51,7 +50,6 @@ constexpr int kPrefillTiles = 2;                                 // 16-row MFMA 
 constexpr int kPrefillWaveRows = 16 * kPrefillTiles;             // chunk rows per wave
 constexpr int kPrefillRows = kPrefillWaves * kPrefillWaveRows;  // chunk rows per workgroup
 constexpr int kXcdCount = 8;  // accelerator complex dies of an MI355X, one L2 each
-constexpr int kPrefillRing = 3;  // K/V register sets per wave: block i computing, i+1 and i+2 loading
 
 template <int DT>
 __device__ __forceinline__ void prefill_store4(const PrefillArgs& a, int64_t idx, const f32x4_t& v) {
@@ -65,19 +63,31 @@ __device__ __forceinline__ void prefill_store4(const PrefillArgs& a, int64_t idx
   }
 }
 
-template <int DT, int D, int NBUF>
-__global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
+// Each wave loads one 16-token block of a stage (K and V tiles as stored, V with the tokens past the
+// context zeroed) and writes it to one of two LDS buffers; every wave then computes its 32 rows
+// against all four blocks.  The PV product's 32-wide contraction takes tokens 4 grp .. 4 grp + 3 of
+// both blocks of a pair, the order in which the score tiles leave them in a lane; P is split into
+// hi + lo in the cache's 16-bit type, so that it enters the product with about 16 significant bits.
+constexpr int kStageBlocks = kPrefillWaves;  // 16-token blocks per stage: one per wave
+
+template <int DT, int D>
+__global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void prefill_tiled_kernel(
     PrefillArgs a) {
   constexpr int KK = D / 32;
   constexpr int NV = D / 16;
   constexpr int NT = kPrefillTiles;
   constexpr int kTileBytes = D * kBlockTokens * 2;
+  // K: [buffer][block of the stage][tile as stored].  V: [buffer][block pair][16-dim group][lane][block of
+  // the pair][4 tokens]: a lane's PV operand (4 tokens of both blocks) is one 16-byte read, and the 64
+  // lanes of a read cover 1 KiB without gaps.
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][kStageBlocks][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][kStageBlocks / 2][NV][kWave * 16];
 
-  // Workgroups go to the 8 XCDs round-robin (workgroup i on XCD i % 8).  The (sequence,
-  // query head) groups are dealt to the XCDs round-robin too, and the k-th workgroup of XCD x
-  // takes tile k % tiles of its (k / tiles)-th group: the tiles of one group run back to back
-  // on one XCD and read the sequence's blocks through its L2 instead of fetching them from HBM
-  // once per tile, while every XCD gets an even share of long and short sequences.
+  // Workgroups go to the 8 XCDs round-robin (workgroup i on XCD i % 8).  The (sequence, query head)
+  // groups are dealt to the XCDs round-robin too, and the k-th workgroup of XCD x takes tile
+  // k % tiles of its (k / tiles)-th group: the tiles of one group run back to back on one XCD and
+  // read the sequence's blocks through its L2 instead of fetching them from HBM once per tile,
+  // while every XCD gets an even share of long and short sequences.
   const int64_t kx = blockIdx.x / kXcdCount;
   const int64_t sj = static_cast<int64_t>(blockIdx.x % kXcdCount) + kXcdCount * (kx / a.tiles);
   if (sj >= a.items / a.tiles) return;
@@ -92,17 +102,21 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
   const int h = j / g;
 
   const int q0 = a.query_start[s];
-  const int c = a.query_start[s + 1] - q0;                  // chunk rows of this sequence
+  const int c = a.query_start[s + 1] - q0;  // chunk rows of this sequence
   int n = a.context_lens[s];
   n = n < 0 ? 0 : (n > a.max_blocks * kBlockTokens ? a.max_blocks * kBlockTokens : n);
-  const int r0 = tile * kPrefillRows + w * kPrefillWaveRows;  // this wave's first chunk row
-  if (c <= 0 || r0 >= c) return;
-  const int r_last = min(c, r0 + kPrefillWaveRows) - 1;
-  const int p_last = n - c + r_last;                       // position of the wave's last row
-  if (p_last < 0) return;                                  // n < c: no row of this wave has a position
+  // Workgroup-uniform exits (before any barrier): no row of the tile, or no row with a position.
+  const int R0 = tile * kPrefillRows;
+  if (c <= 0 || R0 >= c) return;
+  const int p_wg_last = n - c + min(c, R0 + kPrefillRows) - 1;
+  if (p_wg_last < 0) return;
+  const int nblk = p_wg_last / kBlockTokens + 1;  // blocks holding tokens 0 .. p_wg_last
+  const int nstage = (nblk + kStageBlocks - 1) / kStageBlocks;
 
-  // This lane's columns: chunk row r0 + 16 t + col of tile t at position p[t] (-1 = no row /
-  // no position).
+  // This wave's rows: r0 .. r0 + 31; the last stage it needs (-1: none).
+  const int r0 = R0 + w * kPrefillWaveRows;
+  const int p_w_last = r0 < c ? n - c + min(c, r0 + kPrefillWaveRows) - 1 : -1;
+  const int w_last_stage = p_w_last >= 0 ? p_w_last / (kBlockTokens * kStageBlocks) : -1;
   int64_t row[NT];
   bool real[NT];
   int p[NT];
@@ -113,8 +127,15 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
     real[t] = r < c && n - c + r >= 0 && row[t] >= 0 && row[t] < a.num_tokens;
     p[t] = real[t] ? n - c + r : -1;
   }
+  const int p_first = n - c + r0;  // position of the wave's first row (rows before it see every earlier token)
 
-  // Q^T operands: lane (column col, k-group grp) holds dims (kk*4 + grp)*8 .. +8 of its rows.
+  // The exponent is taken as exp2(kscale * s - m) with one FMA per score and the maximum over raw
+  // scores, which needs kscale > 0: a negative scale negates Q instead (exact: a sign flip of every
+  // element), and a zero scale (every visible token weighs the same) zeroes Q with kscale = 1.
+  const float scl = a.scale_log2;
+  const bool qzero = scl == 0.f;
+  const uint32_t qflip = scl < 0.f ? 0x80008000u : 0u;
+  const float kscale = qzero ? 1.f : fabsf(scl);
   using st = uint16_t;
   const st* qp = static_cast<const st*>(a.q);
   u32x4_t qop[NT][KK];
@@ -124,24 +145,26 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qp + qrow + (kk * 4 + grp) * 8);
-      qop[t][kk] = real[t] ? x : u32x4_t{0, 0, 0, 0};
+      qop[t][kk] = real[t] && !qzero ? (x ^ qflip) : u32x4_t{0, 0, 0, 0};
     }
   }
 
-  const int nblk = p_last / kBlockTokens + 1;  // blocks holding tokens 0 .. p_last
+  // Block ids of this wave's blocks (stage st holds block st * 4 + w): lane i holds the id of stage
+  // base + i.
   const int32_t* tab = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
-  // Block ids, 64 per register: lane i holds block base + i (clamped into the row).
-  auto load_ids = [&](int base) { return tab[min(base + lane, a.max_blocks - 1)]; };
+  auto load_ids = [&](int base) { return tab[min((base + lane) * kStageBlocks + w, a.max_blocks - 1)]; };
+  int ids_base = 0;
+  int32_t ids = load_ids(0);
 
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + static_cast<int64_t>(h) * kTileBytes;
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + static_cast<int64_t>(h) * kTileBytes;
   const int64_t blk_stride = static_cast<int64_t>(a.hkv) * kTileBytes;
   const int k_off = lane * 16;
   const int v_off = col * 32 + grp * 8;
-  // A block past the wave's last one, or an id outside the pool, gets an empty resource:
-  // its loads return zeros and touch no memory.
-  auto load = [&](KVRegs<D>& rg, int32_t phys, bool ok) {
-    ok = ok && phys >= 0 && phys < a.num_blocks;
+  // Load block b (this wave's block of a stage) into registers; a block past the workgroup's last one
+  // or an id outside the pool gets an empty resource (zeros, no memory touched).
+  auto gload = [&](KVRegs<D>& rg, int b, int32_t phys) {
+    const bool ok = b < nblk && phys >= 0 && phys < a.num_blocks;
     const int64_t off = ok ? static_cast<int64_t>(phys) * blk_stride : 0;
     const int nrec = ok ? kTileBytes : 0;
     const __amdgpu_buffer_rsrc_t rk =
@@ -155,6 +178,26 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
     for (int nn = 0; nn < NV; ++nn)
       rg.v[nn] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, nn * 512, 0));
   };
+  // Block b's tiles into buffer buf, in the layout they have in the cache; V tokens past the context
+  // (which may hold anything, even NaN) are zeroed so that no product reads them.
+  auto lwrite = [&](KVRegs<D>& rg, int buf, int b, int32_t phys) {
+    int nv = n - b * kBlockTokens;
+    nv = nv > kBlockTokens ? kBlockTokens : (nv < 0 ? 0 : nv);
+    if (b >= nblk || phys < 0 || phys >= a.num_blocks) nv = 0;
+    uint8_t* kt = k_lds[buf][w];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) *reinterpret_cast<u32x4_t*>(kt + k_off + kk * 1024) = rg.k[kk];
+    uint32_t keep[2];
+#pragma unroll
+    for (int wd = 0; wd < 2; ++wd) {
+      const int t0 = grp * 4 + 2 * wd;
+      keep[wd] = (t0 < nv ? 0x0000ffffu : 0u) | (t0 + 1 < nv ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn)
+      *reinterpret_cast<u32x2_t*>(&v_lds[buf][w >> 1][nn][lane * 16 + (w & 1) * 8]) =
+          u32x2_t{rg.v[nn][0] & keep[0], rg.v[nn][1] & keep[1]};
+  };
 
   f32x4_t o[NT][NV];
   float m[NT], l[NT];
@@ -166,116 +209,115 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
     l[t] = 0.f;
   }
 
-  // A block whose 16 tokens all lie in the context and before the wave's first row is seen
-  // whole by every row: no token needs masking (rows past the chunk are never written).
-  const int p_first = n - c + r0;
-  // S^T tiles of a block: the matrix-core half of a block's work, issued one block ahead.
-  auto qk = [&](const KVRegs<D>& rg, f32x4_t (&s)[NT]) {
+  // One stage (buffer buf, blocks b0 .. b0 + 3) for this wave's rows.
+  auto compute = [&](int buf, int b0) {
+    // Scores: lane (row col of tile t, k-group grp) gets tokens 4 grp .. 4 grp + 3 of each block.
+    f32x4_t sc[NT][kStageBlocks];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int bb = 0; bb < kStageBlocks; ++bb) {
+      u32x4_t kop[KK];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) s[t] = mfma_qk<DT>(rg.k[kk], qop[t][kk], s[t]);
-    }
-  };
-  // The rest of block b's work: online softmax over its scores and O^T += V^T P^T.
-  auto finish = [&](KVRegs<D>& rg, int b, int32_t phys, const f32x4_t (&s)[NT]) {
-    int nv = n - b * kBlockTokens;  // tokens of the block in the context
-    nv = nv > kBlockTokens ? kBlockTokens : nv;
-    if (phys < 0 || phys >= a.num_blocks) nv = 0;
-    const bool whole = nv == kBlockTokens && b * kBlockTokens + kBlockTokens - 1 <= p_first;
-    u32x2_t p_hi[NT], p_lo[NT];
+      for (int kk = 0; kk < KK; ++kk)
+        kop[kk] = *reinterpret_cast<const u32x4_t*>(k_lds[buf][bb] + k_off + kk * 1024);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const f32x4_t sacc = s[t];
-      float x[4];
-      if (whole) {
+      for (int t = 0; t < NT; ++t) {
+        sc[t][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = sacc[e] * a.scale_log2;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tok = grp * 4 + e;
-          x[e] = (tok < nv && b * kBlockTokens + tok <= p[t]) ? sacc[e] * a.scale_log2 : -INFINITY;
-        }
+        for (int kk = 0; kk < KK; ++kk) sc[t][bb] = mfma_qk<DT>(kop[kk], qop[t][kk], sc[t][bb]);
       }
-      const float bm = rows4_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    }
+    // Stage tokens b0 * 16 .. b0 * 16 + 63: those past the context or after a row's position count
+    // nothing for that row.  A stage every row of the wave sees whole (all but the last one or two
+    // of a wave) needs no mask: the branch is uniform across the wave.
+    const int t_end = min(n, (b0 + kStageBlocks) * kBlockTokens) - 1;  // last token of the stage in the context
+    const bool whole = t_end == (b0 + kStageBlocks) * kBlockTokens - 1 && t_end <= p_first;
+    // Raw scores, those a row does not see set to -inf (kscale * -inf = -inf, exp2 of it 0).
+    if (!whole) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        // Token tok counts for row t of this lane when tok <= lim (p = -1 for a row past the chunk).
+        const int lim = min(t_end, p[t]) - (b0 * kBlockTokens + grp * 4);
+#pragma unroll
+        for (int bb = 0; bb < kStageBlocks; ++bb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[t][bb][e] = bb * kBlockTokens + e <= lim ? sc[t][bb][e] : -INFINITY;
+      }
+    }
+    u32x4_t p_hi[NT][kStageBlocks / 2], p_lo[NT][kStageBlocks / 2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float bm = fmaxf(fmaxf(sc[t][0][0], sc[t][0][1]), fmaxf(sc[t][0][2], sc[t][0][3]));
+#pragma unroll
+      for (int bb = 1; bb < kStageBlocks; ++bb)
+        bm = fmaxf(bm, fmaxf(fmaxf(sc[t][bb][0], sc[t][bb][1]), fmaxf(sc[t][bb][2], sc[t][bb][3])));
+      bm = rows4_max(bm) * kscale;
       const float m_new = fmaxf(m[t], bm);
-      // Once the rows' running maxima settle, most blocks raise none of them: then every
-      // correction factor is 1 and the rescale of the tile's O (32 accumulators a lane) is
-      // skipped for the whole wave.
       const bool rescale = __builtin_amdgcn_ballot_w64(m_new != m[t]) != 0;
       const float alpha = (m[t] == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m[t] - m_new);
-      float pr[4];
+      // A row that has seen no token yet keeps m = -inf; exponents are taken against 0 then, and
+      // exp2(-inf) = 0 gives its masked tokens their weight without a select.
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      float pr[kStageBlocks][4];
+      float sum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pr[e] = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m_new);
-      l[t] = l[t] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      for (int bb = 0; bb < kStageBlocks; ++bb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pr[bb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][bb][e], kscale, -m_use));
+          sum += pr[bb][e];
+        }
+      l[t] = l[t] * alpha + sum;
       m[t] = m_new;
       if (rescale) {
 #pragma unroll
         for (int nn = 0; nn < NV; ++nn) o[t][nn] *= alpha;
       }
-      PSplit<DT>::split(pr, p_hi[t], p_lo[t]);
-    }
-    // Tokens past the context may hold anything, even NaN: a block that is not full has them
-    // selected out of its V registers (in place: the ring reloads them next); a full block needs
-    // no mask.
-    if (nv < kBlockTokens) {
-      uint32_t keep[2];
 #pragma unroll
-      for (int wd = 0; wd < 2; ++wd) {
-        const int t0 = grp * 4 + 2 * wd;
-        keep[wd] = (t0 < nv ? 0x0000ffffu : 0u) | (t0 + 1 < nv ? 0xffff0000u : 0u);
+      for (int pp = 0; pp < kStageBlocks / 2; ++pp) {
+        u32x2_t ha, la, hb, lb;
+        PSplit<DT>::split(pr[2 * pp], ha, la);
+        PSplit<DT>::split(pr[2 * pp + 1], hb, lb);
+        p_hi[t][pp] = u32x4_t{ha[0], ha[1], hb[0], hb[1]};
+        p_lo[t][pp] = u32x4_t{la[0], la[1], lb[0], lb[1]};
       }
-#pragma unroll
-      for (int nn = 0; nn < NV; ++nn) rg.v[nn] = u32x2_t{rg.v[nn][0] & keep[0], rg.v[nn][1] & keep[1]};
     }
-    // Both tiles use each V register of the block.
+    // O^T += V^T P^T over block pairs: the V operand of lane (dim col, k-group grp) is tokens
+    // 4 grp .. 4 grp + 3 of both blocks of the pair.
 #pragma unroll
-    for (int nn = 0; nn < NV; ++nn) {
+    for (int pp = 0; pp < kStageBlocks / 2; ++pp) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        o[t][nn] = mfma_pv<DT>(rg.v[nn], p_hi[t], o[t][nn]);
-        o[t][nn] = mfma_pv<DT>(rg.v[nn], p_lo[t], o[t][nn]);
+      for (int nn = 0; nn < NV; ++nn) {
+        const u32x4_t vop = *reinterpret_cast<const u32x4_t*>(&v_lds[buf][pp][nn][lane * 16]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          o[t][nn] = mfma_qk<DT>(vop, p_hi[t][pp], o[t][nn]);
+          o[t][nn] = mfma_qk<DT>(vop, p_lo[t][pp], o[t][nn]);
+        }
       }
     }
   };
 
-  // A ring of NBUF register sets: blocks b+1 .. b+NBUF-1 are loading while block b computes.
-  // The scores of block b+1 are computed before block b's softmax and PV, so the matrix cores
-  // work on the next block while the vector units take this one's softmax.  Block ids come 64
-  // to a register; ids_next holds the 64 after, loaded 64 blocks ahead of its first use, and
-  // the pair advances once the blocks reach past the first register.
-  int base = 0;
-  int32_t ids = load_ids(0);
-  int32_t ids_next = load_ids(64);
-  auto phys_at = [&](int pos) {
-    return pos < base + 64 ? __builtin_amdgcn_readlane(ids, pos - base) : __builtin_amdgcn_readlane(ids_next, pos - base - 64);
-  };
-  KVRegs<D> ring[NBUF];
-#pragma unroll
-  for (int jj = 0; jj < NBUF - 1; ++jj) load(ring[jj], phys_at(jj), jj < nblk);
-  f32x4_t s_next[NT];
-  qk(ring[0], s_next);
-  for (int b = 0; b < nblk; b += NBUF) {
-    if (b - base >= 64) {
-      base += 64;
-      ids = ids_next;
-      ids_next = load_ids(base + 64);
-    }
-#pragma unroll
-    for (int jj = 0; jj < NBUF; ++jj) {
-      const int i = b + jj;
-      const int la = i + NBUF - 1;
-      load(ring[(jj + NBUF - 1) % NBUF], phys_at(la), la < nblk);
-      if (i < nblk) {
-        f32x4_t s_cur[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) s_cur[t] = s_next[t];
-        if (i + 1 < nblk) qk(ring[(jj + 1) % NBUF], s_next);
-        finish(ring[jj], i, phys_at(i), s_cur);
+  KVRegs<D> rg;
+  {
+    const int32_t phys = __builtin_amdgcn_readlane(ids, 0);
+    gload(rg, w, phys);
+    lwrite(rg, 0, w, phys);
+  }
+  __syncthreads();
+  for (int stg = 0; stg < nstage; ++stg) {
+    const int nxt = stg + 1;
+    int32_t phys_n = -1;
+    if (nxt < nstage) {
+      if (nxt - ids_base >= 64) {
+        ids_base += 64;
+        ids = load_ids(ids_base);
       }
+      phys_n = __builtin_amdgcn_readlane(ids, nxt - ids_base);
+      gload(rg, nxt * kStageBlocks + w, phys_n);
     }
+    if (stg <= w_last_stage) compute(stg & 1, stg * kStageBlocks);
+    if (nxt < nstage) lwrite(rg, nxt & 1, nxt * kStageBlocks + w, phys_n);
+    __syncthreads();
   }
 
 #pragma unroll
@@ -347,14 +389,14 @@ extern "C" int32_t paged_attention_prefill(const void* q, const void* k_cache, c
   const dim3 block(kPrefillWaves * kWave);
   if (c.dtype == PA_BF16) {
     if (c.head_dim == 64)
-      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_BF16, 64, kPrefillRing>), grid, block, 0, st, start, stop, 0, a);
+      hipExtLaunchKernelGGL((prefill_tiled_kernel<PA_BF16, 64>), grid, block, 0, st, start, stop, 0, a);
     else
-      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_BF16, 128, kPrefillRing>), grid, block, 0, st, start, stop, 0, a);
+      hipExtLaunchKernelGGL((prefill_tiled_kernel<PA_BF16, 128>), grid, block, 0, st, start, stop, 0, a);
   } else {
     if (c.head_dim == 64)
-      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_F16, 64, kPrefillRing>), grid, block, 0, st, start, stop, 0, a);
+      hipExtLaunchKernelGGL((prefill_tiled_kernel<PA_F16, 64>), grid, block, 0, st, start, stop, 0, a);
     else
-      hipExtLaunchKernelGGL((prefill_mfma_kernel<PA_F16, 128, kPrefillRing>), grid, block, 0, st, start, stop, 0, a);
+      hipExtLaunchKernelGGL((prefill_tiled_kernel<PA_F16, 128>), grid, block, 0, st, start, stop, 0, a);
   }
   return PA_HIP_STATUS("paged_attention_prefill", hipGetLastError());
 }

@@ -75,6 +75,9 @@ def test_gqa_and_head_dim_64():
 
 
 def test_first_position_of_a_whole_sequence_chunk_is_its_value():
+    # Position 0 sees token 0 alone, whose weight is 1: the output is V[0].  The kernel takes the
+    # exponent as one fused multiply-add of the raw score against the rounded maximum, so the lone
+    # token's weight is exp2 of that rounding error (below 2^-22 here), not exp2(0): V[0] to 2^-20.
     cfg = synth.scaled(synth.C3, lens=[48, 20])
     pd = PagedDecode(cfg)
     chunks = [48, 20]
@@ -83,7 +86,31 @@ def test_first_position_of_a_whole_sequence_chunk_is_its_value():
     for s in range(2):
         _, v = pd.truth[s]
         expect = np.repeat(synth.decode_f64(v[0], cfg.dtype), cfg.group, axis=0)   # [H_q, D]
-        assert np.array_equal(got[qs[s]], expect.astype(np.float32))
+        np.testing.assert_allclose(got[qs[s]], expect, rtol=2 ** -20, atol=0)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+def test_negative_and_zero_scale(scale):
+    # A negative scale flips which tokens dominate; a zero scale weighs every visible token the same.
+    lens = [70, 33, 200]
+    chunks = [70, 9, 150]
+    cfg = synth.scaled(synth.C3, lens=lens)
+    pd = PagedDecode(cfg)
+    q_np = _chunk_queries(cfg, chunks, 8)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = to_torch(q_np, cfg.dtype, "cuda")
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    pa.paged_attention_prefill(q, pd.k_cache, pd.v_cache, pd.block_tables, pd.context_lens,
+                               torch.from_numpy(qs).cuda(), scale, out, max_query_len=int(max(chunks)))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    worst = 0.0
+    for s, c in enumerate(chunks):
+        k, v = pd.truth[s]
+        ref = prefill_attention_seq(synth.decode_f64(q_np[qs[s]:qs[s + 1]], cfg.dtype), synth.decode_f64(k, cfg.dtype),
+                                    synth.decode_f64(v, cfg.dtype), scale)
+        worst = max(worst, float(np.max(np.abs(got[qs[s]:qs[s + 1]] - ref))))
+    assert worst <= 5e-3, worst
 
 
 def test_last_chunk_row_equals_decode():
