@@ -91,8 +91,9 @@ struct DecodeArgs {
   // at most two, [k][slot][column][D] (and [k][slot][column][2]), slot 0 for the run's last segment and
   // slot 1 for its first segment when another context follows it in the run.
   int32_t part_cols;
-  // split: log2 of the 16-token tiles per cache block (block_tokens = 16 << sub_log2); the split
-  // kernel then counts blocks and partitions (part_blocks) in 16-token tiles.
+  // split: log2 of the 16-token tiles per cache block (block_tokens = 16 << sub_log2), or -1 for
+  // 8-token blocks, two to a tile; the split kernel counts blocks and partitions (part_blocks) in
+  // 16-token tiles.
   int32_t sub_log2;
 };
 
@@ -412,10 +413,13 @@ struct Item {
 // At least two waves per SIMD for head_dim 64 and 128: the compiler keeps the kernel within 256
 // VGPRs.  Head_dim 256 (plain mode, 4 wavefronts, 16-token blocks) runs one wave per SIMD with the
 // accumulators partly in AGPRs: twice the bytes per ring slot keep as many bytes in flight per CU.
-// MULTI: cache blocks of 16 << a.sub_log2 tokens (32, 64, ...), streamed as 16-token tiles:
-// tile b of a row is tile b % SB of the row's cache block b / SB (SB = 1 << sub_log2); every
-// count below (blocks, partitions, shared blocks) is then in tiles.  Without MULTI, SB = 1.
-template <int DT, int D, int NBUF, int MODE, int WV, bool MULTI>
+// Block kinds of the split kernel.  kBk16: 16-token cache blocks, one per ring position.
+// kBkMulti: cache blocks of 16 << a.sub_log2 tokens (32, 64, ...), streamed as 16-token tiles:
+// tile b of a row is tile b % SB of the row's cache block b / SB (SB = 1 << sub_log2).  kBkHalf:
+// 8-token cache blocks (plain mode), two to a 16-token tile: tile b of a row is its cache blocks
+// 2b and 2b + 1.  Every count below (blocks, partitions, shared blocks) is in 16-token tiles.
+constexpr int kBk16 = 0, kBkMulti = 1, kBkHalf = 2;
+template <int DT, int D, int NBUF, int MODE, int WV, int BK>
 __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2))) void decode_split_kernel(
     DecodeArgs a) {
   constexpr int KK = D / 32;
@@ -423,6 +427,9 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
   constexpr int kTileBytes = D * kBlockTokens * 2;  // one 16-token tile of one KV head
   constexpr int kThreads = WV * kWave;
   constexpr int NT = MODE == kGroup ? 2 : 1;  // 16-column MFMA tiles of query columns
+  constexpr bool MULTI = BK == kBkMulti;
+  constexpr bool HALF = BK == kBkHalf;
+  static_assert(!HALF || MODE == kPlain, "8-token blocks run in plain mode");
   __shared__ __attribute__((aligned(16))) float sm_o[WV][16][D];
   __shared__ float sm_m[WV][16];
   __shared__ float sm_l[WV][16];
@@ -664,9 +671,17 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       sl.ids = a.block_tables[static_cast<int64_t>(row) * a.max_blocks + min(max(pos, 0) >> lsb, a.max_blocks - 1)];
     } else {
       qrow[0] = (static_cast<int64_t>(it.s) * a.hq + it.h * g + (col < g ? col : 0)) * D;
-      const int u = (PAIR ? it.b0 >> 1 : it.b0) + unit_of(lane);  // partitions start on a block
-      sl.meta = (u & um) << 16;
-      sl.ids = a.block_tables[static_cast<int64_t>(it.s) * a.max_blocks + min(u >> lu, a.max_blocks - 1)];
+      if constexpr (HALF) {
+        // Lane i < 32: the first cache block of ring position i's tile; lane 32 + i: its second (a
+        // wave holds at most 64 tiles / 4 waves = 16 positions of a partition).
+        const int u = it.b0 + unit_of(lane & 31);
+        sl.meta = 0;
+        sl.ids = a.block_tables[static_cast<int64_t>(it.s) * a.max_blocks + min(2 * u + (lane >> 5), a.max_blocks - 1)];
+      } else {
+        const int u = (PAIR ? it.b0 >> 1 : it.b0) + unit_of(lane);  // partitions start on a block
+        sl.meta = (u & um) << 16;
+        sl.ids = a.block_tables[static_cast<int64_t>(it.s) * a.max_blocks + min(u >> lu, a.max_blocks - 1)];
+      }
     }
     // Keep the id load ahead of the query loads: the lookahead waits for it while the
     // query loads may still be in flight.
@@ -698,7 +713,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
   // A (cache block, KV head) holds 16 * SB tokens: K as [D/8][16 * SB][8] and V as [D][16 * SB]
   // (SB = 1 without MULTI).  Ring unit t of it (kUnitTokens tokens) starts t * 16 * kUnitTokens
   // bytes into each K row of 8 dims and t * 2 * kUnitTokens bytes into each V row.
-  const int head_bytes = kTileBytes << lsb;
+  const int head_bytes = HALF ? kTileBytes / 2 : kTileBytes << lsb;
   const int64_t blk_stride = static_cast<int64_t>(hkv) * head_bytes;
   // Per-lane byte offsets: K chunk c = grp of the lane's token (K half h in PAIR), and V dim col
   // at the lane's first token.
@@ -746,6 +761,30 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
         r.v[nn] = __builtin_bit_cast(
             u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, (nn * 512) << lsb, kLoadV));
     }
+  };
+  // kBkHalf: the tile of ring position i is cache blocks p0 (tokens 0-7) and p1 (tokens 8-15), each
+  // [D/8][8][8] for K and [D][8] for V.  A lane's K row (token col) and its V tokens (4 grp .. 4 grp + 3)
+  // lie in one of the two, so every lane reads through its own address: one load per K chunk and V
+  // group as with 16-token blocks.  A block outside the pool or past the partition reads the first
+  // tile of the cache instead (in bounds); its tokens are masked where they are used.
+  auto load_half = [&](KVRegs<D>& r, int32_t p0, int32_t p1, int i, int my_n, int h) {
+    const bool ok0 = i < my_n && p0 >= 0 && p0 < a.num_blocks;
+    const bool ok1 = i < my_n && p1 >= 0 && p1 < a.num_blocks;
+    const int64_t hb = static_cast<int64_t>(h) * head_bytes;
+    const int64_t o0 = ok0 ? static_cast<int64_t>(p0) * blk_stride + hb : 0;
+    const int64_t o1 = ok1 ? static_cast<int64_t>(p1) * blk_stride + hb : 0;
+    const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(kc + (col < 8 ? o0 : o1) + grp * 128 + (col & 7) * 16);
+    const u32x2_t* vp = reinterpret_cast<const u32x2_t*>(vc + (grp < 2 ? o0 : o1) + col * 16 + (grp & 1) * 8);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) r.k[kk] = __builtin_nontemporal_load(kp + kk * 32);
+#pragma unroll
+    for (int nn = 0; nn < NV; ++nn) r.v[nn] = __builtin_nontemporal_load(vp + nn * 32);
+  };
+  // Ring position i's loads: ids0 / ids1 hold the tile's (first, second) cache block (kBkHalf) or ids0
+  // the block and t its tile or unit (the other kinds).
+  auto load_pos = [&](Regs& r, int32_t ids0, int32_t ids1, int t, int i, int my_n, int h) {
+    if constexpr (HALF) load_half(r, ids0, ids1, i, my_n, h);
+    else load_tile(r, ids0, t, i, my_n, h);
   };
   // Ring positions per partition: a multiple of NBUF, at least NBUF; those past my_n are empty.
   auto steps_of = [&](const Item& it) { return max(NBUF, (it.my_n + NBUF - 1) / NBUF * NBUF); };
@@ -894,7 +933,8 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       }
     };
     auto compute_tile = [&](KVRegs<D>& r, int i) {
-      const int32_t phys = __builtin_amdgcn_readlane(cur_ids, i < 63 ? i : 63);
+      constexpr int kLastPos = HALF ? 31 : 63;  // lanes of cur_ids holding a position's (first) block
+      const int32_t phys = __builtin_amdgcn_readlane(cur_ids, i < kLastPos ? i : kLastPos);
       int nv;          // tokens of the block
       int nv_col[NT];  // tokens of the block this lane's query column sees, per column tile
       int t_lo = 0, t_hi = NT - 1;  // column tiles to compute (wave-uniform)
@@ -913,8 +953,18 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
         const int bl = cur.b0 + unit_of(i);
         nv = cur.n - bl * kBlockTokens;
         nv = nv > kBlockTokens ? kBlockTokens : nv;
-        if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
-        nv_col[0] = nv;
+        if constexpr (HALF) {
+          // This lane's tokens (and V dims' tokens) lie in block grp >> 1 of the tile; a block id
+          // outside the pool leaves its 8 tokens out.
+          const int32_t p1 = __builtin_amdgcn_readlane(cur_ids, (i < 31 ? i : 31) + 32);
+          const bool ok0 = phys >= 0 && phys < a.num_blocks, ok1 = p1 >= 0 && p1 < a.num_blocks;
+          if (i >= cur.my_n) nv = 0;
+          nv_col[0] = (grp < 2 ? ok0 : ok1) ? nv : 0;
+          if (!ok0 || !ok1) nv = min(nv, kBlockTokens - 1);  // some lane masks: take the V mask below
+        } else {
+          if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
+          nv_col[0] = nv;
+        }
       }
 
       float alpha[NT];
@@ -943,11 +993,12 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       // not full has them selected out of its V registers (in place: the ring reloads them next);
       // a full block (all but a context's last) needs no mask.
       if (nv < kBlockTokens) {
+        const int nvl = HALF ? nv_col[0] : nv;  // kBkHalf: a lane's own block may be out
         uint32_t keep[2];
 #pragma unroll
         for (int wd = 0; wd < 2; ++wd) {
           const int t0 = grp * 4 + 2 * wd;
-          keep[wd] = (t0 < nv ? 0x0000ffffu : 0u) | (t0 + 1 < nv ? 0xffff0000u : 0u);
+          keep[wd] = (t0 < nvl ? 0x0000ffffu : 0u) | (t0 + 1 < nvl ? 0xffff0000u : 0u);
         }
 #pragma unroll
         for (int nn = 0; nn < NV; ++nn) r.v[nn] = u32x2_t{r.v[nn][0] & keep[0], r.v[nn][1] & keep[1]};
@@ -975,7 +1026,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       for (int j = 0; j < NBUF; ++j) {
         // Ring lookahead position; past this partition's last step it is the next one's.
         int la = i + j + NBUF - 1;
-        int32_t phys;
+        int32_t phys, phys1 = 0;
         int tile = 0;
         int mn = cur.my_n, hh = cur.h;
         if (la >= steps) {
@@ -985,7 +1036,12 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
           int32_t t = nx_ids;
           asm volatile("" : "+v"(t));
           la -= steps;
-          phys = __builtin_amdgcn_readlane(t, la < 63 ? la : 63);
+          if constexpr (HALF) {
+            phys = __builtin_amdgcn_readlane(t, la < 31 ? la : 31);
+            phys1 = __builtin_amdgcn_readlane(t, (la < 31 ? la : 31) + 32);
+          } else {
+            phys = __builtin_amdgcn_readlane(t, la < 63 ? la : 63);
+          }
           if constexpr (MULTI) {
             int32_t tm = nx_meta;
             asm volatile("" : "+v"(tm));
@@ -993,11 +1049,14 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
           }
           mn = nx_my_n;
           hh = nxi.h;
+        } else if constexpr (HALF) {
+          phys = __builtin_amdgcn_readlane(cur_ids, la < 31 ? la : 31);
+          phys1 = __builtin_amdgcn_readlane(cur_ids, (la < 31 ? la : 31) + 32);
         } else {
           phys = __builtin_amdgcn_readlane(cur_ids, la < 63 ? la : 63);
           if constexpr (MULTI) tile = __builtin_amdgcn_readlane(cur_meta, la < 63 ? la : 63) >> 16;
         }
-        load_tile(ring[(j + NBUF - 1) % NBUF], phys, tile, la, mn, hh);
+        load_pos(ring[(j + NBUF - 1) % NBUF], phys, phys1, tile, la, mn, hh);
         if (i + j < cur.my_n) compute(ring[j], i + j);  // positions past my_n only pad the ring
       }
     }
@@ -1121,8 +1180,8 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
   seg_p0 = A.it.p;
 #pragma unroll
   for (int j = 0; j < NBUF - 1; ++j)
-    load_tile(ring[j], __builtin_amdgcn_readlane(A.ids, j), MULTI ? __builtin_amdgcn_readlane(A.meta, j) >> 16 : 0, j,
-              A.it.my_n, A.it.h);
+    load_pos(ring[j], __builtin_amdgcn_readlane(A.ids, j), HALF ? __builtin_amdgcn_readlane(A.ids, j + 32) : 0,
+             MULTI ? __builtin_amdgcn_readlane(A.meta, j) >> 16 : 0, j, A.it.my_n, A.it.h);
   // Weighted length of a partition: its blocks, C, and CE if it ends its context.
   auto wlen = [&](const Item& it) { return it.len + C + (it.p == it.np - 1 ? CE : 0); };
   off += wlen(A.it);
@@ -1359,7 +1418,7 @@ struct Plan {
   int32_t ctx_limit;
   int32_t max_parts;      // partitions of the longest context
   Route route;
-  int32_t sub_log2;       // kSplit: log2 of the 16-token tiles per cache block
+  int32_t sub_log2;       // kSplit: log2 of the 16-token tiles per cache block; -1: two 8-token blocks per tile
   bool group;             // kSplit: over groups of sequences sharing leading blocks
   int32_t part_cols;      // kSplit: query columns per partial slot
   size_t ml_offset;       // floats from the workspace start to the (max, sum) pairs
@@ -1407,18 +1466,20 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
   int32_t lsb = 0;
   while (lsb < 6 && (kBlockTokens << lsb) < B) ++lsb;
   const bool tiles = (kBlockTokens << lsb) == B;
+  // 8-token blocks, two to a tile; partitions must hold whole tiles.
+  const bool half_blocks = 2 * B == kBlockTokens && pt % kBlockTokens == 0;
   const bool half = c.dtype != PA_F32 && g <= 16;
   const bool shape = half && (D == 64 || D == 128);
   const bool wide = half && D == 256 && B == kBlockTokens;
   // The split kernel indexes the weighted tiles of all (sequence, KV head) pairs with int32.
-  const bool split = ((shape && tiles) || wide) && p->num_seqs <= kMaxScanSeqs &&
+  const bool split = ((shape && (tiles || half_blocks)) || wide) && p->num_seqs <= kMaxScanSeqs &&
                      int64_t{p->num_seqs} * c.num_kv_heads *
                              ((int64_t{p->max_blocks_per_seq} << lsb) + int64_t{kPartCost} * (parts + 1) + kCtxCost) <
                          0x7fffffffLL;
   out->route = split ? kRouteSplit : (shape && B == kBlockTokens) ? kRouteMfma : kRouteGeneric;
-  out->sub_log2 = split ? lsb : 0;
-  // Head_dim 256 runs sequence by sequence (its grouped form would spill).
-  out->group = split && !wide && p->shared && p->shared->num_groups > 0;
+  out->sub_log2 = split ? (half_blocks ? -1 : lsb) : 0;
+  // Head_dim 256 runs sequence by sequence (its grouped form would spill), and so do 8-token blocks.
+  out->group = split && !wide && !half_blocks && p->shared && p->shared->num_groups > 0;
 
   if (split) {
     // Partials per run (see DecodeArgs::part_cols); a context of one partition never spans runs.  A
@@ -1505,15 +1566,15 @@ int32_t device_cus(int* out) {
 }
 
 // Launch the split kernel with WV wavefronts per workgroup; sets args->run_grid / run_rounds.
-template <int DT, int D, int MODE, int WV, bool MULTI>
+template <int DT, int D, int MODE, int WV, int BK>
 int32_t launch_split_waves(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  const void* fn = reinterpret_cast<const void*>(&decode_split_kernel<DT, D, kPersistRing, MODE, WV, MULTI>);
+  const void* fn = reinterpret_cast<const void*>(&decode_split_kernel<DT, D, kPersistRing, MODE, WV, BK>);
   int resident = 0;
   const int32_t rc = resident_workgroups(fn, WV * kWave, &resident);
   if (rc != PA_OK) return rc;
   args->run_rounds = kSplitRounds;
   args->run_grid = std::min(kSplitRounds * resident, kMaxRuns / kSplitRounds * kSplitRounds);
-  hipExtLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing, MODE, WV, MULTI>),
+  hipExtLaunchKernelGGL((decode_split_kernel<DT, D, kPersistRing, MODE, WV, BK>),
                         dim3(static_cast<uint32_t>(args->run_grid)), dim3(WV * kWave), 0, st, start, stop, 0, *args);
   return PA_OK;
 }
@@ -1523,31 +1584,34 @@ int32_t launch_split_waves(DecodeArgs* args, hipStream_t st, hipEvent_t start, h
 // of 8 wavefronts per CU then halves the runs, partials and merges of each context.  Measured on
 // MI355X: 4 sequences of 131072 tokens, 8 KV heads: 356 -> 339 us; with 512 to 2048 contexts the
 // 8-wavefront form was 2-21% slower.
-template <int DT, int D, int MODE, bool MULTI>
+template <int DT, int D, int MODE, int BK>
 int32_t launch_split(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   int cus = 0;
   const int32_t rc = device_cus(&cus);
   if (rc != PA_OK) return rc;
   const int64_t contexts = int64_t{MODE == kGroup ? args->num_groups : args->num_seqs} * args->hkv;
-  if (contexts < cus) return launch_split_waves<DT, D, MODE, 8, MULTI>(args, st, start, stop);
-  return launch_split_waves<DT, D, MODE, 4, MULTI>(args, st, start, stop);
+  if (contexts < cus) return launch_split_waves<DT, D, MODE, 8, BK>(args, st, start, stop);
+  return launch_split_waves<DT, D, MODE, 4, BK>(args, st, start, stop);
 }
 
 // One launch: over groups when the batch comes with shared prefixes, else over sequences.
-template <int DT, int D, bool MULTI>
+template <int DT, int D, int BK>
 int32_t launch_split_all(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  if (args->num_groups > 0) return launch_split<DT, D, kGroup, MULTI>(args, st, start, stop);
-  return launch_split<DT, D, kPlain, MULTI>(args, st, start, stop);
+  if constexpr (BK != kBkHalf) {
+    if (args->num_groups > 0) return launch_split<DT, D, kGroup, BK>(args, st, start, stop);
+  }
+  return launch_split<DT, D, kPlain, BK>(args, st, start, stop);
 }
 
 template <int DT, int D>
 int32_t launch_split_blocks(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   if constexpr (D == 256) {
     // Plain mode on 16-token blocks only: the other forms would spill.
-    return launch_split_waves<DT, 256, kPlain, 4, false>(args, st, start, stop);
+    return launch_split_waves<DT, 256, kPlain, 4, kBk16>(args, st, start, stop);
   } else {
-    if (args->sub_log2 > 0) return launch_split_all<DT, D, true>(args, st, start, stop);
-    return launch_split_all<DT, D, false>(args, st, start, stop);
+    if (args->sub_log2 > 0) return launch_split_all<DT, D, kBkMulti>(args, st, start, stop);
+    if (args->sub_log2 < 0) return launch_split_all<DT, D, kBkHalf>(args, st, start, stop);
+    return launch_split_all<DT, D, kBk16>(args, st, start, stop);
   }
 }
 
@@ -1562,7 +1626,7 @@ int32_t launch_decode(DecodeArgs args, const Plan& plan, hipStream_t st, hipEven
   if (plan.route == kRouteSplit) {
     // One launch: the split kernel merges its runs in place; it counts in 16-token tiles.
     args.sub_log2 = plan.sub_log2;
-    args.part_blocks <<= plan.sub_log2;
+    args.part_blocks = plan.sub_log2 >= 0 ? args.part_blocks << plan.sub_log2 : args.part_blocks >> 1;
     if constexpr (DT != PA_F32) {
       if (D == 64) return launch_split_blocks<DT, 64>(&args, st, start, stop);
       if (D == 256) return launch_split_blocks<DT, 256>(&args, st, start, stop);

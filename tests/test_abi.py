@@ -89,7 +89,10 @@ def test_workspace_bytes():
     (pa.PA_BF16, 64, 8, 64, 1024, "decode_split_kernel"),
     (pa.PA_BF16, 128, 4, 4096, 32, "decode_generic_kernel"),
     (pa.PA_BF16, 128, 4, 64, 48, "decode_generic_kernel"),
-    (pa.PA_BF16, 128, 4, 64, 8, "decode_generic_kernel"),
+    (pa.PA_BF16, 128, 4, 64, 8, "decode_split_kernel"),
+    (pa.PA_F16, 64, 2, 64, 8, "decode_split_kernel"),
+    (pa.PA_BF16, 128, 4, 4096, 8, "decode_generic_kernel"),
+    (pa.PA_F32, 128, 1, 64, 8, "decode_generic_kernel"),
     (pa.PA_BF16, 256, 4, 64, 16, "decode_split_kernel"),
     (pa.PA_BF16, 256, 4, 64, 32, "decode_generic_kernel"),
     (pa.PA_BF16, 256, 4, 4096, 16, "decode_generic_kernel"),
@@ -104,6 +107,15 @@ def test_decode_kernel_query(dtype, d, g, S, bs, kernel):
     assert pa.lib.paged_attention_decode_kernel(ctypes.byref(_params(S=0))) == b""
     assert pa.lib.paged_attention_decode_kernel(ctypes.byref(_params(hq=6))) == b""
     assert pa.lib.paged_attention_decode_kernel(None) == b""
+
+
+@pytest.mark.parametrize("part,kernel", [(0, "decode_split_kernel"), (16, "decode_split_kernel"),
+                                         (1024, "decode_split_kernel"), (8, "decode_generic_kernel"),
+                                         (24, "decode_generic_kernel")])
+def test_eight_token_blocks_need_partitions_of_whole_tiles(part, kernel):
+    # 8-token blocks go to the split kernel two to a 16-token tile, so a partition must hold whole tiles.
+    p = _params(S=64, hq=16, hkv=4, d=128, bs=8, maxb=256, maxctx=2048, dtype=pa.PA_BF16, part=part)
+    assert pa.lib.paged_attention_decode_kernel(ctypes.byref(p)) == kernel.encode()
 
 
 def test_decode_binding_checks_metadata_shapes():

@@ -274,11 +274,12 @@ def test_start_and_stop_events_bracket_the_kernels(part):
     assert start.elapsed_time(stop) >= 0.0
 
 
-@pytest.mark.parametrize("dtype,B", [("bf16", 8), ("bf16", 32), ("f32", 32), ("f16", 64)])
+@pytest.mark.parametrize("dtype,B", [("bf16", 8), ("bf16", 32), ("f32", 32), ("f16", 64), ("f32", 8)])
 def test_other_block_sizes(dtype, B):
-    # Blocks of 8 tokens, and fp32 caches, take the VALU kernel (and the partition merge); bf16/fp16
-    # blocks of 32 and 64 tokens take the split kernel as 16-token tiles.  Lengths around the block
-    # size, several blocks and several partitions.
+    # fp32 caches take the VALU kernel (and the partition merge); bf16/fp16 blocks of 8 tokens take
+    # the split kernel two to a 16-token tile, and blocks of 32 and 64 tokens as 16-token tiles (a
+    # partition of 4 * 8 = 32 tokens holds two tiles).  Lengths around the block size, several
+    # blocks and several partitions.
     lens = [1, B - 1, B, B + 1, 2 * B + 3, 300, 1000]
     cfg = synth.scaled(synth.C3, lens=lens, dtype=dtype, block_size=B)
     pd = PagedDecode(cfg)
@@ -324,6 +325,58 @@ def test_multi_tile_blocks_match_16_token_blocks(dtype):
     assert float(np.max(np.abs(outs[1] - outs[0]))) <= 1e-5
     assert float(np.max(np.abs(outs[2] - outs[0]))) <= 1e-5
     assert max_err(torch.from_numpy(outs[2]), pd) <= tol_for(dtype)
+
+
+@pytest.mark.parametrize("base,dtype,D", [(synth.C3, "bf16", 128), (synth.C2, "f16", 128), (synth.C3, "f16", 64),
+                                         (synth.C2, "bf16", 64)])
+def test_eight_token_blocks(base, dtype, D):
+    # Blocks of 8 tokens go to the split kernel, two to a 16-token tile: contexts ending inside a
+    # tile's first block, on the block edge inside a tile, on a tile edge, and spanning several
+    # 512-token partitions.  Partitions of one tile and of 1024 tokens; a partition of 8 tokens
+    # (half a tile) takes the VALU kernel.
+    import paged_kv_cache_358_amd as pa
+    lens = [1, 7, 8, 9, 15, 16, 17, 23, 24, 25, 511, 512, 513, 1500, 2047]
+    cfg = synth.scaled(base, lens=lens, dtype=dtype, block_size=8, head_dim=D)
+    pd = PagedDecode(cfg)
+    assert pd.k_cache.shape[3] == 8
+    out = torch.empty(pd.q.shape, dtype=torch.float32, device="cuda")
+    args = (pd.q, pd.k_cache, pd.v_cache, pd.block_tables, out, pd.max_context_len)
+    assert pa.paged_attention_decode_kernel(*args) == "decode_split_kernel"
+    assert pa.paged_attention_decode_kernel(*args, partition_size=8) == "decode_generic_kernel"
+    for part in (None, 16, 1024, 8):
+        assert max_err(pd.run(partition_size=part), pd) <= tol_for(dtype), part
+    o16 = pd.run(out_dtype=pd.q.dtype).float().cpu().numpy()
+    check_16bit_output(o16, pd.run().cpu().numpy(), dtype)
+    for s in range(cfg.num_seqs):
+        ref = pd.oracle(s)
+        assert np.all(np.abs(o16[s] - ref) <= bound_16bit(ref, dtype)), s
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_eight_token_blocks_match_16_token_blocks(dtype):
+    # Two 8-token blocks make the same 16-token tile as one 16-token block, and the waves take the
+    # tiles in the same order: the same sequences in caches of 8- and 16-token blocks give the same
+    # bits.
+    lens = [1, 8, 16, 33, 200, 511, 512, 513, 777, 1024, 1500, 2047, 3000]
+    outs = []
+    for B in (16, 8):
+        pd = PagedDecode(synth.scaled(synth.C3, lens=lens, dtype=dtype, block_size=B))
+        outs.append(pd.run())
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_eight_token_blocks_ignore_table_entries_past_the_context():
+    # Past each context the table may hold anything, also in the second block of the context's last
+    # tile; a context ending on a block edge inside a tile leaves that block unread.
+    cfg = synth.scaled(synth.C3, lens=[8, 20, 300, 1, 24], block_size=8)
+    pd = PagedDecode(cfg)
+    ref = pd.run()
+    t = pd.tables_np.copy()
+    for s, n in enumerate(pd.lens):
+        t[s, -(-int(n) // 8):] = 2 ** 30
+    assert torch.equal(ref, pd.run(block_tables=torch.from_numpy(t).cuda()))
+    t[:, :] = np.where(t == 2 ** 30, -1, t)
+    assert torch.equal(ref, pd.run(block_tables=torch.from_numpy(t).cuda()))
 
 
 @pytest.mark.parametrize("dtype,hq,hkv", [("bf16", 16, 4), ("f16", 8, 8), ("bf16", 32, 2)])
