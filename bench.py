@@ -542,6 +542,7 @@ def run_prefill(args):
     q = torch.randn(T, hq, D, device=dev).to(torch.bfloat16)
     out = torch.empty(T, hq, D, device=dev, dtype=torch.float32)
     bt, cl, qst = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (tables, lens_np, qs))
+    order = torch.from_numpy(pa.prefill_order(lens_np, qs)).to(dev)  # heaviest sequences first
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for a, b in ev:
         a.record()
@@ -549,7 +550,7 @@ def run_prefill(args):
 
     def launch(events=None):
         pa.paged_attention_prefill(q, k_cache, v_cache, bt, cl, qst, cfg.softmax_scale, out,
-                                   max_query_len=int(chunks.max()),
+                                   max_query_len=int(chunks.max()), seq_order=order,
                                    start_event=None if events is None else events[0],
                                    stop_event=None if events is None else events[1])
 

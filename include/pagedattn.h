@@ -246,6 +246,11 @@ typedef struct pa_prefill_params {
   void* stream;                /* hipStream_t */
   void* start_event;           /* hipEvent_t or NULL, as for paged_attention_decode */
   void* stop_event;            /* hipEvent_t or NULL, as for paged_attention_decode */
+  const int32_t* seq_order;    /* NULL, or [S] int32 (device or pinned host): the order in which the sequences'
+                                  workgroups are started, a permutation of 0 .. S-1 (pa_prefill_order gives
+                                  the heaviest first).  It changes the launch's tail, never the results;
+                                  sequences it names twice are computed twice, sequences it leaves out are
+                                  not written, entries outside 0 .. S-1 are skipped */
 } pa_prefill_params;
 
 /*
@@ -268,6 +273,15 @@ typedef struct pa_prefill_params {
 int32_t paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                 const int32_t* context_lens, const int32_t* query_start, float scale, void* out,
                                 const pa_prefill_params* p);
+
+/*
+ * pa_prefill_order: the scheduling order for paged_attention_prefill's seq_order, on the host: sequences by
+ * descending work (the (row, token) pairs their chunk attends over), ties in batch order.
+ *   context_lens [S], query_start [S + 1]  host int32, as for paged_attention_prefill
+ *   order        [S] host int32, written with a permutation of 0 .. S-1
+ * PA_ERR_INVALID_ARG for S < 0 or a NULL pointer with S > 0.
+ */
+int32_t pa_prefill_order(const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs, int32_t* order);
 
 /*
  * pa_device_address: the address a kernel uses for p, which is device memory (returned as is) or pinned host

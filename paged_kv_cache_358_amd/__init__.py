@@ -49,7 +49,7 @@ class DecodeParams(ctypes.Structure):
 class PrefillParams(ctypes.Structure):
     _fields_ = [("num_seqs", _i32), ("num_tokens", _i32), ("num_q_heads", _i32), ("max_blocks_per_seq", _i32),
                 ("max_query_len", _i32), ("out_dtype", _i32), ("cache", CacheDesc), ("stream", _vp),
-                ("start_event", _vp), ("stop_event", _vp)]
+                ("start_event", _vp), ("stop_event", _vp), ("seq_order", _vp)]
 
 
 _PAllocPtr = ctypes.POINTER(_vp)
@@ -83,6 +83,7 @@ SIGNATURES = {
     "pa_free_list": (_i32, [_vp, _P32, _i32, _P32]),
     "pa_build_batch": (_i32, [_vp, _P64, _i32, _i32, _P32, _P32]),
     "pa_shared_prefixes": (_i32, [_P32, _P32, _i32, _i32, _i32, _i32, _i32, _P32, _i32, _P32]),
+    "pa_prefill_order": (_i32, [_P32, _P32, _i32, _P32]),
 }
 
 
@@ -354,12 +355,14 @@ def paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, context_le
 
 
 def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float, out, *,
-                            max_query_len: int, stream=None, start_event=None, stop_event=None):
+                            max_query_len: int, stream=None, start_event=None, stop_event=None, seq_order=None):
     """out[row, j] = causal attention of chunk row `row` over its sequence's cached tokens.
 
     q / out [T, H_q, D]; query_start int32 [S + 1] (device) gives each sequence's first row;
     context_lens int32 [S] counts the sequence's tokens including its chunk (already appended);
-    ``max_query_len`` is a host-known upper bound of the chunk lengths.
+    ``max_query_len`` is a host-known upper bound of the chunk lengths.  ``seq_order`` (int32 [S],
+    device or pinned host, from ``prefill_order``) starts the heaviest sequences first; it changes
+    the launch's tail, not the results.
     """
     torch = _torch()
     _require_device(q, k_cache, v_cache, block_tables, context_lens, query_start, out)
@@ -377,12 +380,31 @@ def paged_attention_prefill(q, k_cache, v_cache, block_tables, context_lens, que
     S = block_tables.shape[0]
     if query_start.numel() != S + 1 or context_lens.numel() != S:
         raise ValueError("query_start must have S + 1 entries and context_lens S")
+    if seq_order is not None:
+        _require_index(seq_order)
+        if seq_order.dtype != torch.int32 or seq_order.numel() != S:
+            raise ValueError("seq_order must be int32 with S entries")
     p = PrefillParams(S, T, hq, block_tables.shape[1], int(max_query_len), torch_dtype_code(out.dtype), c,
-                      _stream_ptr(stream).value, _event_ptr(start_event), _event_ptr(stop_event))
+                      _stream_ptr(stream).value, _event_ptr(start_event), _event_ptr(stop_event),
+                      _iptr(seq_order).value)
     _check(lib.paged_attention_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
                                        _ptr(query_start), float(scale), _ptr(out), ctypes.byref(p)),
            "paged_attention_prefill")
     return out
+
+
+def prefill_order(context_lens, query_start):
+    """Host int32 [S]: the sequences by descending prefill work (the (row, token) pairs of their chunk),
+    ties in batch order, for ``paged_attention_prefill(..., seq_order=...)``.  context_lens [S] and
+    query_start [S + 1] are host arrays."""
+    ln, lptr = _as_i32(context_lens)
+    qs, qptr = _as_i32(query_start)
+    S = int(ln.size)
+    if qs.size != S + 1:
+        raise ValueError("query_start must have S + 1 entries")
+    order = np.empty(S, dtype=np.int32)
+    _check(lib.pa_prefill_order(lptr, qptr, S, order.ctypes.data_as(_P32)), "pa_prefill_order")
+    return order
 
 
 def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, *, stream=None):

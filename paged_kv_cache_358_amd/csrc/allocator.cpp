@@ -322,4 +322,26 @@ int32_t pa_shared_prefixes(const int32_t* tables, const int32_t* lens, int32_t n
   return PA_OK;
 }
 
+// Prefill scheduling order: sequences by descending work, the (row, token) pairs of their chunk (a row at
+// position p sees p + 1 tokens), ties in batch order.  Started first, the longest workgroups no longer
+// make the launch's tail.
+int32_t pa_prefill_order(const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs, int32_t* order) {
+  if (num_seqs < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!context_lens || !query_start || !order) return PA_ERR_INVALID_ARG;
+  std::vector<int64_t> work(static_cast<size_t>(num_seqs));
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t n = std::max<int32_t>(0, context_lens[s]);
+    const int64_t c = std::max<int64_t>(0, int64_t{query_start[s + 1]} - query_start[s]);
+    // rows i = 0 .. c - 1 at positions n - c + i; those at position >= 0 see n - c + i + 1 tokens
+    const int64_t first = std::max<int64_t>(0, c - n);  // rows before it have no position
+    const int64_t lo = n - c + first + 1, hi = n;     // tokens seen by the first and last such row
+    work[static_cast<size_t>(s)] = c > first ? (lo + hi) * (c - first) / 2 : 0;
+    order[s] = s;
+  }
+  std::stable_sort(order, order + num_seqs,
+                   [&](int32_t a, int32_t b) { return work[static_cast<size_t>(a)] > work[static_cast<size_t>(b)]; });
+  return PA_OK;
+}
+
 }  // extern "C"

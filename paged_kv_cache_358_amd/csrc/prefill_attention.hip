@@ -43,6 +43,8 @@ struct PrefillArgs {
   int32_t per_xcd;    // workgroups per XCD
   int64_t items;      // sequences x query heads x tiles
   int64_t num_blocks;
+  const int32_t* seq_order;  // [S]: the sequence of each scheduling rank, or null (batch order)
+  int32_t num_seqs;
 };
 
 constexpr int kPrefillWaves = 4;
@@ -93,7 +95,12 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
   if (sj >= a.items / a.tiles) return;
   const int tile = static_cast<int>(kx % a.tiles);
   const int j = static_cast<int>(sj % a.hq);
-  const int s = static_cast<int>(sj / a.hq);
+  // Groups go out in rank order: rank r is sequence seq_order[r] when an order is given.
+  int s = static_cast<int>(sj / a.hq);
+  if (a.seq_order) {
+    s = a.seq_order[s];
+    if (s < 0 || s >= a.num_seqs) return;
+  }
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;
@@ -379,6 +386,8 @@ extern "C" int32_t paged_attention_prefill(const void* q, const void* k_cache, c
   a.max_blocks = p->max_blocks_per_seq;
   a.out_f32 = p->out_dtype == PA_F32 ? 1 : 0;
   a.num_blocks = c.num_blocks;
+  a.seq_order = p->seq_order;
+  a.num_seqs = p->num_seqs;
   a.tiles = (p->max_query_len + kPrefillRows - 1) / kPrefillRows;
   a.items = static_cast<int64_t>(p->num_seqs) * p->num_q_heads * a.tiles;
   const int64_t groups = static_cast<int64_t>(p->num_seqs) * p->num_q_heads;

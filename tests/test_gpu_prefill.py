@@ -151,6 +151,37 @@ def test_long_context_chunk_sampled_rows():
     _check(pd, chunks, q_np, got, qs, rows_per_seq=[0, 1, 63, 64, 200, 255, 511])
 
 
+def test_scheduling_order_changes_no_bit():
+    # seq_order only changes which workgroups start first: the heaviest-first order, a reversed one
+    # and the batch order give the same bits; an order that leaves a sequence out leaves its rows
+    # unwritten.
+    lens = [300, 17, 1025, 64, 700, 5]
+    chunks = [120, 17, 400, 1, 256, 5]
+    cfg = synth.scaled(synth.C2, lens=lens)
+    pd = PagedDecode(cfg)
+    q_np = _chunk_queries(cfg, chunks, 9)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = to_torch(q_np, cfg.dtype, "cuda")
+
+    def run(order):
+        out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+        pa.paged_attention_prefill(q, pd.k_cache, pd.v_cache, pd.block_tables, pd.context_lens,
+                                   torch.from_numpy(qs).cuda(), cfg.softmax_scale, out, max_query_len=max(chunks),
+                                   seq_order=None if order is None else torch.from_numpy(np.asarray(order, np.int32)).cuda())
+        torch.cuda.synchronize()
+        return out.cpu()
+
+    heavy = pa.prefill_order(np.asarray(lens, np.int32), qs)
+    assert heavy[0] == 2 and heavy[-1] == 5
+    ref = run(None)
+    assert torch.equal(run(heavy), ref)
+    assert torch.equal(run(heavy[::-1].copy()), ref)
+    partial = run([2, 0, 1, 3, 4, 99])                     # sequence 5 left out, 99 skipped
+    assert torch.equal(partial[:qs[5]], ref[:qs[5]])
+    assert torch.isnan(partial[qs[5]:]).all()
+    _check(pd, chunks, q_np, ref.numpy(), qs)
+
+
 def test_rejects_what_it_does_not_cover():
     cfg = synth.scaled(synth.C3, lens=[16])
     pd = PagedDecode(cfg)
