@@ -71,6 +71,7 @@ __device__ __forceinline__ void prefill_store4(const PrefillArgs& a, int64_t idx
 // both blocks of a pair, the order in which the score tiles leave them in a lane; P is split into
 // hi + lo in the cache's 16-bit type, so that it enters the product with about 16 significant bits.
 constexpr int kStageBlocks = kPrefillWaves;  // 16-token blocks per stage: one per wave
+constexpr float kLazyLog2 = 8.0f;  // how far (log2 units) a score may exceed the softmax reference point m
 
 template <int DT, int D>
 __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void prefill_tiled_kernel(
@@ -258,12 +259,22 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
       for (int bb = 1; bb < kStageBlocks; ++bb)
         bm = fmaxf(bm, fmaxf(fmaxf(sc[t][bb][0], sc[t][bb][1]), fmaxf(sc[t][bb][2], sc[t][bb][3])));
       bm = rows4_max(bm) * kscale;
-      const float m_new = fmaxf(m[t], bm);
-      const bool rescale = __builtin_amdgcn_ballot_w64(m_new != m[t]) != 0;
-      const float alpha = (m[t] == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m[t] - m_new);
-      // A row that has seen no token yet keeps m = -inf; exponents are taken against 0 then, and
-      // exp2(-inf) = 0 gives its masked tokens their weight without a select.
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      // m is a reference point, not the running maximum: the weights exp2(k s - m) of any m give the
+      // same softmax once divided by their sum.  It moves (and l and O are rescaled) only when some
+      // row of the wave sees a score more than kLazyLog2 above it, so weights stay below
+      // 2^kLazyLog2 and most stages skip the rescale.  A row that has seen no token has m = -inf and
+      // moves at its first visible token.
+      if (__builtin_amdgcn_ballot_w64(bm > m[t] + kLazyLog2) != 0) {
+        const float m_new = fmaxf(m[t], bm);
+        const float alpha = (m[t] == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m[t] - m_new);
+        l[t] *= alpha;
+#pragma unroll
+        for (int nn = 0; nn < NV; ++nn) o[t][nn] *= alpha;
+        m[t] = m_new;
+      }
+      // Exponents of a row still at m = -inf (no visible token yet) are taken against 0: exp2(-inf) = 0
+      // weighs its masked tokens without a select.
+      const float m_use = m[t] == -INFINITY ? 0.0f : m[t];
       float pr[kStageBlocks][4];
       float sum = 0.f;
 #pragma unroll
@@ -273,12 +284,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
           pr[bb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][bb][e], kscale, -m_use));
           sum += pr[bb][e];
         }
-      l[t] = l[t] * alpha + sum;
-      m[t] = m_new;
-      if (rescale) {
-#pragma unroll
-        for (int nn = 0; nn < NV; ++nn) o[t][nn] *= alpha;
-      }
+      l[t] += sum;
 #pragma unroll
       for (int pp = 0; pp < kStageBlocks / 2; ++pp) {
         u32x2_t ha, la, hb, lb;
