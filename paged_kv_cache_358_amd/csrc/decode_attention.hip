@@ -452,18 +452,15 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
   const int sbm = (1 << lsb) - 1;
   // PAIR (plain mode on blocks of 32 or more tokens): a ring position holds 32 tokens, two
   // tiles, so that every V load covers 32 consecutive tokens of each V row (the whole row of a
-  // 32-token block) and the PV product runs on 16x16x32 MFMAs; waves take blocks in turn and a wave streams all pairs of its block on
-  // consecutive positions.  Group mode keeps one tile per position and per turn: a member's own
-  // tiles need not start on a block boundary of the group's tile sequence.
+  // 32-token block) and the PV product runs on 16x16x32 MFMAs; waves take the pairs in turn.
+  // Group mode keeps one tile per position and per turn: a member's own tiles need not start on a
+  // block boundary of the group's tile sequence.
   constexpr bool PAIR = MULTI && MODE == kPlain;
   constexpr int kUnitTokens = PAIR ? 2 * kBlockTokens : kBlockTokens;  // tokens per ring position
   const int lu = PAIR ? lsb - 1 : lsb;  // log2 of the ring units per cache block
   const int um = (1 << lu) - 1;
   // Unit (from the partition's first) of this wave's ring position i.
-  auto unit_of = [&](int i) {
-    if constexpr (PAIR) return ((w + WV * (i >> lu)) << lu) + (i & um);
-    else return w + WV * i;
-  };
+  auto unit_of = [&](int i) { return w + WV * i; };
   const int g = a.group;
   const int J = gridDim.x;          // chunks = NR rounds of R
   const int C = a.part_cost;        // fixed cost of a partition, in blocks of streaming
@@ -624,17 +621,10 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       it.np = (nb + PB - 1) / PB;
       it.len = min(PB, nb - p * PB);
       it.b0 = p * PB;
-      if constexpr (PAIR) {
-        // Pairs and blocks of the partition (only a context's last can be partial) and this
-        // wave's share of the pairs.
-        const int lenu = (it.len + 1) >> 1;
-        const int lenb = (lenu + um) >> lu;
-        const int myb = lenb > w ? (lenb - w + WV - 1) / WV : 0;
-        it.my_n = myb << lu;
-        if (myb > 0 && w + WV * (myb - 1) == lenb - 1) it.my_n -= (lenb << lu) - lenu;
-      } else {
-        it.my_n = (it.len > w) ? (it.len - w + WV - 1) / WV : 0;
-      }
+      // This wave's share of the partition's ring units (pairs of tiles in PAIR; only a context's
+      // last pair can be half full), dealt to the waves in turn.
+      const int lenu = PAIR ? (it.len + 1) >> 1 : it.len;
+      it.my_n = (lenu > w) ? (lenu - w + WV - 1) / WV : 0;
     }
     int64_t qrow[NT];
     if constexpr (MODE == kGroup) {
@@ -720,7 +710,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
   int k_off[PAIR ? 2 : 1];
   if constexpr (PAIR) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) k_off[h] = ((grp << (4 + lsb)) + 8 * (col >> 2) + 4 * h + (col & 3)) * 16;
+    for (int h = 0; h < 2; ++h) k_off[h] = ((grp << (4 + lsb)) + 16 * h + col) * 16;
   } else {
     k_off[0] = MULTI ? ((grp << (4 + lsb)) + col) * 16 : lane * 16;
   }
@@ -898,9 +888,21 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) sacc[hh] = mfma_qk<DT>(r.k[hh][kk], qc[0][kk], sacc[hh]);
       }
-      float x[8];  // token 8 grp + j of the unit: half j / 4, row 4 grp + j % 4
+      // Half h's score tile holds token 16 h + 4 grp + e of the unit in lane (col, grp), element e; the PV
+      // operand wants tokens 8 grp .. 8 grp + 7 in lane group grp.  Two permlane swaps move them there:
+      // lane groups 2, 3 of half 0 with groups 0, 1 of half 1, then the odd groups' first four with
+      // the even groups' last four.
+      float x[8];  // token 8 grp + j of the unit
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = (grp * 8 + j < nv) ? sacc[j >> 2][j & 3] * a.scale_log2 : -INFINITY;
+      for (int e = 0; e < 4; ++e) {
+        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sacc[0][e]), __float_as_uint(sacc[1][e]),
+                                                          false, false);
+        const auto s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
+        x[e] = __uint_as_float(s16[0]);
+        x[4 + e] = __uint_as_float(s16[1]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = (grp * 8 + j < nv) ? x[j] * a.scale_log2 : -INFINITY;
       const float bm = rows4_max(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                                        fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
       const float m_new = fmaxf(m[0], bm);

@@ -89,10 +89,10 @@ struct KVRegs {
   u32x2_t v[D / 16];  // V^T operand, 4 tokens of one dim per PV MFMA
 };
 
-// 32 tokens of one cache block: K as two 16-row operands (rows of half h are tokens
-// 8 (r / 4) + 4 h + r % 4), V^T with 8 consecutive tokens of one dim per lane, the operand of a
-// 16x16x32 PV MFMA.  Lane group j then holds the probabilities of tokens 8 j .. 8 j + 7 from the
-// two halves' score tiles, in the order the PV operand needs.
+// 32 tokens of one cache block: K as two 16-row operands (row r of half h is token 16 h + r, so
+// that every K load reads whole 256-byte runs of a chunk), V^T with 8 consecutive tokens of one
+// dim per lane, the operand of a 16x16x32 PV MFMA.  Two permlane swaps bring the probabilities of
+// tokens 8 j .. 8 j + 7 to lane group j, in the order the PV operand needs.
 template <int D>
 struct KVPairRegs {
   u32x4_t k[2][D / 32];
