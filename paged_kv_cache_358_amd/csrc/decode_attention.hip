@@ -27,7 +27,7 @@
 // input's 16-bit type, and each half goes through its own PV MFMA, so the probabilities
 // enter with ~16 significant bits instead of 8 while V and the accumulation stay exact
 // fp32.  Blocks of 32 or more tokens (plain mode) take 32 tokens per step with
-// 16x16x32 PV MFMAs.
+// 16x16x32 PV MFMAs; 8-token blocks are taken two to a 16-token tile.
 // The cache layout makes every load a contiguous run per instruction: K is stored in
 // 16-byte chunks [D/8][B tokens][8], so the 64 lanes of one QK operand load read 16
 // tokens of 4 chunks; V is stored transposed [D][B tokens], so a PV operand load reads
