@@ -1,14 +1,14 @@
 """A seeded sweep of decode shapes on the GPU against the fp64 oracle.
 
-Each case draws its shape from a fixed list (block size 16, 32 or 64 tokens, head_dim 64, 128
+Each case draws its shape from a fixed list (block size 8, 16, 32 or 64 tokens, head_dim 64, 128
 or 256, query heads per KV head 1..16, bf16 or fp16 inputs, fp32 or input-dtype output, the
 default partition or one of 16 * 2^k tokens) and its context lengths from a seeded mix of
 short, block-edge and multi-partition lengths, so that every kernel form the library
-dispatches to (split kernel in plain mode on 16-token tiles or 32-token units, head_dim 256,
-the VALU kernel for the rest) meets ragged tails.  Tolerance: max abs error 5e-3 with fp32
-output (bf16/fp16 inputs, fp32 accumulation); a 16-bit output must be the fp32 result rounded
-once: within half an ulp of the output type at the value (half the subnormal spacing for fp16's
-smallest values).
+dispatches to (split kernel in plain mode on 16-token tiles, on pairs of 8-token blocks or on
+32-token units, head_dim 256, the VALU kernel for the rest) meets ragged tails.  Tolerance: max
+abs error 5e-3 with fp32 output (bf16/fp16 inputs, fp32 accumulation); a 16-bit output must be the
+fp32 result rounded once: within half an ulp of the output type at the value (half the subnormal
+spacing for fp16's smallest values).
 """
 import numpy as np
 import pytest
@@ -24,6 +24,7 @@ SHAPES = [
     (16, 128, 8, 8, "bf16"), (16, 128, 16, 4, "f16"), (16, 64, 16, 1, "bf16"), (16, 256, 8, 2, "f16"),
     (16, 256, 16, 16, "bf16"), (16, 128, 24, 8, "bf16"), (32, 128, 8, 8, "f16"), (32, 64, 32, 4, "bf16"),
     (32, 128, 16, 1, "bf16"), (64, 128, 12, 4, "bf16"), (64, 64, 8, 8, "f16"), (32, 256, 4, 2, "bf16"),
+    (8, 128, 16, 2, "bf16"), (8, 64, 8, 8, "f16"), (8, 128, 24, 8, "f16"),
 ]
 
 
