@@ -49,8 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all", choices=["all", "c1", "c2", "c3", "c4", "c5", "prefill"],
                     help="all decode workloads (default), one of them, or chunked prefill on c2's sequences")
-    ap.add_argument("--dtype", default="", choices=["", "bf16", "f16"],
-                    help="16-bit type of the c2/c3/c4/c5 caches (default: the workload's bf16)")
+    ap.add_argument("--dtype", default="", choices=["", "bf16", "f16", "f32"],
+                    help="type of the c2/c3/c4/c5 caches (default: the workload's bf16); f32 runs the VALU kernel")
     ap.add_argument("--chunk", type=int, default=512, help="prefill: chunk rows per sequence (at most its length)")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-context partition in tokens (0 = the workload's own)")
