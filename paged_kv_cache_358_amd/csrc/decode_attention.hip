@@ -1225,36 +1225,46 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
 
 constexpr int kMaxPartTokens = 1024;
 constexpr int kMaxGenericD = 256;
+constexpr int kMaxGenericHeads = 8;  // query heads of one KV head that a generic workgroup serves at once
 
-template <int DT>
+// One wavefront per (partition, KV head, sequence, chunk of at most GH of the KV head's query heads),
+// so that every K/V element it reads serves all GH heads of the chunk.  Scores: a lane per token,
+// its K row read 16 bytes at a time and dotted with the chunk's queries.  Softmax over the
+// partition per head.  Output: a lane per dim, its V row read 16 bytes (several tokens) at a time.
+// Blocks whose id is outside the pool count as empty.  LDS (dynamic): scores [GH][partition
+// tokens], block ids [partition blocks].
+template <int DT, int GH>
 __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
   using st = typename Elem<DT>::storage;
-  constexpr int X = 16 / sizeof(st);
-  __shared__ float q_s[kMaxGenericD];
-  __shared__ float sc[kMaxPartTokens];
-  __shared__ int32_t ids[kMaxPartTokens];  // one per block of the partition (blocks of >= 1 token)
-
-  const int wg = blockIdx.x;
-  const int p = wg % a.max_parts;
-  const int rest = wg / a.max_parts;
-  const int j = rest % a.hq;
-  const int s = rest / a.hq;
-  const int n = clamp_ctx(a, s);
+  constexpr int X = 16 / sizeof(st);  // elements per 16 bytes
+  extern __shared__ float gen_lds[];
+  const int D = a.head_dim;
   const int B = a.block_tokens;
+  const int g = a.group;
+  const int pt = a.part_blocks * B;
+  float* sc = gen_lds;
+  int32_t* ids = reinterpret_cast<int32_t*>(sc + GH * pt);
+
+  const int nch = (g + GH - 1) / GH;
+  int rest = blockIdx.x;
+  const int p = rest % a.max_parts;
+  rest /= a.max_parts;
+  const int hc = rest % nch;
+  rest /= nch;
+  const int h = rest % a.hkv;
+  const int s = rest / a.hkv;
+  const int n = clamp_ctx(a, s);
   const int nparts = num_parts(n, a.part_blocks, B);
   if (p >= nparts) return;
   const int lane = threadIdx.x;
-  const int D = a.head_dim;
-  const int h = j / a.group;
-  const int64_t row = static_cast<int64_t>(s) * a.hq + j;
+  const int j0 = h * g + hc * GH;       // first query head of the chunk
+  const int gh = min(GH, g - hc * GH);  // heads in the chunk
+  const int64_t row0 = static_cast<int64_t>(s) * a.hq + j0;
 
   if (n == 0) {
-    for (int d = lane; d < D; d += kWave) store_out<DT>(a, row * D + d, 0.0f);
+    for (int i = lane; i < gh * D; i += kWave) store_out<DT>(a, (row0 + i / D) * D + i % D, 0.0f);
     return;
   }
-  const st* q = static_cast<const st*>(a.q);
-  for (int d = lane; d < D; d += kWave) q_s[d] = Elem<DT>::to_float(q[row * D + d]);
-  const int pt = a.part_blocks * B;
   const int t0 = p * pt;
   const int t1 = min(n, t0 + pt);
   const int bl0 = t0 / B;
@@ -1267,49 +1277,154 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
 
   const st* kc = static_cast<const st*>(a.k);
   const st* vc = static_cast<const st*>(a.v);
-  const int64_t head_stride = static_cast<int64_t>(D) * B;
-  float mx = -INFINITY;
-  for (int t = t0 + lane; t < t1; t += kWave) {
-    const int id = ids[(t - t0) / B];
-    float x = -INFINITY;
-    if (id >= 0) {
-      const st* kb = kc + (static_cast<int64_t>(id) * a.hkv + h) * head_stride;
-      const int off = t % B;
-      float dot = 0.f;
-      for (int d = 0; d < D; ++d) dot = fmaf(q_s[d], Elem<DT>::to_float(kb[((d / X) * B + off) * X + d % X]), dot);
-      x = dot * a.scale_log2;
+  const int64_t head_elems = static_cast<int64_t>(D) * B;  // one (block, KV head) tile of K or V
+  auto unpack = [](const u32x4_t& raw, float (&f)[X]) {
+    if constexpr (X == 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(raw[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = Elem<DT>::to_float(static_cast<st>(raw[e] & 0xffffu));
+        f[2 * e + 1] = Elem<DT>::to_float(static_cast<st>(raw[e] >> 16));
+      }
     }
-    sc[t - t0] = x;
-    mx = fmaxf(mx, x);
+  };
+
+  // Scores, a lane per token, TPL tokens a lane at a time: K is [D / X][B][X] per tile, so a lane's
+  // 16-byte read is X dims of one token.  The queries are the same for every lane: they are read
+  // from memory at uniform addresses (scalar loads) chunk by chunk, and each chunk serves the lane's
+  // TPL tokens.
+  constexpr int TPL = 4;
+  const st* __restrict__ qg = static_cast<const st*>(a.q);
+  float mx[GH];
+#pragma unroll
+  for (int jj = 0; jj < GH; ++jj) mx[jj] = -INFINITY;
+  for (int tb = t0; tb < t1; tb += kWave * TPL) {
+    const st* kb[TPL];
+    bool ok[TPL];
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      const int t = tb + u * kWave + lane;
+      const int id = t < t1 ? ids[(t - t0) / B] : -1;
+      ok[u] = id >= 0;
+      // A token outside the partition, or of a block outside the pool, reads the cache's first tile
+      // (in bounds) and scores -inf.
+      kb[u] = kc + (ok[u] ? (static_cast<int64_t>(id) * a.hkv + h) * head_elems + static_cast<int64_t>(t % B) * X : 0);
+    }
+    float acc[TPL][GH];
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+#pragma unroll
+      for (int jj = 0; jj < GH; ++jj) acc[u][jj] = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < D / X; ++c) {
+      float qf[GH][X];
+#pragma unroll
+      for (int jj = 0; jj < GH; ++jj)
+#pragma unroll
+        for (int e = 0; e < X; ++e)
+          qf[jj][e] = jj < gh ? Elem<DT>::to_float(qg[(row0 + jj) * D + c * X + e]) : 0.f;
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        float kf[X];
+        unpack(*reinterpret_cast<const u32x4_t*>(kb[u] + static_cast<int64_t>(c) * B * X), kf);
+#pragma unroll
+        for (int jj = 0; jj < GH; ++jj)
+#pragma unroll
+          for (int e = 0; e < X; ++e) acc[u][jj] = fmaf(qf[jj][e], kf[e], acc[u][jj]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      const int t = tb + u * kWave + lane;
+      if (t >= t1) continue;
+#pragma unroll
+      for (int jj = 0; jj < GH; ++jj) {
+        const float x = ok[u] ? acc[u][jj] * a.scale_log2 : -INFINITY;
+        sc[jj * pt + (t - t0)] = x;
+        mx[jj] = fmaxf(mx[jj], x);
+      }
+    }
   }
-  mx = wave_max(mx);
-  float lsum = 0.f;
-  for (int t = t0 + lane; t < t1; t += kWave) {
-    const float e = (mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[t - t0] - mx);
-    sc[t - t0] = e;
-    lsum += e;
+  float L[GH];
+#pragma unroll
+  for (int jj = 0; jj < GH; ++jj) {
+    mx[jj] = wave_max(mx[jj]);
+    float lsum = 0.f;
+    for (int t = t0 + lane; t < t1; t += kWave) {
+      const float e = (mx[jj] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[jj * pt + (t - t0)] - mx[jj]);
+      sc[jj * pt + (t - t0)] = e;
+      lsum += e;
+    }
+    L[jj] = wave_sum(lsum);
   }
-  const float L = wave_sum(lsum);
   __syncthreads();
 
-  const bool single = nparts == 1;
-  for (int d = lane; d < D; d += kWave) {
-    float acc = 0.f;
-    for (int t = t0; t < t1; ++t) {
-      const int id = ids[(t - t0) / B];
-      if (id < 0) continue;
-      const st* vb = vc + (static_cast<int64_t>(id) * a.hkv + h) * head_stride;
-      acc = fmaf(sc[t - t0], Elem<DT>::to_float(vb[d * B + t % B]), acc);
-    }
-    const float res = L > 0.f ? acc / L : 0.f;
-    if (single) {
-      store_out<DT>(a, row * D + d, res);
+  // Output, a lane per dim: V is [D][B] per tile, so a lane's 16-byte read is X tokens of its dim.
+  constexpr int ND = kMaxGenericD / kWave;  // dims per lane, at most
+  float acc[GH][ND];
+#pragma unroll
+  for (int jj = 0; jj < GH; ++jj)
+#pragma unroll
+    for (int dd = 0; dd < ND; ++dd) acc[jj][dd] = 0.f;
+  const bool vec = B % X == 0;
+  for (int b = 0; b < nb; ++b) {
+    const int id = ids[b];
+    if (id < 0) continue;  // uniform: every lane takes the same block
+    const st* vb = vc + (static_cast<int64_t>(id) * a.hkv + h) * head_elems;
+    const int tb = t0 + b * B;              // first token of the block
+    const int tn = min(B, t1 - tb);         // its tokens in the partition
+    if (vec) {
+#pragma unroll 4
+      for (int e0 = 0; e0 < tn; e0 += X) {
+#pragma unroll
+        for (int dd = 0; dd < ND; ++dd) {
+          const int d = lane + dd * kWave;
+          if (d >= D) break;
+          float vf[X];
+          unpack(*reinterpret_cast<const u32x4_t*>(vb + static_cast<int64_t>(d) * B + e0), vf);
+#pragma unroll
+          for (int e = 0; e < X; ++e) {
+            if (e0 + e >= tn) break;  // tokens past the context may hold anything
+#pragma unroll
+            for (int jj = 0; jj < GH; ++jj) acc[jj][dd] = fmaf(sc[jj * pt + (tb - t0) + e0 + e], vf[e], acc[jj][dd]);
+          }
+        }
+      }
     } else {
-      const int64_t prow = row * a.max_parts + p;
-      a.part_o[prow * D + d] = res;
-      if (d == 0) {
-        a.part_ml[prow * 2] = mx;
-        a.part_ml[prow * 2 + 1] = L;
+      for (int e = 0; e < tn; ++e) {
+#pragma unroll
+        for (int dd = 0; dd < ND; ++dd) {
+          const int d = lane + dd * kWave;
+          if (d >= D) break;
+          const float v = Elem<DT>::to_float(vb[static_cast<int64_t>(d) * B + e]);
+#pragma unroll
+          for (int jj = 0; jj < GH; ++jj) acc[jj][dd] = fmaf(sc[jj * pt + (tb - t0) + e], v, acc[jj][dd]);
+        }
+      }
+    }
+  }
+
+  const bool single = nparts == 1;
+#pragma unroll
+  for (int jj = 0; jj < GH; ++jj) {
+    if (jj >= gh) break;
+    const int64_t row = row0 + jj;
+#pragma unroll
+    for (int dd = 0; dd < ND; ++dd) {
+      const int d = lane + dd * kWave;
+      if (d >= D) break;
+      const float res = L[jj] > 0.f ? acc[jj][dd] / L[jj] : 0.f;
+      if (single) {
+        store_out<DT>(a, row * D + d, res);
+      } else {
+        const int64_t prow = row * a.max_parts + p;
+        a.part_o[prow * D + d] = res;
+        if (d == 0) {
+          a.part_ml[prow * 2] = mx[jj];
+          a.part_ml[prow * 2 + 1] = L[jj];
+        }
       }
     }
   }
@@ -1651,10 +1766,24 @@ int32_t launch_decode(DecodeArgs args, const Plan& plan, hipStream_t st, hipEven
                               dim3(kWaves * kWave), 0, st, start, main_stop, 0, args);
     }
   } else {
-    const int64_t nwg = int64_t{args.max_parts} * args.hq * args.num_seqs;
+    // Chunks of up to kMaxGenericHeads query heads per KV head: GH = the smallest power of two
+    // that holds the group (or a chunk of it).
+    const int g = args.group;
+    const int gh = g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : kMaxGenericHeads;
+    const int64_t chunks = (g + gh - 1) / gh;
+    const int64_t nwg = int64_t{args.max_parts} * args.hkv * args.num_seqs * chunks;
     if (nwg > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
-    hipExtLaunchKernelGGL(decode_generic_kernel<DT>, dim3(static_cast<uint32_t>(nwg)), dim3(kWave), 0, st, start,
-                          main_stop, 0, args);
+    const int64_t pt = int64_t{args.part_blocks} * args.block_tokens;
+    const size_t lds = static_cast<size_t>(gh * pt + args.part_blocks) * 4;
+    const dim3 grid(static_cast<uint32_t>(nwg)), block(kWave);
+    switch (gh) {
+      case 1: hipExtLaunchKernelGGL((decode_generic_kernel<DT, 1>), grid, block, lds, st, start, main_stop, 0, args); break;
+      case 2: hipExtLaunchKernelGGL((decode_generic_kernel<DT, 2>), grid, block, lds, st, start, main_stop, 0, args); break;
+      case 4: hipExtLaunchKernelGGL((decode_generic_kernel<DT, 4>), grid, block, lds, st, start, main_stop, 0, args); break;
+      default:
+        hipExtLaunchKernelGGL((decode_generic_kernel<DT, kMaxGenericHeads>), grid, block, lds, st, start, main_stop, 0,
+                              args);
+    }
   }
   if (merge) launch_reduce<DT>(args, st, stop);
   return PA_OK;
