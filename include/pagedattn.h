@@ -73,8 +73,8 @@ typedef struct pa_cache_desc {
   int32_t block_size;    /* tokens per block, <= 1024.  Decode takes 8 (partitions of whole 16-token tiles;
                             plain mode, a pa_shared_prefix description is not used) and 16 << j (16, 32,
                             ..., 1024) on the MFMA path (bf16/fp16, head_dim 64 or 128, H_q / H_kv <= 16,
-                            num_seqs <= 2048 beyond 16), other sizes on the VALU kernel; prefill takes 16
-                            only */
+                            num_seqs <= 2048 beyond 16), other sizes on the VALU kernel; prefill takes 8
+                            and 16 << j */
   int32_t dtype;         /* pa_dtype of K and V */
 } pa_cache_desc;
 
@@ -268,7 +268,8 @@ typedef struct pa_prefill_params {
  *   query_start  [S + 1] int32, non-decreasing, query_start[0] = 0, query_start[S] = T, device
  *   out          [T][H_q][D] fp32 or the cache dtype
  * Rows whose position would be negative (a chunk longer than its context) are left unwritten.
- * bf16 / fp16 caches with head_dim 64 or 128 (else PA_ERR_UNSUPPORTED); asynchronous on the stream.
+ * bf16 / fp16 caches with head_dim 64 or 128 and blocks of 8 or 16 << j tokens (else PA_ERR_UNSUPPORTED);
+ * asynchronous on the stream.
  */
 int32_t paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                 const int32_t* context_lens, const int32_t* query_start, float scale, void* out,

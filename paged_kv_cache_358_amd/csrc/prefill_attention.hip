@@ -45,6 +45,8 @@ struct PrefillArgs {
   int64_t num_blocks;
   const int32_t* seq_order;  // [S]: the sequence of each scheduling rank, or null (batch order)
   int32_t num_seqs;
+  int32_t block_tokens;  // B: 8 or 16 << sub_log2
+  int32_t sub_log2;      // log2 of the 16-token tiles per block (B >= 16), -1 for 8-token blocks
 };
 
 constexpr int kPrefillWaves = 4;
@@ -73,7 +75,11 @@ __device__ __forceinline__ void prefill_store4(const PrefillArgs& a, int64_t idx
 constexpr int kStageBlocks = kPrefillWaves;  // 16-token blocks per stage: one per wave
 constexpr float kLazyLog2 = 8.0f;  // how far (log2 units) a score may exceed the softmax reference point m
 
-template <int DT, int D>
+// Block kinds: kPb16, 16-token blocks; kPbMulti, blocks of 16 << sub_log2 tokens (32, 64, ...);
+// kPbHalf, 8-token blocks.
+constexpr int kPb16 = 0, kPbMulti = 1, kPbHalf = 2;
+
+template <int DT, int D, int BK>
 __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void prefill_tiled_kernel(
     PrefillArgs a) {
   constexpr int KK = D / 32;
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
   const int q0 = a.query_start[s];
   const int c = a.query_start[s + 1] - q0;  // chunk rows of this sequence
   int n = a.context_lens[s];
-  n = n < 0 ? 0 : (n > a.max_blocks * kBlockTokens ? a.max_blocks * kBlockTokens : n);
+  n = n < 0 ? 0 : (n > a.max_blocks * a.block_tokens ? a.max_blocks * a.block_tokens : n);
   // Workgroup-uniform exits (before any barrier): no row of the tile, or no row with a position.
   const int R0 = tile * kPrefillRows;
   if (c <= 0 || R0 >= c) return;
@@ -157,41 +163,82 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
     }
   }
 
-  // Block ids of this wave's blocks (stage st holds block st * 4 + w): lane i holds the id of stage
-  // base + i.
+  // Everything counts in 16-token tiles: stage st holds tiles st * 4 .. st * 4 + 3, and this wave loads
+  // tile st * 4 + w.  Tile u is tile u % SB of cache block u / SB for blocks of 16 << sub_log2 tokens
+  // (SB = 1 << sub_log2), and cache blocks 2u and 2u + 1 for 8-token blocks.  Block ids of this wave's
+  // tiles: lane i of ids (and of ids2, the second block of an 8-token pair) holds stage base + i's.
+  const int lsb = BK == kPbMulti ? a.sub_log2 : 0;
+  constexpr bool half = BK == kPbHalf;
   const int32_t* tab = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
-  auto load_ids = [&](int base) { return tab[min((base + lane) * kStageBlocks + w, a.max_blocks - 1)]; };
+  auto tile_block = [&](int base, int second) {
+    const int u = (base + lane) * kStageBlocks + w;
+    return tab[min(half ? 2 * u + second : u >> lsb, a.max_blocks - 1)];
+  };
+  auto load_ids = [&](int base) { return tile_block(base, 0); };
   int ids_base = 0;
   int32_t ids = load_ids(0);
+  int32_t ids2 = half ? tile_block(0, 1) : 0;
 
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + static_cast<int64_t>(h) * kTileBytes;
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + static_cast<int64_t>(h) * kTileBytes;
-  const int64_t blk_stride = static_cast<int64_t>(a.hkv) * kTileBytes;
+  // A (cache block, KV head) holds K as [D/8][B][8] and V as [D][B].
+  const int head_bytes = half ? kTileBytes / 2 : kTileBytes << lsb;
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + static_cast<int64_t>(h) * head_bytes;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + static_cast<int64_t>(h) * head_bytes;
+  const int64_t blk_stride = static_cast<int64_t>(a.hkv) * head_bytes;
+  // Lane (col, grp): K token col of chunk kk * 4 + grp, V dim col (of each 16-dim group) at the
+  // tile's tokens 4 grp .. 4 grp + 3.  Offsets into a block of 16 << lsb tokens, tile 0 (k_goff,
+  // v_off), and into the tile's K in LDS, which is kept as a 16-token block's (k_off).
+  const int k_goff = ((grp << (4 + lsb)) + col) * 16;
   const int k_off = lane * 16;
-  const int v_off = col * 32 + grp * 8;
-  // Load block b (this wave's block of a stage) into registers; a block past the workgroup's last one
-  // or an id outside the pool gets an empty resource (zeros, no memory touched).
-  auto gload = [&](KVRegs<D>& rg, int b, int32_t phys) {
-    const bool ok = b < nblk && phys >= 0 && phys < a.num_blocks;
+  const int v_off = ((col * 32) << lsb) + grp * 8;
+  // Load tile b (this wave's tile of a stage) into registers.  A tile past the workgroup's last one, or
+  // a block id outside the pool, loads zeros: an empty resource (no memory touched) or, for 8-token
+  // blocks, whose lanes each read through their own address, a select after reading the cache's first
+  // tile (in bounds).
+  auto gload = [&](KVRegs<D>& rg, int b, int32_t phys, int32_t phys2) {
+    const bool in = b < nblk;
+    if constexpr (half) {
+      const bool ok0 = in && phys >= 0 && phys < a.num_blocks;
+      const bool ok1 = in && phys2 >= 0 && phys2 < a.num_blocks;
+      const int64_t o0 = ok0 ? static_cast<int64_t>(phys) * blk_stride : 0;
+      const int64_t o1 = ok1 ? static_cast<int64_t>(phys2) * blk_stride : 0;
+      const bool kok = col < 8 ? ok0 : ok1, vok = grp < 2 ? ok0 : ok1;
+      const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(kbase + (col < 8 ? o0 : o1) + grp * 128 + (col & 7) * 16);
+      const u32x2_t* vp = reinterpret_cast<const u32x2_t*>(vbase + (grp < 2 ? o0 : o1) + col * 16 + (grp & 1) * 8);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4_t x = __builtin_nontemporal_load(kp + kk * 32);
+        rg.k[kk] = kok ? x : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int nn = 0; nn < NV; ++nn) {
+        const u32x2_t x = __builtin_nontemporal_load(vp + nn * 32);
+        rg.v[nn] = vok ? x : u32x2_t{0, 0};
+      }
+      return;
+    }
+    const bool ok = in && phys >= 0 && phys < a.num_blocks;
+    const int sub = b & ((1 << lsb) - 1);  // tile of its cache block
     const int64_t off = ok ? static_cast<int64_t>(phys) * blk_stride : 0;
-    const int nrec = ok ? kTileBytes : 0;
+    const int tk = ok ? sub * 256 : 0, tv = ok ? sub * 32 : 0;
+    const int nrec = ok ? head_bytes : 0;
     const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kbase + off), 0, nrec, kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kbase + off + tk), 0, nrec - tk, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vbase + off), 0, nrec, kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vbase + off + tv), 0, nrec - tv, kRsrcWord3);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      rg.k[kk] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, kk * 1024, 0));
+      rg.k[kk] =
+          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, k_goff, (kk * 1024) << lsb, 0));
 #pragma unroll
     for (int nn = 0; nn < NV; ++nn)
-      rg.v[nn] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, nn * 512, 0));
+      rg.v[nn] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, (nn * 512) << lsb, 0));
   };
   // Block b's tiles into buffer buf, in the layout they have in the cache; V tokens past the context
   // (which may hold anything, even NaN) are zeroed so that no product reads them.
   auto lwrite = [&](KVRegs<D>& rg, int buf, int b, int32_t phys) {
     int nv = n - b * kBlockTokens;
     nv = nv > kBlockTokens ? kBlockTokens : (nv < 0 ? 0 : nv);
-    if (b >= nblk || phys < 0 || phys >= a.num_blocks) nv = 0;
+    if (b >= nblk || (!half && (phys < 0 || phys >= a.num_blocks))) nv = 0;
     uint8_t* kt = k_lds[buf][w];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) *reinterpret_cast<u32x4_t*>(kt + k_off + kk * 1024) = rg.k[kk];
@@ -313,7 +360,7 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
   KVRegs<D> rg;
   {
     const int32_t phys = __builtin_amdgcn_readlane(ids, 0);
-    gload(rg, w, phys);
+    gload(rg, w, phys, half ? __builtin_amdgcn_readlane(ids2, 0) : 0);
     lwrite(rg, 0, w, phys);
   }
   __syncthreads();
@@ -324,9 +371,10 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
       if (nxt - ids_base >= 64) {
         ids_base += 64;
         ids = load_ids(ids_base);
+        if (half) ids2 = tile_block(ids_base, 1);
       }
       phys_n = __builtin_amdgcn_readlane(ids, nxt - ids_base);
-      gload(rg, nxt * kStageBlocks + w, phys_n);
+      gload(rg, nxt * kStageBlocks + w, phys_n, half ? __builtin_amdgcn_readlane(ids2, nxt - ids_base) : 0);
     }
     if (stg <= w_last_stage) compute(stg & 1, stg * kStageBlocks);
     if (nxt < nstage) lwrite(rg, nxt & 1, nxt * kStageBlocks + w, phys_n);
@@ -344,6 +392,17 @@ __global__ __launch_bounds__(kPrefillWaves * kWave) __attribute__((amdgpu_waves_
   }
 }
 
+template <int DT, int D>
+void launch_prefill(int bk, dim3 grid, dim3 block, hipStream_t st, hipEvent_t start, hipEvent_t stop,
+                    const PrefillArgs& a) {
+  if (bk == kPbHalf)
+    hipExtLaunchKernelGGL((prefill_tiled_kernel<DT, D, kPbHalf>), grid, block, 0, st, start, stop, 0, a);
+  else if (bk == kPbMulti)
+    hipExtLaunchKernelGGL((prefill_tiled_kernel<DT, D, kPbMulti>), grid, block, 0, st, start, stop, 0, a);
+  else
+    hipExtLaunchKernelGGL((prefill_tiled_kernel<DT, D, kPb16>), grid, block, 0, st, start, stop, 0, a);
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -359,8 +418,13 @@ extern "C" int32_t paged_attention_prefill(const void* q, const void* k_cache, c
     return PA_ERR_INVALID_ARG;
   if (p->num_q_heads % c.num_kv_heads != 0 || !valid_dtype(c.dtype)) return PA_ERR_INVALID_ARG;
   if (p->out_dtype != PA_F32 && p->out_dtype != c.dtype) return PA_ERR_INVALID_ARG;
-  if (c.block_size != kBlockTokens || c.dtype == PA_F32 || (c.head_dim != 64 && c.head_dim != 128))
-    return PA_ERR_UNSUPPORTED;
+  int32_t sub_log2 = -1;  // 8-token blocks
+  if (c.block_size != kBlockTokens / 2) {
+    sub_log2 = 0;
+    while (sub_log2 < 6 && (kBlockTokens << sub_log2) < c.block_size) ++sub_log2;
+    if ((kBlockTokens << sub_log2) != c.block_size) return PA_ERR_UNSUPPORTED;
+  }
+  if (c.dtype == PA_F32 || (c.head_dim != 64 && c.head_dim != 128)) return PA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(p->stream);
   hipEvent_t start = static_cast<hipEvent_t>(p->start_event), stop = static_cast<hipEvent_t>(p->stop_event);
@@ -394,6 +458,8 @@ extern "C" int32_t paged_attention_prefill(const void* q, const void* k_cache, c
   a.num_blocks = c.num_blocks;
   a.seq_order = p->seq_order;
   a.num_seqs = p->num_seqs;
+  a.block_tokens = c.block_size;
+  a.sub_log2 = sub_log2;
   a.tiles = (p->max_query_len + kPrefillRows - 1) / kPrefillRows;
   a.items = static_cast<int64_t>(p->num_seqs) * p->num_q_heads * a.tiles;
   const int64_t groups = static_cast<int64_t>(p->num_seqs) * p->num_q_heads;
@@ -402,16 +468,17 @@ extern "C" int32_t paged_attention_prefill(const void* q, const void* k_cache, c
   a.per_xcd = static_cast<int32_t>(per_xcd);
   const dim3 grid(static_cast<uint32_t>(per_xcd * kXcdCount));
   const dim3 block(kPrefillWaves * kWave);
+  const int bk = sub_log2 < 0 ? kPbHalf : sub_log2 > 0 ? kPbMulti : kPb16;
   if (c.dtype == PA_BF16) {
     if (c.head_dim == 64)
-      hipExtLaunchKernelGGL((prefill_tiled_kernel<PA_BF16, 64>), grid, block, 0, st, start, stop, 0, a);
+      launch_prefill<PA_BF16, 64>(bk, grid, block, st, start, stop, a);
     else
-      hipExtLaunchKernelGGL((prefill_tiled_kernel<PA_BF16, 128>), grid, block, 0, st, start, stop, 0, a);
+      launch_prefill<PA_BF16, 128>(bk, grid, block, st, start, stop, a);
   } else {
     if (c.head_dim == 64)
-      hipExtLaunchKernelGGL((prefill_tiled_kernel<PA_F16, 64>), grid, block, 0, st, start, stop, 0, a);
+      launch_prefill<PA_F16, 64>(bk, grid, block, st, start, stop, a);
     else
-      hipExtLaunchKernelGGL((prefill_tiled_kernel<PA_F16, 128>), grid, block, 0, st, start, stop, 0, a);
+      launch_prefill<PA_F16, 128>(bk, grid, block, st, start, stop, a);
   }
   return PA_HIP_STATUS("paged_attention_prefill", hipGetLastError());
 }

@@ -182,6 +182,24 @@ def test_scheduling_order_changes_no_bit():
     _check(pd, chunks, q_np, ref.numpy(), qs)
 
 
+@pytest.mark.parametrize("B", [8, 32, 64])
+def test_other_block_sizes(B):
+    # The kernel streams 16-token tiles whatever the block size: blocks of 8 tokens two to a tile,
+    # blocks of 32 and 64 tokens a tile at a time.  Against the oracle, and bit for bit against the
+    # same sequences on 16-token blocks (the same tiles in the same order).
+    lens = [1, 7, 9, 40, 129, 530, 1000]
+    chunks = [1, 7, 9, 33, 129, 200, 64]
+    outs = []
+    for bs in (16, B):
+        cfg = synth.scaled(synth.C3, lens=lens, block_size=bs)
+        pd = PagedDecode(cfg)
+        q_np = _chunk_queries(cfg, chunks, 10)
+        got, qs = _run(pd, chunks, q_np)
+        _check(pd, chunks, q_np, got, qs)
+        outs.append(got)
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_rejects_what_it_does_not_cover():
     cfg = synth.scaled(synth.C3, lens=[16])
     pd = PagedDecode(cfg)
