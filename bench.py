@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-context partition in tokens (0 = the workload's own)")
     ap.add_argument("--block-size", type=int, default=16,
-                    help="decode c2/c3/c5: tokens per cache block (16; 8, 32, 64, ...)")
+                    help="decode c2/c3/c4/c5 and prefill: tokens per cache block (16; 8, 32, 64, ...)")
     ap.add_argument("--head-dim", type=int, default=0,
                     help="decode c2/c3/c5: head_dim other than the workload's 128 (64 or 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -83,10 +83,6 @@ def main():
               "the paged decode path has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]
-    if (args.block_size != 16 or args.head_dim) and "c4" in names:
-        if args.workload == "c4":
-            sys.exit("bench.py: the sampling workload runs on 16-token blocks and head_dim 128 only")
-        names.remove("c4")
     if args.dtype and "c1" in names and args.workload == "all":
         names.remove("c1")  # the tiny workload is fp32 by definition
 
@@ -164,22 +160,32 @@ def run_decode(args, w, dev, pool):
     from paged_kv_cache_358_amd.engine import PagedDecodeLayer
 
     W, K = args.warmup, args.steps
-    BS = args.block_size if w != "c4" else 16
+    BS = args.block_size
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
     t_setup = time.perf_counter()
 
     if w == "c4":
         cfg = synth.C4
+        kw, name = {}, cfg.name
         if args.dtype:
+            kw["dtype"] = args.dtype
+            name = name.replace("bf16", args.dtype)
+        if args.head_dim:
+            kw["head_dim"] = args.head_dim
+            name += f"_d{args.head_dim}"
+        if BS != 16:
+            kw["block_size"] = BS
+            name += f"_b{BS}"
+        if kw:  # the same prompts and steps with another 16-bit type, head size or block size
             import dataclasses
-            cfg = dataclasses.replace(cfg, dtype=args.dtype, name=cfg.name.replace("bf16", args.dtype))
+            cfg = dataclasses.replace(cfg, name=name, **kw)
         part = args.partition_size or cfg.partition_size
         if W + K > cfg.steps:
             sys.exit(f"c4 runs at most {cfg.steps} decode steps")
         S, hq, hkv, D, dtype = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.dtype
-        max_blocks = -(-(cfg.prefix_len + cfg.steps) // 16)
+        max_blocks = -(-(cfg.prefix_len + cfg.steps) // BS)
         layer = PagedDecodeLayer(cfg.pool_blocks(), hkv, D, hq, tdt[dtype], S, max_blocks,
-                                 free_order=cfg.free_order(), partition_size=part, device=dev)
+                                 free_order=cfg.free_order(), partition_size=part, device=dev, block_size=BS)
         heads = list(range(hkv))
         for i in range(cfg.num_prompts):
             root = i * cfg.samples
@@ -195,7 +201,7 @@ def run_decode(args, w, dev, pool):
         kvbpt = cfg.kv_bytes_per_token()
         workload = {"workload": cfg.name, "prompts": cfg.num_prompts, "samples": cfg.samples,
                     "prefix_len": cfg.prefix_len, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D,
-                    "block_size": 16, "partition_size": part, "timed_steps": f"{W + 1}..{W + K}"}
+                    "block_size": BS, "partition_size": part, "timed_steps": f"{W + 1}..{W + K}"}
         lens0 = None
     else:
         cfg = synth.CONFIGS[WORKLOADS[w]]
@@ -523,19 +529,23 @@ def run_prefill(args):
     W, K = args.warmup, args.steps
     dev = torch.device("cuda:0")
     cfg = synth.C2
+    BS = args.block_size
+    if BS != 16:  # the same contexts laid out in other blocks
+        import dataclasses
+        cfg = dataclasses.replace(cfg, block_size=BS)
     lens = synth.context_lens(cfg).astype(np.int64)
     chunks = np.minimum(lens, args.chunk)
     S, hq, hkv, D = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
     plan = synth.pool_plan(cfg, lens)
     torch.manual_seed(cfg.cfg_id)
-    k_cache, v_cache = pa.alloc_kv_cache(plan.num_blocks, hkv, D, torch.bfloat16, dev)
+    k_cache, v_cache = pa.alloc_kv_cache(plan.num_blocks, hkv, D, torch.bfloat16, dev, block_size=BS)
     k_cache.normal_()
     v_cache.normal_()
-    alloc = pa.BlockAllocator(plan.num_blocks, 16, plan.free_order)
+    alloc = pa.BlockAllocator(plan.num_blocks, BS, plan.free_order)
     for s_ in range(S):
         alloc.add(s_)
         alloc.append(s_, int(lens[s_]))
-    max_blocks = int(synth.blocks_for(lens.max()))
+    max_blocks = int(synth.blocks_for(lens.max(), BS))
     tables, lens_np = alloc.build_batch(list(range(S)), max_blocks)
     qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
     T = int(qs[-1])
@@ -573,7 +583,7 @@ def run_prefill(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (torch-seeded N(0,1) q/K/V, seeded context lengths and shuffled block pool)",
         "config": {"workload": "c2_mha_bf16 chunked prefill", "num_seqs": S, "chunk": args.chunk,
-                   "rows": T, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D, "block_size": 16},
+                   "rows": T, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": D, "block_size": BS},
         "kernel_ms": round(kern_s * 1e3, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,

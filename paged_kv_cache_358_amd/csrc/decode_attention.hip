@@ -429,7 +429,6 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
   constexpr int NT = MODE == kGroup ? 2 : 1;  // 16-column MFMA tiles of query columns
   constexpr bool MULTI = BK == kBkMulti;
   constexpr bool HALF = BK == kBkHalf;
-  static_assert(!HALF || MODE == kPlain, "8-token blocks run in plain mode");
   __shared__ __attribute__((aligned(16))) float sm_o[WV][16][D];
   __shared__ float sm_m[WV][16];
   __shared__ float sm_l[WV][16];
@@ -495,6 +494,10 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
   auto group_shared = [&](int v) {
     if constexpr (MULTI) {
       return max(0, min(a.share_groups[3 * v + 2], (a.ctx_limit / kBlockTokens) >> lsb)) << lsb;
+    } else if constexpr (HALF) {
+      // Whole tiles of shared 8-token blocks; an odd last shared block is read through each member's
+      // own row (which holds the same id).
+      return max(0, min(a.share_groups[3 * v + 2], min(a.max_blocks, a.ctx_limit / (kBlockTokens / 2)))) >> 1;
     } else {
       return max(0, min(a.share_groups[3 * v + 2], min(a.max_blocks, a.ctx_limit / kBlockTokens)));
     }
@@ -639,7 +642,8 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
         const int c = t * 16 + col < mm * g ? t * 16 + col : 0;
         qrow[t] = (static_cast<int64_t>(first + c / g) * a.hq + it.h * g + c % g) * D;
       }
-      const int b = it.b0 + w + WV * lane;
+      // kBkHalf: lane i and lane 32 + i hold ring position i's two 8-token blocks.
+      const int b = it.b0 + w + WV * (HALF ? (lane & 31) : lane);
       int row = first, pos = b, owner = 0, nv = kBlockTokens;
       if (b >= k) {
         int r = b - k;
@@ -658,7 +662,8 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       }
       sl.meta = (owner << 8) | nv;
       if constexpr (MULTI) sl.meta |= (pos & sbm) << 16;
-      sl.ids = a.block_tables[static_cast<int64_t>(row) * a.max_blocks + min(max(pos, 0) >> lsb, a.max_blocks - 1)];
+      const int tb = HALF ? 2 * max(pos, 0) + (lane >> 5) : max(pos, 0) >> lsb;
+      sl.ids = a.block_tables[static_cast<int64_t>(row) * a.max_blocks + min(tb, a.max_blocks - 1)];
     } else {
       qrow[0] = (static_cast<int64_t>(it.s) * a.hq + it.h * g + (col < g ? col : 0)) * D;
       if constexpr (HALF) {
@@ -937,36 +942,43 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
     auto compute_tile = [&](KVRegs<D>& r, int i) {
       constexpr int kLastPos = HALF ? 31 : 63;  // lanes of cur_ids holding a position's (first) block
       const int32_t phys = __builtin_amdgcn_readlane(cur_ids, i < kLastPos ? i : kLastPos);
-      int nv;          // tokens of the block
-      int nv_col[NT];  // tokens of the block this lane's query column sees, per column tile
-      int t_lo = 0, t_hi = NT - 1;  // column tiles to compute (wave-uniform)
+      int nv;          // tokens of the tile in the context (0: nothing to add)
+      int owner = 0;   // kGroup: 0 for a shared tile, else 1 + the member whose own tile it is
       if constexpr (MODE == kGroup) {
-        const int meta = __builtin_amdgcn_readlane(cur_meta, i < 63 ? i : 63);
+        const int meta = __builtin_amdgcn_readlane(cur_meta, i < kLastPos ? i : kLastPos);
         nv = meta & 0xff;
-        const int owner = MULTI ? (meta >> 8) & 0xff : meta >> 8;
-        if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) nv_col[t] = (owner == 0 || owner - 1 == (t * 16 + col) / g) ? nv : 0;
-        // Column tiles with no column that sees the block (a member's own block is seen by its g
-        // columns only; tiles past the group's columns hold none) would add exact zeros: skipped.
-        t_lo = owner == 0 ? 0 : ((owner - 1) * g) / 16;
-        t_hi = owner == 0 ? cur.nt - 1 : ((owner - 1) * g + g - 1) / 16;
+        owner = MULTI ? (meta >> 8) & 0xff : meta >> 8;
       } else {
         const int bl = cur.b0 + unit_of(i);
         nv = cur.n - bl * kBlockTokens;
         nv = nv > kBlockTokens ? kBlockTokens : nv;
-        if constexpr (HALF) {
-          // This lane's tokens (and V dims' tokens) lie in block grp >> 1 of the tile; a block id
-          // outside the pool leaves its 8 tokens out.
-          const int32_t p1 = __builtin_amdgcn_readlane(cur_ids, (i < 31 ? i : 31) + 32);
-          const bool ok0 = phys >= 0 && phys < a.num_blocks, ok1 = p1 >= 0 && p1 < a.num_blocks;
-          if (i >= cur.my_n) nv = 0;
-          nv_col[0] = (grp < 2 ? ok0 : ok1) ? nv : 0;
-          if (!ok0 || !ok1) nv = min(nv, kBlockTokens - 1);  // some lane masks: take the V mask below
-        } else {
-          if (i >= cur.my_n || phys < 0 || phys >= a.num_blocks) nv = 0;
-          nv_col[0] = nv;
-        }
+      }
+      if (i >= cur.my_n) nv = 0;
+      // The tokens this lane's K row and V tokens see: an id outside the pool leaves its block's
+      // tokens out (kBkHalf: this lane's tokens lie in block grp >> 1 of the tile).  vmask: some lane
+      // has tokens to clear from its V registers (uniform).
+      int nv_lane = nv;
+      bool vmask = nv < kBlockTokens;
+      if constexpr (HALF) {
+        const int32_t p1 = __builtin_amdgcn_readlane(cur_ids, (i < 31 ? i : 31) + 32);
+        const bool ok0 = phys >= 0 && phys < a.num_blocks, ok1 = p1 >= 0 && p1 < a.num_blocks;
+        nv_lane = (grp < 2 ? ok0 : ok1) ? nv : 0;
+        vmask = vmask || !ok0 || !ok1;
+      } else {
+        if (phys < 0 || phys >= a.num_blocks) nv_lane = nv = 0;
+        vmask = nv < kBlockTokens;
+      }
+      int nv_col[NT];  // tokens of the tile this lane's query column sees, per column tile
+      int t_lo = 0, t_hi = NT - 1;  // column tiles to compute (wave-uniform)
+      if constexpr (MODE == kGroup) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) nv_col[t] = (owner == 0 || owner - 1 == (t * 16 + col) / g) ? nv_lane : 0;
+        // Column tiles with no column that sees the tile (a member's own tile is seen by its g
+        // columns only; tiles past the group's columns hold none) would add exact zeros: skipped.
+        t_lo = owner == 0 ? 0 : ((owner - 1) * g) / 16;
+        t_hi = owner == 0 ? cur.nt - 1 : ((owner - 1) * g + g - 1) / 16;
+      } else {
+        nv_col[0] = nv_lane;
       }
 
       float alpha[NT];
@@ -994,8 +1006,8 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       // O^T += V^T P^T.  Tokens past the context may hold anything, even NaN: a block that is
       // not full has them selected out of its V registers (in place: the ring reloads them next);
       // a full block (all but a context's last) needs no mask.
-      if (nv < kBlockTokens) {
-        const int nvl = HALF ? nv_col[0] : nv;  // kBkHalf: a lane's own block may be out
+      if (vmask) {
+        const int nvl = nv_lane;
         uint32_t keep[2];
 #pragma unroll
         for (int wd = 0; wd < 2; ++wd) {
@@ -1573,8 +1585,11 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
     if (sh.num_groups < 0 || sh.num_groups > p->num_seqs) return PA_ERR_INVALID_ARG;
     if (sh.num_groups > 0 && !sh.groups) return PA_ERR_INVALID_ARG;
     const int64_t members = std::max(1, std::min(kMaxCols / (p->num_q_heads / c.num_kv_heads), std::max(1, p->num_seqs)));
-    const int64_t gblocks = members * ((int64_t{limit} + B - 1) / B);
-    gparts = std::max<int64_t>(1, (gblocks + out->part_blocks - 1) / out->part_blocks);
+    // Counted in the units the kernel streams: 8-token blocks go two to a tile, and each member's
+    // last tile may hold a single block.
+    const int32_t unit = (2 * B == kBlockTokens && pt % kBlockTokens == 0) ? kBlockTokens : B;
+    const int64_t gblocks = members * ((int64_t{limit} + unit - 1) / unit);
+    gparts = std::max<int64_t>(1, (gblocks + pt / unit - 1) / (pt / unit));
     if (gparts > 8192) return PA_ERR_UNSUPPORTED;
   }
 
@@ -1595,8 +1610,8 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
                          0x7fffffffLL;
   out->route = split ? kRouteSplit : (shape && B == kBlockTokens) ? kRouteMfma : kRouteGeneric;
   out->sub_log2 = split ? (half_blocks ? -1 : lsb) : 0;
-  // Head_dim 256 runs sequence by sequence (its grouped form would spill), and so do 8-token blocks.
-  out->group = split && !wide && !half_blocks && p->shared && p->shared->num_groups > 0;
+  // Head_dim 256 runs sequence by sequence (its grouped form would spill).
+  out->group = split && !wide && p->shared && p->shared->num_groups > 0;
 
   if (split) {
     // Partials per run (see DecodeArgs::part_cols); a context of one partition never spans runs.  A
@@ -1714,9 +1729,7 @@ int32_t launch_split(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEven
 // One launch: over groups when the batch comes with shared prefixes, else over sequences.
 template <int DT, int D, int BK>
 int32_t launch_split_all(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-  if constexpr (BK != kBkHalf) {
-    if (args->num_groups > 0) return launch_split<DT, D, kGroup, BK>(args, st, start, stop);
-  }
+  if (args->num_groups > 0) return launch_split<DT, D, kGroup, BK>(args, st, start, stop);
   return launch_split<DT, D, kPlain, BK>(args, st, start, stop);
 }
 

@@ -214,6 +214,10 @@ def test_workspace_bytes_with_shared_prefixes():
     # MHA: at most the batch's 3 sequences per group, 63 blocks each -> 12 partitions of 256
     assert ws(ctypes.byref(shared(S=3, hq=4, hkv=4, d=64, maxb=100, maxctx=1000, part=256))) == \
         _split_ws(32, 64, 3 * 4)
+    # 8-token blocks count in 16-token tiles: 3 members of 168 tokens hold 11 tiles each, 33 tiles that
+    # need 2 partitions of 32 tiles (the same context counted in 8-token blocks, 63, would fit in one)
+    assert ws(ctypes.byref(shared(S=3, hq=4, hkv=4, d=64, maxb=32, maxctx=168, bs=8))) == _split_ws(32, 64, 3 * 4)
+    assert ws(ctypes.byref(shared(S=3, hq=4, hkv=4, d=64, maxb=32, maxctx=160, bs=8))) == 0
     # head_dim 256 runs sequence by sequence: its partials have g columns
     assert ws(ctypes.byref(shared(S=3, hq=8, hkv=2, d=256, maxb=100, maxctx=1000))) == _split_ws(4, 256, 3 * 2)
     # more groups than sequences, a negative count, or groups without an array: rejected

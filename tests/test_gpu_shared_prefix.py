@@ -240,3 +240,25 @@ def test_member_heads_straddling_column_tiles(hq, hkv):
     gr, _ = check(fb)
     g = hq // hkv
     assert gr[0].tolist() == [0, min(10, 32 // g), 400 // B]
+
+
+@pytest.mark.parametrize("hq,hkv,part", [(32, 8, 512), (24, 8, 48), (8, 8, 16)])
+def test_eight_token_blocks(hq, hkv, part):
+    # 8-token blocks stream two to a 16-token tile.  Prompt 0 shares 87 full blocks (an odd count: the
+    # last shared block sits in a member's first own tile and is read through each member's row),
+    # prompt 1 shares 12; samples own 0 to 500 tokens, so a member's last tile may hold one block.
+    prompts = [(700, [0, 1, 4, 5, 12, 13, 500, 9, 31, 2]), (96, [1, 8, 9])]
+    fb = ForkedBatch(10, hq, hkv, 128, "bf16", prompts, lone=[65, 0], partition_size=part, block_size=8)
+    assert fb.k_cache.shape[3] == 8
+    gr, _ = check(fb)
+    g = hq // hkv
+    assert gr[0].tolist() == [0, min(10, 32 // g), 700 // 8]
+    check(fb, max_members=3)
+
+
+def test_eight_token_blocks_group_spans_two_partitions():
+    # MHA, three samples of 168 tokens that share one block: 11 tiles each, 33 in all, so the
+    # group's context needs two 512-token partitions (and the partial slots that go with them).
+    fb = ForkedBatch(11, 4, 4, 64, "f16", [(8, [160, 160, 160])], block_size=8)
+    gr, _ = check(fb)
+    assert gr.tolist() == [[0, 3, 1]]
