@@ -329,6 +329,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
 
 // ------------------------------------------------------------------ split MFMA path
 
+constexpr float kLazyLog2 = 8.0f;  // how far (log2 units) a score may exceed the softmax reference point
 constexpr int kMaxScanSeqs = 2048;  // sequences the split kernel's in-LDS index covers
 constexpr int kPersistRing = 2;     // ring depth of the split kernel
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X, each with its own L2
@@ -878,6 +879,21 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
   // segment, merge the four waves and write the output or the run's partial.
   auto run = [&](const Item cur, const int32_t cur_ids, const int32_t cur_meta, const u32x4_t (&qc)[NT][KK],
                  const Item nxi, const bool nx_ok, const int32_t nx_ids, const int32_t nx_meta) {
+    // m is a reference point, not the running maximum: the weights exp2(x - m) of any m give the
+    // same softmax once divided by their sum.  It moves (and l and O are rescaled) only when a score
+    // of some column of the wave exceeds it by more than kLazyLog2, so weights stay below
+    // 2^kLazyLog2 and most tiles leave O alone.  A column that has seen no token has m = -inf and
+    // moves at its first visible token.
+    auto lazy_rescale = [&](int t, float bm) {
+      if (__builtin_amdgcn_ballot_w64(bm > m[t] + kLazyLog2) != 0) {
+        const float m_new = fmaxf(m[t], bm);
+        const float alpha = (m[t] == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m[t] - m_new);
+        l[t] *= alpha;
+#pragma unroll
+        for (int nn = 0; nn < NV; ++nn) o[t][nn] *= alpha;
+        m[t] = m_new;
+      }
+    };
     // PAIR: one 32-token unit.  Scores of the two K halves, one softmax update over the 32
     // tokens, and O^T += V^T P^T as 16x16x32 MFMAs (lane group j holds tokens 8 j .. 8 j + 7 of
     // both V and P).
@@ -910,13 +926,11 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       for (int j = 0; j < 8; ++j) x[j] = (grp * 8 + j < nv) ? x[j] * a.scale_log2 : -INFINITY;
       const float bm = rows4_max(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                                        fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
-      const float m_new = fmaxf(m[0], bm);
-      const float alpha = (m[0] == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m[0] - m_new);
+      lazy_rescale(0, bm);
       float pr[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pr[j] = (x[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[j] - m_new);
-      l[0] = l[0] * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
-      m[0] = m_new;
+      for (int j = 0; j < 8; ++j) pr[j] = (x[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[j] - m[0]);
+      l[0] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
       u32x2_t h0, l0, h1, l1;
       PSplit<DT>::split(pr, h0, l0);
       PSplit<DT>::split(pr + 4, h1, l1);
@@ -934,7 +948,6 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
       }
 #pragma unroll
       for (int nn = 0; nn < NV; ++nn) {
-        o[0][nn] *= alpha;
         o[0][nn] = mfma_qk<DT>(r.v[nn], p_hi, o[0][nn]);
         o[0][nn] = mfma_qk<DT>(r.v[nn], p_lo, o[0][nn]);
       }
@@ -981,7 +994,6 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
         nv_col[0] = nv_lane;
       }
 
-      float alpha[NT];
       u32x2_t p_hi[NT], p_lo[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -994,13 +1006,11 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = (grp * 4 + e < nv_col[t]) ? sacc[e] * a.scale_log2 : -INFINITY;
         const float bm = rows4_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-        const float m_new = fmaxf(m[t], bm);
-        alpha[t] = (m[t] == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m[t] - m_new);
+        lazy_rescale(t, bm);
         float pr[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pr[e] = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m_new);
-        l[t] = l[t] * alpha[t] + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-        m[t] = m_new;
+        for (int e = 0; e < 4; ++e) pr[e] = (x[e] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[e] - m[t]);
+        l[t] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         PSplit<DT>::split(pr, p_hi[t], p_lo[t]);
       }
       // O^T += V^T P^T.  Tokens past the context may hold anything, even NaN: a block that is
@@ -1022,9 +1032,7 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           if (NT > 1 && (t < t_lo || t > t_hi)) continue;
-          o[t][nn] *= alpha[t];
-          o[t][nn] = mfma_pv<DT>(r.v[nn], p_hi[t], o[t][nn]);
-          o[t][nn] = mfma_pv<DT>(r.v[nn], p_lo[t], o[t][nn]);
+          o[t][nn] = mfma_pv_split<DT>(r.v[nn], p_hi[t], p_lo[t], o[t][nn]);
         }
       }
     };

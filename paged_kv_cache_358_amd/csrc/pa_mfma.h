@@ -66,6 +66,16 @@ __device__ __forceinline__ f32x4_t mfma_pv(const u32x2_t& a, const u32x2_t& b, c
   }
 }
 
+// O^T tile over 16 tokens with split probabilities in one v_mfma_f32_16x16x32: the contraction
+// runs over (token, half) pairs.  Lane group kg holds its tokens 4 kg .. 4 kg + 3 twice on the V
+// side and the hi then the lo halves of their probabilities on the P side, so one instruction adds
+// V^T (P_hi + P_lo)^T; it takes the issue time of one 16x16x16 product, not two.
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_pv_split(const u32x2_t& v, const u32x2_t& hi, const u32x2_t& lo,
+                                                 const f32x4_t& c) {
+  return mfma_qk<DT>(u32x4_t{v[0], v[1], v[0], v[1]}, u32x4_t{hi[0], hi[1], lo[0], lo[1]}, c);
+}
+
 // Max and sum over the four 16-lane rows of a wavefront (lanes l, l^16, l^32, l^48: one MFMA
 // output column's four k-groups), with the gfx950 permlane swaps, which stay in the vector ALU,
 // instead of shuffles routed through LDS.  Swapping a register with itself leaves x at lane l and
