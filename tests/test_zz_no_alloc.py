@@ -67,6 +67,27 @@ def test_noalloc_groups_and_mha():
     assert _worst(got, mha, range(4), [0, 31]) <= tol_for("bf16")
 
 
+def test_noalloc_groups_on_8_token_blocks():
+    # Group mode streams 8-token blocks two to a tile; an odd shared count (81 blocks) puts the last shared
+    # block in each member's first own tile.  Two calls in a row: grouped, then plain on fewer sequences.
+    cfg = synth.scaled(synth.C3, lens=[700] * 4 + [1300, 40], block_size=8)
+    pd = PagedDecode(cfg, keep_truth=False)
+    t = pd.tables_np.copy()
+    t[1:4, :81] = t[0, :81]                    # sequences 1..3 read sequence 0's first 81 blocks
+    pd.block_tables = torch.from_numpy(t).cuda()
+    groups = torch.tensor([[0, 4, 81], [4, 1, 0], [5, 1, 0]], dtype=torch.int32, device="cuda")
+    ref = torch.empty(pd.q.shape, dtype=torch.float32, device="cuda")
+    pa.paged_attention_decode(pd.q, pd.k_cache, pd.v_cache, pd.block_tables, pd.context_lens, cfg.softmax_scale,
+                              ref, max_context_len=pd.max_context_len, shared=groups)
+    got = _noalloc(pd, shared=groups)
+    assert torch.isfinite(got).all()
+    assert torch.equal(ref, got)
+    small = PagedDecode(synth.scaled(synth.C3, lens=[600, 33, 1500], block_size=8), keep_truth=False)
+    ref, got = small.run(), _noalloc(small)
+    assert torch.equal(ref, got)
+    assert _worst(got, small, range(3), [0, 9, 63]) <= tol_for(small.cfg.dtype)
+
+
 def test_noalloc_rejects_what_its_scratch_cannot_hold():
     # More sequences than the split kernel indexes, with many partitions: the per-partition kernels
     # would need more partial rows than the scratch holds.  Rejected before anything is launched.
