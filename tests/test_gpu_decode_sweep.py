@@ -57,3 +57,15 @@ def test_decode_shape_sweep(case):
     # subnormal, spaced 2^-24)
     o16 = pd.run(out_dtype=pd.q.dtype, partition_size=part or None).float().cpu().numpy()
     check_16bit_output(o16, o, dtype)
+
+
+def test_head_dim_64_one_workgroup_per_context():
+    # 20 sequences x 32 heads at head_dim 64: 640 contexts, at least two per CU and fewer than the
+    # resident workgroups, so the grid is one workgroup per context.
+    rng = np.random.default_rng(77)
+    lens = lengths(rng, 16, 20)
+    cfg = synth.DecodeConfig("grid64", 77, len(lens), 32, 32, 64, "bf16", "fixed", tuple(lens))
+    pd = PagedDecode(cfg)
+    o = pd.run().float().cpu().numpy()
+    worst = max(float(np.max(np.abs(o[s] - pd.oracle(s)))) for s in range(cfg.num_seqs))
+    assert np.all(np.isfinite(o)) and worst <= tol_for("bf16"), (lens, worst)

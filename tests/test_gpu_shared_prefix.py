@@ -262,3 +262,12 @@ def test_eight_token_blocks_group_spans_two_partitions():
     fb = ForkedBatch(11, 4, 4, 64, "f16", [(8, [160, 160, 160])], block_size=8)
     gr, _ = check(fb)
     assert gr.tolist() == [[0, 3, 1]]
+
+
+def test_head_dim_64_one_workgroup_per_group_context():
+    # 64 prompts x 2 samples, 8 KV heads, head_dim 64: 512 group contexts, at least two per CU and fewer
+    # than the resident workgroups, so the grid is one workgroup per context (none cut into runs).
+    prompts = [(100 + 7 * i, [5 + i % 3, 9]) for i in range(64)]
+    fb = ForkedBatch(12, 16, 8, 64, "bf16", prompts)
+    gr, _ = check(fb)
+    assert len(gr) == 64 and np.all(gr[:, 1] == 2)
