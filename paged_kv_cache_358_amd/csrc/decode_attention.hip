@@ -20,14 +20,14 @@
 // bf16/fp16 fast path (MFMA).  All g = H_q / H_kv query heads of a KV head share
 // each K/V block, so a 16-token tile is one dense contraction on the matrix cores:
 //   S^T[16 tokens x 16 heads] = K[16 x D] . Q^T[D x 16]     (D/32 v_mfma_f32_16x16x32)
-//   O^T[D x 16 heads]        += V^T[D x 16] . P^T[16 x 16]  (D/16 v_mfma_f32_16x16x16, twice)
+//   O^T[D x 16 heads]        += V^T[D x 16] . P^T[16 x 16]  (D/16 v_mfma_f32_16x16x32)
 // Query heads beyond g are zero columns.  The lane that holds S for (head, 4 tokens)
 // after the first product is exactly the lane that must supply P for them in the
 // second, so scores never leave registers.  P is split as P_hi + P_lo, both in the
-// input's 16-bit type, and each half goes through its own PV MFMA, so the probabilities
-// enter with ~16 significant bits instead of 8 while V and the accumulation stay exact
-// fp32.  Blocks of 32 or more tokens (plain mode) take 32 tokens per step with
-// 16x16x32 PV MFMAs; 8-token blocks are taken two to a 16-token tile.
+// input's 16-bit type, and one PV MFMA contracts over (token, half) pairs, so the
+// probabilities enter with ~16 significant bits instead of 8 while V and the accumulation
+// stay exact fp32.  Blocks of 32 or more tokens (plain mode) take 32 tokens per step with
+// 16x16x32 PV MFMAs per half; 8-token blocks are taken two to a 16-token tile.
 // The cache layout makes every load a contiguous run per instruction: K is stored in
 // 16-byte chunks [D/8][B tokens][8], so the 64 lanes of one QK operand load read 16
 // tokens of 4 chunks; V is stored transposed [D][B tokens], so a PV operand load reads
