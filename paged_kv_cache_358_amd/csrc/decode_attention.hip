@@ -84,7 +84,8 @@ struct DecodeArgs {
   uint64_t* run_done; // split: per (sequence, KV head) arrival counters [S * H_kv] (workspace); tag << 32 | partitions
   uint32_t launch_tag; // split: this launch's counter tag
   // Groups of sequences sharing leading blocks (split kernel only): [num_groups][3] = first
-  // sequence, members, prefix blocks; the groups cover the batch in order.
+  // sequence, members, prefix blocks; the groups cover the batch in order.  Null with num_groups =
+  // num_seqs: every sequence is a group of its own (more than 16 query heads per KV head).
   const int32_t* share_groups;
   int32_t num_groups;
   // split: query columns per partial slot.  The split kernel's partials are indexed by run: run k writes
@@ -484,15 +485,18 @@ __global__ __launch_bounds__(WV * kWave) __attribute__((amdgpu_waves_per_eu(D ==
   // kGroup: group v's first sequence, members and shared blocks, clamped so that every row stays
   // inside the batch, the columns inside the NT 16-wide tiles and the shared blocks inside a table row.
   auto group_first = [&](int v) {
+    if (!a.share_groups) return v;
     const int f = a.share_groups[3 * v];
     return f < 0 ? 0 : (f >= a.num_seqs ? a.num_seqs - 1 : f);
   };
   auto group_members = [&](int v, int first) {
+    if (!a.share_groups) return 1;
     const int mm = a.share_groups[3 * v + 1];
     return max(1, min(min(mm, a.num_seqs - first), 16 * NT / g));
   };
   // The description counts cache blocks; the context counts tiles.
   auto group_shared = [&](int v) {
+    if (!a.share_groups) return 0;
     if constexpr (MULTI) {
       return max(0, min(a.share_groups[3 * v + 2], (a.ctx_limit / kBlockTokens) >> lsb)) << lsb;
     } else if constexpr (HALF) {
@@ -1609,22 +1613,25 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
   // 8-token blocks, two to a tile; partitions must hold whole tiles.
   const bool half_blocks = 2 * B == kBlockTokens && pt % kBlockTokens == 0;
   const bool half = c.dtype != PA_F32 && g <= 16;
-  const bool shape = half && (D == 64 || D == 128);
+  // 17 to 32 query heads per KV head fill both 16-column tiles of the split kernel's group mode: every
+  // sequence runs as a group of its own.
+  const bool wide_g = c.dtype != PA_F32 && g > 16 && g <= kMaxCols;
+  const bool shape = (half || wide_g) && (D == 64 || D == 128);
   const bool wide = half && D == 256 && B == kBlockTokens;
   // The split kernel indexes the weighted tiles of all (sequence, KV head) pairs with int32.
   const bool split = ((shape && (tiles || half_blocks)) || wide) && p->num_seqs <= kMaxScanSeqs &&
                      int64_t{p->num_seqs} * c.num_kv_heads *
                              ((int64_t{p->max_blocks_per_seq} << lsb) + int64_t{kPartCost} * (parts + 1) + kCtxCost) <
                          0x7fffffffLL;
-  out->route = split ? kRouteSplit : (shape && B == kBlockTokens) ? kRouteMfma : kRouteGeneric;
+  out->route = split ? kRouteSplit : (shape && half && B == kBlockTokens) ? kRouteMfma : kRouteGeneric;
   out->sub_log2 = split ? (half_blocks ? -1 : lsb) : 0;
   // Head_dim 256 runs sequence by sequence (its grouped form would spill).
-  out->group = split && !wide && p->shared && p->shared->num_groups > 0;
+  out->group = split && !wide && ((p->shared && p->shared->num_groups > 0) || wide_g);
 
   if (split) {
     // Partials per run (see DecodeArgs::part_cols); a context of one partition never spans runs.  A
     // description of shared prefixes sizes for whole groups' columns, with or without groups.
-    out->part_cols = (p->shared && !wide) ? kMaxCols : g;
+    out->part_cols = ((p->shared && !wide) || wide_g) ? kMaxCols : g;
     const bool partials = (p->shared && !wide) ? gparts > 1 : parts > 1;
     const size_t slots = size_t{kMaxRuns} * 2 * out->part_cols;
     out->ml_offset = slots * D;
@@ -1922,8 +1929,13 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
                    ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(p->workspace) + plan.counter_offset)
                    : nullptr;
   if (plan.group) {
-    a.share_groups = p->shared->groups;
-    a.num_groups = p->shared->num_groups;
+    if (p->shared && p->shared->num_groups > 0) {
+      a.share_groups = p->shared->groups;
+      a.num_groups = p->shared->num_groups;
+    } else {  // more than 16 query heads per KV head: one group per sequence
+      a.share_groups = nullptr;
+      a.num_groups = p->num_seqs;
+    }
   }
   // A tag no earlier call of this process used, seeded per process (a workspace may hold
   // counters another process left): the arrival counters need no clearing.

@@ -96,7 +96,10 @@ def test_workspace_bytes():
     (pa.PA_BF16, 256, 4, 64, 16, "decode_split_kernel"),
     (pa.PA_BF16, 256, 4, 64, 32, "decode_generic_kernel"),
     (pa.PA_BF16, 256, 4, 4096, 16, "decode_generic_kernel"),
-    (pa.PA_BF16, 128, 32, 64, 16, "decode_generic_kernel"),
+    (pa.PA_BF16, 128, 32, 64, 16, "decode_split_kernel"),   # 17..32 query heads: groups of one sequence
+    (pa.PA_F16, 64, 24, 64, 8, "decode_split_kernel"),
+    (pa.PA_BF16, 128, 32, 4096, 16, "decode_generic_kernel"),  # beyond the split kernel's sequences
+    (pa.PA_BF16, 128, 48, 64, 16, "decode_generic_kernel"),
     (pa.PA_BF16, 96, 4, 64, 16, "decode_generic_kernel"),
     (pa.PA_F32, 128, 1, 64, 16, "decode_generic_kernel"),
 ])
@@ -218,6 +221,9 @@ def test_workspace_bytes_with_shared_prefixes():
     # need 2 partitions of 32 tiles (the same context counted in 8-token blocks, 63, would fit in one)
     assert ws(ctypes.byref(shared(S=3, hq=4, hkv=4, d=64, maxb=32, maxctx=168, bs=8))) == _split_ws(32, 64, 3 * 4)
     assert ws(ctypes.byref(shared(S=3, hq=4, hkv=4, d=64, maxb=32, maxctx=160, bs=8))) == 0
+    # 17..32 query heads per KV head: every sequence a group of its own, partial slots of 32 columns
+    assert ws(ctypes.byref(_params(S=4, hq=24, hkv=1, d=64, maxb=100, maxctx=1000, part=256, dtype=pa.PA_BF16))) == \
+        _split_ws(32, 64, 4)
     # head_dim 256 runs sequence by sequence: its partials have g columns
     assert ws(ctypes.byref(shared(S=3, hq=8, hkv=2, d=256, maxb=100, maxctx=1000))) == _split_ws(4, 256, 3 * 2)
     # more groups than sequences, a negative count, or groups without an array: rejected
