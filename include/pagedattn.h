@@ -72,7 +72,7 @@ typedef struct pa_cache_desc {
                             blocks (one sequence at a time: a pa_shared_prefix description is not used) */
   int32_t block_size;    /* tokens per block, <= 1024.  Decode takes 8 (two to a 16-token tile: partitions
                             of whole tiles) and 16 << j (16, 32, ..., 1024) on the MFMA path (bf16/fp16,
-                            head_dim 64 or 128, H_q / H_kv <= 16, num_seqs <= 2048 beyond 16), with or
+                            head_dim 64 or 128, H_q / H_kv <= 32, num_seqs <= 2048 beyond 16), with or
                             without a pa_shared_prefix description; other sizes on the VALU kernel;
                             prefill takes 8 and 16 << j */
   int32_t dtype;         /* pa_dtype of K and V */
