@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--block-size", type=int, default=16,
                     help="decode c2/c3/c4/c5 and prefill: tokens per cache block (16; 8, 32, 64, ...)")
     ap.add_argument("--head-dim", type=int, default=0,
-                    help="decode c2/c3/c5: head_dim other than the workload's 128 (64 or 256)")
+                    help="decode c2/c3/c4/c5: head_dim other than the workload's 128 (64, 96 or 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle time budget of the headline CPU baseline (the other workloads get a third)")

@@ -1616,14 +1616,16 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
   // 17 to 32 query heads per KV head fill both 16-column tiles of the split kernel's group mode: every
   // sequence runs as a group of its own.
   const bool wide_g = c.dtype != PA_F32 && g > 16 && g <= kMaxCols;
-  const bool shape = (half || wide_g) && (D == 64 || D == 128);
+  const bool shape = (half || wide_g) && (D == 64 || D == 96 || D == 128);
   const bool wide = half && D == 256 && B == kBlockTokens;
   // The split kernel indexes the weighted tiles of all (sequence, KV head) pairs with int32.
   const bool split = ((shape && (tiles || half_blocks)) || wide) && p->num_seqs <= kMaxScanSeqs &&
                      int64_t{p->num_seqs} * c.num_kv_heads *
                              ((int64_t{p->max_blocks_per_seq} << lsb) + int64_t{kPartCost} * (parts + 1) + kCtxCost) <
                          0x7fffffffLL;
-  out->route = split ? kRouteSplit : (shape && half && B == kBlockTokens) ? kRouteMfma : kRouteGeneric;
+  out->route = split                                                     ? kRouteSplit
+               : (half && (D == 64 || D == 128) && B == kBlockTokens) ? kRouteMfma
+                                                                        : kRouteGeneric;
   out->sub_log2 = split ? (half_blocks ? -1 : lsb) : 0;
   // Head_dim 256 runs sequence by sequence (its grouped form would spill).
   out->group = split && !wide && ((p->shared && p->shared->num_groups > 0) || wide_g);
@@ -1786,6 +1788,7 @@ int32_t launch_decode(DecodeArgs args, const Plan& plan, hipStream_t st, hipEven
     args.part_blocks = plan.sub_log2 >= 0 ? args.part_blocks << plan.sub_log2 : args.part_blocks >> 1;
     if constexpr (DT != PA_F32) {
       if (D == 64) return launch_split_blocks<DT, 64>(&args, st, start, stop);
+      if (D == 96) return launch_split_blocks<DT, 96>(&args, st, start, stop);
       if (D == 256) return launch_split_blocks<DT, 256>(&args, st, start, stop);
       return launch_split_blocks<DT, 128>(&args, st, start, stop);
     }

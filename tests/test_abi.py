@@ -100,7 +100,9 @@ def test_workspace_bytes():
     (pa.PA_F16, 64, 24, 64, 8, "decode_split_kernel"),
     (pa.PA_BF16, 128, 32, 4096, 16, "decode_generic_kernel"),  # beyond the split kernel's sequences
     (pa.PA_BF16, 128, 48, 64, 16, "decode_generic_kernel"),
-    (pa.PA_BF16, 96, 4, 64, 16, "decode_generic_kernel"),
+    (pa.PA_BF16, 96, 4, 64, 16, "decode_split_kernel"),
+    (pa.PA_BF16, 96, 4, 4096, 16, "decode_generic_kernel"),   # the per-partition MFMA kernel covers 64 and 128
+    (pa.PA_BF16, 80, 4, 64, 16, "decode_generic_kernel"),
     (pa.PA_F32, 128, 1, 64, 16, "decode_generic_kernel"),
 ])
 def test_decode_kernel_query(dtype, d, g, S, bs, kernel):

@@ -1,7 +1,7 @@
 """A seeded sweep of decode shapes on the GPU against the fp64 oracle.
 
-Each case draws its shape from a fixed list (block size 8, 16, 32 or 64 tokens, head_dim 64, 128
-or 256, query heads per KV head 1..16, bf16 or fp16 inputs, fp32 or input-dtype output, the
+Each case draws its shape from a fixed list (block size 8, 16, 32 or 64 tokens, head_dim 64, 96,
+128 or 256, query heads per KV head 1..24, bf16 or fp16 inputs, fp32 or input-dtype output, the
 default partition or one of 16 * 2^k tokens) and its context lengths from a seeded mix of
 short, block-edge and multi-partition lengths, so that every kernel form the library
 dispatches to (split kernel in plain mode on 16-token tiles, on pairs of 8-token blocks or on
@@ -25,6 +25,7 @@ SHAPES = [
     (16, 256, 16, 16, "bf16"), (16, 128, 24, 8, "bf16"), (32, 128, 8, 8, "f16"), (32, 64, 32, 4, "bf16"),
     (32, 128, 16, 1, "bf16"), (64, 128, 12, 4, "bf16"), (64, 64, 8, 8, "f16"), (32, 256, 4, 2, "bf16"),
     (8, 128, 16, 2, "bf16"), (8, 64, 8, 8, "f16"), (8, 128, 24, 8, "f16"),
+    (16, 96, 32, 32, "bf16"), (32, 96, 8, 2, "f16"), (8, 96, 12, 4, "bf16"), (16, 96, 24, 1, "bf16"),
 ]
 
 

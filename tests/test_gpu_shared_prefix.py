@@ -271,3 +271,10 @@ def test_head_dim_64_one_workgroup_per_group_context():
     fb = ForkedBatch(12, 16, 8, 64, "bf16", prompts)
     gr, _ = check(fb)
     assert len(gr) == 64 and np.all(gr[:, 1] == 2)
+
+
+def test_head_dim_96():
+    # head_dim 96 (three 32-dim score chunks, six 16-dim output tiles) in group mode
+    prompts = [(333, [40, 0, 500, 7, 16, 16, 1, 90]), (200, [1, 2])]
+    fb = ForkedBatch(13, 16, 8, 96, "bf16", prompts, lone=[1])
+    check(fb)
