@@ -68,11 +68,12 @@ typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
 typedef struct pa_cache_desc {
   int64_t num_blocks;    /* physical blocks in the pool, > 0 */
   int32_t num_kv_heads;  /* H_kv, > 0 */
-  int32_t head_dim;      /* D, a multiple of X; the decode MFMA path covers 64 and 128, and 256 on 16-token
-                            blocks (one sequence at a time: a pa_shared_prefix description is not used) */
+  int32_t head_dim;      /* D, a multiple of X; the decode MFMA path covers 64, 96 and 128, and 256 on
+                            16-token blocks (one sequence at a time: a pa_shared_prefix description is not
+                            used) */
   int32_t block_size;    /* tokens per block, <= 1024.  Decode takes 8 (two to a 16-token tile: partitions
                             of whole tiles) and 16 << j (16, 32, ..., 1024) on the MFMA path (bf16/fp16,
-                            head_dim 64 or 128, H_q / H_kv <= 32, num_seqs <= 2048 beyond 16), with or
+                            head_dim 64, 96 or 128, H_q / H_kv <= 32, num_seqs <= 2048 beyond 16), with or
                             without a pa_shared_prefix description; other sizes on the VALU kernel;
                             prefill takes 8 and 16 << j */
   int32_t dtype;         /* pa_dtype of K and V */
