@@ -424,7 +424,7 @@ extern "C" int32_t paged_attention_prefill(const void* q, const void* k_cache, c
     while (sub_log2 < 6 && (kBlockTokens << sub_log2) < c.block_size) ++sub_log2;
     if ((kBlockTokens << sub_log2) != c.block_size) return PA_ERR_UNSUPPORTED;
   }
-  if (c.dtype == PA_F32 || (c.head_dim != 64 && c.head_dim != 128)) return PA_ERR_UNSUPPORTED;
+  if (c.dtype == PA_F32 || (c.head_dim != 64 && c.head_dim != 96 && c.head_dim != 128)) return PA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(p->stream);
   hipEvent_t start = static_cast<hipEvent_t>(p->start_event), stop = static_cast<hipEvent_t>(p->stop_event);
@@ -472,11 +472,15 @@ extern "C" int32_t paged_attention_prefill(const void* q, const void* k_cache, c
   if (c.dtype == PA_BF16) {
     if (c.head_dim == 64)
       launch_prefill<PA_BF16, 64>(bk, grid, block, st, start, stop, a);
+    else if (c.head_dim == 96)
+      launch_prefill<PA_BF16, 96>(bk, grid, block, st, start, stop, a);
     else
       launch_prefill<PA_BF16, 128>(bk, grid, block, st, start, stop, a);
   } else {
     if (c.head_dim == 64)
       launch_prefill<PA_F16, 64>(bk, grid, block, st, start, stop, a);
+    else if (c.head_dim == 96)
+      launch_prefill<PA_F16, 96>(bk, grid, block, st, start, stop, a);
     else
       launch_prefill<PA_F16, 128>(bk, grid, block, st, start, stop, a);
   }

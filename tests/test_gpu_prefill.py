@@ -64,10 +64,12 @@ def test_mha_chunks_of_every_shape(dtype):
     _check(pd, chunks, q_np, got, qs)
 
 
-def test_gqa_and_head_dim_64():
+def test_gqa_and_head_dims_64_and_96():
     for cfg, lens, chunks in ((synth.scaled(synth.C3, lens=[40, 700, 129, 1000]), [40, 700, 129, 1000], [40, 77, 129, 3]),
                               (synth.DecodeConfig("pf_d64", 51, 3, 16, 4, 64, "bf16", "fixed", (33, 250, 96)),
-                               [33, 250, 96], [33, 64, 95])):
+                               [33, 250, 96], [33, 64, 95]),
+                              (synth.DecodeConfig("pf_d96", 52, 3, 12, 4, 96, "f16", "fixed", (130, 333, 17)),
+                               [130, 333, 17], [130, 200, 17])):
         pd = PagedDecode(cfg)
         q_np = _chunk_queries(cfg, chunks, 2)
         got, qs = _run(pd, chunks, q_np)
