@@ -94,7 +94,7 @@ typedef struct pa_cache_desc {
  *   groups   int32 [num_groups][3] (device or pinned host memory): first sequence, members, prefix_blocks
  * members * (H_q / H_kv) must not exceed 32 (the query columns of two matrix-core tiles).  A description
  * that does not match the tables gives undefined results (never out-of-bounds accesses).  Used by the
- * bf16/fp16, head_dim 64/128, up-to-2048-sequence path; the other paths ignore it.
+ * bf16/fp16, head_dim 64/96/128, up-to-2048-sequence path; the other paths ignore it.
  */
 typedef struct pa_shared_prefix {
   const int32_t* groups;
@@ -139,11 +139,11 @@ const char* pa_last_error(void);
 
 /* Device workspace bytes paged_attention_decode needs for these parameters (0 when no context can span more
  * than one partition).  The call takes one of three kernels (paged_attention_decode_kernel names it):
- *   decode_split_kernel (bf16/fp16; head_dim 64 or 128 on blocks of 16 << j tokens, or 256 on 16-token blocks;
- *     H_q / H_kv <= 16; num_seqs <= 2048): at most 1024 workgroups ("runs") each write at most two partials,
- *     so the workspace is 1024 * 2 * C fp32 rows of head_dim + 2 values (C = H_q / H_kv query columns, or 32
- *     when p->shared is set), then num_seqs * H_kv uint64 arrival counters.  Its size does not grow with the
- *     batch's context lengths.
+ *   decode_split_kernel (bf16/fp16; head_dim 64, 96 or 128 on blocks of 8 or 16 << j tokens, or 256 on
+ *     16-token blocks; H_q / H_kv <= 32 (<= 16 at head_dim 256); num_seqs <= 2048): at most 1024 workgroups
+ *     ("runs") each write at most two partials, so the workspace is 1024 * 2 * C fp32 rows of head_dim + 2
+ *     values (C = H_q / H_kv query columns, or 32 when p->shared is set or H_q / H_kv > 16), then
+ *     num_seqs * H_kv uint64 arrival counters.  Its size does not grow with the batch's context lengths.
  *   decode_mfma_kernel / decode_generic_kernel (other shapes, larger batches): P = num_seqs * H_q * n fp32
  *     partial rows of head_dim + 2 values, n = ceil(min(max_context_len, max_blocks_per_seq * block_size) /
  *     partition_size).
@@ -269,7 +269,7 @@ typedef struct pa_prefill_params {
  *   query_start  [S + 1] int32, non-decreasing, query_start[0] = 0, query_start[S] = T, device
  *   out          [T][H_q][D] fp32 or the cache dtype
  * Rows whose position would be negative (a chunk longer than its context) are left unwritten.
- * bf16 / fp16 caches with head_dim 64 or 128 and blocks of 8 or 16 << j tokens (else PA_ERR_UNSUPPORTED);
+ * bf16 / fp16 caches with head_dim 64, 96 or 128 and blocks of 8 or 16 << j tokens (else PA_ERR_UNSUPPORTED);
  * asynchronous on the stream.
  */
 int32_t paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
