@@ -1617,7 +1617,7 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
   // sequence runs as a group of its own.
   const bool wide_g = c.dtype != PA_F32 && g > 16 && g <= kMaxCols;
   const bool shape = (half || wide_g) && (D == 64 || D == 96 || D == 128);
-  const bool wide = half && D == 256 && B == kBlockTokens;
+  const bool wide = half && D == 256 && (tiles || half_blocks);
   // The split kernel indexes the weighted tiles of all (sequence, KV head) pairs with int32.
   const bool split = ((shape && (tiles || half_blocks)) || wide) && p->num_seqs <= kMaxScanSeqs &&
                      int64_t{p->num_seqs} * c.num_kv_heads *
@@ -1761,12 +1761,14 @@ int32_t launch_split_all(DecodeArgs* args, hipStream_t st, hipEvent_t start, hip
 template <int DT, int D>
 int32_t launch_split_blocks(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   if constexpr (D == 256) {
-    // Plain mode on 16-token blocks only: the other forms would spill.
+    // Plain mode only: the grouped form would spill.
     int cus = 0;
     const int32_t rc = device_cus(&cus);
     if (rc != PA_OK) return rc;
-    return launch_split_waves<DT, 256, kPlain, 4, kBk16>(args, int64_t{args->num_seqs} * args->hkv, cus, st, start,
-                                                         stop);
+    const int64_t contexts = int64_t{args->num_seqs} * args->hkv;
+    if (args->sub_log2 > 0) return launch_split_waves<DT, 256, kPlain, 4, kBkMulti>(args, contexts, cus, st, start, stop);
+    if (args->sub_log2 < 0) return launch_split_waves<DT, 256, kPlain, 4, kBkHalf>(args, contexts, cus, st, start, stop);
+    return launch_split_waves<DT, 256, kPlain, 4, kBk16>(args, contexts, cus, st, start, stop);
   } else {
     if (args->sub_log2 > 0) return launch_split_all<DT, D, kBkMulti>(args, st, start, stop);
     if (args->sub_log2 < 0) return launch_split_all<DT, D, kBkHalf>(args, st, start, stop);

@@ -94,7 +94,9 @@ def test_workspace_bytes():
     (pa.PA_BF16, 128, 4, 4096, 8, "decode_generic_kernel"),
     (pa.PA_F32, 128, 1, 64, 8, "decode_generic_kernel"),
     (pa.PA_BF16, 256, 4, 64, 16, "decode_split_kernel"),
-    (pa.PA_BF16, 256, 4, 64, 32, "decode_generic_kernel"),
+    (pa.PA_BF16, 256, 4, 64, 32, "decode_split_kernel"),
+    (pa.PA_BF16, 256, 4, 64, 8, "decode_split_kernel"),
+    (pa.PA_BF16, 256, 4, 64, 48, "decode_generic_kernel"),
     (pa.PA_BF16, 256, 4, 4096, 16, "decode_generic_kernel"),
     (pa.PA_BF16, 128, 32, 64, 16, "decode_split_kernel"),   # 17..32 query heads: groups of one sequence
     (pa.PA_F16, 64, 24, 64, 8, "decode_split_kernel"),

@@ -75,11 +75,12 @@ def test_head_dim_64_and_group_4():
 
 
 def test_generic_path_shapes():
-    # group 48 (> 32 query heads per KV head), fp32 head_dim 256 and head_dim 256 on 32-token blocks
+    # group 48 (> 32 query heads per KV head), fp32 head_dim 256 and head_dim 256 on 48-token blocks
     # take the VALU kernel
     for cfg in (synth.DecodeConfig("g48", 32, 3, 48, 1, 128, "bf16", "fixed", (5, 600, 1100)),
                 synth.DecodeConfig("d256_f32", 33, 3, 4, 2, 256, "f32", "fixed", (7, 530, 40)),
-                synth.DecodeConfig("d256_b32", 33, 3, 4, 2, 256, "bf16", "fixed", (7, 530, 40), block_size=32),
+                synth.DecodeConfig("d256_b48", 33, 3, 4, 2, 256, "bf16", "fixed", (7, 530, 40), block_size=48,
+                                   partition_size=480),
                 synth.DecodeConfig("f32_gqa", 34, 3, 8, 2, 64, "f32", "fixed", (3, 1030, 48))):
         pd = PagedDecode(cfg)
         out = pd.run()

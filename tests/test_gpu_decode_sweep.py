@@ -26,6 +26,7 @@ SHAPES = [
     (32, 128, 16, 1, "bf16"), (64, 128, 12, 4, "bf16"), (64, 64, 8, 8, "f16"), (32, 256, 4, 2, "bf16"),
     (8, 128, 16, 2, "bf16"), (8, 64, 8, 8, "f16"), (8, 128, 24, 8, "f16"),
     (16, 96, 32, 32, "bf16"), (32, 96, 8, 2, "f16"), (8, 96, 12, 4, "bf16"), (16, 96, 24, 1, "bf16"),
+    (8, 256, 8, 2, "f16"), (64, 256, 2, 1, "bf16"),
 ]
 
 
