@@ -68,9 +68,8 @@ typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
 typedef struct pa_cache_desc {
   int64_t num_blocks;    /* physical blocks in the pool, > 0 */
   int32_t num_kv_heads;  /* H_kv, > 0 */
-  int32_t head_dim;      /* D, a multiple of X; the decode MFMA path covers 64, 96 and 128, and 256 on
-                            16-token blocks (one sequence at a time: a pa_shared_prefix description is not
-                            used) */
+  int32_t head_dim;      /* D, a multiple of X; the decode MFMA path covers 64, 96, 128 and 256 (256 one
+                            sequence at a time: a pa_shared_prefix description is not used) */
   int32_t block_size;    /* tokens per block, <= 1024.  Decode takes 8 (two to a 16-token tile: partitions
                             of whole tiles) and 16 << j (16, 32, ..., 1024) on the MFMA path (bf16/fp16,
                             head_dim 64, 96 or 128, H_q / H_kv <= 32, num_seqs <= 2048 beyond 16), with or
@@ -139,8 +138,8 @@ const char* pa_last_error(void);
 
 /* Device workspace bytes paged_attention_decode needs for these parameters (0 when no context can span more
  * than one partition).  The call takes one of three kernels (paged_attention_decode_kernel names it):
- *   decode_split_kernel (bf16/fp16; head_dim 64, 96 or 128 on blocks of 8 or 16 << j tokens, or 256 on
- *     16-token blocks; H_q / H_kv <= 32 (<= 16 at head_dim 256); num_seqs <= 2048): at most 1024 workgroups
+ *   decode_split_kernel (bf16/fp16; head_dim 64, 96, 128 or 256 on blocks of 8 or 16 << j tokens;
+ *     H_q / H_kv <= 32 (<= 16 at head_dim 256); num_seqs <= 2048): at most 1024 workgroups
  *     ("runs") each write at most two partials, so the workspace is 1024 * 2 * C fp32 rows of head_dim + 2
  *     values (C = H_q / H_kv query columns, or 32 when p->shared is set or H_q / H_kv > 16), then
  *     num_seqs * H_kv uint64 arrival counters.  Its size does not grow with the batch's context lengths.
