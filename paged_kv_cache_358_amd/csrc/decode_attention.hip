@@ -1618,17 +1618,22 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
   const bool wide_g = c.dtype != PA_F32 && g > 16 && g <= kMaxCols;
   const bool shape = (half || wide_g) && (D == 64 || D == 96 || D == 128);
   const bool wide = half && D == 256 && (tiles || half_blocks);
-  // The split kernel indexes the weighted tiles of all (sequence, KV head) pairs with int32.
-  const bool split = ((shape && (tiles || half_blocks)) || wide) && p->num_seqs <= kMaxScanSeqs &&
-                     int64_t{p->num_seqs} * c.num_kv_heads *
+  // Beyond kMaxScanSeqs sequences the split kernel runs once per slice of kMaxScanSeqs (its in-LDS index
+  // covers that many); 16-token blocks at head_dim 64 or 128 with up to 16 query heads per KV head take the
+  // per-partition MFMA kernel there instead.  The split kernel indexes the weighted tiles of a launch's
+  // (sequence, KV head) pairs with int32.
+  const bool big = p->num_seqs > kMaxScanSeqs;
+  const bool mfma_fits = half && (D == 64 || D == 128) && B == kBlockTokens;
+  const int64_t launch_seqs = std::min<int64_t>(p->num_seqs, kMaxScanSeqs);
+  const bool split = ((shape && (tiles || half_blocks)) || wide) && !(big && mfma_fits) &&
+                     launch_seqs * c.num_kv_heads *
                              ((int64_t{p->max_blocks_per_seq} << lsb) + int64_t{kPartCost} * (parts + 1) + kCtxCost) <
                          0x7fffffffLL;
-  out->route = split                                                     ? kRouteSplit
-               : (half && (D == 64 || D == 128) && B == kBlockTokens) ? kRouteMfma
-                                                                        : kRouteGeneric;
+  out->route = split ? kRouteSplit : mfma_fits ? kRouteMfma : kRouteGeneric;
   out->sub_log2 = split ? (half_blocks ? -1 : lsb) : 0;
-  // Head_dim 256 runs sequence by sequence (its grouped form would spill).
-  out->group = split && !wide && ((p->shared && p->shared->num_groups > 0) || wide_g);
+  // Head_dim 256 runs sequence by sequence (its grouped form would spill), and so does a batch cut into
+  // slices (a description's groups index the whole batch).
+  out->group = split && !wide && ((p->shared && p->shared->num_groups > 0 && !big) || wide_g);
 
   if (split) {
     // Partials per run (see DecodeArgs::part_cols); a context of one partition never spans runs.  A
@@ -1776,6 +1781,9 @@ int32_t launch_split_blocks(DecodeArgs* args, hipStream_t st, hipEvent_t start, 
   }
 }
 
+// Launches of the split kernel for a batch of S sequences: one per slice of kMaxScanSeqs.
+int split_slices(int S) { return std::max(1, (S + kMaxScanSeqs - 1) / kMaxScanSeqs); }
+
 template <int DT>
 int32_t launch_decode(DecodeArgs args, const Plan& plan, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   const int64_t D = args.head_dim;
@@ -1785,14 +1793,35 @@ int32_t launch_decode(DecodeArgs args, const Plan& plan, hipStream_t st, hipEven
   args.run_rounds = 0;
   if (!plan.group) args.num_groups = 0;  // every sequence on its own
   if (plan.route == kRouteSplit) {
-    // One launch: the split kernel merges its runs in place; it counts in 16-token tiles.
+    // One launch per slice of at most kMaxScanSeqs sequences (one for all but the largest batches): the
+    // split kernel merges its runs in place; it counts in 16-token tiles.  Slices run one after another
+    // on the stream, each with its own counter tag; they share the workspace.
     args.sub_log2 = plan.sub_log2;
     args.part_blocks = plan.sub_log2 >= 0 ? args.part_blocks << plan.sub_log2 : args.part_blocks >> 1;
     if constexpr (DT != PA_F32) {
-      if (D == 64) return launch_split_blocks<DT, 64>(&args, st, start, stop);
-      if (D == 96) return launch_split_blocks<DT, 96>(&args, st, start, stop);
-      if (D == 256) return launch_split_blocks<DT, 256>(&args, st, start, stop);
-      return launch_split_blocks<DT, 128>(&args, st, start, stop);
+      const int S = args.num_seqs;
+      const int slices = split_slices(S);
+      const int64_t q_row = int64_t{args.hq} * D * elem_bytes(DT);
+      const int64_t out_row = int64_t{args.hq} * D * (args.out_f32 ? 4 : elem_bytes(DT));
+      for (int c = 0; c < slices; ++c) {
+        DecodeArgs sa = args;
+        const int s0 = c * kMaxScanSeqs;
+        sa.num_seqs = std::min(kMaxScanSeqs, S - s0);
+        if (!sa.share_groups && sa.num_groups > 0) sa.num_groups = sa.num_seqs;  // groups of one sequence
+        sa.q = static_cast<const uint8_t*>(args.q) + s0 * q_row;
+        sa.out = static_cast<uint8_t*>(args.out) + s0 * out_row;
+        sa.block_tables = args.block_tables + int64_t{s0} * args.max_blocks;
+        sa.context_lens = args.context_lens + s0;
+        sa.launch_tag = args.launch_tag + static_cast<uint32_t>(c);
+        hipEvent_t e0 = c == 0 ? start : nullptr, e1 = c == slices - 1 ? stop : nullptr;
+        int32_t rc;
+        if (D == 64) rc = launch_split_blocks<DT, 64>(&sa, st, e0, e1);
+        else if (D == 96) rc = launch_split_blocks<DT, 96>(&sa, st, e0, e1);
+        else if (D == 256) rc = launch_split_blocks<DT, 256>(&sa, st, e0, e1);
+        else rc = launch_split_blocks<DT, 128>(&sa, st, e0, e1);
+        if (rc != PA_OK) return rc;
+      }
+      return PA_OK;
     }
     return PA_ERR_UNSUPPORTED;
   }
@@ -1947,7 +1976,8 @@ extern "C" int32_t paged_attention_decode(const void* q, const void* k_cache, co
   static std::atomic<uint32_t> next_tag{static_cast<uint32_t>(
       std::chrono::steady_clock::now().time_since_epoch().count() * 0x9e3779b97f4a7c15ull >> 32) ^
       static_cast<uint32_t>(getpid())};
-  a.launch_tag = next_tag.fetch_add(1, std::memory_order_relaxed);
+  a.launch_tag = next_tag.fetch_add(
+      plan.route == kRouteSplit ? static_cast<uint32_t>(split_slices(p->num_seqs)) : 1u, std::memory_order_relaxed);
 
   hipStream_t stream = static_cast<hipStream_t>(p->stream);
   (void)hipGetLastError();  // drop an error some earlier, unrelated HIP call left behind

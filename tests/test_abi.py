@@ -87,23 +87,23 @@ def test_workspace_bytes():
     (pa.PA_BF16, 128, 4, 2049, 16, "decode_mfma_kernel"),
     (pa.PA_BF16, 128, 4, 64, 32, "decode_split_kernel"),
     (pa.PA_BF16, 64, 8, 64, 1024, "decode_split_kernel"),
-    (pa.PA_BF16, 128, 4, 4096, 32, "decode_generic_kernel"),
+    (pa.PA_BF16, 128, 4, 4096, 32, "decode_split_kernel"),    # beyond 2048 sequences: one launch per 2048
     (pa.PA_BF16, 128, 4, 64, 48, "decode_generic_kernel"),
     (pa.PA_BF16, 128, 4, 64, 8, "decode_split_kernel"),
     (pa.PA_F16, 64, 2, 64, 8, "decode_split_kernel"),
-    (pa.PA_BF16, 128, 4, 4096, 8, "decode_generic_kernel"),
+    (pa.PA_BF16, 128, 4, 4096, 8, "decode_split_kernel"),
     (pa.PA_F32, 128, 1, 64, 8, "decode_generic_kernel"),
     (pa.PA_BF16, 256, 4, 64, 16, "decode_split_kernel"),
     (pa.PA_BF16, 256, 4, 64, 32, "decode_split_kernel"),
     (pa.PA_BF16, 256, 4, 64, 8, "decode_split_kernel"),
     (pa.PA_BF16, 256, 4, 64, 48, "decode_generic_kernel"),
-    (pa.PA_BF16, 256, 4, 4096, 16, "decode_generic_kernel"),
+    (pa.PA_BF16, 256, 4, 4096, 16, "decode_split_kernel"),
     (pa.PA_BF16, 128, 32, 64, 16, "decode_split_kernel"),   # 17..32 query heads: groups of one sequence
     (pa.PA_F16, 64, 24, 64, 8, "decode_split_kernel"),
-    (pa.PA_BF16, 128, 32, 4096, 16, "decode_generic_kernel"),  # beyond the split kernel's sequences
+    (pa.PA_BF16, 128, 32, 4096, 16, "decode_split_kernel"),
     (pa.PA_BF16, 128, 48, 64, 16, "decode_generic_kernel"),
     (pa.PA_BF16, 96, 4, 64, 16, "decode_split_kernel"),
-    (pa.PA_BF16, 96, 4, 4096, 16, "decode_generic_kernel"),   # the per-partition MFMA kernel covers 64 and 128
+    (pa.PA_BF16, 96, 4, 4096, 16, "decode_split_kernel"),
     (pa.PA_BF16, 80, 4, 64, 16, "decode_generic_kernel"),
     (pa.PA_F32, 128, 1, 64, 16, "decode_generic_kernel"),
 ])

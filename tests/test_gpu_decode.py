@@ -202,6 +202,44 @@ def test_more_sequences_than_the_persistent_index_covers():
     assert max_err(out, pd, seqs=picks.tolist()) <= 5e-3
 
 
+@pytest.mark.parametrize("dtype,B,D,hq,hkv", [
+    ("bf16", 32, 128, 8, 2),   # 32-token blocks
+    ("f16", 8, 64, 8, 2),      # 8-token blocks, two to a 16-token tile
+    ("bf16", 16, 96, 8, 2),    # head_dim 96
+    ("bf16", 16, 128, 32, 1),  # 32 query heads per KV head: groups of one sequence
+    ("f16", 32, 256, 4, 1),    # head_dim 256
+])
+def test_more_sequences_than_one_split_launch_covers(dtype, B, D, hq, hkv):
+    # 4500 sequences on shapes the per-partition MFMA kernel does not take: the split kernel runs
+    # once per slice of 2048 sequences (2048, 2048, 404), each on its own rows of q, out, the
+    # tables and the lengths.  Sequences at the slice edges, empty ones, one longer than a
+    # partition, and random picks from every slice.
+    rng = np.random.default_rng(14)
+    lens = rng.integers(1, 300, size=4500)
+    edges = {0: 1, 2047: 299, 2048: 700, 2049: 0, 4095: 17, 4096: 513, 4499: 64}
+    for s, n in edges.items():
+        lens[s] = n
+    cfg = synth.DecodeConfig("many_seqs_split", 44, 4500, hq, hkv, D, dtype, "fixed",
+                             tuple(int(x) for x in lens), block_size=B)
+    pd = PagedDecode(cfg, keep_truth=False)
+    out = pd.run()
+    o = out.cpu().numpy()
+    assert np.all(np.isfinite(o))
+    assert np.all(o[2049] == 0)
+    picks = sorted(set(rng.choice(cfg.num_seqs, size=36, replace=False).tolist()) | set(edges) - {2049})
+    heads = [0, hq // 2, hq - 1]
+    for s in picks:
+        if lens[s] == 0:
+            assert np.all(o[s] == 0)
+            continue
+        ref = pd.oracle_sampled(s, heads)
+        assert np.max(np.abs(o[s, heads] - ref)) <= tol_for(dtype), s
+    # a call with another partition size over the same cache reuses the workspace with new tags
+    o2 = pd.run(partition_size=4 * B).cpu().numpy()
+    for s in (2047, 2048, 4096):
+        assert np.max(np.abs(o2[s, heads] - pd.oracle_sampled(s, heads))) <= tol_for(dtype), s
+
+
 def test_mixed_empty_short_and_long_contexts():
     # Zero-length, one-token, partial-block and multi-partition contexts side by side:
     # the persistent split cuts runs inside long contexts and the merge recombines them.
@@ -268,7 +306,11 @@ def test_start_and_stop_events_bracket_the_kernels(part):
     # split kernel indexes) ends with the merge kernel, which carries the stop event.
     import paged_kv_cache_358_amd as pa
     many = synth.DecodeConfig("many_seqs_ev", 43, 2050, 8, 2, 64, "bf16", "fixed", (40, 600) * 1025)
-    for cfg in (synth.scaled(synth.C2, lens=[700, 33, 2048]), many):
+    # 32-token blocks beyond 2048 sequences: two launches of the split kernel, the start event on
+    # the first and the stop event on the second
+    sliced = synth.DecodeConfig("many_seqs_ev32", 45, 2050, 8, 2, 64, "bf16", "fixed", (40, 600) * 1025,
+                                block_size=32)
+    for cfg in (synth.scaled(synth.C2, lens=[700, 33, 2048]), many, sliced):
         pd = PagedDecode(cfg, keep_truth=False)
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record()
@@ -276,7 +318,7 @@ def test_start_and_stop_events_bracket_the_kernels(part):
         out = torch.empty(pd.q.shape, dtype=torch.float32, device=pd.q.device)
         pa.paged_attention_decode(pd.q, pd.k_cache, pd.v_cache, pd.block_tables, pd.context_lens,
                                   cfg.softmax_scale, out, max_context_len=pd.max_context_len,
-                                  partition_size=part, start_event=start, stop_event=stop)
+                                  partition_size=max(part, cfg.block_size), start_event=start, stop_event=stop)
         stop.synchronize()
         ms = start.elapsed_time(stop)
         assert 0.0 < ms < 1000.0
