@@ -72,9 +72,8 @@ typedef struct pa_cache_desc {
                             sequence at a time: a pa_shared_prefix description is not used) */
   int32_t block_size;    /* tokens per block, <= 1024.  Decode takes 8 (two to a 16-token tile: partitions
                             of whole tiles) and 16 << j (16, 32, ..., 1024) on the MFMA path (bf16/fp16,
-                            head_dim 64, 96 or 128, H_q / H_kv <= 32, num_seqs <= 2048 beyond 16), with or
-                            without a pa_shared_prefix description; other sizes on the VALU kernel;
-                            prefill takes 8 and 16 << j */
+                            head_dim 64, 96 or 128, H_q / H_kv <= 32), with or without a pa_shared_prefix
+                            description; other sizes on the VALU kernel; prefill takes 8 and 16 << j */
   int32_t dtype;         /* pa_dtype of K and V */
 } pa_cache_desc;
 
@@ -92,8 +91,9 @@ typedef struct pa_cache_desc {
  * the tables and lengths.
  *   groups   int32 [num_groups][3] (device or pinned host memory): first sequence, members, prefix_blocks
  * members * (H_q / H_kv) must not exceed 32 (the query columns of two matrix-core tiles).  A description
- * that does not match the tables gives undefined results (never out-of-bounds accesses).  Used by the
- * bf16/fp16, head_dim 64/96/128, up-to-2048-sequence path; the other paths ignore it.
+ * that does not match the tables gives undefined results (never out-of-bounds accesses).  Used by the split
+ * kernel at head_dim 64/96/128 (bf16/fp16) in batches of up to 2048 sequences; larger batches, head_dim 256
+ * and the other kernels ignore it.
  */
 typedef struct pa_shared_prefix {
   const int32_t* groups;
@@ -139,13 +139,16 @@ const char* pa_last_error(void);
 /* Device workspace bytes paged_attention_decode needs for these parameters (0 when no context can span more
  * than one partition).  The call takes one of three kernels (paged_attention_decode_kernel names it):
  *   decode_split_kernel (bf16/fp16; head_dim 64, 96, 128 or 256 on blocks of 8 or 16 << j tokens;
- *     H_q / H_kv <= 32 (<= 16 at head_dim 256); num_seqs <= 2048): at most 1024 workgroups
- *     ("runs") each write at most two partials, so the workspace is 1024 * 2 * C fp32 rows of head_dim + 2
- *     values (C = H_q / H_kv query columns, or 32 when p->shared is set or H_q / H_kv > 16), then
- *     num_seqs * H_kv uint64 arrival counters.  Its size does not grow with the batch's context lengths.
- *   decode_mfma_kernel / decode_generic_kernel (other shapes, larger batches): P = num_seqs * H_q * n fp32
+ *     H_q / H_kv <= 32 (<= 16 at head_dim 256)): at most 1024 workgroups ("runs") each write at most two
+ *     partials, so the workspace is 1024 * 2 * C fp32 rows of head_dim + 2 values (C = H_q / H_kv query
+ *     columns, or 32 when p->shared is set or H_q / H_kv > 16), then num_seqs * H_kv uint64 arrival
+ *     counters.  Its size does not grow with the batch's context lengths.  A batch of more than 2048
+ *     sequences runs as one launch per 2048, in stream order, sharing the workspace.
+ *   decode_mfma_kernel (batches of more than 2048 sequences on 16-token blocks, head_dim 64 or 128,
+ *     H_q / H_kv <= 16, whose contexts all fit one partition; or a block table too wide for the split
+ *     kernel's int32 tile index) / decode_generic_kernel (other shapes): P = num_seqs * H_q * n fp32
  *     partial rows of head_dim + 2 values, n = ceil(min(max_context_len, max_blocks_per_seq * block_size) /
- *     partition_size).
+ *     partition_size), when n > 1.
  * Returns 0 for invalid parameters (the decode call then reports the error).  The contents need no
  * initialisation (the counters carry a per-call tag) and are scratch between calls; two calls in flight at
  * once must not share a workspace. */

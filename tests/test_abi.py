@@ -75,8 +75,14 @@ def test_workspace_bytes():
     # 48-token blocks: the default partition rounds 512 down to 480
     p = _params(maxb=100, maxctx=1000, bs=48)
     assert ws(ctypes.byref(p)) == _part_ws(4, 4, 3, 64)
-    # more than 2048 sequences: the per-partition MFMA kernel
+    # more than 2048 sequences: the split kernel per slice of 2048 (its counters cover the whole batch) ...
     p = _params(S=3000, hq=8, hkv=2, d=128, maxb=64, maxctx=1024, dtype=pa.PA_BF16)
+    assert ws(ctypes.byref(p)) == _split_ws(4, 128, 3000 * 2)
+    # ... or, with every context in one partition, the per-partition MFMA kernel, which needs no partials
+    p = _params(S=3000, hq=8, hkv=2, d=128, maxb=64, maxctx=512, dtype=pa.PA_BF16)
+    assert ws(ctypes.byref(p)) == 0
+    # fp32 beyond 2048 sequences: the per-partition VALU kernel
+    p = _params(S=3000, hq=8, hkv=2, d=128, maxb=64, maxctx=1024)
     assert ws(ctypes.byref(p)) == _part_ws(3000, 8, 2, 128)
     assert ws(None) == 0
 
@@ -84,10 +90,10 @@ def test_workspace_bytes():
 @pytest.mark.parametrize("dtype,d,g,S,bs,kernel", [
     (pa.PA_BF16, 128, 1, 64, 16, "decode_split_kernel"),
     (pa.PA_F16, 64, 16, 2048, 16, "decode_split_kernel"),
-    (pa.PA_BF16, 128, 4, 2049, 16, "decode_mfma_kernel"),
+    (pa.PA_BF16, 128, 4, 2049, 16, "decode_split_kernel"),  # beyond 2048 sequences: one launch per 2048
     (pa.PA_BF16, 128, 4, 64, 32, "decode_split_kernel"),
     (pa.PA_BF16, 64, 8, 64, 1024, "decode_split_kernel"),
-    (pa.PA_BF16, 128, 4, 4096, 32, "decode_split_kernel"),    # beyond 2048 sequences: one launch per 2048
+    (pa.PA_BF16, 128, 4, 4096, 32, "decode_split_kernel"),
     (pa.PA_BF16, 128, 4, 64, 48, "decode_generic_kernel"),
     (pa.PA_BF16, 128, 4, 64, 8, "decode_split_kernel"),
     (pa.PA_F16, 64, 2, 64, 8, "decode_split_kernel"),
@@ -114,6 +120,23 @@ def test_decode_kernel_query(dtype, d, g, S, bs, kernel):
     assert pa.lib.paged_attention_decode_kernel(ctypes.byref(_params(S=0))) == b""
     assert pa.lib.paged_attention_decode_kernel(ctypes.byref(_params(hq=6))) == b""
     assert pa.lib.paged_attention_decode_kernel(None) == b""
+
+
+@pytest.mark.parametrize("d,g,bs,maxctx,part,kernel", [
+    (128, 4, 16, 512, 0, "decode_mfma_kernel"),      # one partition per context
+    (128, 4, 16, 513, 0, "decode_split_kernel"),     # two
+    (128, 4, 16, 1000, 1024, "decode_mfma_kernel"),  # one, with 1024-token partitions
+    (64, 16, 16, 200, 0, "decode_mfma_kernel"),
+    (64, 32, 16, 200, 0, "decode_split_kernel"),     # more than 16 query heads per KV head
+    (96, 4, 16, 512, 0, "decode_split_kernel"),      # head_dim 96
+    (128, 4, 32, 512, 0, "decode_split_kernel"),     # 32-token blocks
+])
+def test_batches_beyond_2048_sequences(d, g, bs, maxctx, part, kernel):
+    # Beyond the split kernel's 2048-sequence index, 16-token blocks at head_dim 64/128 with up to 16
+    # query heads per KV head take the per-partition MFMA kernel when every context fits one
+    # partition; every other MFMA-path shape runs the split kernel once per 2048 sequences.
+    p = _params(S=5000, hq=4 * g, hkv=4, d=d, bs=bs, maxb=64, maxctx=maxctx, dtype=pa.PA_BF16, part=part)
+    assert pa.lib.paged_attention_decode_kernel(ctypes.byref(p)) == kernel.encode()
 
 
 @pytest.mark.parametrize("part,kernel", [(0, "decode_split_kernel"), (16, "decode_split_kernel"),

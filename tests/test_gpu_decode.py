@@ -190,16 +190,47 @@ def test_full_c5_long_context_every_row():
 
 # ----------------------------------------------------------------- scheduling paths of the MFMA kernels
 def test_more_sequences_than_the_persistent_index_covers():
-    # 2100 sequences (> 2048) take the one-workgroup-per-partition kernel, with partials
-    # (256-token partitions, contexts up to 700).
+    # 2100 sequences (> 2048) at head_dim 64 on 16-token blocks, contexts up to 700 tokens.  With
+    # 1024-token partitions every context is one partition and the batch takes the per-partition
+    # MFMA kernel (one workgroup per sequence and KV head, no merge); with 256-token partitions the
+    # split kernel runs once per slice of 2048 sequences.
+    import paged_kv_cache_358_amd as pa
     lens = np.random.default_rng(11).integers(1, 700, size=2100)
     cfg = synth.DecodeConfig("many_seqs", 41, 2100, 8, 2, 64, "bf16", "fixed", tuple(int(x) for x in lens),
-                             partition_size=256)
+                             partition_size=1024)
     pd = PagedDecode(cfg)
-    out = pd.run()
-    assert torch.isfinite(out).all()
-    picks = np.random.default_rng(12).choice(cfg.num_seqs, size=60, replace=False)
-    assert max_err(out, pd, seqs=picks.tolist()) <= 5e-3
+    picks = sorted(set(np.random.default_rng(12).choice(cfg.num_seqs, size=60, replace=False).tolist())
+                   | {0, 2047, 2048, 2099})
+    for part, kernel in ((1024, "decode_mfma_kernel"), (256, "decode_split_kernel")):
+        out = torch.empty(pd.q.shape, dtype=torch.float32, device="cuda")
+        assert pa.paged_attention_decode_kernel(pd.q, pd.k_cache, pd.v_cache, pd.block_tables, out,
+                                                pd.max_context_len, part) == kernel
+        out = pd.run(partition_size=part)
+        assert torch.isfinite(out).all()
+        assert max_err(out, pd, seqs=picks) <= 5e-3, part
+
+
+def test_per_partition_mfma_kernel_with_merges():
+    # A block table so wide that the split kernel's int32 tile index could overflow (2049 sequences
+    # x 8 KV heads x 131072 entries) sends the batch to the per-partition MFMA kernel even with
+    # contexts over several partitions: partials and the merge kernel.  Table entries past each
+    # context are zero, and never read.
+    import paged_kv_cache_358_amd as pa
+    lens = np.random.default_rng(15).integers(1, 40, size=2049)
+    lens[[0, 1, 2, 1000, 2048]] = [1500, 512, 513, 1100, 2000]
+    cfg = synth.DecodeConfig("wide_table", 46, 2049, 32, 8, 128, "bf16", "fixed", tuple(int(x) for x in lens))
+    pd = PagedDecode(cfg, keep_truth=False)
+    wide = torch.zeros(cfg.num_seqs, 131072, dtype=torch.int32, device="cuda")
+    wide[:, :pd.block_tables.shape[1]] = pd.block_tables
+    out = torch.empty(pd.q.shape, dtype=torch.float32, device="cuda")
+    assert pa.paged_attention_decode_kernel(pd.q, pd.k_cache, pd.v_cache, wide, out, pd.max_context_len,
+                                            512) == "decode_mfma_kernel"
+    out = pd.run(block_tables=wide).cpu().numpy()
+    heads = [0, 13, 31]
+    for s in (0, 1, 2, 1000, 2048):
+        assert np.max(np.abs(out[s, heads] - pd.oracle_sampled(s, heads))) <= 5e-3, s
+    del wide
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("dtype,B,D,hq,hkv", [
@@ -305,7 +336,8 @@ def test_start_and_stop_events_bracket_the_kernels(part):
     # The events travel with the launches; the per-partition path (more sequences than the
     # split kernel indexes) ends with the merge kernel, which carries the stop event.
     import paged_kv_cache_358_amd as pa
-    many = synth.DecodeConfig("many_seqs_ev", 43, 2050, 8, 2, 64, "bf16", "fixed", (40, 600) * 1025)
+    # fp32 beyond 2048 sequences: the per-partition VALU kernel and the merge kernel
+    many = synth.DecodeConfig("many_seqs_ev", 43, 2050, 8, 2, 64, "f32", "fixed", (40, 600) * 1025)
     # 32-token blocks beyond 2048 sequences: two launches of the split kernel, the start event on
     # the first and the stop event on the second
     sliced = synth.DecodeConfig("many_seqs_ev32", 45, 2050, 8, 2, 64, "bf16", "fixed", (40, 600) * 1025,
