@@ -1545,11 +1545,12 @@ namespace {
 constexpr int kPartCost = 5;
 constexpr int kCtxCost = 5;
 
-// Which kernel serves a call.  kSplit: decode_split_kernel (bf16/fp16, head_dim 64/128 on blocks of
-// 16 << j tokens or head_dim 256 on 16-token blocks, at most 16 query heads per KV head, at most
-// kMaxScanSeqs sequences); it merges split contexts itself.  kMfma: decode_mfma_kernel, one workgroup per
-// (partition, KV head, sequence), for larger batches on 16-token blocks.  kGeneric: decode_generic_kernel
-// (VALU) for every other shape.  The last two write per-partition partials that
+// Which kernel serves a call.  kSplit: decode_split_kernel (bf16/fp16, head_dim 64/96/128/256 on blocks of
+// 8 or 16 << j tokens, at most 32 query heads per KV head (16 at head_dim 256), one launch per kMaxScanSeqs
+// sequences); it merges split contexts itself.  kMfma: decode_mfma_kernel, one workgroup per (partition, KV
+// head, sequence), for batches beyond kMaxScanSeqs sequences on 16-token blocks whose contexts each fit one
+// partition, and for block tables too wide for the split kernel's int32 tile index.  kGeneric:
+// decode_generic_kernel (VALU) for every other shape.  The last two write per-partition partials that
 // reduce_partitions_kernel merges.
 enum Route : int32_t { kRouteSplit = 0, kRouteMfma = 1, kRouteGeneric = 2 };
 
