@@ -89,13 +89,39 @@ def test_noalloc_groups_on_8_token_blocks():
 
 
 def test_noalloc_rejects_what_its_scratch_cannot_hold():
-    # More sequences than the split kernel indexes, with many partitions: the per-partition kernels
-    # would need more partial rows than the scratch holds.  Rejected before anything is launched.
+    # fp32 caches with many partitions: the per-partition kernel would need more partial rows than the
+    # scratch holds.  Rejected before anything is launched (the pointers below are not device memory,
+    # so the sizes are checked first and the call is made only when the rejection is certain).
     S, hq, D, parts = 4096, 64, 128, 16
     need = S * hq * parts * (D + 2) * 4
-    assert need > pa.lib.paged_attention_noalloc_scratch_bytes()
-    c = pa.CacheDesc(1024, 8, D, 16, pa.PA_BF16)
+    c = pa.CacheDesc(1024, 8, D, 16, pa.PA_F32)
     p = pa.DecodeParams(S, hq, 512, 512 * parts, 512, pa.PA_F32, c, None, 0, None, None)
+    assert pa.lib.paged_attention_decode_kernel(ctypes.byref(p)) == b"decode_generic_kernel"
+    assert pa.lib.paged_attention_workspace_bytes(ctypes.byref(p)) == need
+    assert need > pa.lib.paged_attention_noalloc_scratch_bytes()
     fake = ctypes.c_void_p(256)
     assert pa.lib.paged_attention_decode_noalloc(fake, fake, fake, fake, fake, 0.1, fake, ctypes.byref(p)) == \
         pa.PA_ERR_WORKSPACE
+
+
+def test_noalloc_batches_beyond_2048_sequences():
+    # 4500 sequences on 32-token blocks: the split kernel once per slice of 2048 sequences, each slice
+    # reusing the scratch; then a smaller batch (2100 sequences, one partition each at head_dim 64 on
+    # 16-token blocks: the per-partition kernel, no partials).
+    rng = np.random.default_rng(16)
+    lens = rng.integers(1, 300, size=4500)
+    lens[[0, 2047, 2048, 4096, 4499]] = [700, 513, 1100, 600, 1]
+    big = PagedDecode(synth.DecodeConfig("noalloc_many", 47, 4500, 8, 2, 128, "bf16", "fixed",
+                                         tuple(int(x) for x in lens), block_size=32), keep_truth=False)
+    assert pa.paged_attention_workspace_bytes(big.q, big.k_cache, big.v_cache, big.block_tables,
+                                              torch.empty(big.q.shape, device="cuda"), big.max_context_len,
+                                              big.cfg.partition_size) <= pa.lib.paged_attention_noalloc_scratch_bytes()
+    ref, got = big.run(), _noalloc(big)
+    assert torch.equal(ref, got)
+    assert _worst(got, big, [0, 2047, 2048, 4096, 4499], [0, 7]) <= tol_for("bf16")
+    lens2 = rng.integers(1, 500, size=2100)
+    small = PagedDecode(synth.DecodeConfig("noalloc_many_small", 48, 2100, 8, 2, 64, "bf16", "fixed",
+                                           tuple(int(x) for x in lens2)), keep_truth=False)
+    ref, got = small.run(), _noalloc(small)
+    assert torch.equal(ref, got)
+    assert _worst(got, small, [0, 2047, 2048, 2099], [0, 7]) <= tol_for("bf16")
