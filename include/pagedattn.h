@@ -92,9 +92,13 @@ typedef struct pa_cache_desc {
  *   groups   int32 [num_groups][3] (device or pinned host memory): first sequence, members, prefix_blocks
  * members * (H_q / H_kv) must not exceed 32 (the query columns of two matrix-core tiles).  A description
  * that does not match the tables gives undefined results (never out-of-bounds accesses).  Used by the split
- * kernel at head_dim 64/96/128 (bf16/fp16) in batches of up to 2048 sequences; larger batches, head_dim 256
- * and the other kernels ignore it.
+ * kernel at head_dim 64/96/128 (bf16/fp16) in batches of up to PA_MAX_GROUPED_SEQS sequences; larger
+ * batches, head_dim 256 and the other kernels ignore it.  A caller with a larger batch can cut it at group
+ * boundaries into calls of at most PA_MAX_GROUPED_SEQS sequences each, with the groups' first sequences
+ * counted from the call's first sequence (the Python engine does so).
  */
+#define PA_MAX_GROUPED_SEQS 2048
+
 typedef struct pa_shared_prefix {
   const int32_t* groups;
   int32_t num_groups;  /* 0 (= no sharing) or the number of groups covering the batch, <= num_seqs */

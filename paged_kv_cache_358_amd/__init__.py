@@ -22,6 +22,8 @@ LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(_PKG, "libpagedattn.s
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_OUT_OF_BLOCKS, PA_ERR_HIP, PA_ERR_WORKSPACE = range(6)
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
+# The most sequences one decode call reads through a shared-prefix description (PA_MAX_GROUPED_SEQS).
+PA_MAX_GROUPED_SEQS = 2048
 BLOCK_SIZE = 16
 
 # Every symbol the header declares, with its ctypes signature.

@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(DecodeArgs 
 // ------------------------------------------------------------------ split MFMA path
 
 constexpr float kLazyLog2 = 8.0f;  // how far (log2 units) a score may exceed the softmax reference point
-constexpr int kMaxScanSeqs = 2048;  // sequences the split kernel's in-LDS index covers
+constexpr int kMaxScanSeqs = PA_MAX_GROUPED_SEQS;  // sequences the split kernel's in-LDS index covers
 constexpr int kPersistRing = 2;     // ring depth of the split kernel
 constexpr int kXcds = 8;            // accelerator complex dies of an MI355X, each with its own L2
 constexpr int kMaxRuns = 1024;      // chunks (workgroups, runs) of the split kernel, at most

@@ -25,8 +25,29 @@ import ctypes
 import numpy as np
 import torch
 
-from . import (PA_OK, BlockAllocator, DecodeParams, PagedAttnError, SharedPrefix, _P32, _P64, alloc_kv_cache,
-               block_copy, cache_desc, kv_append, lib, paged_attention_workspace_bytes, stage_copy, torch_dtype_code)
+from . import (PA_MAX_GROUPED_SEQS, PA_OK, BlockAllocator, DecodeParams, PagedAttnError, SharedPrefix, _P32, _P64,
+               alloc_kv_cache, block_copy, cache_desc, kv_append, lib, paged_attention_workspace_bytes, stage_copy,
+               torch_dtype_code)
+
+
+def group_batches(groups: np.ndarray, num_seqs: int, limit: int = PA_MAX_GROUPED_SEQS):
+    """Cut a batch whose groups (rows [first, members, shared blocks], consecutive and covering
+    sequences 0 .. num_seqs - 1 in order) are read through one description into runs of whole
+    groups of at most ``limit`` sequences: [(s0, s1, g0, g1)], sequences s0 .. s1 - 1 and groups
+    g0 .. g1 - 1 of each run.  Every group holds at most ``limit`` members."""
+    ng = len(groups)
+    if ng == 0 or num_seqs <= limit:
+        return [(0, num_seqs, 0, ng)]
+    ends = groups[:, 0].astype(np.int64) + groups[:, 1]
+    runs = []
+    s0 = g0 = 0
+    while g0 < ng:
+        # the last group that ends within limit sequences of s0 (at least the first: members <= limit)
+        g1 = max(g0 + 1, int(np.searchsorted(ends, s0 + limit, side="right")))
+        s1 = int(groups[g1, 0]) if g1 < ng else num_seqs
+        runs.append((s0, s1, g0, g1))
+        s0, g0 = s1, g1
+    return runs
 
 
 class _Staging:
@@ -101,12 +122,17 @@ class PagedDecodeLayer:
         self._c_ones = self._ones.ctypes.data_as(_P32)
         self._npairs = ctypes.c_int32(0)
         self._ngroups = ctypes.c_int32(0)
-        probe_q = torch.empty(max_seqs, num_q_heads, head_dim, dtype=dtype, device=device)
-        probe_t = torch.empty(max_seqs, max_blocks_per_seq, dtype=torch.int32, device=device)
-        ws = paged_attention_workspace_bytes(probe_q, self.k_cache, self.v_cache, probe_t,
-                                             torch.empty_like(probe_q, dtype=torch.float32),
-                                             max_blocks_per_seq * block_size, partition_size, shared=share_prefixes)
-        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
+        # Sized for a whole batch and, with sharing, for a run of PA_MAX_GROUPED_SEQS grouped sequences
+        # (a larger grouped batch is read in such runs).
+        ws = 16
+        for n in {max_seqs, min(max_seqs, PA_MAX_GROUPED_SEQS)}:
+            probe_q = torch.empty(n, num_q_heads, head_dim, dtype=dtype, device=device)
+            probe_t = torch.empty(n, max_blocks_per_seq, dtype=torch.int32, device=device)
+            ws = max(ws, paged_attention_workspace_bytes(probe_q, self.k_cache, self.v_cache, probe_t,
+                                                         torch.empty_like(probe_q, dtype=torch.float32),
+                                                         max_blocks_per_seq * block_size, partition_size,
+                                                         shared=share_prefixes))
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
         # The per-step library calls go straight to the C ABI with argument blocks built here once:
         # the layer owns the caches, staging buffers and workspace, so only the step's tensors,
         # sizes and events change between calls.
@@ -184,6 +210,12 @@ class PagedDecodeLayer:
             if rc != PA_OK:
                 raise PagedAttnError(rc, "pa_shared_prefixes")
             ngroups = self._ngroups.value if self._ngroups.value < S else 0
+        group_rows = st.h_groups[:ngroups].copy() if ngroups else None
+        # A grouped batch of more than PA_MAX_GROUPED_SEQS sequences goes to the library in runs of whole
+        # groups, each description counting its first sequences from the run's first.
+        runs = group_batches(st.h_groups[:ngroups], S) if ngroups else [(0, S, 0, 0)]
+        for s0, _, g0, g1 in runs[1:]:
+            st.h_groups[g0:g1, 0] -= s0
         used = st.o_tables + S * self.max_blocks  # lengths, slots, pairs, sharing and the first S table rows
         if npairs:
             # copy-on-write blocks are copied before the append writes into them
@@ -200,23 +232,30 @@ class PagedDecodeLayer:
         # the staging copies (earlier in the stream) are done when the attention kernels are
         st.done = st.own_done if timing is None else timing[1]
         p = self._params
-        p.num_seqs = S
         p.max_context_len = max_ctx
         p.out_dtype = torch_dtype_code(out.dtype)
-        p.start_event = None if timing is None else timing[0].cuda_event
-        p.stop_event = st.done.cuda_event
-        if ngroups:
-            self._shared.groups = st.dev_ptr + 4 * st.o_groups
-            self._shared.num_groups = ngroups
-            p.shared = ctypes.pointer(self._shared)
-        else:
-            p.shared = None
-        rc = lib.paged_attention_decode(q.data_ptr(), self._k_ptr, self._v_ptr, st.dev_ptr + 4 * st.o_tables,
-                                        st.dev_ptr + 4 * st.o_lens, float(scale), out.data_ptr(), ctypes.byref(p))
-        if rc != PA_OK:
-            raise PagedAttnError(rc, "paged_attention_decode")
+        q_row = hq * D * q.element_size()
+        out_row = hq * D * out.element_size()
+        for i, (s0, s1, g0, g1) in enumerate(runs):
+            p.num_seqs = s1 - s0
+            # the start event on the first call, the end event on the last
+            p.start_event = None if timing is None or i > 0 else timing[0].cuda_event
+            p.stop_event = st.done.cuda_event if i == len(runs) - 1 else None
+            if g1 > g0:
+                self._shared.groups = st.dev_ptr + 4 * (st.o_groups + 3 * g0)
+                self._shared.num_groups = g1 - g0
+                p.shared = ctypes.pointer(self._shared)
+            else:
+                p.shared = None
+            rc = lib.paged_attention_decode(q.data_ptr() + s0 * q_row, self._k_ptr, self._v_ptr,
+                                            st.dev_ptr + 4 * (st.o_tables + s0 * self.max_blocks),
+                                            st.dev_ptr + 4 * (st.o_lens + s0), float(scale),
+                                            out.data_ptr() + s0 * out_row, ctypes.byref(p))
+            if rc != PA_OK:
+                raise PagedAttnError(rc, "paged_attention_decode")
+        self.last_runs = runs
         self.last_groups = ngroups
-        self.last_group_rows = st.h_groups[:ngroups].copy() if ngroups else None
+        self.last_group_rows = group_rows
         self.last_lens = np_lens.copy()
         self.last_tables = np_tables  # view into the pinned staging buffer: valid until three steps later
         return npairs

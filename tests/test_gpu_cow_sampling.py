@@ -110,3 +110,20 @@ def test_cow_sampling_full_sampled():
     rng = np.random.default_rng(4)
     check = sorted(rng.choice(cfg.num_seqs, 12, replace=False).tolist() + [0, 7, 511])
     run_sampling(cfg, {1, 2, 17, 100, 200}, check)
+
+
+@pytest.mark.parametrize("share_prefixes", [True, False])
+def test_cow_sampling_beyond_the_grouped_call_limit(share_prefixes):
+    # 264 prompts x 8 samples = 2112 sequences, more than one call reads through a shared-prefix
+    # description: the engine cuts the groups into runs of whole groups (2048 and 64 sequences), each
+    # description counted from its run's first sequence.  Without sharing the library runs the batch
+    # itself, one split launch per 2048 sequences.
+    cfg = dataclasses.replace(synth.C4, num_prompts=264, prefix_len=100, steps=3, slack_blocks=16)
+    rng = np.random.default_rng(17)
+    check = sorted(set(rng.choice(cfg.num_seqs, 10, replace=False).tolist()) | {0, 7, 2040, 2047, 2048, 2055, 2111})
+    layer = run_sampling(cfg, {1, 3}, check, share_prefixes)
+    if share_prefixes:
+        assert layer.last_runs == [(0, 2048, 0, 256), (2048, 2112, 256, 264)]
+        assert layer.last_group_rows[256, 0] == 2048  # the engine's record keeps batch-wide indices
+    else:
+        assert layer.last_runs == [(0, cfg.num_seqs, 0, 0)]
