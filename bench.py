@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--block-size", type=int, default=16,
                     help="decode c2/c3/c4/c5 and prefill: tokens per cache block (16; 8, 32, 64, ...)")
     ap.add_argument("--head-dim", type=int, default=0,
-                    help="decode c2/c3/c4/c5: head_dim other than the workload's 128 (64, 96 or 256)")
+                    help="decode c2/c3/c4/c5 and prefill: head_dim other than the workload's 128 (64, 96 or 256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle time budget of the headline CPU baseline (the other workloads get a third)")
@@ -530,9 +530,9 @@ def run_prefill(args):
     dev = torch.device("cuda:0")
     cfg = synth.C2
     BS = args.block_size
-    if BS != 16:  # the same contexts laid out in other blocks
+    if BS != 16 or args.head_dim:  # the same contexts laid out in other blocks, or with another head size
         import dataclasses
-        cfg = dataclasses.replace(cfg, block_size=BS)
+        cfg = dataclasses.replace(cfg, block_size=BS, head_dim=args.head_dim or cfg.head_dim)
     lens = synth.context_lens(cfg).astype(np.int64)
     chunks = np.minimum(lens, args.chunk)
     S, hq, hkv, D = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim

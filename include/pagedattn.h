@@ -275,8 +275,8 @@ typedef struct pa_prefill_params {
  *   query_start  [S + 1] int32, non-decreasing, query_start[0] = 0, query_start[S] = T, device
  *   out          [T][H_q][D] fp32 or the cache dtype
  * Rows whose position would be negative (a chunk longer than its context) are left unwritten.
- * bf16 / fp16 caches with head_dim 64, 96 or 128 and blocks of 8 or 16 << j tokens (else PA_ERR_UNSUPPORTED);
- * asynchronous on the stream.
+ * bf16 / fp16 caches with head_dim 64, 96, 128 or 256 and blocks of 8 or 16 << j tokens (else
+ * PA_ERR_UNSUPPORTED); asynchronous on the stream.
  */
 int32_t paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                 const int32_t* context_lens, const int32_t* query_start, float scale, void* out,

@@ -11,7 +11,7 @@ import torch
 import paged_kv_cache_358_amd as pa
 import synth
 from oracle.prefill import prefill_attention_seq
-from paged_setup import PagedDecode, to_torch
+from paged_setup import PagedDecode, check_16bit_output, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +74,23 @@ def test_gqa_and_head_dims_64_and_96():
         q_np = _chunk_queries(cfg, chunks, 2)
         got, qs = _run(pd, chunks, q_np)
         _check(pd, chunks, q_np, got, qs)
+
+
+@pytest.mark.parametrize("dtype,B,hq,hkv", [("bf16", 16, 8, 2), ("f16", 8, 4, 4), ("bf16", 32, 16, 1)])
+def test_head_dim_256(dtype, B, hq, hkv):
+    # head_dim 256 runs one workgroup per CU (128 KiB of LDS stages): chunks around the 128-row
+    # workgroup tile, a chunk of several tiles at the end of a longer context, whole-sequence chunks,
+    # and 8-, 16- and 32-token blocks
+    lens = [300, 129, 1000, 17, 128]
+    chunks = [300, 129, 257, 17, 127]
+    cfg = synth.DecodeConfig("pf_d256", 53, len(lens), hq, hkv, 256, dtype, "fixed", tuple(lens), block_size=B)
+    pd = PagedDecode(cfg)
+    q_np = _chunk_queries(cfg, chunks, 4)
+    got, qs = _run(pd, chunks, q_np)
+    _check(pd, chunks, q_np, got, qs)
+    # 16-bit output: the fp32 result rounded once
+    got16, _ = _run(pd, chunks, q_np, out_dtype=pd.q.dtype)
+    check_16bit_output(got16, got, dtype)
 
 
 def test_first_position_of_a_whole_sequence_chunk_is_its_value():
