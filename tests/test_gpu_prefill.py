@@ -93,6 +93,20 @@ def test_head_dim_256(dtype, B, hq, hkv):
     check_16bit_output(got16, got, dtype)
 
 
+@pytest.mark.parametrize("B,D,hq,hkv", [(16, 64, 4, 4), (8, 128, 8, 2), (48, 96, 6, 3), (32, 256, 4, 1)])
+def test_fp32_caches(B, D, hq, hkv):
+    # fp32 caches take the VALU kernel (one wavefront per chunk row and query head): any block size,
+    # head_dim a multiple of 4 up to 256; tolerance 1e-5 as for fp32 decode.  Chunks of one row, of a
+    # whole sequence, and at the end of contexts longer than a 64-token pass.
+    lens = [1, 40, 300, 129, 70]
+    chunks = [1, 40, 37, 129, 5]
+    cfg = synth.DecodeConfig("pf_f32", 54, len(lens), hq, hkv, D, "f32", "fixed", tuple(lens), block_size=B)
+    pd = PagedDecode(cfg)
+    q_np = _chunk_queries(cfg, chunks, 5)
+    got, qs = _run(pd, chunks, q_np)
+    _check(pd, chunks, q_np, got, qs, tol=1e-5)
+
+
 def test_first_position_of_a_whole_sequence_chunk_is_its_value():
     # Position 0 sees token 0 alone, whose weight is 1: the output is V[0].  The kernel takes the
     # exponent as one fused multiply-add of the raw score against the rounded maximum, so the lone
@@ -227,10 +241,12 @@ def test_rejects_what_it_does_not_cover():
     with pytest.raises(ValueError):       # query_start must have S + 1 entries
         pa.paged_attention_prefill(q, pd.k_cache, pd.v_cache, pd.block_tables, pd.context_lens,
                                    torch.zeros(1, dtype=torch.int32, device="cuda"), 0.1, out, max_query_len=16)
-    kc, vc = pa.alloc_kv_cache(4, 2, 128, torch.float32)
-    q32 = torch.zeros(1, 2, 128, dtype=torch.float32, device="cuda")
-    with pytest.raises(pa.PagedAttnError):
-        pa.paged_attention_prefill(q32, kc, vc, torch.zeros(1, 1, dtype=torch.int32, device="cuda"),
-                                   torch.ones(1, dtype=torch.int32, device="cuda"),
-                                   torch.tensor([0, 1], dtype=torch.int32, device="cuda"), 0.1,
-                                   torch.zeros_like(q32), max_query_len=1)
+    # head sizes outside the kernels' (bf16 80; fp32 above 256): rejected on the host, nothing launched
+    for dtype, D in ((torch.bfloat16, 80), (torch.float32, 260)):
+        kc, vc = pa.alloc_kv_cache(4, 2, D, dtype)
+        qx = torch.zeros(1, 2, D, dtype=dtype, device="cuda")
+        with pytest.raises(pa.PagedAttnError):
+            pa.paged_attention_prefill(qx, kc, vc, torch.zeros(1, 1, dtype=torch.int32, device="cuda"),
+                                       torch.ones(1, dtype=torch.int32, device="cuda"),
+                                       torch.tensor([0, 1], dtype=torch.int32, device="cuda"), 0.1,
+                                       torch.zeros(qx.shape, dtype=torch.float32, device="cuda"), max_query_len=1)
