@@ -73,8 +73,8 @@ typedef struct pa_cache_desc {
   int32_t block_size;    /* tokens per block, <= 1024.  Decode takes 8 (two to a 16-token tile: partitions
                             of whole tiles) and 16 << j (16, 32, ..., 1024) on the MFMA path (bf16/fp16,
                             head_dim 64, 96 or 128, H_q / H_kv <= 32), with or without a pa_shared_prefix
-                            description; other sizes on the VALU kernel; prefill takes 8 and 16 << j
-                            (any size up to 1024 for fp32) */
+                            description; other sizes on the VALU kernel; prefill likewise (8 and 16 << j on
+                            its MFMA kernel, other sizes up to 1024 on its VALU kernel) */
   int32_t dtype;         /* pa_dtype of K and V */
 } pa_cache_desc;
 
@@ -276,9 +276,10 @@ typedef struct pa_prefill_params {
  *   query_start  [S + 1] int32, non-decreasing, query_start[0] = 0, query_start[S] = T, device
  *   out          [T][H_q][D] fp32 or the cache dtype
  * Rows whose position would be negative (a chunk longer than its context) are left unwritten.
- * bf16 / fp16 caches with head_dim 64, 96, 128 or 256 and blocks of 8 or 16 << j tokens (the MFMA kernel),
- * fp32 caches with head_dim a multiple of 4 up to 256 and blocks of up to 1024 tokens (a VALU kernel, one
- * wavefront per chunk row and query head); else PA_ERR_UNSUPPORTED.  Asynchronous on the stream.
+ * bf16 / fp16 caches with head_dim 64, 96, 128 or 256 and blocks of 8 or 16 << j tokens run the MFMA kernel;
+ * fp32 caches and the other 16-bit shapes up to head_dim 256 (a multiple of X) and blocks of up to 1024 tokens
+ * run a VALU kernel (one wavefront per chunk row and query head); else PA_ERR_UNSUPPORTED.  Asynchronous on
+ * the stream.
  */
 int32_t paged_attention_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                                 const int32_t* context_lens, const int32_t* query_start, float scale, void* out,

@@ -395,20 +395,46 @@ prefill_tiled_kernel(PrefillArgs a) {
   }
 }
 
-// fp32 caches: a VALU kernel, one wavefront per (chunk row, query head), four to a workgroup (consecutive
-// rows of one (sequence, head)).  The row's visible tokens go in passes of 64, a lane per token: the lane
-// scores its token against the row's query (K in 16-byte chunks of 4 dims), the pass updates the row's
-// online softmax (max and sum over the wave), then every lane accumulates output dims lane, lane + 64, ...
-// over the pass's tokens, each token's weight and block id broadcast from its lane.  Any head_dim that is
-// a multiple of 4 up to 256 and any block size.  A block id outside the pool leaves its tokens out.
-constexpr int kPrefillF32Waves = 4;
-constexpr int kPrefillF32MaxD = 256;
+// The VALU kernel: fp32 caches, and 16-bit caches of the shapes the MFMA kernel does not take (head_dim
+// other than 64, 96, 128, 256; blocks other than 8 and 16 << j tokens).  One wavefront per (chunk row,
+// query head), four to a workgroup (consecutive rows of one (sequence, head)).  The row's visible tokens go
+// in passes of 64, a lane per token: the lane scores its token against the row's query (K in 16-byte
+// chunks of X dims), the pass updates the row's online softmax (max and sum over the wave), then every
+// lane accumulates output dims lane, lane + 64, ... over the pass's tokens, each token's weight and block
+// id broadcast from its lane.  Any head_dim that is a multiple of X up to 256 and any block size up to
+// 1024.  A block id outside the pool leaves its tokens out.
+constexpr int kPrefillValuWaves = 4;
+constexpr int kPrefillValuMaxD = 256;
 
-__global__ __launch_bounds__(kPrefillF32Waves * kWave) void prefill_f32_kernel(PrefillArgs a, int32_t D) {
+// Dot product of 16 bytes of K and of the query (X elements each).
+template <int DT>
+__device__ __forceinline__ float dot16(const void* k, const void* q) {
+  if constexpr (DT == PA_F32) {
+    const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(k);
+    const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(q);
+    return kv[0] * qv[0] + kv[1] * qv[1] + kv[2] * qv[2] + kv[3] * qv[3];
+  } else {
+    const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(k);
+    const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(q);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc += Elem<DT>::to_float(static_cast<uint16_t>(kv[e] & 0xffffu)) *
+             Elem<DT>::to_float(static_cast<uint16_t>(qv[e] & 0xffffu));
+      acc += Elem<DT>::to_float(static_cast<uint16_t>(kv[e] >> 16)) * Elem<DT>::to_float(static_cast<uint16_t>(qv[e] >> 16));
+    }
+    return acc;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kPrefillValuWaves * kWave) void prefill_valu_kernel(PrefillArgs a, int32_t D) {
+  using T = typename Elem<DT>::storage;
+  constexpr int X = 16 / static_cast<int>(sizeof(T));  // dims per 16-byte K chunk
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rows_pad = a.tiles * kPrefillF32Waves;  // row slots per (sequence rank, query head)
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * kPrefillF32Waves + w;
+  const int rows_pad = a.tiles * kPrefillValuWaves;  // row slots per (sequence rank, query head)
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * kPrefillValuWaves + w;
   const int i = static_cast<int>(item % rows_pad);
   const int64_t sj = item / rows_pad;
   if (sj >= static_cast<int64_t>(a.num_seqs) * a.hq) return;
@@ -428,17 +454,17 @@ __global__ __launch_bounds__(kPrefillF32Waves * kWave) void prefill_f32_kernel(P
   if (i >= c || pos < 0 || row < 0 || row >= a.num_tokens) return;
   const int h = j / (a.hq / a.hkv);
 
-  const float* qrow = static_cast<const float*>(a.q) + (row * a.hq + j) * D;
-  const int64_t head_elems = static_cast<int64_t>(D) * B;  // floats of one (block, KV head) tile of K or V
-  const float* kbase = static_cast<const float*>(a.k) + h * head_elems;
-  const float* vbase = static_cast<const float*>(a.v) + h * head_elems;
+  const T* qrow = static_cast<const T*>(a.q) + (row * a.hq + j) * D;
+  const int64_t head_elems = static_cast<int64_t>(D) * B;  // elements of one (block, KV head) tile of K or V
+  const T* kbase = static_cast<const T*>(a.k) + h * head_elems;
+  const T* vbase = static_cast<const T*>(a.v) + h * head_elems;
   const int64_t blk_elems = static_cast<int64_t>(a.hkv) * head_elems;
   const int32_t* tab = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
 
   float m = -INFINITY, l = 0.f;
-  float o[kPrefillF32MaxD / kWave];
+  float o[kPrefillValuMaxD / kWave];
 #pragma unroll
-  for (int k = 0; k < kPrefillF32MaxD / kWave; ++k) o[k] = 0.f;
+  for (int k = 0; k < kPrefillValuMaxD / kWave; ++k) o[k] = 0.f;
   for (int t0 = 0; t0 <= pos; t0 += kWave) {
     const int t = t0 + lane;
     int32_t phys = -1;
@@ -447,13 +473,9 @@ __global__ __launch_bounds__(kPrefillF32Waves * kWave) void prefill_f32_kernel(P
       const int32_t id = tab[t / B];
       if (id >= 0 && id < a.num_blocks) {
         phys = id;
-        const float* kp = kbase + id * blk_elems + (t % B) * 4;
+        const T* kp = kbase + id * blk_elems + (t % B) * X;  // chunk dc at + dc * B * X
         float acc = 0.f;
-        for (int d4 = 0; d4 < D / 4; ++d4) {
-          const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(kp + static_cast<int64_t>(d4) * B * 4);
-          const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(qrow + 4 * d4);
-          acc += kv[0] * qv[0] + kv[1] * qv[1] + kv[2] * qv[2] + kv[3] * qv[3];
-        }
+        for (int dc = 0; dc < D / X; ++dc) acc += dot16<DT>(kp + static_cast<int64_t>(dc) * B * X, qrow + dc * X);
         x = acc * a.scale_log2;
       }
     }
@@ -463,27 +485,31 @@ __global__ __launch_bounds__(kPrefillF32Waves * kWave) void prefill_f32_kernel(P
     const float pw = x == -INFINITY ? 0.f : exp2f(x - m_new);
     l = l * alpha + wave_sum(pw);
 #pragma unroll
-    for (int k = 0; k < kPrefillF32MaxD / kWave; ++k) o[k] *= alpha;
+    for (int k = 0; k < kPrefillValuMaxD / kWave; ++k) o[k] *= alpha;
     m = m_new;
     const int ntok = min(kWave, pos + 1 - t0);
     for (int tt = 0; tt < ntok; ++tt) {
       const float p_t = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pw), tt));
       const int32_t ph = __builtin_amdgcn_readlane(phys, tt);
       if (ph < 0 || p_t == 0.f) continue;  // wave-uniform
-      const float* vp = vbase + ph * blk_elems + (t0 + tt) % B;
+      const T* vp = vbase + ph * blk_elems + (t0 + tt) % B;
 #pragma unroll
-      for (int k = 0; k < kPrefillF32MaxD / kWave; ++k) {
+      for (int k = 0; k < kPrefillValuMaxD / kWave; ++k) {
         const int d = lane + k * kWave;
-        if (d < D) o[k] += p_t * vp[static_cast<int64_t>(d) * B];
+        if (d < D) o[k] += p_t * Elem<DT>::to_float(vp[static_cast<int64_t>(d) * B]);
       }
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  float* orow = static_cast<float*>(a.out) + (row * a.hq + j) * D;
+  const int64_t obase = (row * a.hq + j) * D;
 #pragma unroll
-  for (int k = 0; k < kPrefillF32MaxD / kWave; ++k) {
+  for (int k = 0; k < kPrefillValuMaxD / kWave; ++k) {
     const int d = lane + k * kWave;
-    if (d < D) orow[d] = o[k] * inv;
+    if (d >= D) continue;
+    if (a.out_f32)
+      static_cast<float*>(a.out)[obase + d] = o[k] * inv;
+    else
+      static_cast<T*>(a.out)[obase + d] = static_cast<T>(Elem<DT>::from_float(o[k] * inv));
   }
 }
 
@@ -509,24 +535,23 @@ extern "C" int32_t paged_attention_prefill(const void* q, const void* k_cache, c
   if (!p) return PA_ERR_INVALID_ARG;
   const pa_cache_desc& c = p->cache;
   if (p->num_seqs < 0 || p->num_tokens < 0 || p->num_q_heads <= 0 || p->max_blocks_per_seq <= 0 ||
-      p->max_query_len < 0 || c.num_blocks <= 0 || c.num_kv_heads <= 0 || c.head_dim <= 0)
+      p->max_query_len < 0 || c.num_blocks <= 0 || c.num_kv_heads <= 0 || c.head_dim <= 0 || c.block_size <= 0)
     return PA_ERR_INVALID_ARG;
   if (p->num_q_heads % c.num_kv_heads != 0 || !valid_dtype(c.dtype)) return PA_ERR_INVALID_ARG;
   if (p->out_dtype != PA_F32 && p->out_dtype != c.dtype) return PA_ERR_INVALID_ARG;
-  const bool f32 = c.dtype == PA_F32;
+  // The MFMA kernel: bf16/fp16, head_dim 64, 96, 128 or 256, blocks of 8 or 16 << j tokens.  Everything else
+  // within head_dim <= 256 (a multiple of 16 bytes of elements) and blocks of up to 1024 tokens: the VALU kernel.
   int32_t sub_log2 = -1;  // 8-token blocks
-  if (f32) {
-    // the VALU kernel: any block size, head_dim a multiple of 4 up to 256
-    if (c.block_size <= 0 || c.block_size > 1024 || c.head_dim % 4 != 0 || c.head_dim > kPrefillF32MaxD)
-      return PA_ERR_UNSUPPORTED;
-  } else {
-    if (c.block_size != kBlockTokens / 2) {
-      sub_log2 = 0;
-      while (sub_log2 < 6 && (kBlockTokens << sub_log2) < c.block_size) ++sub_log2;
-      if ((kBlockTokens << sub_log2) != c.block_size) return PA_ERR_UNSUPPORTED;
-    }
-    if (c.head_dim != 64 && c.head_dim != 96 && c.head_dim != 128 && c.head_dim != 256) return PA_ERR_UNSUPPORTED;
+  if (c.block_size != kBlockTokens / 2) {
+    sub_log2 = 0;
+    while (sub_log2 < 6 && (kBlockTokens << sub_log2) < c.block_size) ++sub_log2;
   }
+  const bool mfma_blocks = c.block_size == kBlockTokens / 2 || (kBlockTokens << sub_log2) == c.block_size;
+  const bool mfma = c.dtype != PA_F32 && mfma_blocks &&
+                    (c.head_dim == 64 || c.head_dim == 96 || c.head_dim == 128 || c.head_dim == 256);
+  if (!mfma && (c.block_size > 1024 || c.head_dim % (16 / elem_bytes(c.dtype)) != 0 ||
+                c.head_dim > kPrefillValuMaxD))
+    return PA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(p->stream);
   hipEvent_t start = static_cast<hipEvent_t>(p->start_event), stop = static_cast<hipEvent_t>(p->stop_event);
@@ -562,13 +587,18 @@ extern "C" int32_t paged_attention_prefill(const void* q, const void* k_cache, c
   a.num_seqs = p->num_seqs;
   a.block_tokens = c.block_size;
   a.sub_log2 = sub_log2;
-  if (f32) {
+  if (!mfma) {
     // four rows of one (sequence, query head) per workgroup
-    a.tiles = (p->max_query_len + kPrefillF32Waves - 1) / kPrefillF32Waves;
+    a.tiles = (p->max_query_len + kPrefillValuWaves - 1) / kPrefillValuWaves;
     a.items = static_cast<int64_t>(p->num_seqs) * p->num_q_heads * a.tiles;
     if (a.items > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
-    hipExtLaunchKernelGGL(prefill_f32_kernel, dim3(static_cast<uint32_t>(a.items)), dim3(kPrefillF32Waves * kWave), 0,
-                          st, start, stop, 0, a, c.head_dim);
+    const dim3 vgrid(static_cast<uint32_t>(a.items)), vblock(kPrefillValuWaves * kWave);
+    if (c.dtype == PA_F32)
+      hipExtLaunchKernelGGL(prefill_valu_kernel<PA_F32>, vgrid, vblock, 0, st, start, stop, 0, a, c.head_dim);
+    else if (c.dtype == PA_BF16)
+      hipExtLaunchKernelGGL(prefill_valu_kernel<PA_BF16>, vgrid, vblock, 0, st, start, stop, 0, a, c.head_dim);
+    else
+      hipExtLaunchKernelGGL(prefill_valu_kernel<PA_F16>, vgrid, vblock, 0, st, start, stop, 0, a, c.head_dim);
     return PA_HIP_STATUS("paged_attention_prefill", hipGetLastError());
   }
   a.tiles = (p->max_query_len + kPrefillRows - 1) / kPrefillRows;

@@ -93,18 +93,24 @@ def test_head_dim_256(dtype, B, hq, hkv):
     check_16bit_output(got16, got, dtype)
 
 
-@pytest.mark.parametrize("B,D,hq,hkv", [(16, 64, 4, 4), (8, 128, 8, 2), (48, 96, 6, 3), (32, 256, 4, 1)])
-def test_fp32_caches(B, D, hq, hkv):
-    # fp32 caches take the VALU kernel (one wavefront per chunk row and query head): any block size,
-    # head_dim a multiple of 4 up to 256; tolerance 1e-5 as for fp32 decode.  Chunks of one row, of a
-    # whole sequence, and at the end of contexts longer than a 64-token pass.
+@pytest.mark.parametrize("dtype,B,D,hq,hkv", [("f32", 16, 64, 4, 4), ("f32", 8, 128, 8, 2), ("f32", 48, 96, 6, 3),
+                                              ("f32", 32, 256, 4, 1), ("bf16", 16, 80, 8, 2), ("bf16", 48, 128, 4, 4),
+                                              ("f16", 24, 160, 6, 1)])
+def test_valu_kernel_shapes(dtype, B, D, hq, hkv):
+    # fp32 caches, and 16-bit caches with head sizes or blocks the MFMA kernel does not take, run the VALU
+    # kernel (one wavefront per chunk row and query head); tolerance 1e-5 for fp32 as for fp32 decode,
+    # 5e-3 for 16-bit inputs.  Chunks of one row, of a whole sequence, and at the end of contexts longer
+    # than a 64-token pass.
     lens = [1, 40, 300, 129, 70]
     chunks = [1, 40, 37, 129, 5]
-    cfg = synth.DecodeConfig("pf_f32", 54, len(lens), hq, hkv, D, "f32", "fixed", tuple(lens), block_size=B)
+    cfg = synth.DecodeConfig("pf_valu", 54, len(lens), hq, hkv, D, dtype, "fixed", tuple(lens), block_size=B)
     pd = PagedDecode(cfg)
     q_np = _chunk_queries(cfg, chunks, 5)
     got, qs = _run(pd, chunks, q_np)
-    _check(pd, chunks, q_np, got, qs, tol=1e-5)
+    _check(pd, chunks, q_np, got, qs, tol=1e-5 if dtype == "f32" else 5e-3)
+    if dtype != "f32":  # 16-bit output: the fp32 result rounded once
+        got16, _ = _run(pd, chunks, q_np, out_dtype=pd.q.dtype)
+        check_16bit_output(got16, got, dtype)
 
 
 def test_first_position_of_a_whole_sequence_chunk_is_its_value():
@@ -241,9 +247,9 @@ def test_rejects_what_it_does_not_cover():
     with pytest.raises(ValueError):       # query_start must have S + 1 entries
         pa.paged_attention_prefill(q, pd.k_cache, pd.v_cache, pd.block_tables, pd.context_lens,
                                    torch.zeros(1, dtype=torch.int32, device="cuda"), 0.1, out, max_query_len=16)
-    # head sizes outside the kernels' (bf16 80; fp32 above 256): rejected on the host, nothing launched
-    for dtype, D in ((torch.bfloat16, 80), (torch.float32, 260)):
-        kc, vc = pa.alloc_kv_cache(4, 2, D, dtype)
+    # head sizes above 256 and blocks above 1024 tokens: rejected on the host, nothing launched
+    for dtype, D, B in ((torch.bfloat16, 264, 16), (torch.float32, 260, 16), (torch.float16, 64, 2048)):
+        kc, vc = pa.alloc_kv_cache(4, 2, D, dtype, block_size=B)
         qx = torch.zeros(1, 2, D, dtype=dtype, device="cuda")
         with pytest.raises(pa.PagedAttnError):
             pa.paged_attention_prefill(qx, kc, vc, torch.zeros(1, 1, dtype=torch.int32, device="cuda"),
