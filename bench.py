@@ -78,6 +78,10 @@ def host_threads():
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.workload == "prefill" and (args.head_dim not in (0, 64, 96, 128, 256) or
+                                       (args.block_size != 8 and (args.block_size < 16 or
+                                                                  args.block_size & (args.block_size - 1)))):
+        sys.exit("prefill bench: head_dim 64, 96, 128 or 256 and blocks of 8 or 16 << j tokens (the MFMA kernel)")
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "the paged decode path has no multi-GPU mode", file=sys.stderr)
