@@ -68,8 +68,7 @@ typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
 typedef struct pa_cache_desc {
   int64_t num_blocks;    /* physical blocks in the pool, > 0 */
   int32_t num_kv_heads;  /* H_kv, > 0 */
-  int32_t head_dim;      /* D, a multiple of X; the decode MFMA path covers 64, 96, 128 and 256 (256 one
-                            sequence at a time: a pa_shared_prefix description is not used) */
+  int32_t head_dim;      /* D, a multiple of X; the decode MFMA path covers 64, 96, 128 and 256 */
   int32_t block_size;    /* tokens per block, <= 1024.  Decode takes 8 (two to a 16-token tile: partitions
                             of whole tiles) and 16 << j (16, 32, ..., 1024) on the MFMA path (bf16/fp16,
                             head_dim 64, 96 or 128, H_q / H_kv <= 32), with or without a pa_shared_prefix
@@ -94,7 +93,7 @@ typedef struct pa_cache_desc {
  * members * (H_q / H_kv) must not exceed 32 (the query columns of two matrix-core tiles).  A description
  * that does not match the tables gives undefined results (never out-of-bounds accesses).  Used by the split
  * kernel at head_dim 64/96/128 (bf16/fp16) in batches of up to PA_MAX_GROUPED_SEQS sequences; larger
- * batches, head_dim 256 and the other kernels ignore it.  A caller with a larger batch can cut it at group
+ * batches and the other kernels ignore it.  A caller with a larger batch can cut it at group
  * boundaries into calls of at most PA_MAX_GROUPED_SEQS sequences each, with the groups' first sequences
  * counted from the call's first sequence (the Python engine does so).
  */
@@ -198,7 +197,7 @@ int32_t paged_attention_decode(const void* q, const void* k_cache, const void* v
  * paged_attention_decode_noalloc: paged_attention_decode for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments
  * and results; p->workspace and p->workspace_bytes are ignored.  The partials and arrival counters live in
- * a scratch array of paged_attention_noalloc_scratch_bytes() (64 MiB) that the library keeps on each GPU
+ * a scratch array of paged_attention_noalloc_scratch_bytes() (72 MiB) that the library keeps on each GPU
  * it runs on until the process ends.  Nothing is allocated per call (no hipMalloc, hipFree or allocating
  * library routine).  The scratch needs no clearing (the counters carry a per-call tag) and holds the last
  * call's contents.  Returns PA_ERR_WORKSPACE, launching nothing, when paged_attention_workspace_bytes(p)

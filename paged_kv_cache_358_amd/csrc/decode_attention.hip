@@ -413,8 +413,8 @@ struct Item {
 // loaded one partition ahead into the other of two slots (A/B), so no loaded value is copied
 // before it is used.  Per-block arithmetic is that of decode_mfma_kernel.
 // At least two waves per SIMD for head_dim 64 and 128: the compiler keeps the kernel within 256
-// VGPRs.  Head_dim 256 (plain mode, 4 wavefronts, 16-token blocks) runs one wave per SIMD with the
-// accumulators partly in AGPRs: twice the bytes per ring slot keep as many bytes in flight per CU.
+// VGPRs.  Head_dim 256 (4 wavefronts) runs one wave per SIMD with the accumulators partly in AGPRs:
+// twice the bytes per ring slot keep as many bytes in flight per CU.
 // Block kinds of the split kernel.  kBk16: 16-token cache blocks, one per ring position.
 // kBkMulti: cache blocks of 16 << a.sub_log2 tokens (32, 64, ...), streamed as 16-token tiles:
 // tile b of a row is tile b % SB of the row's cache block b / SB (SB = 1 << sub_log2).  kBkHalf:
@@ -1635,15 +1635,14 @@ int32_t make_plan(const pa_decode_params* p, Plan* out) {
                          0x7fffffffLL;
   out->route = split ? kRouteSplit : mfma_fits ? kRouteMfma : kRouteGeneric;
   out->sub_log2 = split ? (half_blocks ? -1 : lsb) : 0;
-  // Head_dim 256 runs sequence by sequence (its grouped form would spill), and so does a batch cut into
-  // slices (a description's groups index the whole batch).
-  out->group = split && !wide && ((p->shared && p->shared->num_groups > 0 && !big) || wide_g);
+  // A batch cut into slices runs sequence by sequence (a description's groups index the whole batch).
+  out->group = split && ((p->shared && p->shared->num_groups > 0 && !big) || wide_g);
 
   if (split) {
     // Partials per run (see DecodeArgs::part_cols); a context of one partition never spans runs.  A
     // description of shared prefixes sizes for whole groups' columns, with or without groups.
-    out->part_cols = ((p->shared && !wide) || wide_g) ? kMaxCols : g;
-    const bool partials = (p->shared && !wide) ? gparts > 1 : parts > 1;
+    out->part_cols = (p->shared || wide_g) ? kMaxCols : g;
+    const bool partials = p->shared ? gparts > 1 : parts > 1;
     const size_t slots = size_t{kMaxRuns} * 2 * out->part_cols;
     out->ml_offset = slots * D;
     out->counter_offset = slots * (size_t{static_cast<uint32_t>(D)} + 2) * sizeof(float);
@@ -1770,10 +1769,18 @@ int32_t launch_split_all(DecodeArgs* args, hipStream_t st, hipEvent_t start, hip
 template <int DT, int D>
 int32_t launch_split_blocks(DecodeArgs* args, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
   if constexpr (D == 256) {
-    // Plain mode only: the grouped form would spill.
+    // Workgroups of 4 wavefronts, one wave per SIMD.  The group mode spills about 60 VGPRs of its 512
+    // registers and still reads a shared prefix once per group: on the sampling workload at head_dim 256
+    // (MI355X) 518 us sequence by sequence against 225 us in groups.
     int cus = 0;
     const int32_t rc = device_cus(&cus);
     if (rc != PA_OK) return rc;
+    if (args->num_groups > 0) {
+      const int64_t contexts = int64_t{args->num_groups} * args->hkv;
+      if (args->sub_log2 > 0) return launch_split_waves<DT, 256, kGroup, 4, kBkMulti>(args, contexts, cus, st, start, stop);
+      if (args->sub_log2 < 0) return launch_split_waves<DT, 256, kGroup, 4, kBkHalf>(args, contexts, cus, st, start, stop);
+      return launch_split_waves<DT, 256, kGroup, 4, kBk16>(args, contexts, cus, st, start, stop);
+    }
     const int64_t contexts = int64_t{args->num_seqs} * args->hkv;
     if (args->sub_log2 > 0) return launch_split_waves<DT, 256, kPlain, 4, kBkMulti>(args, contexts, cus, st, start, stop);
     if (args->sub_log2 < 0) return launch_split_waves<DT, 256, kPlain, 4, kBkHalf>(args, contexts, cus, st, start, stop);
@@ -1874,7 +1881,7 @@ int32_t launch_decode(DecodeArgs args, const Plan& plan, hipStream_t st, hipEven
 // Scratch of paged_attention_decode_noalloc: a file-scope device array, one copy per GPU for the life of
 // the process.  Host code never passes `scratch` itself to a kernel (its host-side name is a stand-in, not
 // a device address): each device's address comes from hipGetSymbolAddress, once per device.
-constexpr size_t kScratchBytes = size_t{64} << 20;
+constexpr size_t kScratchBytes = size_t{72} << 20;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {

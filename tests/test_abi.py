@@ -251,8 +251,9 @@ def test_workspace_bytes_with_shared_prefixes():
     # 17..32 query heads per KV head: every sequence a group of its own, partial slots of 32 columns
     assert ws(ctypes.byref(_params(S=4, hq=24, hkv=1, d=64, maxb=100, maxctx=1000, part=256, dtype=pa.PA_BF16))) == \
         _split_ws(32, 64, 4)
-    # head_dim 256 runs sequence by sequence: its partials have g columns
-    assert ws(ctypes.byref(shared(S=3, hq=8, hkv=2, d=256, maxb=100, maxctx=1000))) == _split_ws(4, 256, 3 * 2)
+    # head_dim 256 in group mode: partial slots of 32 columns, within the no-alloc scratch
+    assert ws(ctypes.byref(shared(S=3, hq=8, hkv=2, d=256, maxb=100, maxctx=1000))) == _split_ws(32, 256, 3 * 2)
+    assert _split_ws(32, 256, 2048 * 8) <= pa.lib.paged_attention_noalloc_scratch_bytes()
     # more groups than sequences, a negative count, or groups without an array: rejected
     for bad in (pa.SharedPrefix(None, 5), pa.SharedPrefix(None, -1), pa.SharedPrefix(None, 1)):
         p = _params(S=4)

@@ -278,3 +278,12 @@ def test_head_dim_96():
     prompts = [(333, [40, 0, 500, 7, 16, 16, 1, 90]), (200, [1, 2])]
     fb = ForkedBatch(13, 16, 8, 96, "bf16", prompts, lone=[1])
     check(fb)
+
+
+@pytest.mark.parametrize("bs,hq,hkv,dtype", [(16, 16, 4, "bf16"), (32, 8, 8, "f16"), (8, 32, 8, "bf16")])
+def test_head_dim_256(bs, hq, hkv, dtype):
+    # head_dim 256 in group mode (one wave per SIMD, part of the state spilled): 16-, 32- and 8-token
+    # blocks, MHA and GQA, groups of up to 32 / g members
+    prompts = [(333, [40, 0, 500, 7, 16, 16, 1, 90][: 32 // (hq // hkv)]), (200, [1, 2])]
+    fb = ForkedBatch(21, hq, hkv, 256, dtype, prompts, lone=[1], block_size=bs)
+    check(fb)

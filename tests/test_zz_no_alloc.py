@@ -88,6 +88,23 @@ def test_noalloc_groups_on_8_token_blocks():
     assert _worst(got, small, range(3), [0, 9, 63]) <= tol_for(small.cfg.dtype)
 
 
+def test_noalloc_groups_at_head_dim_256():
+    # The largest partial slots a call can need (32 columns of 258 floats per slot) fit the scratch.
+    cfg = synth.scaled(synth.C3, lens=[700] * 4 + [1300, 40], head_dim=256)
+    pd = PagedDecode(cfg, keep_truth=False)
+    t = pd.tables_np.copy()
+    t[1:4, :40] = t[0, :40]                    # sequences 1..3 read sequence 0's first 40 blocks
+    pd.block_tables = torch.from_numpy(t).cuda()
+    groups = torch.tensor([[0, 4, 40], [4, 1, 0], [5, 1, 0]], dtype=torch.int32, device="cuda")
+    ref = torch.empty(pd.q.shape, dtype=torch.float32, device="cuda")
+    pa.paged_attention_decode(pd.q, pd.k_cache, pd.v_cache, pd.block_tables, pd.context_lens, cfg.softmax_scale,
+                              ref, max_context_len=pd.max_context_len, shared=groups)
+    got = _noalloc(pd, shared=groups)
+    assert torch.isfinite(got).all()
+    assert torch.equal(ref, got)
+    assert _worst(got, pd, [4, 5], [0, 63]) <= tol_for(cfg.dtype)
+
+
 def test_noalloc_rejects_what_its_scratch_cannot_hold():
     # fp32 caches with many partitions: the per-partition kernel would need more partial rows than the
     # scratch holds.  Rejected before anything is launched (the pointers below are not device memory,
